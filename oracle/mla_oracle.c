@@ -1,0 +1,334 @@
+/*
+ * Plain fp64 CPU oracle for absorbed-MQA paged MLA decode.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the bench's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the GPU path, and the GPU path never calls it.
+ *
+ * What is computed (one request b, one query head h), following the pages:
+ *  - "Benchmarking MLA" (flashinfer issue 700), the comments on the
+ *    matrix-absorbed form: the score contraction runs over
+ *    (kpe-dim + ckv-dim) = 64 + 512, the value head dim is 512 and the ckv
+ *    cache serves as both key and value; the query heads all share one latent
+ *    KV stream (MQA with a group size of up to 128).
+ *  - same page, nvbench byte accounting: the inputs are q_nope, q_pe, ckv,
+ *    kpe, kv_indptr, kv_indices and kv_last_page_len; the output is o.
+ *  - FlashMLA PR 233, "What is added": paged caches with page sizes 16/32/64,
+ *    and an 8-bit cache (FP8 e4m3 or INT8) with one scale per token that is
+ *    dequantised before use.
+ *
+ *   n_b  = kv_indptr[b+1] - kv_indptr[b]                       (pages)
+ *   L_b  = 0 if n_b == 0 else (n_b - 1) * P + kv_last_page_len[b]
+ *   token t < L_b lives in page kv_indices[kv_indptr[b] + t / P], slot t % P
+ *   K_t  = dec(ckv[page, slot, :]) * sigma_t   (512 values)
+ *   R_t  = dec(kpe[page, slot, :]) * sigma_t   (64 values)
+ *          sigma_t = kv_scale[page, slot] for 8-bit caches, 1 for bf16
+ *   s_t  = sm_scale * (q_nope[b,h,:] . K_t + q_pe[b,h,:] . R_t)
+ *   m    = max_t s_t,  Z = sum_t exp(s_t - m)
+ *   LSE  = m + ln Z                     (natural log of the scaled scores)
+ *   O    = sum_t (exp(s_t - m) / Z) * K_t   (512 values)
+ *   An empty request (L_b = 0) gives O = 0 and LSE = -inf.
+ *
+ * The softmax is taken in two plain passes (max first, then sums), in logical
+ * token order, in fp64, with no online rescaling, no blocking and no
+ * reordering.  The split-KV merge (one partial (O_i, LSE_i) per token chunk,
+ * merged with weights exp(LSE_i - LSE)) is a separate function, used only to
+ * check that merging partials reproduces the unsplit result.
+ *
+ * Decoders (written from the format definitions, not from any library):
+ *   bf16      : the upper 16 bits of an IEEE binary32.
+ *   e4m3fn    : OCP 8-bit float, 1 sign, 4 exponent (bias 7), 3 mantissa bits;
+ *               exponent 0 is subnormal (m/8 * 2^-6); S.1111.111 is NaN; there
+ *               is no infinity; the largest finite value is 448.
+ *   int8      : two's complement.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define D_CKV 512
+#define D_KPE 64
+
+enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1, ORC_INT8 = 2 };
+
+double oracle_dec_bf16(uint16_t bits) {
+  uint32_t w = ((uint32_t)bits) << 16;
+  float f;
+  memcpy(&f, &w, sizeof f);
+  return (double)f;
+}
+
+double oracle_dec_e4m3fn(uint8_t code) {
+  int sign = (code >> 7) & 1;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    v = ldexp((double)m / 8.0, -6);
+  else
+    v = ldexp(1.0 + (double)m / 8.0, e - 7);
+  return sign ? -v : v;
+}
+
+double oracle_dec_int8(uint8_t code) { return (double)(int8_t)code; }
+
+/* Number of tokens of request b. */
+int64_t oracle_kv_len(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t page_size,
+                      int32_t b) {
+  int64_t n = (int64_t)kv_indptr[b + 1] - (int64_t)kv_indptr[b];
+  if (n <= 0) return 0;
+  return (n - 1) * (int64_t)page_size + (int64_t)kv_last_page_len[b];
+}
+
+typedef struct {
+  int32_t batch, num_heads, page_size, kv_dtype;
+  const uint16_t* q_nope; /* bf16 bits [B, H, 512] */
+  const uint16_t* q_pe;   /* bf16 bits [B, H, 64] */
+  const void* ckv;        /* [pages, P, 512] bf16 bits or 8-bit codes */
+  const void* kpe;        /* [pages, P, 64]  bf16 bits or 8-bit codes */
+  const float* kv_scale;  /* [pages, P] or NULL for bf16 */
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_last_page_len;
+  double sm_scale;
+} oracle_inputs;
+
+/* Decoded latent row of logical token t of request b: K (512) and R (64). */
+static void load_token(const oracle_inputs* in, int32_t b, int64_t t, double* K, double* R) {
+  int64_t P = in->page_size;
+  int64_t page = in->kv_indices[(int64_t)in->kv_indptr[b] + t / P];
+  int64_t slot = t % P;
+  int64_t row = page * P + slot;
+  double sigma = 1.0;
+  int i;
+  if (in->kv_dtype == ORC_BF16) {
+    const uint16_t* c = (const uint16_t*)in->ckv + row * D_CKV;
+    const uint16_t* k = (const uint16_t*)in->kpe + row * D_KPE;
+    for (i = 0; i < D_CKV; ++i) K[i] = oracle_dec_bf16(c[i]);
+    for (i = 0; i < D_KPE; ++i) R[i] = oracle_dec_bf16(k[i]);
+    return;
+  }
+  sigma = (double)in->kv_scale[row];
+  {
+    const uint8_t* c = (const uint8_t*)in->ckv + row * D_CKV;
+    const uint8_t* k = (const uint8_t*)in->kpe + row * D_KPE;
+    for (i = 0; i < D_CKV; ++i)
+      K[i] = (in->kv_dtype == ORC_FP8_E4M3 ? oracle_dec_e4m3fn(c[i]) : oracle_dec_int8(c[i])) * sigma;
+    for (i = 0; i < D_KPE; ++i)
+      R[i] = (in->kv_dtype == ORC_FP8_E4M3 ? oracle_dec_e4m3fn(k[i]) : oracle_dec_int8(k[i])) * sigma;
+  }
+}
+
+/*
+ * Attention of head h of request b over the logical token range [t0, t1)
+ * (t1 <= L_b).  Writes the normalised output (512) and the log-sum-exp.
+ * An empty range gives O = 0, LSE = -inf.  Returns 0, or -1 on allocation
+ * failure.
+ */
+static int attend_range(const oracle_inputs* in, int32_t b, int32_t h, int64_t t0, int64_t t1,
+                        double* o, double* lse) {
+  const uint16_t* qn = in->q_nope + ((int64_t)b * in->num_heads + h) * D_CKV;
+  const uint16_t* qp = in->q_pe + ((int64_t)b * in->num_heads + h) * D_KPE;
+  double q[D_CKV + D_KPE];
+  double K[D_CKV], R[D_KPE];
+  int64_t n = t1 - t0, t;
+  double* s;
+  double m, Z;
+  int i;
+
+  for (i = 0; i < D_CKV; ++i) o[i] = 0.0;
+  if (n <= 0) {
+    *lse = -INFINITY;
+    return 0;
+  }
+  for (i = 0; i < D_CKV; ++i) q[i] = oracle_dec_bf16(qn[i]);
+  for (i = 0; i < D_KPE; ++i) q[D_CKV + i] = oracle_dec_bf16(qp[i]);
+
+  s = (double*)malloc((size_t)n * sizeof(double));
+  if (!s) return -1;
+
+  /* pass 1: scores */
+  for (t = 0; t < n; ++t) {
+    double dot = 0.0;
+    load_token(in, b, t0 + t, K, R);
+    for (i = 0; i < D_CKV; ++i) dot += q[i] * K[i];
+    for (i = 0; i < D_KPE; ++i) dot += q[D_CKV + i] * R[i];
+    s[t] = in->sm_scale * dot;
+  }
+  /* max, normaliser, log-sum-exp */
+  m = s[0];
+  for (t = 1; t < n; ++t)
+    if (s[t] > m) m = s[t];
+  Z = 0.0;
+  for (t = 0; t < n; ++t) Z += exp(s[t] - m);
+  *lse = m + log(Z);
+  /* pass 2: probability-weighted sum of the ckv rows */
+  for (t = 0; t < n; ++t) {
+    double p = exp(s[t] - m) / Z;
+    load_token(in, b, t0 + t, K, R);
+    for (i = 0; i < D_CKV; ++i) o[i] += p * K[i];
+  }
+  free(s);
+  return 0;
+}
+
+typedef struct {
+  const oracle_inputs* in;
+  const int32_t* rows; /* flattened b*H + h, or NULL for all */
+  int64_t n_rows;
+  double* o;
+  double* lse;
+  int64_t begin, end;
+  int status;
+} worker_arg;
+
+static void* worker(void* p) {
+  worker_arg* w = (worker_arg*)p;
+  int64_t r;
+  for (r = w->begin; r < w->end; ++r) {
+    int64_t flat = w->rows ? (int64_t)w->rows[r] : r;
+    int32_t b = (int32_t)(flat / w->in->num_heads);
+    int32_t h = (int32_t)(flat % w->in->num_heads);
+    int64_t L = oracle_kv_len(w->in->kv_indptr, w->in->kv_last_page_len, w->in->page_size, b);
+    if (attend_range(w->in, b, h, 0, L, w->o + r * D_CKV, w->lse + r) != 0) w->status = -1;
+  }
+  return NULL;
+}
+
+/*
+ * Full decode (or a selected list of (b, h) rows).
+ *   rows == NULL: all B*H rows; o_out is [B*H, 512], lse_out [B*H].
+ *   rows != NULL: n_rows entries of b*H + h; o_out is [n_rows, 512].
+ * Rows are distributed over num_threads threads in contiguous blocks; each
+ * row's arithmetic is independent of the thread count.
+ * Returns 0 on success, -1 on bad arguments or allocation failure.
+ */
+int mla_oracle_decode(int32_t batch, int32_t num_heads, int32_t page_size, int32_t kv_dtype,
+                      const uint16_t* q_nope, const uint16_t* q_pe, const void* ckv, const void* kpe,
+                      const float* kv_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
+                      const int32_t* kv_last_page_len, double sm_scale, const int32_t* rows,
+                      int64_t n_rows, double* o_out, double* lse_out, int32_t num_threads) {
+  oracle_inputs in;
+  int64_t total, per, i;
+  pthread_t* th;
+  worker_arg* args;
+  int status = 0;
+
+  if (batch < 0 || num_heads <= 0 || page_size <= 0 || !o_out || !lse_out) return -1;
+  if (kv_dtype != ORC_BF16 && kv_dtype != ORC_FP8_E4M3 && kv_dtype != ORC_INT8) return -1;
+  if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
+  in.batch = batch;
+  in.num_heads = num_heads;
+  in.page_size = page_size;
+  in.kv_dtype = kv_dtype;
+  in.q_nope = q_nope;
+  in.q_pe = q_pe;
+  in.ckv = ckv;
+  in.kpe = kpe;
+  in.kv_scale = kv_scale;
+  in.kv_indptr = kv_indptr;
+  in.kv_indices = kv_indices;
+  in.kv_last_page_len = kv_last_page_len;
+  in.sm_scale = sm_scale;
+
+  total = rows ? n_rows : (int64_t)batch * num_heads;
+  if (total == 0) return 0;
+  if (num_threads < 1) num_threads = 1;
+  if (num_threads > total) num_threads = (int32_t)total;
+  th = (pthread_t*)calloc((size_t)num_threads, sizeof(pthread_t));
+  args = (worker_arg*)calloc((size_t)num_threads, sizeof(worker_arg));
+  if (!th || !args) {
+    free(th);
+    free(args);
+    return -1;
+  }
+  per = (total + num_threads - 1) / num_threads;
+  for (i = 0; i < num_threads; ++i) {
+    args[i].in = &in;
+    args[i].rows = rows;
+    args[i].n_rows = n_rows;
+    args[i].o = o_out;
+    args[i].lse = lse_out;
+    args[i].begin = i * per < total ? i * per : total;
+    args[i].end = (i + 1) * per < total ? (i + 1) * per : total;
+    args[i].status = 0;
+    if (num_threads == 1) {
+      worker(&args[i]);
+    } else if (pthread_create(&th[i], NULL, worker, &args[i]) != 0) {
+      args[i].status = -1;
+      th[i] = 0;
+    }
+  }
+  if (num_threads > 1)
+    for (i = 0; i < num_threads; ++i)
+      if (th[i]) pthread_join(th[i], NULL);
+  for (i = 0; i < num_threads; ++i)
+    if (args[i].status != 0) status = -1;
+  free(th);
+  free(args);
+  return status;
+}
+
+/*
+ * Attention of one (b, h) over the logical token range [t0, t1) only, giving
+ * the partial (O_i, LSE_i) of a split-KV chunk.  Returns -1 if the range is
+ * outside [0, L_b].
+ */
+int mla_oracle_partial(int32_t batch, int32_t num_heads, int32_t page_size, int32_t kv_dtype,
+                       const uint16_t* q_nope, const uint16_t* q_pe, const void* ckv, const void* kpe,
+                       const float* kv_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
+                       const int32_t* kv_last_page_len, double sm_scale, int32_t b, int32_t h,
+                       int64_t t0, int64_t t1, double* o_out, double* lse_out) {
+  oracle_inputs in;
+  int64_t L;
+  if (b < 0 || b >= batch || h < 0 || h >= num_heads) return -1;
+  if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
+  L = oracle_kv_len(kv_indptr, kv_last_page_len, page_size, b);
+  if (t0 < 0 || t1 < t0 || t1 > L) return -1;
+  in.batch = batch;
+  in.num_heads = num_heads;
+  in.page_size = page_size;
+  in.kv_dtype = kv_dtype;
+  in.q_nope = q_nope;
+  in.q_pe = q_pe;
+  in.ckv = ckv;
+  in.kpe = kpe;
+  in.kv_scale = kv_scale;
+  in.kv_indptr = kv_indptr;
+  in.kv_indices = kv_indices;
+  in.kv_last_page_len = kv_last_page_len;
+  in.sm_scale = sm_scale;
+  return attend_range(&in, b, h, t0, t1, o_out, lse_out);
+}
+
+/*
+ * Merge of n split-KV partials of one (b, h), in the fixed order i = 0..n-1
+ * (FlashMLA PR 233, "What is added": split work with a deterministic
+ * combine).  With M = max_i LSE_i:
+ *   LSE = M + ln sum_i exp(LSE_i - M),   O = sum_i exp(LSE_i - LSE) * O_i.
+ * Partials with LSE_i = -inf (empty chunks) carry zero weight; if every
+ * partial is empty the result is O = 0, LSE = -inf.
+ */
+void mla_oracle_combine(int32_t n, const double* lse_parts, const double* o_parts, double* o_out,
+                        double* lse_out) {
+  double M = -INFINITY, sum = 0.0, lse;
+  int32_t i;
+  int j;
+  for (j = 0; j < D_CKV; ++j) o_out[j] = 0.0;
+  for (i = 0; i < n; ++i)
+    if (lse_parts[i] > M) M = lse_parts[i];
+  if (n == 0 || M == -INFINITY) {
+    *lse_out = -INFINITY;
+    return;
+  }
+  for (i = 0; i < n; ++i) sum += exp(lse_parts[i] - M);
+  lse = M + log(sum);
+  for (i = 0; i < n; ++i) {
+    double w = exp(lse_parts[i] - lse);
+    for (j = 0; j < D_CKV; ++j) o_out[j] += w * o_parts[(int64_t)i * D_CKV + j];
+  }
+  *lse_out = lse;
+}
