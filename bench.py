@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of paged MLA decode (absorbed-MQA form) on one MI355X.
+
+One step = one pass of the whole hot path over one batch: the decode kernel
+(page gather -> LDS ring -> QK MFMA -> online softmax -> PV MFMA -> epilogue)
+and the split combine, i.e. one mla_decode_run.  The schedule (mla_decode_plan,
+host side) is built once per batch before the timed region, as a serving loop
+reuses it for every layer of a decode step; its host time is reported
+separately as plan_ms.
+
+Primary line: the memory-bound h_q = 16 workload (batch 64, kv_len 4096,
+page 64, bf16) in HBM GB/s of algorithmic bytes (every input and output once).
+"secondary" holds the h_q = 128 workload in bf16 TFLOP/s.  Inputs are seeded
+synthetic N(0,1) data resident in HBM; consecutive steps alternate between
+`--copies` separate copies of the inputs, so that a step cannot reuse what the
+previous one left in the 256 MB Infinity Cache.
+
+`roofline.achieved` divides the algorithmic bytes (or flops) of one launch by
+the decode kernel's own average duration, measured with HIP events recorded
+around that kernel on its stream by the library over the timed steps.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode: HBM GB/s at h_q=16, bf16 TFLOPS at h_q=128, % of roofline"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", "kernels.hip")
+
+
+class Hip:
+    """The few HIP event calls the bench needs (the runtime torch already loaded)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def kernel_sha() -> str:
+    h = hashlib.sha256()
+    for name in ("kernels.hip", "kernels.h", "api.cpp", "planner.cpp"):
+        with open(os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def device_inputs(inp, copies: int):
+    import numpy as np
+    import torch
+    d = "cuda"
+
+    def bf(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(d)
+
+    def i32(a):
+        return torch.from_numpy(a).to(d)
+
+    sets = []
+    base = dict(q_nope=bf(inp.q_nope), q_pe=bf(inp.q_pe), ckv=bf(inp.ckv), kpe=bf(inp.kpe),
+                kv_indptr=i32(inp.kv_indptr), kv_indices=i32(inp.kv_indices),
+                kv_last_page_len=i32(inp.kv_last_page_len))
+    sets.append(base)
+    for _ in range(copies - 1):
+        sets.append({k: v.clone() for k, v in base.items()})
+    return sets
+
+
+def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip) -> dict:
+    import torch
+    import mla_paged_kv_decode_amd as mla
+    from mla_paged_kv_decode_amd import synth
+
+    inp = synth.make_workload(name)
+    sets = device_inputs(inp, copies)
+    B, H = inp.batch, inp.num_heads
+    ws = torch.empty(mla.workspace_bytes(B, H), dtype=torch.uint8, device="cuda")
+    t0 = time.perf_counter()
+    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, inp.page_size, inp.kv_dtype, ws)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    outs = [(torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((B, H), dtype=torch.float32, device="cuda")) for _ in range(copies)]
+
+    def step(i):
+        s = sets[i % copies]
+        o, lse = outs[i % copies]
+        plan.run(s["q_nope"], s["q_pe"], s["ckv"], s["kpe"], None, s["kv_indptr"],
+                 s["kv_indices"], s["kv_last_page_len"], inp.sm_scale, o, lse)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    before = [hip.event() for _ in range(steps)]
+    after = [hip.event() for _ in range(steps)]
+    start, stop = hip.event(), hip.event()
+    stream = torch.cuda.current_stream().cuda_stream
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    hip.lib.hipEventRecord(start, ctypes.c_void_p(stream))
+    for i in range(steps):
+        plan.set_events(before[i], after[i])
+        step(i)
+    hip.lib.hipEventRecord(stop, ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    plan.set_events(None, None)
+    total_ms = hip.elapsed_ms(start, stop)
+    kern = [hip.elapsed_ms(before[i], after[i]) for i in range(steps)]
+    for e in before + after + [start, stop]:
+        hip.destroy(e)
+    info = plan.info()
+    return dict(name=name, inp=inp, bytes=inp.algorithmic_bytes(), flops=inp.flops(),
+                ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
+                kernel_ms=sum(kern) / len(kern), kernel_ms_min=min(kern), plan_ms=plan_ms,
+                plan=info)
+
+
+def cpu_baseline(inp, target_s: float) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload:
+    the first n (request, head) rows, doubling n until the run takes at least
+    target_s seconds or covers the workload; scaled to GB/s of algorithmic bytes
+    of the rows done."""
+    import numpy as np
+    import oracle
+    threads = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit():
+        threads = min(threads, int(env))
+    total_rows = inp.batch * inp.num_heads
+    n = min(total_rows, max(threads, 16))
+    while True:
+        rows = np.arange(n, dtype=np.int32)
+        t0 = time.perf_counter()
+        oracle.decode(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.kv_indptr, inp.kv_indices,
+                      inp.kv_last_page_len, inp.sm_scale, inp.page_size, inp.kv_dtype,
+                      inp.kv_scale, rows=rows, threads=threads)
+        dt = time.perf_counter() - t0
+        if dt >= target_s or n >= total_rows:
+            break
+        n = min(total_rows, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
+    frac = n / total_rows
+    return {"value": round(inp.algorithmic_bytes() * frac / dt / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "first %d of %d (request, head) rows of the same workload, fp64 C oracle, "
+                      "%.2f s" % (n, total_rows, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mem_b64_h16_l4096_p64")
+    ap.add_argument("--secondary", default="compute_b64_h128_l4096_p64",
+                    help="second workload reported under 'secondary' ('none' to skip)")
+    ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the decode path is built and measured on a "
+              "single MI355X (requests shard across GPUs with no exchange); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    import mla_paged_kv_decode_amd as mla
+    mla.load_library()
+    hip = Hip()
+
+    prim = measure(args.workload, args.steps, args.warmup, args.copies, hip)
+    inp = prim["inp"]
+    gbs = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
+    kern_gbs = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
+    traffic = measured_traffic(args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": inp.batch, "h_q": inp.num_heads,
+                   "kv_len": int(inp.lengths[0]), "page_size": inp.page_size,
+                   "kv_dtype": "bf16", "d_ckv": 512, "d_kpe": 64,
+                   "algorithmic_bytes": prim["bytes"], "flops": prim["flops"],
+                   "input_copies": args.copies, "plan": prim["plan"]},
+        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "mla_decode_bf16_kernel",
+                     "kernel_ms": round(prim["kernel_ms"], 5)},
+        "plan_ms": round(prim["plan_ms"], 4),
+        "wall_ms_per_step": round(prim["wall_ms_per_step"], 5),
+    }
+    if args.secondary != "none":
+        sec = measure(args.secondary, args.steps, args.warmup, args.copies, hip)
+        tfs = sec["flops"] / (sec["ms_per_step"] * 1e-3) / 1e12
+        ktfs = sec["flops"] / (sec["kernel_ms"] * 1e-3) / 1e12
+        out["secondary"] = {
+            "workload": args.secondary, "value": round(tfs, 2), "unit": "TFLOP/s",
+            "ms_per_step": round(sec["ms_per_step"], 5),
+            "hbm_gbs": round(sec["bytes"] / (sec["ms_per_step"] * 1e-3) / 1e9, 2),
+            "roofline": {"bound": "mfma", "achieved": round(ktfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(ktfs / MFMA_BF16_PEAK_TFS, 4),
+                         "hbm_frac": round(sec["bytes"] / (sec["kernel_ms"] * 1e-3) / 1e9
+                                           / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic(args.secondary),
+                         "kernel_ms": round(sec["kernel_ms"], 5)},
+        }
+        del sec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,168 @@
+/*
+ * mla_decode.h - C ABI of the MI355X (gfx950) paged MLA decode library.
+ *
+ * The operation (absorbed-MQA multi-head latent attention decode):
+ *   For request b with H query heads and kv_len L_b latent tokens, gathered
+ *   through a paged cache,
+ *     s[h,t]   = sm_scale * (q_nope[b,h,:] . ckv_t + q_pe[b,h,:] . kpe_t)
+ *     o[b,h,:] = sum_t softmax_t(s[h,:]) * ckv_t              (512 values)
+ *     lse[b,h] = ln sum_t exp(s[h,t])
+ *   Sources:
+ *   - "Benchmarking MLA" (flashinfer issue 700), comments on the
+ *     matrix-absorbed decode: score dims 512 (ckv) + 64 (kpe), value dims 512,
+ *     the ckv cache doubles as key and value, and all query heads share one
+ *     latent stream (MQA, group size up to 128).  The same page lists the
+ *     operands of a decode call: q_nope, q_pe, ckv, kpe, kv_indptr,
+ *     kv_indices, kv_last_page_len, and the output o.
+ *   - "perf: MLA decode kernel implemented by CuTe targeted to SM80"
+ *     (flashinfer PR 844): the tensor shapes q_nope [B*qo_len, H, 512],
+ *     q_pe [B*qo_len, H, 64], ckv [pages, P, 512], kpe [pages, P, 64].
+ *   - FlashMLA PR 233, "What is added": page sizes 16/32/64, an 8-bit cache
+ *     (FP8 e4m3 or INT8) with one scale per token dequantised in the kernel,
+ *     a balanced split scheduler with a deterministic combine, and an API
+ *     whose scheduling metadata is computed before graph capture.
+ *   lse is this library's addition: the natural-log log-sum-exp of the same
+ *   scaled scores that enter the softmax, so that callers can merge results.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are caller-owned, contiguous and row-major.  "device"
+ *     pointers are HIP device allocations on the current device; "host"
+ *     pointers are ordinary CPU memory.
+ *   - Functions return an mla_status and never throw or abort; a HIP failure
+ *     is reported as MLA_ERR_HIP and the text of the last error is available
+ *     from mla_last_error().
+ *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *   - qo_len is 1 (decode): q_nope is [batch, H, 512].
+ */
+#ifndef MLA_DECODE_H
+#define MLA_DECODE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,          /* null pointer, bad size, malformed page table */
+  MLA_ERR_UNSUPPORTED = -2,          /* head count / page size / dtype not built */
+  MLA_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes below what the plan needs */
+  MLA_ERR_HIP = -4,                  /* a HIP runtime call failed */
+  MLA_ERR_NOT_UPLOADED = -5          /* run() on a plan made without a workspace */
+} mla_status;
+
+typedef enum {
+  MLA_KV_BF16 = 0,      /* ckv/kpe are bf16; kv_scale must be NULL */
+  MLA_KV_FP8_E4M3 = 1,  /* ckv/kpe are OCP fp8 e4m3 codes; kv_scale [pages, P] fp32 */
+  MLA_KV_INT8 = 2       /* ckv/kpe are int8 codes; kv_scale [pages, P] fp32 */
+} mla_kv_dtype;
+
+/* Scheduling options; zero-initialise for defaults. */
+typedef struct {
+  int32_t num_cus;      /* compute units to balance over; 0 = query the current device */
+  int32_t force_splits; /* > 0: cut every request into this many near-equal chunks (testing) */
+  int32_t max_workers;  /* > 0: cap on the number of workgroups; 0 = library default */
+  int32_t reserved;
+} mla_plan_opts;
+
+typedef struct mla_plan_s* mla_plan_t;
+
+/* Supported shapes: num_heads in {16, 32, 64, 128}; page_size in {16, 32, 64}. */
+
+/*
+ * Upper bound, in bytes, of the device workspace that mla_decode_plan needs
+ * for any page table of `batch` requests with these heads and options.
+ * Returns 0 for unsupported or invalid arguments (or, when opts->num_cus is
+ * 0, if no HIP device can be queried).
+ */
+size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_plan_opts* opts);
+
+/*
+ * Build the split-KV schedule for one batch (the balanced scheduler; runs on
+ * the host, launches no kernel).
+ *   kv_indptr_host        [batch + 1] int32, host: page-list offsets, non-decreasing, from 0.
+ *   kv_last_page_len_host [batch] int32, host: valid slots of each request's last page,
+ *                          in [1, page_size] when the request has pages (ignored otherwise).
+ *   Request b holds L_b = (n_b - 1) * page_size + kv_last_page_len[b] tokens,
+ *   n_b = kv_indptr[b+1] - kv_indptr[b]; a request without pages is empty
+ *   (its output row is o = 0, lse = -inf).
+ *   workspace             device buffer of workspace_bytes, caller-owned.  The plan
+ *                          copies its work list there with hipMemcpyAsync on `stream`;
+ *                          the workspace must stay allocated, and must not be used by
+ *                          another plan, while runs of this plan may execute.
+ *                          workspace == NULL makes a host-only plan that can be
+ *                          inspected but not run.
+ *   *out receives a new plan owned by the caller (free with mla_decode_plan_destroy).
+ * Errors: MLA_ERR_INVALID_ARG for a malformed page table or null pointers,
+ * MLA_ERR_UNSUPPORTED for shapes outside the supported set,
+ * MLA_ERR_WORKSPACE_TOO_SMALL, MLA_ERR_HIP.
+ */
+mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
+                           const int32_t* kv_last_page_len_host, int32_t batch, int32_t num_heads,
+                           int32_t page_size, mla_kv_dtype kv_dtype, const mla_plan_opts* opts,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Run the decode for a plan: the decode kernel and, if any request was split,
+ * the combine kernel, both on `stream`.  Allocates nothing, never
+ * synchronises and never reads device memory from the host, so it may be
+ * captured in a HIP graph and replayed while the page-table lengths are
+ * unchanged.
+ *   q_nope  device bf16 [batch, H, 512]      q_pe device bf16 [batch, H, 64]
+ *   ckv     device [pages, P, 512]           kpe  device [pages, P, 64]
+ *           (bf16, or 8-bit codes per the plan's kv_dtype)
+ *   kv_scale device fp32 [pages, P] for 8-bit caches, NULL for bf16
+ *   kv_indptr [batch+1], kv_indices [n], kv_last_page_len [batch]: device int32
+ *           copies of the page table the plan was made from.  The kernel never
+ *           reads past a request's device-side length; kv_indices entries must
+ *           be valid page numbers (not checked on the device).
+ *   sm_scale softmax scale applied to the whole 576-wide score
+ *   o       device bf16 [batch, H, 512] (written)
+ *   lse     device fp32 [batch, H] (written)
+ * Results are bit-identical across runs of the same plan and inputs.
+ * Errors: MLA_ERR_INVALID_ARG (null pointers, kv_scale inconsistent with the
+ * dtype), MLA_ERR_NOT_UPLOADED, MLA_ERR_HIP (launch failure).
+ */
+mla_status mla_decode_run(mla_plan_t plan, const void* q_nope, const void* q_pe, const void* ckv,
+                          const void* kpe, const float* kv_scale, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                          float sm_scale, void* o, float* lse, void* stream);
+
+/*
+ * Optional instrumentation for measuring the decode kernel on its own: when
+ * set, mla_decode_run records `before` on its stream right before the decode
+ * kernel and `after` right after it (hipEvent_t values passed as void*; the
+ * caller owns them).  Passing NULL for both turns it off.  Host-only call.
+ */
+mla_status mla_decode_plan_set_events(mla_plan_t plan, void* before, void* after);
+
+/* Free a plan (host memory only; the workspace stays the caller's). NULL is a no-op. */
+void mla_decode_plan_destroy(mla_plan_t plan);
+
+/* Static description of a status code. */
+const char* mla_status_string(mla_status status);
+
+/* Text of the last HIP error seen by this library on the calling thread ("" if none). */
+const char* mla_last_error(void);
+
+/*
+ * Plan inspection (for tests and tools).
+ *   info[0] batch, [1] num_heads, [2] page_size, [3] kv_dtype, [4] num_workers
+ *   (grid size), [5] num_segments, [6] num_partials (split partial slots),
+ *   [7] num_split_requests, [8] split granularity in tokens, [9] waves per
+ *   workgroup.
+ * mla_decode_plan_segments copies the work list: seg[4*i..4*i+3] =
+ * {request, token_begin, token_end, partial_slot (-1 = writes o/lse directly)}
+ * for i < num_segments, and worker_ptr[w], worker_ptr[w+1] delimit the
+ * segments of workgroup w (worker_ptr has num_workers + 1 entries).
+ */
+mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[10]);
+mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* worker_ptr);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_DECODE_H */

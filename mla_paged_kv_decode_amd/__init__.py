@@ -1,0 +1,238 @@
+"""Paged MLA decode (absorbed-MQA form) for MI355X / gfx950.
+
+Thin ctypes binding over the C ABI in ``include/mla_decode.h``
+(``libmla_decode.so``, built in-tree by ``mla_paged_kv_decode_amd.build``).
+This module only marshals arguments: every step of the decode runs in the HIP
+kernels of the library.  PyTorch supplies device memory and streams.  There is
+no CPU fallback: if the library is missing, every call raises.
+
+Names follow the pages' notation: q_nope [B, H, 512], q_pe [B, H, 64],
+ckv [pages, P, 512], kpe [pages, P, 64], kv_indptr / kv_indices /
+kv_last_page_len (the paged KV table), sm_scale, o [B, H, 512] and lse [B, H].
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
+
+MLA_OK = 0
+KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
+D_CKV, D_KPE = 512, 64
+
+EXPORTED_SYMBOLS = (
+    "mla_decode_workspace_bytes",
+    "mla_decode_plan",
+    "mla_decode_run",
+    "mla_decode_plan_destroy",
+    "mla_status_string",
+    "mla_last_error",
+    "mla_decode_plan_info",
+    "mla_decode_plan_segments",
+    "mla_decode_plan_set_events",
+)
+
+_lib = None
+
+
+class MlaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = load_library()
+        msg = lib.mla_status_string(status).decode()
+        detail = lib.mla_last_error().decode()
+        super().__init__("%s: %s (status %d)%s" % (what, msg, status,
+                                                   (" - " + detail) if detail else ""))
+        self.status = status
+
+
+class PlanOpts(ctypes.Structure):
+    _fields_ = [("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
+                ("max_workers", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def load_library(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libmla_decode.so is not built (%s); run "
+                           "`python -m mla_paged_kv_decode_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.mla_decode_workspace_bytes.argtypes = [i32, i32, ctypes.POINTER(PlanOpts)]
+    lib.mla_decode_workspace_bytes.restype = sz
+    lib.mla_decode_plan.argtypes = [ctypes.POINTER(P), P, P, i32, i32, i32, i32,
+                                    ctypes.POINTER(PlanOpts), P, sz, P]
+    lib.mla_decode_plan.restype = ctypes.c_int
+    lib.mla_decode_run.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P]
+    lib.mla_decode_run.restype = ctypes.c_int
+    lib.mla_decode_plan_destroy.argtypes = [P]
+    lib.mla_decode_plan_destroy.restype = None
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_last_error.argtypes = []
+    lib.mla_last_error.restype = ctypes.c_char_p
+    lib.mla_decode_plan_info.argtypes = [P, P]
+    lib.mla_decode_plan_info.restype = ctypes.c_int
+    lib.mla_decode_plan_segments.argtypes = [P, P, P]
+    lib.mla_decode_plan_segments.restype = ctypes.c_int
+    lib.mla_decode_plan_set_events.argtypes = [P, P, P]
+    lib.mla_decode_plan_set_events.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _opts(num_cus=0, force_splits=0, max_workers=0) -> PlanOpts:
+    return PlanOpts(int(num_cus), int(force_splits), int(max_workers), 0)
+
+
+def _host_i32(x) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def _dptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def workspace_bytes(batch: int, num_heads: int, num_cus: int = 0, force_splits: int = 0,
+                    max_workers: int = 0) -> int:
+    o = _opts(num_cus, force_splits, max_workers)
+    n = load_library().mla_decode_workspace_bytes(int(batch), int(num_heads), ctypes.byref(o))
+    if n == 0:
+        raise MlaError(-2, "mla_decode_workspace_bytes")
+    return int(n)
+
+
+class Plan:
+    """A split-KV schedule for one batch (``mla_decode_plan``).
+
+    ``workspace`` is a device uint8 tensor of at least ``workspace_bytes``;
+    ``None`` makes a host-only plan that can be inspected but not run.
+    """
+
+    def __init__(self, kv_indptr, kv_last_page_len, num_heads: int, page_size: int,
+                 kv_dtype: int = KV_BF16, workspace=None, num_cus: int = 0,
+                 force_splits: int = 0, max_workers: int = 0, stream=None):
+        lib = load_library()
+        self._lib = lib
+        ip = _host_i32(kv_indptr)
+        lp = _host_i32(kv_last_page_len)
+        self.batch = int(ip.size - 1)
+        self.num_heads = int(num_heads)
+        self.page_size = int(page_size)
+        self.kv_dtype = int(kv_dtype)
+        self.workspace = workspace
+        o = _opts(num_cus, force_splits, max_workers)
+        h = ctypes.c_void_p()
+        ws_ptr, ws_n, sp = None, 0, None
+        if workspace is not None:
+            ws_ptr = _dptr(workspace)
+            ws_n = workspace.numel() * workspace.element_size()
+            sp = _stream_ptr(stream)
+        st = lib.mla_decode_plan(ctypes.byref(h), ip.ctypes.data_as(ctypes.c_void_p),
+                                 lp.ctypes.data_as(ctypes.c_void_p), self.batch, self.num_heads,
+                                 self.page_size, self.kv_dtype, ctypes.byref(o), ws_ptr, ws_n, sp)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_plan")
+        self._h = h
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            self._lib.mla_decode_plan_destroy(h)
+            self._h = None
+
+    def info(self) -> dict:
+        buf = np.zeros(10, np.int32)
+        st = self._lib.mla_decode_plan_info(self._h, buf.ctypes.data_as(ctypes.c_void_p))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_plan_info")
+        keys = ("batch", "num_heads", "page_size", "kv_dtype", "num_workers", "num_segments",
+                "num_partials", "num_split_requests", "granularity", "waves")
+        return {k: int(v) for k, v in zip(keys, buf)}
+
+    def segments(self):
+        inf = self.info()
+        seg = np.zeros((max(1, inf["num_segments"]), 4), np.int32)
+        wp = np.zeros(inf["num_workers"] + 1, np.int32)
+        st = self._lib.mla_decode_plan_segments(self._h, seg.ctypes.data_as(ctypes.c_void_p),
+                                                wp.ctypes.data_as(ctypes.c_void_p))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_plan_segments")
+        return seg[:inf["num_segments"]], wp
+
+    def set_events(self, before, after) -> None:
+        """Record raw hipEvent_t handles (ints) around the decode kernel in run()."""
+        st = self._lib.mla_decode_plan_set_events(self._h, before, after)
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_plan_set_events")
+
+    def run(self, q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len,
+            sm_scale: float, o, lse, stream=None) -> None:
+        """``mla_decode_run`` on device tensors (o and lse are written)."""
+        import torch
+        B, H = self.batch, self.num_heads
+        if q_nope.dtype != torch.bfloat16 or q_pe.dtype != torch.bfloat16:
+            raise ValueError("q_nope / q_pe must be bfloat16")
+        if tuple(q_nope.shape) != (B, H, D_CKV) or tuple(q_pe.shape) != (B, H, D_KPE):
+            raise ValueError("q_nope / q_pe shape mismatch with the plan")
+        if tuple(o.shape) != (B, H, D_CKV) or o.dtype != torch.bfloat16:
+            raise ValueError("o must be bfloat16 [B, H, 512]")
+        if tuple(lse.shape) != (B, H) or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [B, H]")
+        for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
+                        ("kv_last_page_len", kv_last_page_len)):
+            if t.dtype != torch.int32:
+                raise ValueError(name + " must be int32")
+        if ckv.dim() != 3 or ckv.shape[1] != self.page_size or ckv.shape[2] != D_CKV:
+            raise ValueError("ckv must be [pages, page_size, 512]")
+        if kpe.dim() != 3 or kpe.shape[1] != self.page_size or kpe.shape[2] != D_KPE:
+            raise ValueError("kpe must be [pages, page_size, 64]")
+        if self.kv_dtype == KV_BF16 and (ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16):
+            raise ValueError("bf16 cache expected")
+        st = self._lib.mla_decode_run(
+            self._h, _dptr(q_nope), _dptr(q_pe), _dptr(ckv), _dptr(kpe), _dptr(kv_scale),
+            _dptr(kv_indptr), _dptr(kv_indices), _dptr(kv_last_page_len), float(sm_scale),
+            _dptr(o), _dptr(lse), _stream_ptr(stream))
+        if st != MLA_OK:
+            raise MlaError(st, "mla_decode_run")
+
+
+def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_scale: float,
+           kv_dtype: int = KV_BF16, kv_scale=None, kv_indptr_host=None,
+           kv_last_page_len_host=None, force_splits: int = 0, stream=None):
+    """One-shot plan + run.  Returns (o, lse) as new device tensors."""
+    import torch
+    B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    P = int(ckv.shape[1])
+    ip_h = kv_indptr if kv_indptr_host is None else kv_indptr_host
+    lp_h = kv_last_page_len if kv_last_page_len_host is None else kv_last_page_len_host
+    ws = torch.empty(workspace_bytes(B, H, force_splits=force_splits), dtype=torch.uint8,
+                     device=q_nope.device)
+    plan = Plan(ip_h, lp_h, H, P, kv_dtype, ws, force_splits=force_splits, stream=stream)
+    o = torch.empty((B, H, D_CKV), dtype=torch.bfloat16, device=q_nope.device)
+    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+    plan.run(q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len, sm_scale,
+             o, lse, stream)
+    return o, lse

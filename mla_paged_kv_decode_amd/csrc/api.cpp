@@ -1,0 +1,289 @@
+// C ABI of the paged MLA decode library (declared in include/mla_decode.h).
+//
+// mla_decode_plan runs the split-KV planner on the host copies of the page
+// table and copies the work list into the caller's workspace; mla_decode_run
+// only launches kernels (decode, then combine when a request was split), so it
+// is safe to capture in a HIP graph.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/mla_decode.h"
+#include "kernels.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+mla_status hip_fail(hipError_t e, const char* what) {
+  g_last_error = std::string(what) + ": " + hipGetErrorString(e);
+  return MLA_ERR_HIP;
+}
+
+bool supported_heads(int32_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+int page_shift_of(int32_t p) {
+  switch (p) {
+    case 16: return 4;
+    case 32: return 5;
+    case 64: return 6;
+    default: return -1;
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Layout {
+  size_t segs, wptr, comb, plse, po, total, meta_bytes;
+};
+
+Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, int32_t heads) {
+  Layout L;
+  L.segs = 0;
+  L.wptr = align256(L.segs + (size_t)nseg * 16);
+  L.comb = align256(L.wptr + (size_t)(workers + 1) * 4);
+  L.meta_bytes = L.comb + (size_t)ncomb * 16;
+  L.plse = align256(L.meta_bytes);
+  L.po = align256(L.plse + (size_t)nparts * heads * 4);
+  L.total = align256(L.po + (size_t)nparts * heads * 512 * 4);
+  return L;
+}
+
+// Workgroups to balance over: one per compute unit (every decode variant uses
+// more than half of a CU's 160 KiB of LDS, so one workgroup fits per CU).
+mla_status worker_count(const mla_plan_opts* opts, int32_t* workers) {
+  int32_t cus = opts ? opts->num_cus : 0;
+  if (cus < 0) return MLA_ERR_INVALID_ARG;
+  if (cus == 0) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+  }
+  int32_t w = cus;
+  if (opts && opts->max_workers > 0) w = std::min(w, opts->max_workers);
+  if (w <= 0) return MLA_ERR_INVALID_ARG;
+  *workers = w;
+  return MLA_OK;
+}
+
+}  // namespace
+
+struct mla_plan_s {
+  int32_t batch = 0, heads = 0, page_size = 0, page_shift = 0, kv_dtype = 0;
+  mla_gpu::DecodeConfig cfg{};
+  mla::Plan plan;
+  Layout layout{};
+  std::vector<uint8_t> host_meta;  // staged work list (kept alive for the async copy)
+  uint8_t* workspace = nullptr;
+  hipEvent_t ev_before = nullptr, ev_after = nullptr;
+};
+
+extern "C" {
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MLA_ERR_HIP: return "HIP runtime error";
+    case MLA_ERR_NOT_UPLOADED: return "plan has no device workspace";
+    default: return "unknown status";
+  }
+}
+
+const char* mla_last_error(void) { return g_last_error.c_str(); }
+
+size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_plan_opts* opts) {
+  if (batch < 0 || !supported_heads(num_heads)) return 0;
+  if (opts && opts->force_splits < 0) return 0;
+  int32_t workers = 0;
+  if (worker_count(opts, &workers) != MLA_OK) return 0;
+  mla::PlanParams pp;
+  pp.num_heads = num_heads;
+  pp.num_workers = workers;
+  pp.force_splits = opts ? opts->force_splits : 0;
+  const int64_t nseg = mla::max_segments(batch, pp);
+  const int64_t nparts = mla::max_partials(batch, pp);
+  return layout_for(nseg, workers, batch, nparts, num_heads).total;
+}
+
+mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
+                           const int32_t* kv_last_page_len_host, int32_t batch, int32_t num_heads,
+                           int32_t page_size, mla_kv_dtype kv_dtype, const mla_plan_opts* opts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!out) return MLA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (batch < 0 || !kv_indptr_host || (batch > 0 && !kv_last_page_len_host))
+    return MLA_ERR_INVALID_ARG;
+  if (!supported_heads(num_heads) || page_shift_of(page_size) < 0) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
+  if (opts && (opts->force_splits < 0 || opts->max_workers < 0)) return MLA_ERR_INVALID_ARG;
+
+  mla_plan_s* p = new (std::nothrow) mla_plan_s();
+  if (!p) return MLA_ERR_INVALID_ARG;
+  p->batch = batch;
+  p->heads = num_heads;
+  p->page_size = page_size;
+  p->page_shift = page_shift_of(page_size);
+  p->kv_dtype = kv_dtype;
+  if (mla_gpu::decode_config(num_heads, &p->cfg) != 0) {
+    delete p;
+    return MLA_ERR_UNSUPPORTED;
+  }
+  int32_t workers = 0;
+  mla_status st = worker_count(opts, &workers);
+  if (st != MLA_OK) {
+    delete p;
+    return st;
+  }
+  mla::PlanParams pp;
+  pp.num_heads = num_heads;
+  pp.page_size = page_size;
+  pp.num_workers = workers;
+  pp.granularity = p->cfg.tile;
+  pp.force_splits = opts ? opts->force_splits : 0;
+  static const int32_t kZero = 0;
+  if (mla::build_plan(kv_indptr_host, batch > 0 ? kv_last_page_len_host : &kZero, batch, pp,
+                      &p->plan) != 0) {
+    delete p;
+    return MLA_ERR_INVALID_ARG;
+  }
+  const mla::Plan& pl = p->plan;
+  const int64_t ncomb = (int64_t)pl.combine.size() / 4;
+  p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
+                         num_heads);
+
+  // stage the work list: segments | worker_ptr | combine list
+  p->host_meta.assign(p->layout.meta_bytes, 0);
+  for (size_t i = 0; i < pl.segments.size(); ++i) {
+    const int32_t v[4] = {pl.segments[i].request, pl.segments[i].begin, pl.segments[i].end,
+                          pl.segments[i].slot};
+    std::memcpy(p->host_meta.data() + p->layout.segs + i * 16, v, 16);
+  }
+  std::memcpy(p->host_meta.data() + p->layout.wptr, pl.worker_ptr.data(),
+              pl.worker_ptr.size() * 4);
+  if (!pl.combine.empty())
+    std::memcpy(p->host_meta.data() + p->layout.comb, pl.combine.data(), pl.combine.size() * 4);
+
+  if (workspace) {
+    if (workspace_bytes < p->layout.total) {
+      delete p;
+      return MLA_ERR_WORKSPACE_TOO_SMALL;
+    }
+    p->workspace = static_cast<uint8_t*>(workspace);
+    hipError_t e = hipMemcpyAsync(p->workspace, p->host_meta.data(), p->host_meta.size(),
+                                  hipMemcpyHostToDevice, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "hipMemcpyAsync(work list)");
+    }
+  }
+  *out = p;
+  return MLA_OK;
+}
+
+mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, const void* ckv,
+                          const void* kpe, const float* kv_scale, const int32_t* kv_indptr,
+                          const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                          float sm_scale, void* o, float* lse, void* stream) {
+  if (!p) return MLA_ERR_INVALID_ARG;
+  if (!p->workspace) return MLA_ERR_NOT_UPLOADED;
+  if (p->batch == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !ckv || !kpe || !kv_indptr || !kv_indices || !kv_last_page_len || !o ||
+      !lse)
+    return MLA_ERR_INVALID_ARG;
+  if ((p->kv_dtype == MLA_KV_BF16) != (kv_scale == nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return MLA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = p->workspace;
+
+  mla_gpu::DecodeArgs a;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.ckv = static_cast<const uint8_t*>(ckv);
+  a.kpe = static_cast<const uint8_t*>(kpe);
+  a.kv_scale = kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.kv_last_page_len = kv_last_page_len;
+  a.segs = reinterpret_cast<const int4*>(ws + p->layout.segs);
+  a.worker_ptr = reinterpret_cast<const int32_t*>(ws + p->layout.wptr);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
+  a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.page_shift = p->page_shift;
+  if (p->ev_before) {
+    hipError_t e = hipEventRecord(p->ev_before, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  if (p->plan.num_workers > 0) {
+    hipError_t e = mla_gpu::launch_decode(p->heads, a, p->plan.num_workers, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+  }
+  if (p->ev_after) {
+    hipError_t e = hipEventRecord(p->ev_after, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  const int32_t ncomb = (int32_t)(p->plan.combine.size() / 4);
+  if (ncomb > 0) {
+    mla_gpu::CombineArgs c;
+    c.comb = reinterpret_cast<const int4*>(ws + p->layout.comb);
+    c.part_o = a.part_o;
+    c.part_lse = a.part_lse;
+    c.o = a.o;
+    c.lse = lse;
+    c.num_heads = p->heads;
+    hipError_t e = mla_gpu::launch_combine(c, ncomb, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
+  }
+  return MLA_OK;
+}
+
+void mla_decode_plan_destroy(mla_plan_t p) { delete p; }
+
+mla_status mla_decode_plan_set_events(mla_plan_t p, void* before, void* after) {
+  if (!p || ((before == nullptr) != (after == nullptr))) return MLA_ERR_INVALID_ARG;
+  p->ev_before = static_cast<hipEvent_t>(before);
+  p->ev_after = static_cast<hipEvent_t>(after);
+  return MLA_OK;
+}
+
+mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[10]) {
+  if (!p || !info) return MLA_ERR_INVALID_ARG;
+  info[0] = p->batch;
+  info[1] = p->heads;
+  info[2] = p->page_size;
+  info[3] = p->kv_dtype;
+  info[4] = p->plan.num_workers;
+  info[5] = (int32_t)p->plan.segments.size();
+  info[6] = p->plan.num_partials;
+  info[7] = (int32_t)(p->plan.combine.size() / 4);
+  info[8] = p->cfg.tile;
+  info[9] = p->cfg.waves;
+  return MLA_OK;
+}
+
+mla_status mla_decode_plan_segments(mla_plan_t p, int32_t* seg, int32_t* worker_ptr) {
+  if (!p || !seg || !worker_ptr) return MLA_ERR_INVALID_ARG;
+  for (size_t i = 0; i < p->plan.segments.size(); ++i) {
+    seg[4 * i + 0] = p->plan.segments[i].request;
+    seg[4 * i + 1] = p->plan.segments[i].begin;
+    seg[4 * i + 2] = p->plan.segments[i].end;
+    seg[4 * i + 3] = p->plan.segments[i].slot;
+  }
+  std::memcpy(worker_ptr, p->plan.worker_ptr.data(), p->plan.worker_ptr.size() * 4);
+  return MLA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Launch interface of the gfx950 decode and combine kernels (internal to the
+// library; the public C ABI is include/mla_decode.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla_gpu {
+
+struct DecodeArgs {
+  const uint16_t* q_nope;  // bf16 [B, H, 512]
+  const uint16_t* q_pe;    // bf16 [B, H, 64]
+  const uint8_t* ckv;      // [pages, P, 512] bf16 or 8-bit codes
+  const uint8_t* kpe;      // [pages, P, 64]
+  const float* kv_scale;   // [pages, P] for 8-bit caches
+  const int32_t* kv_indptr;
+  const int32_t* kv_indices;
+  const int32_t* kv_last_page_len;
+  const int4* segs;           // {request, begin, end, slot}
+  const int32_t* worker_ptr;  // grid + 1
+  uint16_t* o;                // bf16 [B, H, 512]
+  float* lse;                 // [B, H]
+  float* part_o;              // [slots, H, 512]
+  float* part_lse;            // [slots, H]
+  float scale_log2;           // sm_scale * log2(e)
+  int32_t page_shift;         // log2(page_size)
+};
+
+struct CombineArgs {
+  const int4* comb;  // {request, first slot, count, 0}
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* o;
+  float* lse;
+  int32_t num_heads;
+};
+
+struct DecodeConfig {
+  int32_t waves;  // waves per workgroup
+  int32_t tile;   // tokens per KV tile = split granularity
+};
+
+int decode_config(int num_heads, DecodeConfig* cfg);
+hipError_t launch_decode(int num_heads, const DecodeArgs& a, int grid, hipStream_t stream);
+hipError_t launch_combine(const CombineArgs& a, int num_split_requests, hipStream_t stream);
+
+}  // namespace mla_gpu

@@ -1,0 +1,196 @@
+// Split-KV work planner: chunk-size search + longest-first assignment.
+//
+// Cost model, in token-equivalents of KV traffic (one token = one 1152-byte
+// latent row in bf16): a chunk of n tokens costs n + kFixed + H (loading the
+// request's H query rows, 1152 B each) and, when the request is cut, another
+// 4H for writing and re-reading its fp32 partial output (2048 B per head, twice).
+// For each candidate chunk size C (a multiple of the granularity) every
+// request is cut into ceil(L / C) near-equal chunks; the chunks are assigned
+// longest-first to the least-loaded worker (ties to the lower index) and the
+// candidate with the smallest largest-load wins, ties going to fewer cuts.
+// Everything depends only on the lengths, so the plan is deterministic.
+#include "planner.h"
+
+#include <algorithm>
+#include <cstdint>
+#include <queue>
+#include <utility>
+#include <vector>
+
+namespace mla {
+namespace {
+
+constexpr int64_t kFixed = 64;  // per-chunk start-up (pipeline fill, epilogue)
+
+struct Piece {
+  int32_t request;
+  int32_t begin;
+  int32_t end;
+  int32_t nsplit;  // chunks of its request
+  int64_t cost;
+};
+
+void cut_requests(const std::vector<int64_t>& len, int64_t chunk, int32_t gran, int32_t heads,
+                  int32_t force, std::vector<Piece>* pieces) {
+  pieces->clear();
+  for (size_t b = 0; b < len.size(); ++b) {
+    const int64_t L = len[b];
+    int64_t n = 1;
+    if (L > 0) {
+      if (force > 0)
+        n = std::min<int64_t>(force, (L + gran - 1) / gran);
+      else
+        n = (L + chunk - 1) / chunk;
+      if (n < 1) n = 1;
+    }
+    // near-equal chunks with boundaries on multiples of gran
+    int64_t step = (L + n - 1) / n;
+    step = ((step + gran - 1) / gran) * gran;
+    if (step <= 0) step = gran;
+    n = L > 0 ? (L + step - 1) / step : 1;
+    for (int64_t k = 0; k < n; ++k) {
+      Piece p;
+      p.request = (int32_t)b;
+      p.begin = (int32_t)std::min<int64_t>(L, k * step);
+      p.end = (int32_t)std::min<int64_t>(L, (k + 1) * step);
+      p.nsplit = (int32_t)n;
+      p.cost = (p.end - p.begin) + kFixed + heads + (n > 1 ? 4 * (int64_t)heads : 0);
+      pieces->push_back(p);
+    }
+  }
+}
+
+// Longest-first assignment; returns the largest worker load.
+int64_t assign(const std::vector<Piece>& pieces, int32_t workers, std::vector<int32_t>* owner) {
+  std::vector<int32_t> order(pieces.size());
+  for (size_t i = 0; i < order.size(); ++i) order[i] = (int32_t)i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t a, int32_t b) { return pieces[a].cost > pieces[b].cost; });
+  typedef std::pair<int64_t, int32_t> Load;  // (load, worker)
+  std::priority_queue<Load, std::vector<Load>, std::greater<Load>> heap;
+  for (int32_t w = 0; w < workers; ++w) heap.push(Load(0, w));
+  owner->assign(pieces.size(), -1);
+  int64_t worst = 0;
+  for (int32_t i : order) {
+    Load top = heap.top();
+    heap.pop();
+    (*owner)[i] = top.second;
+    top.first += pieces[i].cost;
+    worst = std::max(worst, top.first);
+    heap.push(top);
+  }
+  return worst;
+}
+
+}  // namespace
+
+int64_t max_segments(int32_t batch, const PlanParams& p) {
+  if (p.force_splits > 0) return (int64_t)batch * p.force_splits;
+  return (int64_t)batch + 2 * (int64_t)p.num_workers;
+}
+
+int64_t max_partials(int32_t batch, const PlanParams& p) { return max_segments(batch, p); }
+
+int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
+                   const PlanParams& p, Plan* out) {
+  if (!kv_indptr || !kv_last_page_len || !out || batch < 0 || p.num_workers <= 0 ||
+      p.granularity <= 0 || p.page_size <= 0 || p.num_heads <= 0)
+    return -1;
+  if (kv_indptr[0] != 0) return -1;
+  std::vector<int64_t> len((size_t)batch);
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
+    if (n < 0) return -1;
+    if (n == 0) {
+      len[b] = 0;
+      continue;
+    }
+    const int32_t last = kv_last_page_len[b];
+    if (last < 1 || last > p.page_size) return -1;
+    len[b] = (n - 1) * p.page_size + last;
+    if (len[b] > INT32_MAX) return -1;
+    max_len = std::max(max_len, len[b]);
+  }
+
+  const int32_t gran = p.granularity;
+  const int64_t seg_cap = max_segments(batch, p);
+  std::vector<Piece> pieces, best_pieces;
+  std::vector<int32_t> owner, best_owner;
+  int64_t best = -1;
+
+  if (p.force_splits > 0) {
+    cut_requests(len, 0, gran, p.num_heads, p.force_splits, &best_pieces);
+    assign(best_pieces, p.num_workers, &best_owner);
+  } else {
+    // candidate chunk sizes: gran * {1, 2, 3, 4, 6, 8, 12, 16, ...} up to max_len
+    std::vector<int64_t> cands;
+    for (int64_t m = 1;; m *= 2) {
+      cands.push_back(m * gran);
+      if (m * gran >= max_len) break;
+      if (m >= 2) {
+        cands.push_back(m * gran * 3 / 2);
+      }
+    }
+    std::sort(cands.begin(), cands.end(), std::greater<int64_t>());  // fewest cuts first
+    for (int64_t c : cands) {
+      cut_requests(len, c, gran, p.num_heads, 0, &pieces);
+      if ((int64_t)pieces.size() > seg_cap) continue;
+      const int64_t worst = assign(pieces, p.num_workers, &owner);
+      if (best < 0 || worst < best) {
+        best = worst;
+        best_pieces.swap(pieces);
+        best_owner.swap(owner);
+      }
+    }
+    if (best < 0) return -1;  // unreachable: the largest candidate never cuts
+  }
+
+  // group by worker, keep assignment order within a worker stable (request order)
+  std::vector<int32_t> count((size_t)p.num_workers, 0);
+  for (int32_t w : best_owner) ++count[w];
+  std::vector<int32_t> remap((size_t)p.num_workers, -1);
+  int32_t used = 0;
+  for (int32_t w = 0; w < p.num_workers; ++w)
+    if (count[w] > 0) remap[w] = used++;
+  out->batch = batch;
+  out->num_workers = used;
+  out->worker_ptr.assign((size_t)used + 1, 0);
+  for (int32_t w = 0; w < p.num_workers; ++w)
+    if (remap[w] >= 0) out->worker_ptr[remap[w] + 1] = count[w];
+  for (int32_t w = 0; w < used; ++w) out->worker_ptr[w + 1] += out->worker_ptr[w];
+  out->segments.assign(best_pieces.size(), Segment());
+  std::vector<int32_t> fill(out->worker_ptr.begin(), out->worker_ptr.end() - 1);
+
+  // partial slots: consecutive per split request, in token order (cut_requests
+  // emits the pieces of a request consecutively, in token order)
+  std::vector<int32_t> first_slot((size_t)batch, -1), first_piece((size_t)batch, -1);
+  out->combine.clear();
+  int32_t slots = 0;
+  for (size_t i = 0; i < best_pieces.size(); ++i) {
+    const Piece& pc = best_pieces[i];
+    if (first_piece[pc.request] < 0) first_piece[pc.request] = (int32_t)i;
+    if (pc.nsplit > 1 && first_slot[pc.request] < 0) {
+      first_slot[pc.request] = slots;
+      out->combine.push_back(pc.request);
+      out->combine.push_back(slots);
+      out->combine.push_back(pc.nsplit);
+      out->combine.push_back(0);
+      slots += pc.nsplit;
+    }
+  }
+  out->num_partials = slots;
+  for (size_t i = 0; i < best_pieces.size(); ++i) {
+    const Piece& pc = best_pieces[i];
+    Segment s;
+    s.request = pc.request;
+    s.begin = pc.begin;
+    s.end = pc.end;
+    s.slot = pc.nsplit > 1 ? first_slot[pc.request] + ((int32_t)i - first_piece[pc.request]) : -1;
+    const int32_t w = remap[best_owner[i]];
+    out->segments[fill[w]++] = s;
+  }
+  return 0;
+}
+
+}  // namespace mla

@@ -1,0 +1,152 @@
+"""CPU tests of the C ABI: the library loads, exports what the header declares,
+and its split-KV planner (host-only plans, no device) covers every token once,
+cuts on the granularity, numbers partial slots consecutively, is a pure
+function of the lengths, and rejects malformed page tables."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mla_paged_kv_decode_amd as mla
+from mla_paged_kv_decode_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        from mla_paged_kv_decode_amd import build
+        build.build()
+    return mla.load_library()
+
+
+def test_exports_match_header(lib):
+    hdr = open(os.path.join(ROOT, "include", "mla_decode.h")).read()
+    declared = set(re.findall(r"\b(mla_[a-z_]+)\s*\(", hdr))
+    assert declared == set(mla.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4, -5):
+        assert lib.mla_status_string(st)
+
+
+def _table(lengths, P):
+    rng = np.random.default_rng(0)
+    ip, ix, lp, _ = synth.page_table(lengths, P, rng)
+    return ip, lp
+
+
+def _check_plan(plan, lengths, gran):
+    seg, wp = plan.segments()
+    info = plan.info()
+    assert wp[0] == 0 and wp[-1] == len(seg) and np.all(np.diff(wp) > 0)
+    covered = {}
+    for b, t0, t1, slot in seg:
+        covered.setdefault(int(b), []).append((int(t0), int(t1), int(slot)))
+    slots_seen = set()
+    for b, L in enumerate(lengths):
+        pieces = sorted(covered[b])
+        if L == 0:
+            assert pieces == [(0, 0, -1)]
+            continue
+        assert pieces[0][0] == 0 and pieces[-1][1] == L
+        for (a0, a1, _), (b0, _, _) in zip(pieces, pieces[1:]):
+            assert a1 == b0
+        for t0, t1, _ in pieces:
+            assert t1 > t0 and t0 % gran == 0
+        if len(pieces) == 1:
+            assert pieces[0][2] == -1
+        else:
+            sl = [p[2] for p in pieces]
+            assert sl == list(range(sl[0], sl[0] + len(sl)))
+            slots_seen.update(sl)
+    assert len(slots_seen) == info["num_partials"]
+    return seg, wp, info
+
+
+@pytest.mark.parametrize("heads,P,lengths", [
+    (16, 64, [4096] * 64),
+    (128, 64, [4096] * 64),
+    (64, 16, list(np.random.default_rng(4).integers(1, 2049, 768))),
+    (16, 16, [256] * 4),
+    (32, 32, [0, 1, 17, 5000, 33, 0, 64]),
+])
+def test_plan_covers_each_token_once(lib, heads, P, lengths):
+    ip, lp = _table(lengths, P)
+    plan = mla.Plan(ip, lp, heads, P, num_cus=256)
+    _check_plan(plan, lengths, plan.info()["granularity"])
+    assert plan.info()["num_workers"] <= 256
+
+
+def test_plan_balances_uniform_batch(lib):
+    ip, lp = _table([4096] * 64, 64)
+    plan = mla.Plan(ip, lp, 16, 64, num_cus=256)
+    seg, wp, info = _check_plan(plan, [4096] * 64, 64)
+    assert info["num_workers"] == 256
+    assert set((seg[:, 2] - seg[:, 1]).tolist()) == {1024}
+
+
+def test_plan_is_pure_function_of_lengths(lib):
+    lengths = list(np.random.default_rng(9).integers(1, 3000, 300))
+    ip, lp = _table(lengths, 16)
+    a = mla.Plan(ip, lp, 64, 16, num_cus=256).segments()
+    b = mla.Plan(ip.copy(), lp.copy(), 64, 16, num_cus=256).segments()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_force_splits(lib):
+    lengths = [1000, 64, 1, 0]
+    ip, lp = _table(lengths, 16)
+    plan = mla.Plan(ip, lp, 16, 16, num_cus=8, force_splits=3)
+    seg, wp, info = _check_plan(plan, lengths, 64)
+    counts = {b: int((seg[:, 0] == b).sum()) for b in range(4)}
+    assert counts == {0: 3, 1: 1, 2: 1, 3: 1}
+
+
+def test_workspace_bound_covers_plan(lib):
+    lengths = list(np.random.default_rng(5).integers(1, 5000, 100))
+    ip, lp = _table(lengths, 64)
+    for heads in (16, 128):
+        n = mla.workspace_bytes(100, heads, num_cus=256)
+        plan = mla.Plan(ip, lp, heads, 64, num_cus=256)
+        info = plan.info()
+        need = info["num_partials"] * heads * (512 + 1) * 4 + info["num_segments"] * 16
+        assert n >= need
+
+
+@pytest.mark.parametrize("bad", ["indptr_start", "indptr_decreasing", "last_zero", "last_big"])
+def test_malformed_tables_rejected(lib, bad):
+    ip = np.array([0, 2, 4], np.int32)
+    lp = np.array([16, 3], np.int32)
+    if bad == "indptr_start":
+        ip[0] = 1
+    elif bad == "indptr_decreasing":
+        ip = np.array([0, 3, 2], np.int32)
+    elif bad == "last_zero":
+        lp[1] = 0
+    else:
+        lp[0] = 17
+    with pytest.raises(mla.MlaError) as e:
+        mla.Plan(ip, lp, 16, 16, num_cus=4)
+    assert e.value.status == -1
+
+
+@pytest.mark.parametrize("heads,P", [(8, 16), (48, 16), (16, 8), (16, 128)])
+def test_unsupported_shapes_rejected(lib, heads, P):
+    with pytest.raises(mla.MlaError) as e:
+        mla.Plan(np.array([0, 1], np.int32), np.array([1], np.int32), heads, P, num_cus=4)
+    assert e.value.status == -2
+
+
+def test_run_without_workspace_is_refused(lib):
+    plan = mla.Plan(np.array([0, 1], np.int32), np.array([1], np.int32), 16, 16, num_cus=4)
+    P = ctypes.c_void_p
+    st = lib.mla_decode_run(plan._h, P(1), P(1), P(1), P(1), None, P(1), P(1), P(1),
+                            ctypes.c_float(0.1), P(1), P(1), None)
+    assert st == -5

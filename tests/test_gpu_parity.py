@@ -1,0 +1,234 @@
+"""GPU parity of the HIP decode path against the fp64 oracle.
+
+Tolerances (stated for bf16 inputs): cosine distance of the whole flattened O
+<= 1e-4, max |O - O_ref| <= 2e-2, max |LSE - LSE_ref| <= 1e-3; an empty
+request must give O = 0 and LSE = -inf exactly.  Every input is seeded and
+synthetic (mla_paged_kv_decode_amd.synth); at full workload sizes the oracle
+computes a sample of (request, head) rows one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from mla_paged_kv_decode_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+COS_TOL, ABS_TOL, LSE_TOL = 1e-4, 2e-2, 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mla_paged_kv_decode_amd as mla
+    mla.load_library()  # fail loudly if the HIP library is missing
+
+
+def dev(inp):
+    d = "cuda"
+    t = {}
+    t["q_nope"] = torch.from_numpy(inp.q_nope.view(np.int16)).view(torch.bfloat16).to(d)
+    t["q_pe"] = torch.from_numpy(inp.q_pe.view(np.int16)).view(torch.bfloat16).to(d)
+    if inp.kv_dtype == synth.KV_BF16:
+        t["ckv"] = torch.from_numpy(inp.ckv.view(np.int16)).view(torch.bfloat16).to(d)
+        t["kpe"] = torch.from_numpy(inp.kpe.view(np.int16)).view(torch.bfloat16).to(d)
+        t["kv_scale"] = None
+    else:
+        t["ckv"] = torch.from_numpy(inp.ckv).to(d)
+        t["kpe"] = torch.from_numpy(inp.kpe).to(d)
+        t["kv_scale"] = torch.from_numpy(inp.kv_scale).to(d)
+    for k in ("kv_indptr", "kv_indices", "kv_last_page_len"):
+        t[k] = torch.from_numpy(getattr(inp, k)).to(d)
+    return t
+
+
+def gpu_run(inp, t=None, force_splits=0):
+    import mla_paged_kv_decode_amd as mla
+    t = t or dev(inp)
+    o, lse = mla.decode(t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_indptr"],
+                        t["kv_indices"], t["kv_last_page_len"], inp.sm_scale, inp.kv_dtype,
+                        t["kv_scale"], kv_indptr_host=inp.kv_indptr,
+                        kv_last_page_len_host=inp.kv_last_page_len, force_splits=force_splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def host(o, lse):
+    return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def ref(inp, rows=None):
+    return oracle.decode(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.kv_indptr, inp.kv_indices,
+                         inp.kv_last_page_len, inp.sm_scale, inp.page_size, inp.kv_dtype,
+                         inp.kv_scale, rows=rows)
+
+
+def check(o, lse, o_ref, lse_ref):
+    o = o.reshape(-1, 512)
+    lse = lse.reshape(-1)
+    o_ref = o_ref.reshape(-1, 512)
+    lse_ref = lse_ref.reshape(-1)
+    empty = np.isneginf(lse_ref)
+    assert np.all(np.isneginf(lse[empty])) and np.all(o[empty] == 0)
+    ne = ~empty
+    if not ne.any():
+        return
+    a, b = o[ne].ravel(), o_ref[ne].ravel()
+    assert np.all(np.isfinite(a)), "non-finite output"
+    cos = 1.0 - float(a @ b) / (np.linalg.norm(a) * np.linalg.norm(b))
+    err = float(np.abs(a - b).max())
+    lerr = float(np.abs(lse[ne] - lse_ref[ne]).max())
+    assert cos <= COS_TOL, ("cosine distance", cos)
+    assert err <= ABS_TOL, ("max abs", err)
+    assert lerr <= LSE_TOL, ("lse", lerr)
+
+
+RAGGED = [1, 15, 16, 17, 63, 100, 333, 1000, 2049]
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("page", [16, 32, 64])
+def test_ragged_lengths_all_shapes(heads, page):
+    inp = synth.make_inputs(RAGGED, heads, page, seed=100 + heads + page, poison=True,
+                            extra_pages=5)
+    print("case heads=%d page=%d" % (heads, page), flush=True)
+    o, lse = host(*gpu_run(inp))
+    check(o, lse, *ref(inp))
+
+
+def test_tiny_workload():
+    inp = synth.make_workload("tiny_b4_h16_l256_p16")
+    o, lse = host(*gpu_run(inp))
+    check(o, lse, *ref(inp))
+
+
+@pytest.mark.parametrize("heads", [16, 64, 128])
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_forced_splits_match_oracle(heads, splits):
+    inp = synth.make_inputs([700, 64, 1, 1500, 0, 129], heads, 16, seed=200 + splits,
+                            poison=True)
+    o, lse = host(*gpu_run(inp, force_splits=splits))
+    check(o, lse, *ref(inp))
+
+
+def test_kv_len_one_is_bit_exact_row():
+    inp = synth.make_inputs([1] * 5, 16, 16, seed=7, poison=True, extra_pages=3)
+    o, lse = gpu_run(inp)
+    o = o.cpu().view(torch.int16).numpy().view(np.uint16)
+    for b in range(5):
+        pg = int(inp.kv_indices[inp.kv_indptr[b]])
+        for h in range(16):
+            assert np.array_equal(o[b, h], inp.ckv[pg, 0]), (b, h)
+    _, lse_ref = ref(inp)
+    assert float(np.abs(lse.cpu().numpy() - lse_ref).max()) <= LSE_TOL
+
+
+def test_zero_query_gives_mean():
+    inp = synth.make_inputs([37, 300, 4096], 32, 64, seed=8, poison=True)
+    inp.q_nope[:] = 0
+    inp.q_pe[:] = 0
+    o, lse = host(*gpu_run(inp))
+    o_ref, lse_ref = ref(inp)
+    check(o, lse, o_ref, lse_ref)
+    assert np.allclose(lse, np.log([37, 300, 4096])[:, None], atol=1e-5)
+
+
+def test_empty_requests():
+    inp = synth.make_inputs([0, 50, 0, 0, 900, 0], 64, 32, seed=9, poison=True)
+    o, lse = host(*gpu_run(inp))
+    check(o, lse, *ref(inp))
+    assert np.all(np.isneginf(lse[[0, 2, 3, 5]]))
+
+
+def test_reruns_are_bit_identical():
+    inp = synth.make_inputs([3000, 17, 1024, 555], 128, 64, seed=10)
+    t = dev(inp)
+    o0, l0 = gpu_run(inp, t, force_splits=3)
+    for _ in range(10):
+        o1, l1 = gpu_run(inp, t, force_splits=3)
+        assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+        assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+def test_page_permutation_is_bit_identical():
+    inp = synth.make_inputs([777, 2048, 31], 16, 16, seed=11, extra_pages=7)
+    o0, l0 = gpu_run(inp)
+    rng = np.random.default_rng(1)
+    perm = rng.permutation(inp.num_pages)
+    ck = np.empty_like(inp.ckv)
+    kp = np.empty_like(inp.kpe)
+    ck[perm] = inp.ckv
+    kp[perm] = inp.kpe
+    inp.ckv, inp.kpe = ck, kp
+    inp.kv_indices = perm[inp.kv_indices].astype(np.int32)
+    o1, l1 = gpu_run(inp)
+    assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+def test_outputs_stay_in_bounds():
+    """Canaries around o, lse and after the workspace's used part stay intact."""
+    import mla_paged_kv_decode_amd as mla
+    inp = synth.make_inputs([500, 64, 1200], 64, 16, seed=12, poison=True)
+    t = dev(inp)
+    B, H = 3, 64
+    pad = 4096
+    obuf = torch.full((B * H * 512 + 2 * pad,), 12345, dtype=torch.int16, device="cuda")
+    lbuf = torch.full((B * H + 2 * pad,), 7.0, dtype=torch.float32, device="cuda")
+    o = obuf[pad:pad + B * H * 512].view(torch.bfloat16).view(B, H, 512)
+    lse = lbuf[pad:pad + B * H].view(B, H)
+    ws = torch.empty(mla.workspace_bytes(B, H, force_splits=2), dtype=torch.uint8, device="cuda")
+    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 16, workspace=ws, force_splits=2)
+    plan.run(t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], None, t["kv_indptr"], t["kv_indices"],
+             t["kv_last_page_len"], inp.sm_scale, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(obuf[:pad] == 12345) and torch.all(obuf[-pad:] == 12345)
+    assert torch.all(lbuf[:pad] == 7.0) and torch.all(lbuf[-pad:] == 7.0)
+    check(*host(o, lse), *ref(inp))
+
+
+def test_graph_replay_matches_eager():
+    import mla_paged_kv_decode_amd as mla
+    inp = synth.make_inputs([1000, 4000, 64], 16, 64, seed=13)
+    t = dev(inp)
+    B, H = 3, 16
+    ws = torch.empty(mla.workspace_bytes(B, H), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+    with torch.cuda.stream(s):
+        plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 64, workspace=ws, stream=s)
+        args = (t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], None, t["kv_indptr"],
+                t["kv_indices"], t["kv_last_page_len"], inp.sm_scale, o, lse)
+        plan.run(*args, stream=s)
+    torch.cuda.synchronize()
+    o_eager, l_eager = o.clone(), lse.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        plan.run(*args, stream=s)
+    for _ in range(4):
+        o.zero_()
+        lse.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_eager.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), l_eager.view(torch.int32))
+
+
+@pytest.mark.parametrize("name", ["mem_b64_h16_l4096_p64", "compute_b64_h128_l4096_p64",
+                                  "varlen_b768_h64_l1to2048_p16"])
+def test_full_workloads_sampled(name):
+    inp = synth.make_workload(name, poison=True)
+    print("workload", name, flush=True)
+    o, lse = host(*gpu_run(inp))
+    B, H = inp.batch, inp.num_heads
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(B * H, 96, replace=False), [0, B * H - 1]]))
+    o_ref, lse_ref = ref(inp, rows=rows.astype(np.int32))
+    check(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
+    # properties at every row: finite, |O| within the ckv range, LSE above the max score bound
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.abs(o).max() < 8.0
