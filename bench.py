@@ -197,6 +197,11 @@ def main():
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured stream-read / MFMA peak kernels")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run one device copy of this many MiB (a kernel of known "
+                         "traffic for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -213,6 +218,19 @@ def main():
     import mla_paged_kv_decode_amd as mla
     mla.load_library()
     hip = Hip()
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    peaks = {}
+    if not args.no_peaks:
+        peaks["stream_read_gbs"] = round(mla.peak_stream_read_gbs(4 << 30), 1)
+        peaks["mfma_bf16_tflops"] = round(mla.peak_mfma_bf16_tflops(), 1)
+        torch.cuda.empty_cache()
 
     prim = measure(args.workload, args.steps, args.warmup, args.copies, hip)
     inp = prim["inp"]
@@ -236,12 +254,16 @@ def main():
                    "kv_len": int(inp.lengths[0]), "page_size": inp.page_size,
                    "kv_dtype": "bf16", "d_ckv": 512, "d_kpe": 64,
                    "algorithmic_bytes": prim["bytes"], "flops": prim["flops"],
-                   "input_copies": args.copies, "plan": prim["plan"]},
+                   "input_copies": args.copies, "plan": prim["plan"],
+                   "kernel_sha": kernel_sha()},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "mla_decode_bf16_kernel",
-                     "kernel_ms": round(prim["kernel_ms"], 5)},
+                     "kernel_ms": round(prim["kernel_ms"], 5),
+                     "frac_of_measured_read_peak": (round(kern_gbs / peaks["stream_read_gbs"], 4)
+                                                    if peaks else None)},
         "plan_ms": round(prim["plan_ms"], 4),
+        "measured_peaks": peaks,
         "wall_ms_per_step": round(prim["wall_ms_per_step"], 5),
     }
     if args.secondary != "none":
@@ -257,7 +279,9 @@ def main():
                          "hbm_frac": round(sec["bytes"] / (sec["kernel_ms"] * 1e-3) / 1e9
                                            / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic(args.secondary),
-                         "kernel_ms": round(sec["kernel_ms"], 5)},
+                         "kernel_ms": round(sec["kernel_ms"], 5),
+                         "frac_of_measured_mfma_peak": (
+                             round(ktfs / peaks["mfma_bf16_tflops"], 4) if peaks else None)},
         }
         del sec
     if not args.no_cpu_baseline:

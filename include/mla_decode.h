@@ -105,8 +105,9 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Run the decode for a plan: the decode kernel and, if any request was split,
- * the combine kernel, both on `stream`.  Allocates nothing, never
+ * Run the decode for a plan: one kernel on `stream` that also merges the
+ * chunks of requests the plan split (in chunk order, so the result does not
+ * depend on which workgroup finishes last).  Allocates nothing, never
  * synchronises and never reads device memory from the host, so it may be
  * captured in a HIP graph and replayed while the page-table lengths are
  * unchanged.

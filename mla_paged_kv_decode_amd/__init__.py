@@ -35,6 +35,8 @@ EXPORTED_SYMBOLS = (
     "mla_decode_plan_info",
     "mla_decode_plan_segments",
     "mla_decode_plan_set_events",
+    "mla_peak_stream_read",
+    "mla_peak_mfma_bf16",
 )
 
 _lib = None
@@ -84,6 +86,10 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_plan_segments.restype = ctypes.c_int
     lib.mla_decode_plan_set_events.argtypes = [P, P, P]
     lib.mla_decode_plan_set_events.restype = ctypes.c_int
+    lib.mla_peak_stream_read.argtypes = [P, sz, P, i32, ctypes.POINTER(ctypes.c_float), P]
+    lib.mla_peak_stream_read.restype = ctypes.c_int
+    lib.mla_peak_mfma_bf16.argtypes = [P, i32, ctypes.POINTER(ctypes.c_float), P]
+    lib.mla_peak_mfma_bf16.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -217,6 +223,32 @@ class Plan:
             _dptr(o), _dptr(lse), _stream_ptr(stream))
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_run")
+
+
+def peak_stream_read_gbs(nbytes: int = 4 << 30, iters: int = 20, stream=None) -> float:
+    """Measured HBM read bandwidth (GB/s): median pass of a 16-byte-load read
+    over a fresh device buffer of nbytes."""
+    import torch
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    ms = ctypes.c_float()
+    st = load_library().mla_peak_stream_read(_dptr(buf), nbytes, _dptr(sink), int(iters),
+                                             ctypes.byref(ms), _stream_ptr(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_peak_stream_read")
+    return nbytes / (ms.value * 1e-3) / 1e9
+
+
+def peak_mfma_bf16_tflops(iters: int = 10, stream=None) -> float:
+    """Measured dense bf16 MFMA throughput (TFLOP/s)."""
+    import torch
+    sink = torch.empty(1 << 20, dtype=torch.uint8, device="cuda")
+    tf = ctypes.c_float()
+    st = load_library().mla_peak_mfma_bf16(_dptr(sink), int(iters), ctypes.byref(tf),
+                                           _stream_ptr(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_peak_mfma_bf16")
+    return float(tf.value)
 
 
 def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_scale: float,

@@ -1,9 +1,9 @@
 // C ABI of the paged MLA decode library (declared in include/mla_decode.h).
 //
 // mla_decode_plan runs the split-KV planner on the host copies of the page
-// table and copies the work list into the caller's workspace; mla_decode_run
-// only launches kernels (decode, then combine when a request was split), so it
-// is safe to capture in a HIP graph.
+// table and copies the work list (and zeroed arrival counters) into the
+// caller's workspace; mla_decode_run only launches the decode kernel, which
+// also merges split requests, so it is safe to capture in a HIP graph.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,34 +40,40 @@ int page_shift_of(int32_t p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t segs, wptr, comb, plse, po, total, meta_bytes;
+  size_t segs, wptr, counters, plse, po, total, meta_bytes;
 };
 
+// workspace: segments (32 B each) | worker_ptr | arrival counters | partial LSE | partial O
 Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, int32_t heads) {
   Layout L;
   L.segs = 0;
-  L.wptr = align256(L.segs + (size_t)nseg * 16);
-  L.comb = align256(L.wptr + (size_t)(workers + 1) * 4);
-  L.meta_bytes = L.comb + (size_t)ncomb * 16;
+  L.wptr = align256(L.segs + (size_t)nseg * 32);
+  L.counters = align256(L.wptr + (size_t)(workers + 1) * 4);
+  L.meta_bytes = L.counters + (size_t)ncomb * 4;
   L.plse = align256(L.meta_bytes);
   L.po = align256(L.plse + (size_t)nparts * heads * 4);
   L.total = align256(L.po + (size_t)nparts * heads * 512 * 4);
   return L;
 }
 
-// Workgroups to balance over: one per compute unit (every decode variant uses
-// more than half of a CU's 160 KiB of LDS, so one workgroup fits per CU).
-mla_status worker_count(const mla_plan_opts* opts, int32_t* workers) {
+// Workgroups to balance over: CUs x decode workgroups resident per CU.  With
+// an explicit opts->num_cus (host-only planning) the per-CU count comes from
+// the kernel's LDS footprint; on a device it comes from the occupancy query.
+mla_status worker_count(const mla_plan_opts* opts, int32_t num_heads, int32_t* workers) {
   int32_t cus = opts ? opts->num_cus : 0;
   if (cus < 0) return MLA_ERR_INVALID_ARG;
+  mla_gpu::DecodeConfig cfg{};
+  if (mla_gpu::decode_config(num_heads, &cfg) != 0) return MLA_ERR_UNSUPPORTED;
+  int32_t per_cu = std::max(1, (160 * 1024) / cfg.lds_bytes);
   if (cus == 0) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    per_cu = mla_gpu::decode_blocks_per_cu(num_heads);
   }
-  int32_t w = cus;
+  int32_t w = cus * per_cu;
   if (opts && opts->max_workers > 0) w = std::min(w, opts->max_workers);
   if (w <= 0) return MLA_ERR_INVALID_ARG;
   *workers = w;
@@ -106,11 +112,14 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
   if (batch < 0 || !supported_heads(num_heads)) return 0;
   if (opts && opts->force_splits < 0) return 0;
   int32_t workers = 0;
-  if (worker_count(opts, &workers) != MLA_OK) return 0;
+  if (worker_count(opts, num_heads, &workers) != MLA_OK) return 0;
   mla::PlanParams pp;
   pp.num_heads = num_heads;
   pp.num_workers = workers;
   pp.force_splits = opts ? opts->force_splits : 0;
+  mla_gpu::DecodeConfig cfg{};
+  if (mla_gpu::decode_config(num_heads, &cfg) != 0) return 0;
+  pp.max_splits = std::min<int32_t>(256, cfg.lds_bytes / (4 * num_heads));
   const int64_t nseg = mla::max_segments(batch, pp);
   const int64_t nparts = mla::max_partials(batch, pp);
   return layout_for(nseg, workers, batch, nparts, num_heads).total;
@@ -140,7 +149,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
     return MLA_ERR_UNSUPPORTED;
   }
   int32_t workers = 0;
-  mla_status st = worker_count(opts, &workers);
+  mla_status st = worker_count(opts, num_heads, &workers);
   if (st != MLA_OK) {
     delete p;
     return st;
@@ -151,6 +160,8 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   pp.num_workers = workers;
   pp.granularity = p->cfg.tile;
   pp.force_splits = opts ? opts->force_splits : 0;
+  // the merge of a split request keeps one float per (chunk, head) in LDS
+  pp.max_splits = std::min<int32_t>(256, p->cfg.lds_bytes / (4 * num_heads));
   static const int32_t kZero = 0;
   if (mla::build_plan(kv_indptr_host, batch > 0 ? kv_last_page_len_host : &kZero, batch, pp,
                       &p->plan) != 0) {
@@ -162,17 +173,16 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          num_heads);
 
-  // stage the work list: segments | worker_ptr | combine list
+  // stage the work list: segments | worker_ptr | zeroed arrival counters
   p->host_meta.assign(p->layout.meta_bytes, 0);
   for (size_t i = 0; i < pl.segments.size(); ++i) {
-    const int32_t v[4] = {pl.segments[i].request, pl.segments[i].begin, pl.segments[i].end,
-                          pl.segments[i].slot};
-    std::memcpy(p->host_meta.data() + p->layout.segs + i * 16, v, 16);
+    const mla::Segment& g = pl.segments[i];
+    const int32_t v[8] = {g.request, g.begin, g.end, g.slot, g.split_request, g.first_slot,
+                          g.num_splits, 0};
+    std::memcpy(p->host_meta.data() + p->layout.segs + i * 32, v, 32);
   }
   std::memcpy(p->host_meta.data() + p->layout.wptr, pl.worker_ptr.data(),
               pl.worker_ptr.size() * 4);
-  if (!pl.combine.empty())
-    std::memcpy(p->host_meta.data() + p->layout.comb, pl.combine.data(), pl.combine.size() * 4);
 
   if (workspace) {
     if (workspace_bytes < p->layout.total) {
@@ -221,6 +231,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.lse = lse;
   a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
   a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
+  a.counters = reinterpret_cast<int32_t*>(ws + p->layout.counters);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.page_shift = p->page_shift;
   if (p->ev_before) {
@@ -234,18 +245,6 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   if (p->ev_after) {
     hipError_t e = hipEventRecord(p->ev_after, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  const int32_t ncomb = (int32_t)(p->plan.combine.size() / 4);
-  if (ncomb > 0) {
-    mla_gpu::CombineArgs c;
-    c.comb = reinterpret_cast<const int4*>(ws + p->layout.comb);
-    c.part_o = a.part_o;
-    c.part_lse = a.part_lse;
-    c.o = a.o;
-    c.lse = lse;
-    c.num_heads = p->heads;
-    hipError_t e = mla_gpu::launch_combine(c, ncomb, s);
-    if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return MLA_OK;
 }

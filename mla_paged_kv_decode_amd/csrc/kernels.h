@@ -1,4 +1,4 @@
-// Launch interface of the gfx950 decode and combine kernels (internal to the
+// Launch interface of the gfx950 decode kernel (internal to the
 // library; the public C ABI is include/mla_decode.h).
 #pragma once
 
@@ -16,32 +16,28 @@ struct DecodeArgs {
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const int32_t* kv_last_page_len;
-  const int4* segs;           // {request, begin, end, slot}
+  const int4* segs;           // 8 ints each: request, begin, end, slot, split index,
+                              // first slot, number of chunks, 0
   const int32_t* worker_ptr;  // grid + 1
   uint16_t* o;                // bf16 [B, H, 512]
   float* lse;                 // [B, H]
   float* part_o;              // [slots, H, 512]
   float* part_lse;            // [slots, H]
+  int32_t* counters;          // arrival counter per split request (0 between launches)
   float scale_log2;           // sm_scale * log2(e)
   int32_t page_shift;         // log2(page_size)
-};
-
-struct CombineArgs {
-  const int4* comb;  // {request, first slot, count, 0}
-  const float* part_o;
-  const float* part_lse;
-  uint16_t* o;
-  float* lse;
-  int32_t num_heads;
 };
 
 struct DecodeConfig {
   int32_t waves;  // waves per workgroup
   int32_t tile;   // tokens per KV tile = split granularity
+  int32_t lds_bytes;  // LDS per workgroup (also bounds the split merge scratch)
 };
 
 int decode_config(int num_heads, DecodeConfig* cfg);
+// Workgroups of the decode kernel that fit on one CU (HIP occupancy query on
+// the current device; an LDS-based estimate if the query fails).
+int decode_blocks_per_cu(int num_heads);
 hipError_t launch_decode(int num_heads, const DecodeArgs& a, int grid, hipStream_t stream);
-hipError_t launch_combine(const CombineArgs& a, int num_split_requests, hipStream_t stream);
 
 }  // namespace mla_gpu

@@ -30,8 +30,12 @@
 //
 // Output: each segment is either a whole request (o bf16 and lse fp32 written
 // directly) or a chunk of one (normalised fp32 partial O and its LSE written to
-// a partial slot).  The combine kernel merges the chunks of a request in
-// chunk order, weighting each by exp(LSE_i - LSE), which is deterministic.
+// a partial slot).  The workgroup that finishes the last chunk of a split
+// request (an arrival counter per request, behind agent-scope release/acquire
+// fences so that partials written on other XCDs are visible) merges the
+// chunks in chunk order, weighting each by exp(LSE_i - LSE); which workgroup
+// does it never changes the arithmetic, so results are deterministic.  The
+// counter is reset by that workgroup, ready for the next launch.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,6 +48,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -63,15 +68,25 @@ __device__ __forceinline__ void vm_wait_n() {
 
 // Wait until tile `it` has landed in LDS, given that `later` tiles were issued
 // after it, each with ITEMS loads from this wave.
-template <int ITEMS>
+template <int ITEMS, int MAXLATER>
 __device__ __forceinline__ void wait_tile(int later) {
-  static_assert(3 * ITEMS < 64, "vmcnt range");
-  switch (later) {
-    case 0: vm_wait_n<0>(); break;
-    case 1: vm_wait_n<ITEMS>(); break;
-    case 2: vm_wait_n<2 * ITEMS>(); break;
-    default: vm_wait_n<3 * ITEMS>(); break;
+  static_assert(MAXLATER * ITEMS < 64, "vmcnt range");
+  if constexpr (MAXLATER >= 3) {
+    if (later >= 3) {
+      vm_wait_n<3 * ITEMS>();
+      return;
+    }
   }
+  if constexpr (MAXLATER >= 2) {
+    if (later == 2) {
+      vm_wait_n<2 * ITEMS>();
+      return;
+    }
+  }
+  if (later == 1)
+    vm_wait_n<ITEMS>();
+  else
+    vm_wait_n<0>();
 }
 
 // Workgroup barrier for LDS hand-off.  __syncthreads() also fences global
@@ -106,6 +121,30 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// Device-coherent access to the split partials.  Partials are written and
+// read with the sc1 cache policy (coherent at device scope, as for agent-scope
+// atomic loads and stores), so a workgroup on another XCD sees them without a
+// cache-wide L2 writeback or invalidate, which would also evict the KV data
+// other workgroups are streaming.
+constexpr int kCoherent = 16;  // cache-policy bit SC1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ void store_coherent(const __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ void store_coherent(const __amdgpu_buffer_rsrc_t r, uint32_t off,
+                                               float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kCoherent);
+}
+__device__ __forceinline__ f32x4 load_coherent4(const __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
+}
+__device__ __forceinline__ float load_coherent1(const __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
+}
+
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ (r >> 3); }
 
 __device__ __forceinline__ float wave_max_16(float v) {
@@ -121,6 +160,209 @@ __device__ __forceinline__ float wave_sum_16(float v) {
   return v;
 }
 
+// Merge the n partials (slots slot0 .. slot0 + n - 1, in that order) of
+// request b: LSE = M + ln sum_i exp(LSE_i - M), O = sum_i exp(LSE_i - LSE) O_i.
+// `wbuf` is LDS scratch of n * H floats.  Every load of a phase is issued
+// before any result is used, so the merge costs a few memory round trips.
+template <int H, int NT>
+__device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int slot0, int n,
+                                                int tid, float* wbuf) {
+  // 1. the n * H partial LSEs (consecutive slots are contiguous)
+  const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + (size_t)slot0 * H);
+  for (int x = tid; x < n * H; x += NT) wbuf[x] = load_coherent1(rl, (uint32_t)(x * 4));
+  lds_barrier();
+  // 2. per head: merged LSE and the weights exp(LSE_i - LSE), in place
+  for (int hd = tid; hd < H; hd += NT) {
+    float M = -INFINITY;
+    for (int i = 0; i < n; ++i) M = fmaxf(M, wbuf[i * H + hd]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float sum = 0.f;
+    for (int i = 0; i < n; ++i) sum += __expf(wbuf[i * H + hd] - Mu);
+    const bool empty = !(sum > 0.f);
+    const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
+    for (int i = 0; i < n; ++i) wbuf[i * H + hd] = empty ? 0.f : __expf(wbuf[i * H + hd] - lse_v);
+    a.lse[(size_t)b * H + hd] = lse_v;
+  }
+  lds_barrier();
+  // 3. O, item = (head, 8 columns); splits in groups of 4 with all loads in flight
+  const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + (size_t)slot0 * H * 512);
+  for (int e = tid; e < H * 64; e += NT) {
+    const int hd = e >> 6;
+    const int col = (e & 63) * 8;
+    float o8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o8[j] = 0.f;
+    for (int i0 = 0; i0 < n; i0 += 4) {
+      f32x4 x[4][2];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int i = min(i0 + u, n - 1);
+        const uint32_t off = (uint32_t)(((i * H + hd) * 512 + col) * 4);
+        x[u][0] = load_coherent4(ro, off);
+        x[u][1] = load_coherent4(ro, off + 16);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (i0 + u < n) {
+          const float w = wbuf[(i0 + u) * H + hd];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            o8[j] += w * x[u][0][j];
+            o8[4 + j] += w * x[u][1][j];
+          }
+        }
+      }
+    }
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
+    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
+  }
+}
+
+// End of a segment: normalise (merging the TS token-split waves of every head
+// group through LDS), then write o/lse for a whole request or the partial of a
+// chunk; the workgroup that completes the last chunk of a split request merges
+// its partials.  acc holds O^T (lane = head lane & 15, columns 16 cb + 4 (lane
+// >> 4) + i), m_run the log2-domain running max, l_run this lane's share of
+// the running sum.
+constexpr int kMergeStride = 512 + 4;  // floats per head row in the merge area
+
+template <int H, int HG, int TS>
+constexpr int merge_bytes() {
+  return TS > 1 ? HG * TS * 16 * kMergeStride * 4 + HG * TS * 16 * 8 : 0;
+}
+
+template <int H, int HG, int TS, int NT>
+__device__ __forceinline__ void segment_epilogue(const DecodeArgs& a, f32x4 (&acc)[32],
+                                                 float m_run, float l_run, int b, int slot,
+                                                 int split_req, int slot0, int nsplit, int wave,
+                                                 int lane, int tid, uint8_t* smem, int* s_last) {
+  constexpr int kWaves = HG * TS;
+  const int hg = wave % HG;
+  const int ts = wave / HG;
+  const int qr = lane & 15;
+  const int head = hg * 16 + qr;
+  const float l_tot = wave_sum_16(l_run);
+  if constexpr (TS == 1) {
+    const bool empty = !(l_tot > 0.f);
+    const float inv = empty ? 0.f : 1.f / l_tot;
+    const float lse_v = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
+    const size_t orow = (size_t)b * H + head;
+    if (slot < 0) {
+      uint16_t* op = a.o + orow * 512;
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb) {
+        bf16x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[cb][i] * inv);
+        *reinterpret_cast<bf16x4*>(op + cb * 16 + 4 * (lane >> 4)) = v;
+      }
+      if (lane < 16) a.lse[orow] = lse_v;
+    } else {
+      const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + ((size_t)slot * H) * 512);
+      const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + (size_t)slot * H);
+#pragma unroll
+      for (int cb = 0; cb < 32; ++cb)
+        store_coherent(ro, (uint32_t)((head * 512 + cb * 16 + 4 * (lane >> 4)) * 4),
+                       acc[cb] * inv);
+      if (lane < 16) store_coherent(rl, (uint32_t)(head * 4), lse_v);
+    }
+  } else {
+    // merge the TS token-split waves of each head group through LDS
+    float* mo = reinterpret_cast<float*>(smem);
+    float* mstat = mo + kWaves * 16 * kMergeStride;  // [wave][16][2] (m, l)
+    float* mine = mo + wave * 16 * kMergeStride;
+#pragma unroll
+    for (int cb = 0; cb < 32; ++cb)
+      *reinterpret_cast<f32x4*>(mine + qr * kMergeStride + cb * 16 + 4 * (lane >> 4)) =
+          acc[cb];
+    if (lane < 16) {
+      mstat[(wave * 16 + lane) * 2 + 0] = m_run;
+      mstat[(wave * 16 + lane) * 2 + 1] = l_tot;
+    }
+    lds_barrier();
+    // wave (hg, ts) finalises columns [128*ts, 128*ts + 128) of its 16 heads
+    constexpr int kCols = 512 / TS;
+    constexpr int kIters = 16 * kCols / 8 / 64;
+#pragma unroll
+    for (int k = 0; k < kIters; ++k) {
+      const int e = k * 64 + lane;
+      const int hh = e / (kCols / 8);
+      const int col = ts * kCols + (e % (kCols / 8)) * 8;
+      float mw[TS];
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < TS; ++u) {
+        mw[u] = mstat[((u * HG + hg) * 16 + hh) * 2 + 0];
+        M = fmaxf(M, mw[u]);
+      }
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float L = 0.f;
+      float o8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o8[i] = 0.f;
+#pragma unroll
+      for (int u = 0; u < TS; ++u) {
+        const float w = __builtin_amdgcn_exp2f(mw[u] - Mu);
+        L += w * mstat[((u * HG + hg) * 16 + hh) * 2 + 1];
+        const float* src = mo + (u * HG + hg) * 16 * kMergeStride + hh * kMergeStride + col;
+        const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o8[i] += w * x0[i];
+          o8[4 + i] += w * x1[i];
+        }
+      }
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      const float lse_v = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
+      const int hd = hg * 16 + hh;
+      if (slot < 0) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = (__bf16)(o8[i] * inv);
+        *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
+        if (ts == 0 && (e % (kCols / 8)) == 0) a.lse[(size_t)b * H + hd] = lse_v;
+      } else {
+        const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + ((size_t)slot * H) * 512);
+        f32x4 y0, y1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          y0[i] = o8[i] * inv;
+          y1[i] = o8[4 + i] * inv;
+        }
+        store_coherent(ro, (uint32_t)((hd * 512 + col) * 4), y0);
+        store_coherent(ro, (uint32_t)((hd * 512 + col + 4) * 4), y1);
+        if (ts == 0 && (e % (kCols / 8)) == 0)
+          store_coherent(coherent_rsrc(a.part_lse + (size_t)slot * H), (uint32_t)(hd * 4), lse_v);
+      }
+    }
+    lds_barrier();  // merge area free before the next segment's loads
+  }
+
+  // ---- last chunk of a split request merges the request's partials --------
+  if (slot >= 0) {
+    vm_wait_n<0>();  // this wave's coherent partial stores have completed
+    lds_barrier();
+    if (tid == 0) {
+      // system scope: the add is performed at memory, coherent for every XCD
+      const int prev = __hip_atomic_fetch_add(a.counters + split_req, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_SYSTEM);
+      const int last = prev == nsplit - 1;
+      if (last)
+        __hip_atomic_store(a.counters + split_req, 0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_SYSTEM);
+      *s_last = last;
+    }
+    lds_barrier();
+    if (*s_last) combine_request<H, NT>(a, b, slot0, nsplit, tid,
+                                                reinterpret_cast<float*>(smem));
+    lds_barrier();  // merge scratch free before the next segment's loads
+  }
+}
+
 template <int HG, int TS, int MB, int NSTAGE>
 struct DecodeShape {
   static constexpr int kPvBatch = HG * TS > 4 ? 2 : 8;  // PV operand reads in flight
@@ -133,8 +375,7 @@ struct DecodeShape {
   static constexpr int kItemsMin = kItems / kWaves;
   static constexpr int kItemsRem = kItems % kWaves;
   static constexpr int kStageBytes = kTile * kRowBytes;
-  static constexpr int kMergeStride = 512 + 4;  // floats per head row in the merge area
-  static constexpr int kMergeBytes = TS > 1 ? kWaves * 16 * kMergeStride * 4 + kWaves * 16 * 8 : 0;
+  static constexpr int kMergeBytes = merge_bytes<16 * HG, HG, TS>();
   static constexpr int kLdsBytes =
       (NSTAGE * kStageBytes > kMergeBytes) ? NSTAGE * kStageBytes : kMergeBytes;
   static constexpr bool kOneBarrier = NSTAGE >= 3;
@@ -149,6 +390,7 @@ __global__ void __launch_bounds__(64 * HG * TS)
   constexpr int H = S::kHeads;
   constexpr int T = S::kTile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
+  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -182,11 +424,14 @@ __global__ void __launch_bounds__(64 * HG * TS)
   const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
-    const int* sgp = reinterpret_cast<const int*>(a.segs + si);
+    const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
     const int b = ld_const(sgp + 0);
     const int t0 = ld_const(sgp + 1);
     const int send = ld_const(sgp + 2);
     const int slot = ld_const(sgp + 3);
+    const int split_req = ld_const(sgp + 4);
+    const int slot0 = ld_const(sgp + 5);
+    const int nsplit = ld_const(sgp + 6);
     const int pbeg = ld_const(a.kv_indptr + b);
     const int npg = ld_const(a.kv_indptr + b + 1) - pbeg;
     const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + b) : 0;
@@ -200,9 +445,27 @@ __global__ void __launch_bounds__(64 * HG * TS)
     for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // issue the direct-to-LDS loads of tile k into stage st
+    // Page numbers of the row groups of tile k (one scalar load per group;
+    // a group past the end reuses the group of the last valid token).
+    const int last_group = t1 > 0 ? ((t1 - 1) >> 4) << 4 : 0;
+    int pg_next[S::kGroups];
+    auto tile_pages = [&](int k) {
+      const int tile_start = t0 + k * T;
+#pragma unroll
+      for (int g = 0; g < S::kGroups; ++g) {
+        const int gs = min(tile_start + 16 * g, last_group);
+        pg_next[g] = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
+      }
+    };
+
+    // Issue the direct-to-LDS loads of tile k into stage st, then prefetch the
+    // page numbers of tile k + 1 so that the next issue does not wait on them.
     auto issue_tile = [&](int k, int st) {
       const int tile_start = t0 + k * T;
-      const int last_group = ((t1 - 1) >> 4) << 4;
+      int pg[S::kGroups];
+#pragma unroll
+      for (int g = 0; g < S::kGroups; ++g) pg[g] = pg_next[g];
+      if (k + 1 < ntiles) tile_pages(k + 1);
       uint8_t* stage = smem + st * S::kStageBytes;
       for (int j = 0; j < my_items; ++j) {
         const int item = item0 + j;
@@ -210,8 +473,10 @@ __global__ void __launch_bounds__(64 * HG * TS)
         const int blk = item - g * 18;
         const int rh = blk >= 9 ? 1 : 0;
         const int cb = blk - rh * 9;
+        int page = pg[0];
+#pragma unroll
+        for (int gg = 1; gg < S::kGroups; ++gg) page = g == gg ? pg[gg] : page;
         const int gs = min(tile_start + 16 * g, last_group);
-        const int page = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
         const int r = rh * 8 + ld_r_lo;
         const int tok = min(gs + r, t1 - 1);
         const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
@@ -225,12 +490,14 @@ __global__ void __launch_bounds__(64 * HG * TS)
     };
 
     auto wait_for = [&](int later) {
+      constexpr int kMaxLater = S::kOneBarrier ? NSTAGE - 2 : NSTAGE - 1;
       if (my_items == S::kItemsMin)
-        wait_tile<S::kItemsMin>(later);
+        wait_tile<S::kItemsMin, kMaxLater>(later);
       else
-        wait_tile<S::kItemsMin + 1>(later);
+        wait_tile<S::kItemsMin + 1, kMaxLater>(later);
     };
 
+    if (ntiles > 0) tile_pages(0);
     for (int k = 0; k < NSTAGE - 1 && k < ntiles; ++k) issue_tile(k, k);
 
     // ---- Q^T operand for head hg*16 + (lane & 15): 18 x 8 dims -----------
@@ -380,139 +647,218 @@ __global__ void __launch_bounds__(64 * HG * TS)
     if constexpr (S::kOneBarrier) lds_barrier();  // ring free before the merge / next segment
 
     // ---- epilogue -----------------------------------------------------------
-    const float l_tot = wave_sum_16(l_run);
-    if constexpr (TS == 1) {
-      const bool empty = !(l_tot > 0.f);
-      const float inv = empty ? 0.f : 1.f / l_tot;
-      const float lse_v = empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2;
-      const size_t orow = (size_t)b * H + head;
-      if (slot < 0) {
-        uint16_t* op = a.o + orow * 512;
-#pragma unroll
-        for (int cb = 0; cb < 32; ++cb) {
-          bf16x4 v;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[cb][i] * inv);
-          *reinterpret_cast<bf16x4*>(op + cb * 16 + 4 * (lane >> 4)) = v;
-        }
-        if (lane < 16) a.lse[orow] = lse_v;
-      } else {
-        const size_t prow = (size_t)slot * H + head;
-        float* op = a.part_o + prow * 512;
-#pragma unroll
-        for (int cb = 0; cb < 32; ++cb)
-          *reinterpret_cast<f32x4*>(op + cb * 16 + 4 * (lane >> 4)) = acc[cb] * inv;
-        if (lane < 16) a.part_lse[prow] = lse_v;
-      }
-    } else {
-      // merge the TS token-split waves of each head group through LDS
-      float* mo = reinterpret_cast<float*>(smem);
-      float* mstat = mo + S::kWaves * 16 * S::kMergeStride;  // [wave][16][2] (m, l)
-      float* mine = mo + wave * 16 * S::kMergeStride;
-#pragma unroll
-      for (int cb = 0; cb < 32; ++cb)
-        *reinterpret_cast<f32x4*>(mine + qr * S::kMergeStride + cb * 16 + 4 * (lane >> 4)) =
-            acc[cb];
-      if (lane < 16) {
-        mstat[(wave * 16 + lane) * 2 + 0] = m_run;
-        mstat[(wave * 16 + lane) * 2 + 1] = l_tot;
-      }
-      lds_barrier();
-      // wave (hg, ts) finalises columns [128*ts, 128*ts + 128) of its 16 heads
-      constexpr int kCols = 512 / TS;
-      constexpr int kIters = 16 * kCols / 8 / 64;
-#pragma unroll
-      for (int k = 0; k < kIters; ++k) {
-        const int e = k * 64 + lane;
-        const int hh = e / (kCols / 8);
-        const int col = ts * kCols + (e % (kCols / 8)) * 8;
-        float mw[TS];
-        float M = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < TS; ++u) {
-          mw[u] = mstat[((u * HG + hg) * 16 + hh) * 2 + 0];
-          M = fmaxf(M, mw[u]);
-        }
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f;
-        float o8[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o8[i] = 0.f;
-#pragma unroll
-        for (int u = 0; u < TS; ++u) {
-          const float w = __builtin_amdgcn_exp2f(mw[u] - Mu);
-          L += w * mstat[((u * HG + hg) * 16 + hh) * 2 + 1];
-          const float* src = mo + (u * HG + hg) * 16 * S::kMergeStride + hh * S::kMergeStride + col;
-          const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-          const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            o8[i] += w * x0[i];
-            o8[4 + i] += w * x1[i];
-          }
-        }
-        const bool empty = !(L > 0.f);
-        const float inv = empty ? 0.f : 1.f / L;
-        const float lse_v = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
-        const int hd = hg * 16 + hh;
-        if (slot < 0) {
-          bf16x8 v;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) v[i] = (__bf16)(o8[i] * inv);
-          *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
-          if (ts == 0 && (e % (kCols / 8)) == 0) a.lse[(size_t)b * H + hd] = lse_v;
-        } else {
-          float* dst = a.part_o + ((size_t)slot * H + hd) * 512 + col;
-          f32x4 y0, y1;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            y0[i] = o8[i] * inv;
-            y1[i] = o8[4 + i] * inv;
-          }
-          *reinterpret_cast<f32x4*>(dst) = y0;
-          *reinterpret_cast<f32x4*>(dst + 4) = y1;
-          if (ts == 0 && (e % (kCols / 8)) == 0) a.part_lse[(size_t)slot * H + hd] = lse_v;
-        }
-      }
-      lds_barrier();  // merge area free before the next segment's loads
-    }
+    segment_epilogue<H, HG, TS, S::kThreads>(a, acc, m_run, l_run, b, slot, split_req, slot0,
+                                              nsplit, wave, lane, tid, smem, &s_last);
   }
 }
 
-// One block per (split request, group of 4 heads); thread = (head, 8 columns).
-__global__ void __launch_bounds__(256) mla_combine_kernel(const CombineArgs a) {
-  const int4 cmb = a.comb[blockIdx.x];
-  const int b = cmb.x, slot0 = cmb.y, n = cmb.z;
-  const int hd = blockIdx.y * 4 + (threadIdx.x >> 6);
-  const int col = (threadIdx.x & 63) * 8;
-  const int H = a.num_heads;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, a.part_lse[(size_t)(slot0 + i) * H + hd]);
-  const float Mu = M == -INFINITY ? 0.f : M;
-  float sum = 0.f;
-  for (int i = 0; i < n; ++i) sum += __expf(a.part_lse[(size_t)(slot0 + i) * H + hd] - Mu);
-  const bool empty = !(sum > 0.f);
-  const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
-  float o8[8];
+
+// ---------------------------------------------------------------------------
+// Register-staged variant for 16 query heads (one head group).  The work is
+// memory bound (about 30 flop per byte of KV), so what matters is the number
+// of bytes in flight per CU and keeping the waves out of each other's way:
+//   * TS waves split a segment's 16-token groups round-robin (wave w takes
+//     groups w, w + TS, ...); each wave runs its own pipeline with no
+//     workgroup barrier until the end of the segment.
+//   * a group (16 rows x 1152 B) is fetched with 18 coalesced 16-byte loads
+//     per lane into registers, NBUF groups ahead, so the vector register file
+//     (not LDS) holds the data in flight: NBUF x 18 KiB per wave;
+//   * the group is then written to a wave-private 18 KiB LDS buffer (same
+//     swizzled layout as the LDS ring) and consumed by the QK and PV MFMAs;
+//   * Q^T (16 heads x 576) sits in LDS once per segment, [chunk][head], so the
+//     registers go to the groups in flight.
+// ---------------------------------------------------------------------------
+template <int TS, int NBUF>
+struct WaveShape {
+  static constexpr int kThreads = 64 * TS;
+  static constexpr int kBufBytes = 18 * 1024;       // one 16-row group per wave
+  static constexpr int kQBytes = 72 * 16 * 16;      // Q^T: [chunk][head] x 16 B
+  static constexpr int kQOffset = TS * kBufBytes;
+  static constexpr int kMergeBytes = merge_bytes<16, 1, TS>();
+  static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
+                                                                    : kMergeBytes;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+template <int TS, int NBUF>
+__global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeArgs a) {
+  using S = WaveShape<TS, NBUF>;
+  constexpr int H = 16;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int page_shift = a.page_shift;
+  const int page_mask = (1 << page_shift) - 1;
+  uint8_t* wbuf = smem + wave * S::kBufBytes;
+
+  // loader: lane covers row (rh * 8 + lane / 8) of block (rh, cb), 16-byte
+  // chunk cb * 8 + ((lane & 7) ^ swz(row)); it writes LDS slot `lane` of the block
+  const int ld_r_lo = lane >> 3;
+  // QK operand: token row lane & 15, chunk 4 s + (lane >> 4)
+  const int qr = lane & 15;
+  const int qk_base = (qr >> 3) * kHalfGroupBytes + (qr & 7) * 128;
+  const int qk_off_even = ((lane >> 4) ^ swz(qr)) * 16;
+  const int qk_off_odd = ((4 + (lane >> 4)) ^ swz(qr)) * 16;
+  // PV operand (transpose read), as in the ring kernel
+  const int tr_r = 4 * (lane >> 4) + ((lane >> 2) & 3);
+  const int tr_q = lane & 3;
+  const int tr_base = (tr_r >> 3) * kHalfGroupBytes + (tr_r & 7) * 128 + (tr_q & 1) * 8;
+  int tr_off[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o8[i] = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const float li = a.part_lse[(size_t)(slot0 + i) * H + hd];
-    const float w = empty ? 0.f : __expf(li - lse_v);
-    const float* src = a.part_o + ((size_t)(slot0 + i) * H + hd) * 512 + col;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(src);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 4);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o8[j] += w * x0[j];
-      o8[4 + j] += w * x1[j];
+  for (int A = 0; A < 4; ++A) tr_off[A] = tr_base + (((2 * A) | (tr_q >> 1)) ^ swz(tr_r)) * 16;
+
+  const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
+  const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
+
+  for (int si = seg_begin; si < seg_end; ++si) {
+    const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
+    const int b = ld_const(sgp + 0);
+    const int t0 = ld_const(sgp + 1);
+    const int send = ld_const(sgp + 2);
+    const int slot = ld_const(sgp + 3);
+    const int split_req = ld_const(sgp + 4);
+    const int slot0 = ld_const(sgp + 5);
+    const int nsplit = ld_const(sgp + 6);
+    const int pbeg = ld_const(a.kv_indptr + b);
+    const int npg = ld_const(a.kv_indptr + b + 1) - pbeg;
+    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + b) : 0;
+    const int t1 = min(send, ldev);
+    const int ngroups = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
+    const int nmine = ngroups > wave ? (ngroups - 1 - wave) / TS + 1 : 0;
+
+    // Q^T for the request into LDS: item (chunk c, head h) at (c * 16 + h) * 16
+    uint8_t* qlds = smem + S::kQOffset;
+    lds_barrier();  // previous segment's merge / combine done with this LDS
+    for (int x = tid; x < 72 * 16; x += S::kThreads) {
+      const int c = x >> 4, h = x & 15;
+      const u32x4 v = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
+                             : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
+      *reinterpret_cast<u32x4*>(qlds + x * 16) = v;
     }
-  }
-  bf16x8 v;
+    lds_barrier();
+    const uint8_t* qbase = qlds + ((lane >> 4) * 16 + qr) * 16;  // + s * 1024 for step s
+
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 acc[32];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
-  *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
-  if ((threadIdx.x & 63) == 0) a.lse[(size_t)b * H + hd] = lse_v;
+    for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Fetch this wave's j-th group into registers.  Every call issues the same
+    // 18 loads, also past the last group (then from a fixed, valid address),
+    // so that the number of loads in flight is the same on every path and the
+    // compiler's vmcnt waits only cover the group being consumed.
+    const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q_nope + (size_t)b * H * 512);
+    auto fetch = [&](int j, u32x4 (&st)[18]) __attribute__((always_inline)) {
+      const bool live = j < nmine;
+      const int gs = live ? t0 + 16 * (wave + TS * j) : t0;
+      const int page = live ? ld_const(a.kv_indices + pbeg + (gs >> page_shift)) : 0;
+#pragma unroll
+      for (int blk = 0; blk < 18; ++blk) {
+        const int rh = blk >= 9 ? 1 : 0;
+        const int cb = blk - rh * 9;
+        const int r = rh * 8 + ld_r_lo;
+        const int tok = min(gs + r, t1 - 1);
+        const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
+        const int c = cb * 8 + ((lane & 7) ^ swz(r));
+        const uint8_t* src = c < 64 ? a.ckv + (row * 512 + c * 8) * 2
+                                    : a.kpe + (row * 64 + (c - 64) * 8) * 2;
+        st[blk] = *reinterpret_cast<const u32x4*>(live ? src : dummy);
+      }
+    };
+
+    // Consume group j from registers st: LDS write and refill (always, so the
+    // memory queue looks the same on every path), then QK, online softmax and
+    // PV if the group exists.
+    auto consume = [&](int j, u32x4 (&st)[18]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int blk = 0; blk < 18; ++blk)
+        *reinterpret_cast<u32x4*>(wbuf + blk * 1024 + lane * 16) = st[blk];
+      fetch(j + NBUF, st);  // registers free again: next group in flight
+      if (j >= nmine) return;
+
+      // QK: S^T[16 tokens][16 heads], two partial chains; K and Q^T from LDS
+      const uint8_t* gbase = wbuf + qk_base;
+      f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s0 = 0; s0 < 18; s0 += 6) {
+        bf16x8 kf[6], qf[6];
+#pragma unroll
+        for (int u = 0; u < 6; ++u) {
+          const int s = s0 + u;
+          kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)(gbase + (s >> 1) * 1024 + ((s & 1) ? qk_off_odd : qk_off_even)));
+          qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>((const LDS_AS uint8_t*)(qbase + s * 1024));
+        }
+#pragma unroll
+        for (int u = 0; u < 6; u += 2) {
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[u], c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u + 1], qf[u + 1], c1, 0, 0, 0);
+        }
+      }
+      f32x4 sacc = c0 + c1;
+
+      // online softmax, log2 domain; rows past the segment end are masked
+      const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = (row0 + i < t1) ? sacc[i] * a.scale_log2 : -INFINITY;
+        sacc[i] = x;
+        tmax = fmaxf(tmax, x);
+      }
+      tmax = wave_max_16(tmax);
+      const float m_new = fmaxf(m_run, tmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float psum = 0.f;
+      bf16x4 pb;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sacc[i] - m_use);
+        psum += p;
+        pb[i] = (__bf16)p;
+      }
+      l_run = l_run * alpha + psum;
+      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+      }
+      m_run = m_new;
+
+      // PV: O^T[c][h] += V^T[c][t] P^T[t][h]
+      const s16x4 pv = __builtin_bit_cast(s16x4, pb);
+#pragma unroll
+      for (int c8 = 0; c8 < 32; c8 += 8) {
+        s16x4 vf[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int cb = c8 + u;
+          vf[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_AS s16x4*)((LDS_AS uint8_t*)(wbuf + (cb >> 2) * 1024 + tr_off[cb & 3])));
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          acc[c8 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[u], pv, acc[c8 + u], 0, 0, 0);
+      }
+    };
+
+    static_assert(NBUF == 2, "two register buffers, unrolled by hand");
+    u32x4 stA[18], stB[18];
+    fetch(0, stA);
+    fetch(1, stB);
+    for (int j = 0; j < nmine; j += 2) {
+      consume(j, stA);
+      consume(j + 1, stB);
+    }
+
+    lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
+    segment_epilogue<H, 1, TS, S::kThreads>(a, acc, m_run, l_run, b, slot, split_req, slot0,
+                                             nsplit, wave, lane, tid, smem, &s_last);
+  }
 }
 
 // ---------------------------------------------------------------- launchers
@@ -524,31 +870,90 @@ static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t s
   return hipGetLastError();
 }
 
+// Kernel shape per head count: <head groups, token-split waves, row groups per
+// wave per tile, ring stages>.
+// 16 heads: the register-staged kernel <waves, groups in flight per wave>
+#ifndef MLA_WAVE_H16
+#define MLA_WAVE_H16 4, 2
+#endif
+#ifndef MLA_CFG_H32
+#define MLA_CFG_H32 2, 2, 2, 2
+#endif
+#ifndef MLA_CFG_H64
+#define MLA_CFG_H64 4, 1, 2, 3
+#endif
+#ifndef MLA_CFG_H128
+#define MLA_CFG_H128 8, 1, 2, 3
+#endif
+
+template <int TS, int NBUF>
+static hipError_t launch_wave_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((mla_decode_wave_kernel<TS, NBUF>), dim3(grid), dim3(64 * TS), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int TS, int NBUF>
+static DecodeConfig wave_config_of() {
+  return DecodeConfig{TS, 16, WaveShape<TS, NBUF>::kLdsBytes};
+}
+
+template <int TS, int NBUF>
+static int wave_occupancy_of() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&mla_decode_wave_kernel<TS, NBUF>), 64 * TS, 0) !=
+          hipSuccess ||
+      n < 1)
+    n = (160 * 1024) / WaveShape<TS, NBUF>::kLdsBytes;
+  return n < 1 ? 1 : n;
+}
+
+template <int HG, int TS, int MB, int NSTAGE>
+static DecodeConfig config_of() {
+  using S = DecodeShape<HG, TS, MB, NSTAGE>;
+  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
+}
+
+template <int HG, int TS, int MB, int NSTAGE>
+static int occupancy_of() {
+  using S = DecodeShape<HG, TS, MB, NSTAGE>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&mla_decode_bf16_kernel<HG, TS, MB, NSTAGE>),
+          S::kThreads, 0) != hipSuccess ||
+      n < 1)
+    n = (160 * 1024) / S::kLdsBytes;
+  return n < 1 ? 1 : n;
+}
+
+int decode_blocks_per_cu(int num_heads) {
+  switch (num_heads) {
+    case 16: return wave_occupancy_of<MLA_WAVE_H16>();
+    case 32: return occupancy_of<MLA_CFG_H32>();
+    case 64: return occupancy_of<MLA_CFG_H64>();
+    case 128: return occupancy_of<MLA_CFG_H128>();
+    default: return 1;
+  }
+}
+
 int decode_config(int num_heads, DecodeConfig* cfg) {
   switch (num_heads) {
-    case 16: *cfg = DecodeConfig{4, 64}; return 0;
-    case 32: *cfg = DecodeConfig{4, 64}; return 0;
-    case 64: *cfg = DecodeConfig{4, 32}; return 0;
-    case 128: *cfg = DecodeConfig{8, 32}; return 0;
+    case 16: *cfg = wave_config_of<MLA_WAVE_H16>(); return 0;
+    case 32: *cfg = config_of<MLA_CFG_H32>(); return 0;
+    case 64: *cfg = config_of<MLA_CFG_H64>(); return 0;
+    case 128: *cfg = config_of<MLA_CFG_H128>(); return 0;
     default: return -1;
   }
 }
 
 hipError_t launch_decode(int num_heads, const DecodeArgs& a, int grid, hipStream_t stream) {
   switch (num_heads) {
-    case 16: return launch_decode_cfg<1, 4, 1, 2>(a, grid, stream);
-    case 32: return launch_decode_cfg<2, 2, 2, 2>(a, grid, stream);
-    case 64: return launch_decode_cfg<4, 1, 2, 3>(a, grid, stream);
-    case 128: return launch_decode_cfg<8, 1, 2, 3>(a, grid, stream);
+    case 16: return launch_wave_cfg<MLA_WAVE_H16>(a, grid, stream);
+    case 32: return launch_decode_cfg<MLA_CFG_H32>(a, grid, stream);
+    case 64: return launch_decode_cfg<MLA_CFG_H64>(a, grid, stream);
+    case 128: return launch_decode_cfg<MLA_CFG_H128>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
-}
-
-hipError_t launch_combine(const CombineArgs& a, int num_split_requests, hipStream_t stream) {
-  if (num_split_requests <= 0) return hipSuccess;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3(num_split_requests, a.num_heads / 4), dim3(256), 0,
-                     stream, a);
-  return hipGetLastError();
 }
 
 }  // namespace mla_gpu

@@ -31,7 +31,7 @@ struct Piece {
 };
 
 void cut_requests(const std::vector<int64_t>& len, int64_t chunk, int32_t gran, int32_t heads,
-                  int32_t force, std::vector<Piece>* pieces) {
+                  int32_t force, int32_t max_splits, std::vector<Piece>* pieces) {
   pieces->clear();
   for (size_t b = 0; b < len.size(); ++b) {
     const int64_t L = len[b];
@@ -42,6 +42,7 @@ void cut_requests(const std::vector<int64_t>& len, int64_t chunk, int32_t gran, 
       else
         n = (L + chunk - 1) / chunk;
       if (n < 1) n = 1;
+      if (n > max_splits) n = max_splits;
     }
     // near-equal chunks with boundaries on multiples of gran
     int64_t step = (L + n - 1) / n;
@@ -85,7 +86,7 @@ int64_t assign(const std::vector<Piece>& pieces, int32_t workers, std::vector<in
 }  // namespace
 
 int64_t max_segments(int32_t batch, const PlanParams& p) {
-  if (p.force_splits > 0) return (int64_t)batch * p.force_splits;
+  if (p.force_splits > 0) return (int64_t)batch * std::min(p.force_splits, p.max_splits);
   return (int64_t)batch + 2 * (int64_t)p.num_workers;
 }
 
@@ -94,7 +95,7 @@ int64_t max_partials(int32_t batch, const PlanParams& p) { return max_segments(b
 int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
                    const PlanParams& p, Plan* out) {
   if (!kv_indptr || !kv_last_page_len || !out || batch < 0 || p.num_workers <= 0 ||
-      p.granularity <= 0 || p.page_size <= 0 || p.num_heads <= 0)
+      p.granularity <= 0 || p.page_size <= 0 || p.num_heads <= 0 || p.max_splits < 1)
     return -1;
   if (kv_indptr[0] != 0) return -1;
   std::vector<int64_t> len((size_t)batch);
@@ -120,7 +121,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
   int64_t best = -1;
 
   if (p.force_splits > 0) {
-    cut_requests(len, 0, gran, p.num_heads, p.force_splits, &best_pieces);
+    cut_requests(len, 0, gran, p.num_heads, p.force_splits, p.max_splits, &best_pieces);
     assign(best_pieces, p.num_workers, &best_owner);
   } else {
     // candidate chunk sizes: gran * {1, 2, 3, 4, 6, 8, 12, 16, ...} up to max_len
@@ -134,7 +135,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
     }
     std::sort(cands.begin(), cands.end(), std::greater<int64_t>());  // fewest cuts first
     for (int64_t c : cands) {
-      cut_requests(len, c, gran, p.num_heads, 0, &pieces);
+      cut_requests(len, c, gran, p.num_heads, 0, p.max_splits, &pieces);
       if ((int64_t)pieces.size() > seg_cap) continue;
       const int64_t worst = assign(pieces, p.num_workers, &owner);
       if (best < 0 || worst < best) {
@@ -165,6 +166,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
   // partial slots: consecutive per split request, in token order (cut_requests
   // emits the pieces of a request consecutively, in token order)
   std::vector<int32_t> first_slot((size_t)batch, -1), first_piece((size_t)batch, -1);
+  std::vector<int32_t> split_index((size_t)batch, -1);
   out->combine.clear();
   int32_t slots = 0;
   for (size_t i = 0; i < best_pieces.size(); ++i) {
@@ -172,6 +174,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
     if (first_piece[pc.request] < 0) first_piece[pc.request] = (int32_t)i;
     if (pc.nsplit > 1 && first_slot[pc.request] < 0) {
       first_slot[pc.request] = slots;
+      split_index[pc.request] = (int32_t)(out->combine.size() / 4);
       out->combine.push_back(pc.request);
       out->combine.push_back(slots);
       out->combine.push_back(pc.nsplit);
@@ -187,6 +190,9 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
     s.begin = pc.begin;
     s.end = pc.end;
     s.slot = pc.nsplit > 1 ? first_slot[pc.request] + ((int32_t)i - first_piece[pc.request]) : -1;
+    s.split_request = split_index[pc.request];
+    s.first_slot = first_slot[pc.request];
+    s.num_splits = pc.nsplit;
     const int32_t w = remap[best_owner[i]];
     out->segments[fill[w]++] = s;
   }

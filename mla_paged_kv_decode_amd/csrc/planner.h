@@ -19,6 +19,7 @@ struct PlanParams {
   int32_t num_workers = 0;   // grid size to balance over
   int32_t granularity = 64;  // chunk boundaries are multiples of this many tokens
   int32_t force_splits = 0;  // > 0: every request cut into this many chunks (at most)
+  int32_t max_splits = 256;  // chunks per request at most (the merge keeps n * H floats in LDS)
 };
 
 struct Segment {
@@ -26,6 +27,9 @@ struct Segment {
   int32_t begin;  // first logical token
   int32_t end;    // one past the last token
   int32_t slot;   // partial slot, or -1 when this segment is the whole request
+  int32_t split_request;  // index of the request among the split ones, or -1
+  int32_t first_slot;     // first partial slot of the request (split requests)
+  int32_t num_splits;     // chunks of the request (1 when not split)
 };
 
 struct Plan {

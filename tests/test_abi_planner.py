@@ -25,7 +25,8 @@ def lib():
 
 def test_exports_match_header(lib):
     hdr = open(os.path.join(ROOT, "include", "mla_decode.h")).read()
-    declared = set(re.findall(r"\b(mla_[a-z_]+)\s*\(", hdr))
+    hdr += open(os.path.join(ROOT, "include", "mla_peaks.h")).read()
+    declared = set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", hdr))
     assert declared == set(mla.EXPORTED_SYMBOLS)
     for name in declared:
         assert hasattr(lib, name), name
@@ -87,7 +88,7 @@ def test_plan_covers_each_token_once(lib, heads, P, lengths):
 def test_plan_balances_uniform_batch(lib):
     ip, lp = _table([4096] * 64, 64)
     plan = mla.Plan(ip, lp, 16, 64, num_cus=256)
-    seg, wp, info = _check_plan(plan, [4096] * 64, 64)
+    seg, wp, info = _check_plan(plan, [4096] * 64, plan.info()["granularity"])
     assert info["num_workers"] == 256
     assert set((seg[:, 2] - seg[:, 1]).tolist()) == {1024}
 
@@ -104,9 +105,18 @@ def test_force_splits(lib):
     lengths = [1000, 64, 1, 0]
     ip, lp = _table(lengths, 16)
     plan = mla.Plan(ip, lp, 16, 16, num_cus=8, force_splits=3)
-    seg, wp, info = _check_plan(plan, lengths, 64)
+    seg, wp, info = _check_plan(plan, lengths, plan.info()["granularity"])
     counts = {b: int((seg[:, 0] == b).sum()) for b in range(4)}
-    assert counts == {0: 3, 1: 1, 2: 1, 3: 1}
+    g = info["granularity"]
+
+    def pieces(L):  # near-equal chunks on multiples of the granularity
+        if L == 0:
+            return 1
+        n = min(3, -(-L // g))
+        step = -(-(-(-L // n)) // g) * g
+        return -(-L // step)
+    assert counts == {b: pieces(L) for b, L in enumerate(lengths)}
+    assert counts[0] == 3
 
 
 def test_workspace_bound_covers_plan(lib):
