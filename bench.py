@@ -65,6 +65,11 @@ class Hip:
         self.lib.hipEventDestroy(e)
 
 
+def synth_heads(name: str) -> int:
+    from mla_paged_kv_decode_amd import synth
+    return synth.WORKLOADS[name]["heads"]
+
+
 def kernel_sha() -> str:
     h = hashlib.sha256()
     for name in ("kernels.hip", "kernels.h", "api.cpp", "planner.cpp"):
@@ -107,7 +112,7 @@ def device_inputs(inp, copies: int):
     return sets
 
 
-def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip) -> dict:
+def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_split: int = 0) -> dict:
     import torch
     import mla_paged_kv_decode_amd as mla
     from mla_paged_kv_decode_amd import synth
@@ -115,9 +120,11 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip) -> dict:
     inp = synth.make_workload(name)
     sets = device_inputs(inp, copies)
     B, H = inp.batch, inp.num_heads
-    ws = torch.empty(mla.workspace_bytes(B, H), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(mla.workspace_bytes(B, H, head_split=head_split), dtype=torch.uint8,
+                     device="cuda")
     t0 = time.perf_counter()
-    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, inp.page_size, inp.kv_dtype, ws)
+    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, inp.page_size, inp.kv_dtype, ws,
+                    head_split=head_split)
     plan_ms = (time.perf_counter() - t0) * 1e3
     outs = [(torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda"),
              torch.empty((B, H), dtype=torch.float32, device="cuda")) for _ in range(copies)]
@@ -195,6 +202,8 @@ def main():
     ap.add_argument("--secondary", default="compute_b64_h128_l4096_p64",
                     help="second workload reported under 'secondary' ('none' to skip)")
     ap.add_argument("--copies", type=int, default=2)
+    ap.add_argument("--head-split", type=int, default=0,
+                    help="head split for the measured workloads (0 = the planner's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true",
@@ -232,7 +241,8 @@ def main():
         peaks["mfma_bf16_tflops"] = round(mla.peak_mfma_bf16_tflops(), 1)
         torch.cuda.empty_cache()
 
-    prim = measure(args.workload, args.steps, args.warmup, args.copies, hip)
+    prim = measure(args.workload, args.steps, args.warmup, args.copies, hip,
+                   args.head_split if synth_heads(args.workload) >= 64 else 0)
     inp = prim["inp"]
     gbs = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
     kern_gbs = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
@@ -267,7 +277,7 @@ def main():
         "wall_ms_per_step": round(prim["wall_ms_per_step"], 5),
     }
     if args.secondary != "none":
-        sec = measure(args.secondary, args.steps, args.warmup, args.copies, hip)
+        sec = measure(args.secondary, args.steps, args.warmup, args.copies, hip, args.head_split)
         tfs = sec["flops"] / (sec["ms_per_step"] * 1e-3) / 1e12
         ktfs = sec["flops"] / (sec["kernel_ms"] * 1e-3) / 1e12
         out["secondary"] = {

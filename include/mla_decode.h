@@ -64,7 +64,9 @@ typedef struct {
   int32_t num_cus;      /* compute units to balance over; 0 = query the current device */
   int32_t force_splits; /* > 0: cut every request into this many near-equal chunks (testing) */
   int32_t max_workers;  /* > 0: cap on the number of workgroups; 0 = library default */
-  int32_t reserved;
+  int32_t head_split;   /* 0 = automatic; n >= 1: run each request's heads as n groups of
+                           num_heads / n heads sharing the request's latent cache (n = 1:
+                           all heads in one workgroup).  num_heads / n must be supported. */
 } mla_plan_opts;
 
 typedef struct mla_plan_s* mla_plan_t;
@@ -81,7 +83,11 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
 
 /*
  * Build the split-KV schedule for one batch (the balanced scheduler; runs on
- * the host, launches no kernel).
+ * the host, launches no kernel).  When few requests carry many heads (batch x
+ * num_heads / 32 no more than the workgroups of one wave), the heads of a
+ * request are spread over several workgroups instead of cutting its tokens,
+ * which needs no partial results; those workgroups are placed on one XCD so
+ * that the request's latent cache is fetched from HBM once.
  *   kv_indptr_host        [batch + 1] int32, host: page-list offsets, non-decreasing, from 0.
  *   kv_last_page_len_host [batch] int32, host: valid slots of each request's last page,
  *                          in [1, page_size] when the request has pages (ignored otherwise).
@@ -153,13 +159,15 @@ const char* mla_last_error(void);
  *   info[0] batch, [1] num_heads, [2] page_size, [3] kv_dtype, [4] num_workers
  *   (grid size), [5] num_segments, [6] num_partials (split partial slots),
  *   [7] num_split_requests, [8] split granularity in tokens, [9] waves per
- *   workgroup.
+ *   workgroup, [10] head split, [11] heads per workgroup.  With a head split
+ *   n > 1, segment requests count head groups: row r covers heads
+ *   (r % n) * num_heads / n .. of request r / n.
  * mla_decode_plan_segments copies the work list: seg[4*i..4*i+3] =
  * {request, token_begin, token_end, partial_slot (-1 = writes o/lse directly)}
  * for i < num_segments, and worker_ptr[w], worker_ptr[w+1] delimit the
  * segments of workgroup w (worker_ptr has num_workers + 1 entries).
  */
-mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[10]);
+mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[12]);
 mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* worker_ptr);
 
 #ifdef __cplusplus

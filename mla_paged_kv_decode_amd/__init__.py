@@ -54,7 +54,7 @@ class MlaError(RuntimeError):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
-                ("max_workers", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("max_workers", ctypes.c_int32), ("head_split", ctypes.c_int32)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -94,8 +94,8 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-def _opts(num_cus=0, force_splits=0, max_workers=0) -> PlanOpts:
-    return PlanOpts(int(num_cus), int(force_splits), int(max_workers), 0)
+def _opts(num_cus=0, force_splits=0, max_workers=0, head_split=0) -> PlanOpts:
+    return PlanOpts(int(num_cus), int(force_splits), int(max_workers), int(head_split))
 
 
 def _host_i32(x) -> np.ndarray:
@@ -122,8 +122,8 @@ def _stream_ptr(stream) -> Optional[int]:
 
 
 def workspace_bytes(batch: int, num_heads: int, num_cus: int = 0, force_splits: int = 0,
-                    max_workers: int = 0) -> int:
-    o = _opts(num_cus, force_splits, max_workers)
+                    max_workers: int = 0, head_split: int = 0) -> int:
+    o = _opts(num_cus, force_splits, max_workers, head_split)
     n = load_library().mla_decode_workspace_bytes(int(batch), int(num_heads), ctypes.byref(o))
     if n == 0:
         raise MlaError(-2, "mla_decode_workspace_bytes")
@@ -139,7 +139,8 @@ class Plan:
 
     def __init__(self, kv_indptr, kv_last_page_len, num_heads: int, page_size: int,
                  kv_dtype: int = KV_BF16, workspace=None, num_cus: int = 0,
-                 force_splits: int = 0, max_workers: int = 0, stream=None):
+                 force_splits: int = 0, max_workers: int = 0, head_split: int = 0,
+                 stream=None):
         lib = load_library()
         self._lib = lib
         ip = _host_i32(kv_indptr)
@@ -149,7 +150,7 @@ class Plan:
         self.page_size = int(page_size)
         self.kv_dtype = int(kv_dtype)
         self.workspace = workspace
-        o = _opts(num_cus, force_splits, max_workers)
+        o = _opts(num_cus, force_splits, max_workers, head_split)
         h = ctypes.c_void_p()
         ws_ptr, ws_n, sp = None, 0, None
         if workspace is not None:
@@ -170,12 +171,13 @@ class Plan:
             self._h = None
 
     def info(self) -> dict:
-        buf = np.zeros(10, np.int32)
+        buf = np.zeros(12, np.int32)
         st = self._lib.mla_decode_plan_info(self._h, buf.ctypes.data_as(ctypes.c_void_p))
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_plan_info")
         keys = ("batch", "num_heads", "page_size", "kv_dtype", "num_workers", "num_segments",
-                "num_partials", "num_split_requests", "granularity", "waves")
+                "num_partials", "num_split_requests", "granularity", "waves", "head_split",
+                "kernel_heads")
         return {k: int(v) for k, v in zip(keys, buf)}
 
     def segments(self):
@@ -253,16 +255,18 @@ def peak_mfma_bf16_tflops(iters: int = 10, stream=None) -> float:
 
 def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_scale: float,
            kv_dtype: int = KV_BF16, kv_scale=None, kv_indptr_host=None,
-           kv_last_page_len_host=None, force_splits: int = 0, stream=None):
+           kv_last_page_len_host=None, force_splits: int = 0, head_split: int = 0,
+           stream=None):
     """One-shot plan + run.  Returns (o, lse) as new device tensors."""
     import torch
     B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
     P = int(ckv.shape[1])
     ip_h = kv_indptr if kv_indptr_host is None else kv_indptr_host
     lp_h = kv_last_page_len if kv_last_page_len_host is None else kv_last_page_len_host
-    ws = torch.empty(workspace_bytes(B, H, force_splits=force_splits), dtype=torch.uint8,
-                     device=q_nope.device)
-    plan = Plan(ip_h, lp_h, H, P, kv_dtype, ws, force_splits=force_splits, stream=stream)
+    ws = torch.empty(workspace_bytes(B, H, force_splits=force_splits, head_split=head_split),
+                     dtype=torch.uint8, device=q_nope.device)
+    plan = Plan(ip_h, lp_h, H, P, kv_dtype, ws, force_splits=force_splits, head_split=head_split,
+                stream=stream)
     o = torch.empty((B, H, D_CKV), dtype=torch.bfloat16, device=q_nope.device)
     lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
     plan.run(q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len, sm_scale,

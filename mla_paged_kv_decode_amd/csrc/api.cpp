@@ -56,14 +56,15 @@ Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, 
   return L;
 }
 
-// Workgroups to balance over: CUs x decode workgroups resident per CU.  With
-// an explicit opts->num_cus (host-only planning) the per-CU count comes from
-// the kernel's LDS footprint; on a device it comes from the occupancy query.
-mla_status worker_count(const mla_plan_opts* opts, int32_t num_heads, int32_t* workers) {
+// Workgroups to balance over: CUs x decode workgroups resident per CU, for
+// the kernel that serves `kernel_heads` heads.  With an explicit
+// opts->num_cus (host-only planning) the per-CU count comes from the kernel's
+// LDS footprint; on a device it comes from the occupancy query.
+mla_status worker_count(const mla_plan_opts* opts, int32_t kernel_heads, int32_t* workers) {
   int32_t cus = opts ? opts->num_cus : 0;
   if (cus < 0) return MLA_ERR_INVALID_ARG;
   mla_gpu::DecodeConfig cfg{};
-  if (mla_gpu::decode_config(num_heads, &cfg) != 0) return MLA_ERR_UNSUPPORTED;
+  if (mla_gpu::decode_config(kernel_heads, &cfg) != 0) return MLA_ERR_UNSUPPORTED;
   int32_t per_cu = std::max(1, (160 * 1024) / cfg.lds_bytes);
   if (cus == 0) {
     int dev = 0;
@@ -71,7 +72,7 @@ mla_status worker_count(const mla_plan_opts* opts, int32_t num_heads, int32_t* w
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    per_cu = mla_gpu::decode_blocks_per_cu(num_heads);
+    per_cu = mla_gpu::decode_blocks_per_cu(kernel_heads);
   }
   int32_t w = cus * per_cu;
   if (opts && opts->max_workers > 0) w = std::min(w, opts->max_workers);
@@ -80,10 +81,54 @@ mla_status worker_count(const mla_plan_opts* opts, int32_t num_heads, int32_t* w
   return MLA_OK;
 }
 
+int log2_exact(int32_t x) {
+  int s = 0;
+  while ((1 << s) < x) ++s;
+  return (1 << s) == x ? s : -1;
+}
+
+// Head split for a batch: explicit (opts->head_split) or automatic: spread
+// the heads of each request over H / 32 workgroups when that many rows still
+// fit in one wave of 32-head workgroups, so that no request needs cutting.
+mla_status choose_head_split(int32_t batch, int32_t num_heads, const mla_plan_opts* opts,
+                             int32_t* head_split) {
+  const int32_t req = opts ? opts->head_split : 0;
+  if (req < 0) return MLA_ERR_INVALID_ARG;
+  if (req > 0) {
+    if (num_heads % req != 0 || log2_exact(req) < 0 || !supported_heads(num_heads / req))
+      return MLA_ERR_UNSUPPORTED;
+    *head_split = req;
+    return MLA_OK;
+  }
+  *head_split = 1;
+  if (num_heads >= 64) {
+    int32_t w32 = 0;
+    mla_status st = worker_count(opts, 32, &w32);
+    if (st != MLA_OK) return st;
+    const int32_t hs = num_heads / 32;
+    if ((int64_t)batch * hs <= w32) *head_split = hs;
+  }
+  return MLA_OK;
+}
+
+mla::PlanParams plan_params(int32_t num_heads, int32_t head_split, int32_t workers,
+                            const mla_gpu::DecodeConfig& cfg, const mla_plan_opts* opts) {
+  mla::PlanParams pp;
+  pp.num_heads = num_heads / head_split;
+  pp.num_workers = workers;
+  pp.granularity = cfg.tile;
+  pp.force_splits = opts ? opts->force_splits : 0;
+  pp.head_split = head_split;
+  // the merge of a split request keeps one float per (chunk, head) in LDS
+  pp.max_splits = std::min<int32_t>(256, cfg.lds_bytes / (4 * pp.num_heads));
+  return pp;
+}
+
 }  // namespace
 
 struct mla_plan_s {
   int32_t batch = 0, heads = 0, page_size = 0, page_shift = 0, kv_dtype = 0;
+  int32_t head_split = 1, kernel_heads = 0;
   mla_gpu::DecodeConfig cfg{};
   mla::Plan plan;
   Layout layout{};
@@ -110,19 +155,22 @@ const char* mla_last_error(void) { return g_last_error.c_str(); }
 
 size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_plan_opts* opts) {
   if (batch < 0 || !supported_heads(num_heads)) return 0;
-  if (opts && opts->force_splits < 0) return 0;
-  int32_t workers = 0;
-  if (worker_count(opts, num_heads, &workers) != MLA_OK) return 0;
-  mla::PlanParams pp;
-  pp.num_heads = num_heads;
-  pp.num_workers = workers;
-  pp.force_splits = opts ? opts->force_splits : 0;
-  mla_gpu::DecodeConfig cfg{};
-  if (mla_gpu::decode_config(num_heads, &cfg) != 0) return 0;
-  pp.max_splits = std::min<int32_t>(256, cfg.lds_bytes / (4 * num_heads));
-  const int64_t nseg = mla::max_segments(batch, pp);
-  const int64_t nparts = mla::max_partials(batch, pp);
-  return layout_for(nseg, workers, batch, nparts, num_heads).total;
+  if (opts && (opts->force_splits < 0 || opts->head_split < 0)) return 0;
+  // bound over every head split the plan may choose
+  size_t best = 0;
+  for (int32_t hs = 1; hs <= num_heads / 16; hs *= 2) {
+    if (opts && opts->head_split > 0 && hs != opts->head_split) continue;
+    if (!supported_heads(num_heads / hs)) continue;
+    int32_t workers = 0;
+    if (worker_count(opts, num_heads / hs, &workers) != MLA_OK) return 0;
+    mla_gpu::DecodeConfig cfg{};
+    if (mla_gpu::decode_config(num_heads / hs, &cfg) != 0) return 0;
+    const mla::PlanParams pp = plan_params(num_heads, hs, workers, cfg, opts);
+    const int64_t nseg = mla::max_segments(batch, pp);
+    const int64_t nparts = mla::max_partials(batch, pp);
+    best = std::max(best, layout_for(nseg, workers, (int64_t)batch * hs, nparts, pp.num_heads).total);
+  }
+  return best;
 }
 
 mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
@@ -137,31 +185,33 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   if (kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
   if (opts && (opts->force_splits < 0 || opts->max_workers < 0)) return MLA_ERR_INVALID_ARG;
 
+  if (opts && opts->head_split < 0) return MLA_ERR_INVALID_ARG;
+  int32_t head_split = 1;
+  mla_status st = choose_head_split(batch, num_heads, opts, &head_split);
+  if (st != MLA_OK) return st;
+  const int32_t kernel_heads = num_heads / head_split;
+
   mla_plan_s* p = new (std::nothrow) mla_plan_s();
   if (!p) return MLA_ERR_INVALID_ARG;
   p->batch = batch;
   p->heads = num_heads;
+  p->head_split = head_split;
+  p->kernel_heads = kernel_heads;
   p->page_size = page_size;
   p->page_shift = page_shift_of(page_size);
   p->kv_dtype = kv_dtype;
-  if (mla_gpu::decode_config(num_heads, &p->cfg) != 0) {
+  if (mla_gpu::decode_config(kernel_heads, &p->cfg) != 0) {
     delete p;
     return MLA_ERR_UNSUPPORTED;
   }
   int32_t workers = 0;
-  mla_status st = worker_count(opts, num_heads, &workers);
+  st = worker_count(opts, kernel_heads, &workers);
   if (st != MLA_OK) {
     delete p;
     return st;
   }
-  mla::PlanParams pp;
-  pp.num_heads = num_heads;
+  mla::PlanParams pp = plan_params(num_heads, head_split, workers, p->cfg, opts);
   pp.page_size = page_size;
-  pp.num_workers = workers;
-  pp.granularity = p->cfg.tile;
-  pp.force_splits = opts ? opts->force_splits : 0;
-  // the merge of a split request keeps one float per (chunk, head) in LDS
-  pp.max_splits = std::min<int32_t>(256, p->cfg.lds_bytes / (4 * num_heads));
   static const int32_t kZero = 0;
   if (mla::build_plan(kv_indptr_host, batch > 0 ? kv_last_page_len_host : &kZero, batch, pp,
                       &p->plan) != 0) {
@@ -171,7 +221,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   const mla::Plan& pl = p->plan;
   const int64_t ncomb = (int64_t)pl.combine.size() / 4;
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
-                         num_heads);
+                         kernel_heads);
 
   // stage the work list: segments | worker_ptr | zeroed arrival counters
   p->host_meta.assign(p->layout.meta_bytes, 0);
@@ -234,12 +284,13 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.counters = reinterpret_cast<int32_t*>(ws + p->layout.counters);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.page_shift = p->page_shift;
+  a.head_shift = log2_exact(p->head_split);
   if (p->ev_before) {
     hipError_t e = hipEventRecord(p->ev_before, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   if (p->plan.num_workers > 0) {
-    hipError_t e = mla_gpu::launch_decode(p->heads, a, p->plan.num_workers, s);
+    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, a, p->plan.num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   if (p->ev_after) {
@@ -258,7 +309,7 @@ mla_status mla_decode_plan_set_events(mla_plan_t p, void* before, void* after) {
   return MLA_OK;
 }
 
-mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[10]) {
+mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[12]) {
   if (!p || !info) return MLA_ERR_INVALID_ARG;
   info[0] = p->batch;
   info[1] = p->heads;
@@ -270,6 +321,8 @@ mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[10]) {
   info[7] = (int32_t)(p->plan.combine.size() / 4);
   info[8] = p->cfg.tile;
   info[9] = p->cfg.waves;
+  info[10] = p->head_split;
+  info[11] = p->kernel_heads;
   return MLA_OK;
 }
 

@@ -26,6 +26,8 @@ struct DecodeArgs {
   int32_t* counters;          // arrival counter per split request (0 between launches)
   float scale_log2;           // sm_scale * log2(e)
   int32_t page_shift;         // log2(page_size)
+  int32_t head_shift;         // log2(head split): row b of q/o/lse (of kernel-width heads)
+                              // reads the latent cache of request b >> head_shift
 };
 
 struct DecodeConfig {

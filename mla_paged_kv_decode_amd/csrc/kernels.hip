@@ -220,12 +220,11 @@ __device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int 
   }
 }
 
-// End of a segment: normalise (merging the TS token-split waves of every head
-// group through LDS), then write o/lse for a whole request or the partial of a
-// chunk; the workgroup that completes the last chunk of a split request merges
-// its partials.  acc holds O^T (lane = head lane & 15, columns 16 cb + 4 (lane
-// >> 4) + i), m_run the log2-domain running max, l_run this lane's share of
-// the running sum.
+// End of a segment, one 16-head block: normalise (merging the TS token-split
+// waves of the block through LDS), then write o/lse for a whole request or the
+// partial of a chunk.  acc holds O^T (lane = head lane & 15, columns
+// 16 cb + 4 (lane >> 4) + i), m_run the log2-domain reference max, l_run this
+// lane's share of the running sum.
 constexpr int kMergeStride = 512 + 4;  // floats per head row in the merge area
 
 template <int H, int HG, int TS>
@@ -233,16 +232,14 @@ constexpr int merge_bytes() {
   return TS > 1 ? HG * TS * 16 * kMergeStride * 4 + HG * TS * 16 * 8 : 0;
 }
 
-template <int H, int HG, int TS, int NT>
-__device__ __forceinline__ void segment_epilogue(const DecodeArgs& a, f32x4 (&acc)[32],
+template <int H, int HG, int TS>
+__device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&acc)[32],
                                                  float m_run, float l_run, int b, int slot,
-                                                 int split_req, int slot0, int nsplit, int wave,
-                                                 int lane, int tid, uint8_t* smem, int* s_last) {
-  constexpr int kWaves = HG * TS;
-  const int hg = wave % HG;
-  const int ts = wave / HG;
+                                                 int hg, int ts, int lane, uint8_t* smem) {
+  constexpr int kWaves = HG * TS;  // merge slots: (ts, hg) -> ts * HG + hg
   const int qr = lane & 15;
   const int head = hg * 16 + qr;
+  const int mslot = ts * HG + hg;
   const float l_tot = wave_sum_16(l_run);
   if constexpr (TS == 1) {
     const bool empty = !(l_tot > 0.f);
@@ -272,14 +269,14 @@ __device__ __forceinline__ void segment_epilogue(const DecodeArgs& a, f32x4 (&ac
     // merge the TS token-split waves of each head group through LDS
     float* mo = reinterpret_cast<float*>(smem);
     float* mstat = mo + kWaves * 16 * kMergeStride;  // [wave][16][2] (m, l)
-    float* mine = mo + wave * 16 * kMergeStride;
+    float* mine = mo + mslot * 16 * kMergeStride;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb)
       *reinterpret_cast<f32x4*>(mine + qr * kMergeStride + cb * 16 + 4 * (lane >> 4)) =
           acc[cb];
     if (lane < 16) {
-      mstat[(wave * 16 + lane) * 2 + 0] = m_run;
-      mstat[(wave * 16 + lane) * 2 + 1] = l_tot;
+      mstat[(mslot * 16 + lane) * 2 + 0] = m_run;
+      mstat[(mslot * 16 + lane) * 2 + 1] = l_tot;
     }
     lds_barrier();
     // wave (hg, ts) finalises columns [128*ts, 128*ts + 128) of its 16 heads
@@ -341,7 +338,14 @@ __device__ __forceinline__ void segment_epilogue(const DecodeArgs& a, f32x4 (&ac
     }
     lds_barrier();  // merge area free before the next segment's loads
   }
+}
 
+// After every head block of a segment is written: the workgroup completing
+// the last chunk of a split request merges the request's partials.
+template <int H, int NT>
+__device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int slot, int split_req,
+                                               int slot0, int nsplit, int tid, uint8_t* smem,
+                                               int* s_last) {
   // ---- last chunk of a split request merges the request's partials --------
   if (slot >= 0) {
     vm_wait_n<0>();  // this wave's coherent partial stores have completed
@@ -363,30 +367,48 @@ __device__ __forceinline__ void segment_epilogue(const DecodeArgs& a, f32x4 (&ac
   }
 }
 
-template <int HG, int TS, int MB, int NSTAGE>
-struct DecodeShape {
-  static constexpr int kPvBatch = HG * TS > 4 ? 2 : 8;  // PV operand reads in flight
-  static constexpr int kWaves = HG * TS;
+// ---------------------------------------------------------------------------
+// LDS-ring kernel (32 or more query heads).
+//   HG   16-head blocks of the request (H = 16 HG), all in this workgroup;
+//   HB   16-head blocks per wave: a wave reads each K / V operand from LDS once
+//        and feeds HB MFMAs with it (HB = 2 halves the LDS traffic per flop);
+//   TS   waves splitting a tile's tokens (own softmax state, merged at the end);
+//   MB   16-row groups per wave per tile (MB = 2 lets PV use the 32-deep MFMA);
+//   NSTAGE depth of the HBM -> LDS ring.
+// Waves = (HG / HB) * TS.  Online softmax rescales lazily: the reference max
+// only moves when a score exceeds it by more than 2^8, so the accumulators
+// (in AGPRs when HB = 2) are rarely touched outside the MFMAs.
+// ---------------------------------------------------------------------------
+constexpr float kRescaleSlack = 8.f;  // log2 units
+
+template <int HG, int HB, int TS, int MB, int NSTAGE>
+struct RingShape {
+  static constexpr int kWaveHeads = HG / HB;  // waves per token slice
+  static constexpr int kWaves = kWaveHeads * TS;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kHeads = 16 * HG;
   static constexpr int kTile = TS * MB * 16;
   static constexpr int kGroups = kTile / 16;
   static constexpr int kItems = kGroups * 18;  // 1 KiB load blocks per tile
-  static constexpr int kItemsMin = kItems / kWaves;
-  static constexpr int kItemsRem = kItems % kWaves;
+  // waves issue whole half groups (9 blocks): wave w takes w, w + kWaves, ...
+  static constexpr int kItemsMin = 9 * ((2 * kGroups) / kWaves);
+  static constexpr int kItemsRem = (2 * kGroups) % kWaves;  // waves < this take one more
   static constexpr int kStageBytes = kTile * kRowBytes;
   static constexpr int kMergeBytes = merge_bytes<16 * HG, HG, TS>();
   static constexpr int kLdsBytes =
       (NSTAGE * kStageBytes > kMergeBytes) ? NSTAGE * kStageBytes : kMergeBytes;
   static constexpr bool kOneBarrier = NSTAGE >= 3;
+  static constexpr int kPvBatch = kWaves > 4 ? 2 : (HB == 2 ? 4 : 8);  // PV reads in flight
+  static constexpr int kQkBatch = kWaves > 4 ? 3 : 6;                   // QK reads in flight
+  static_assert(HG % HB == 0, "head blocks per wave");
   static_assert(MB == 1 || MB % 2 == 0, "MB must be 1 or even");
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-template <int HG, int TS, int MB, int NSTAGE>
-__global__ void __launch_bounds__(64 * HG * TS)
-    mla_decode_bf16_kernel(const DecodeArgs a) {
-  using S = DecodeShape<HG, TS, MB, NSTAGE>;
+template <int HG, int HB, int TS, int MB, int NSTAGE>
+__global__ void __launch_bounds__(64 * (HG / HB) * TS)
+    mla_decode_ring_kernel(const DecodeArgs a) {
+  using S = RingShape<HG, HB, TS, MB, NSTAGE>;
   constexpr int H = S::kHeads;
   constexpr int T = S::kTile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
@@ -395,22 +417,21 @@ __global__ void __launch_bounds__(64 * HG * TS)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
   const int lane = tid & 63;
-  const int hg = wave % HG;
-  const int ts = wave / HG;
-  const int my_items = S::kItemsMin + (wave < S::kItemsRem ? 1 : 0);
-  const int item0 = wave * S::kItemsMin + (wave < S::kItemsRem ? wave : S::kItemsRem);
+  const int wh = wave % S::kWaveHeads;  // this wave's heads: blocks wh * HB .. wh * HB + HB - 1
+  const int ts = wave / S::kWaveHeads;
+  const int my_items = S::kItemsMin + (wave < S::kItemsRem ? 9 : 0);
   const int page_shift = a.page_shift;
   const int page_mask = (1 << page_shift) - 1;
 
   // ---- per-lane constant LDS offsets -------------------------------------
   // Loader: lane writes LDS slot `lane` of a block: row r = rh*8 + lane/8,
   // logical chunk = cb*8 + ((lane & 7) ^ swz(r)).
-  const int ld_r_lo = lane >> 3;  // row within the half group
+  const int ld_r_lo = lane >> 3;
   // QK operand: token row r = lane & 15, chunk c = 4*s + (lane >> 4).
   const int qr = lane & 15;
   const int qk_base = (qr >> 3) * kHalfGroupBytes + (qr & 7) * 128;
-  const int qk_off_even = (((lane >> 4)) ^ swz(qr)) * 16;       // s even: c & 7 = g
-  const int qk_off_odd = ((4 + (lane >> 4)) ^ swz(qr)) * 16;    // s odd:  c & 7 = 4 + g
+  const int qk_off_even = ((lane >> 4) ^ swz(qr)) * 16;       // s even: c & 7 = g
+  const int qk_off_odd = ((4 + (lane >> 4)) ^ swz(qr)) * 16;  // s odd:  c & 7 = 4 + g
   // PV operand (transpose read): source lane s = 16G + 4j + q reads row 4G + j,
   // 8 bytes at columns c0 + 4q .. c0 + 4q + 3 of a 16-column block c0.
   const int tr_r = 4 * (lane >> 4) + ((lane >> 2) & 3);
@@ -432,19 +453,13 @@ __global__ void __launch_bounds__(64 * HG * TS)
     const int split_req = ld_const(sgp + 4);
     const int slot0 = ld_const(sgp + 5);
     const int nsplit = ld_const(sgp + 6);
-    const int pbeg = ld_const(a.kv_indptr + b);
-    const int npg = ld_const(a.kv_indptr + b + 1) - pbeg;
-    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + b) : 0;
+    const int kvb = b >> a.head_shift;  // request whose latent cache this segment reads
+    const int pbeg = ld_const(a.kv_indptr + kvb);
+    const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
+    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
     const int t1 = min(send, ldev);
     const int ntiles = t1 > t0 ? (t1 - t0 + T - 1) / T : 0;
 
-    float m_run = -INFINITY;  // running max (log2 domain) of this wave's tokens, head = lane & 15
-    float l_run = 0.f;        // this lane's share of the running sum
-    f32x4 acc[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // issue the direct-to-LDS loads of tile k into stage st
     // Page numbers of the row groups of tile k (one scalar load per group;
     // a group past the end reuses the group of the last valid token).
     const int last_group = t1 > 0 ? ((t1 - 1) >> 4) << 4 : 0;
@@ -460,6 +475,9 @@ __global__ void __launch_bounds__(64 * HG * TS)
 
     // Issue the direct-to-LDS loads of tile k into stage st, then prefetch the
     // page numbers of tile k + 1 so that the next issue does not wait on them.
+    // Wave w loads half groups w, w + waves, ...: 9 blocks of 1 KiB (8 rows x
+    // 8 chunks of ckv, then the kpe chunk) whose lane addresses differ only by
+    // immediate 128-byte steps along one row.
     auto issue_tile = [&](int k, int st) {
       const int tile_start = t0 + k * T;
       int pg[S::kGroups];
@@ -467,12 +485,9 @@ __global__ void __launch_bounds__(64 * HG * TS)
       for (int g = 0; g < S::kGroups; ++g) pg[g] = pg_next[g];
       if (k + 1 < ntiles) tile_pages(k + 1);
       uint8_t* stage = smem + st * S::kStageBytes;
-      for (int j = 0; j < my_items; ++j) {
-        const int item = item0 + j;
-        const int g = item / 18;
-        const int blk = item - g * 18;
-        const int rh = blk >= 9 ? 1 : 0;
-        const int cb = blk - rh * 9;
+      for (int hh = wave; hh < 2 * S::kGroups; hh += S::kWaves) {
+        const int g = hh >> 1;
+        const int rh = hh & 1;
         int page = pg[0];
 #pragma unroll
         for (int gg = 1; gg < S::kGroups; ++gg) page = g == gg ? pg[gg] : page;
@@ -480,12 +495,14 @@ __global__ void __launch_bounds__(64 * HG * TS)
         const int r = rh * 8 + ld_r_lo;
         const int tok = min(gs + r, t1 - 1);
         const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
-        const int c = cb * 8 + ((lane & 7) ^ swz(r));
-        const uint8_t* src = c < 64 ? a.ckv + (row * 512 + c * 8) * 2
-                                    : a.kpe + (row * 64 + (c - 64) * 8) * 2;
+        const int sw = ((lane & 7) ^ swz(r)) * 16;
+        const uint8_t* cbase = a.ckv + row * 1024 + sw;
+        const uint8_t* kbase = a.kpe + row * 128 + sw;
         const uint32_t dst = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + g * kGroupBytes + blk * 1024));
-        dma16(src, dst);
+            (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(stage + g * kGroupBytes + rh * 9 * 1024));
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) dma16(cbase + cb * 128, dst + cb * 1024);
+        dma16(kbase, dst + 8 * 1024);
       }
     };
 
@@ -494,31 +511,40 @@ __global__ void __launch_bounds__(64 * HG * TS)
       if (my_items == S::kItemsMin)
         wait_tile<S::kItemsMin, kMaxLater>(later);
       else
-        wait_tile<S::kItemsMin + 1, kMaxLater>(later);
+        wait_tile<S::kItemsMin + 9, kMaxLater>(later);
     };
 
     if (ntiles > 0) tile_pages(0);
     for (int k = 0; k < NSTAGE - 1 && k < ntiles; ++k) issue_tile(k, k);
 
-    // ---- Q^T operand for head hg*16 + (lane & 15): 18 x 8 dims -----------
-    const int head = hg * 16 + qr;
-    bf16x8 qf[18];
-    {
+    // ---- Q^T operands of this wave's HB head blocks: 18 x 8 dims each -------
+    bf16x8 qf[HB][18];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      const int head = (wh * HB + hb) * 16 + qr;
       const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + head) * 512);
       const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + head) * 64);
 #pragma unroll
       for (int s = 0; s < 18; ++s) {
         const int c = 4 * s + (lane >> 4);
-        qf[s] = s < 16 ? qn[c] : qp[c - 64];
+        qf[hb][s] = s < 16 ? qn[c] : qp[c - 64];
       }
     }
-
     // Q (and the previous segment's stores) complete before the tile loop; the
     // explicit full wait also tells the compiler that no vector load is
     // pending, so it adds no waits inside the loop (where only the LDS DMA,
     // which it does not see, is in flight).
     vm_wait_n<0>();
 
+    float m_ref[HB], l_run[HB];
+    f32x4 acc[HB][32];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      m_ref[hb] = -INFINITY;
+      l_run[hb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     for (int it = 0; it < ntiles; ++it) {
       const int st = it % NSTAGE;
@@ -537,87 +563,101 @@ __global__ void __launch_bounds__(64 * HG * TS)
       const uint8_t* stage = smem + st * S::kStageBytes;
       const int tile_start = t0 + it * T;
 
-      // ---- QK: S^T for this wave's MB row groups -------------------------
-      f32x4 sacc[MB];
+      // ---- QK: S^T for this wave's MB row groups and HB head blocks ----------
+      f32x4 sacc[HB][MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const int gi = ts * MB + mb;
-        const uint8_t* gbase = stage + gi * kGroupBytes + qk_base;
-        bf16x8 kf[18];
+        const uint8_t* gbase = stage + (ts * MB + mb) * kGroupBytes + qk_base;
 #pragma unroll
-        for (int s = 0; s < 18; ++s) {
-          const uint8_t* p = gbase + (s >> 1) * 1024 + ((s & 1) ? qk_off_odd : qk_off_even);
-          kf[s] = *reinterpret_cast<const LDS_AS bf16x8*>((const LDS_AS uint8_t*)p);
+        for (int hb = 0; hb < HB; ++hb) sacc[hb][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s0 = 0; s0 < 18; s0 += S::kQkBatch) {
+          bf16x8 kf[S::kQkBatch];
+#pragma unroll
+          for (int u = 0; u < S::kQkBatch; ++u) {
+            const int s = s0 + u;
+            kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+                (const LDS_AS uint8_t*)(gbase + (s >> 1) * 1024 + ((s & 1) ? qk_off_odd : qk_off_even)));
+          }
+#pragma unroll
+          for (int u = 0; u < S::kQkBatch; ++u)
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+              sacc[hb][mb] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[hb][s0 + u], sacc[hb][mb], 0, 0, 0);
         }
-        f32x4 c4 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 18; ++s)
-          c4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[s], qf[s], c4, 0, 0, 0);
-        sacc[mb] = c4;
       }
 
-      // ---- online softmax (log2 domain) -----------------------------------
-      float tmax = -INFINITY;
+      // ---- online softmax (log2 domain, lazy rescale) ----------------------
+      bf16x4 pb[HB][MB];
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const int row0 = tile_start + (ts * MB + mb) * 16 + 4 * (lane >> 4);
+      for (int hb = 0; hb < HB; ++hb) {
+        float tmax = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = (row0 + i < t1) ? sacc[mb][i] * a.scale_log2 : -INFINITY;
-          sacc[mb][i] = x;
-          tmax = fmaxf(tmax, x);
+        for (int mb = 0; mb < MB; ++mb) {
+          const int row0 = tile_start + (ts * MB + mb) * 16 + 4 * (lane >> 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = (row0 + i < t1) ? sacc[hb][mb][i] * a.scale_log2 : -INFINITY;
+            sacc[hb][mb][i] = x;
+            tmax = fmaxf(tmax, x);
+          }
         }
-      }
-      tmax = wave_max_16(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float psum = 0.f;
-      bf16x4 pb[MB];
+        tmax = wave_max_16(tmax);
+        if (__builtin_amdgcn_ballot_w64(tmax > m_ref[hb] + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_ref[hb], tmax);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[hb] - m_new);  // 0 when m_ref = -inf
+          l_run[hb] *= alpha;
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sacc[mb][i] - m_use);
-          psum += p;
-          pb[mb][i] = (__bf16)p;
+          for (int i = 0; i < 32; ++i) acc[hb][i] *= alpha;
+          m_ref[hb] = m_new;
         }
-      }
-      l_run = l_run * alpha + psum;
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+        const float m_use = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
+        float psum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+        for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = __builtin_amdgcn_exp2f(sacc[hb][mb][i] - m_use);
+            psum += p;
+            pb[hb][mb][i] = (__bf16)p;
+          }
+        }
+        l_run[hb] += psum;
       }
-      m_run = m_new;
 
       // ---- PV: O^T[c, h] += V^T[c, t] P^T[t, h] ----------------------------
       if constexpr (MB == 1) {
         const uint8_t* gbase = stage + (ts * MB) * kGroupBytes;
-        const s16x4 pv = __builtin_bit_cast(s16x4, pb[0]);
 #pragma unroll
         for (int c8 = 0; c8 < 32; c8 += S::kPvBatch) {
           s16x4 vf[S::kPvBatch];
 #pragma unroll
           for (int u = 0; u < S::kPvBatch; ++u) {
             const int cb = c8 + u;
-            const uint8_t* p = gbase + (cb >> 2) * 1024 + tr_off[cb & 3];
-            vf[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)((LDS_AS uint8_t*)p));
+            vf[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (LDS_AS s16x4*)((LDS_AS uint8_t*)(gbase + (cb >> 2) * 1024 + tr_off[cb & 3])));
           }
 #pragma unroll
           for (int u = 0; u < S::kPvBatch; ++u)
-            acc[c8 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[u], pv, acc[c8 + u], 0, 0, 0);
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+              acc[hb][c8 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                  vf[u], __builtin_bit_cast(s16x4, pb[hb][0]), acc[hb][c8 + u], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int mp = 0; mp < MB; mp += 2) {
           const uint8_t* g0 = stage + (ts * MB + mp) * kGroupBytes;
           const uint8_t* g1 = g0 + kGroupBytes;
-          bf16x8 pv;
+          bf16x8 pv[HB];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pv[i] = pb[mp][i];
-            pv[4 + i] = pb[mp + 1][i];
-          }
+          for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              pv[hb][i] = pb[hb][mp][i];
+              pv[hb][4 + i] = pb[hb][mp + 1][i];
+            }
 #pragma unroll
           for (int c8 = 0; c8 < 32; c8 += S::kPvBatch) {
             bf16x8 vf[S::kPvBatch];
@@ -638,7 +678,10 @@ __global__ void __launch_bounds__(64 * HG * TS)
             }
 #pragma unroll
             for (int u = 0; u < S::kPvBatch; ++u)
-              acc[c8 + u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[u], pv, acc[c8 + u], 0, 0, 0);
+#pragma unroll
+              for (int hb = 0; hb < HB; ++hb)
+                acc[hb][c8 + u] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[u], pv[hb], acc[hb][c8 + u], 0, 0, 0);
           }
         }
       }
@@ -647,11 +690,13 @@ __global__ void __launch_bounds__(64 * HG * TS)
     if constexpr (S::kOneBarrier) lds_barrier();  // ring free before the merge / next segment
 
     // ---- epilogue -----------------------------------------------------------
-    segment_epilogue<H, HG, TS, S::kThreads>(a, acc, m_run, l_run, b, slot, split_req, slot0,
-                                              nsplit, wave, lane, tid, smem, &s_last);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      write_head_block<H, HG, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, wh * HB + hb, ts,
+                                  lane, smem);
+    finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Register-staged variant for 16 query heads (one head group).  The work is
@@ -722,9 +767,10 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
     const int split_req = ld_const(sgp + 4);
     const int slot0 = ld_const(sgp + 5);
     const int nsplit = ld_const(sgp + 6);
-    const int pbeg = ld_const(a.kv_indptr + b);
-    const int npg = ld_const(a.kv_indptr + b + 1) - pbeg;
-    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + b) : 0;
+    const int kvb = b >> a.head_shift;  // request whose latent cache this segment reads
+    const int pbeg = ld_const(a.kv_indptr + kvb);
+    const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
+    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
     const int t1 = min(send, ldev);
     const int ngroups = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
     const int nmine = ngroups > wave ? (ngroups - 1 - wave) / TS + 1 : 0;
@@ -750,23 +796,26 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
     // Fetch this wave's j-th group into registers.  Every call issues the same
     // 18 loads, also past the last group (then from a fixed, valid address),
     // so that the number of loads in flight is the same on every path and the
-    // compiler's vmcnt waits only cover the group being consumed.
+    // compiler's vmcnt waits only cover the group being consumed.  A lane
+    // covers one row of each half group: rows lane / 8 and 8 + lane / 8, 16-byte
+    // chunk (lane & 7) ^ swz(row) of every 128-byte block of the row.
     const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q_nope + (size_t)b * H * 512);
     auto fetch = [&](int j, u32x4 (&st)[18]) __attribute__((always_inline)) {
       const bool live = j < nmine;
-      const int gs = live ? t0 + 16 * (wave + TS * j) : t0;
+      const int gs = t0 + 16 * (wave + TS * j);
       const int page = live ? ld_const(a.kv_indices + pbeg + (gs >> page_shift)) : 0;
 #pragma unroll
-      for (int blk = 0; blk < 18; ++blk) {
-        const int rh = blk >= 9 ? 1 : 0;
-        const int cb = blk - rh * 9;
+      for (int rh = 0; rh < 2; ++rh) {
         const int r = rh * 8 + ld_r_lo;
         const int tok = min(gs + r, t1 - 1);
         const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
-        const int c = cb * 8 + ((lane & 7) ^ swz(r));
-        const uint8_t* src = c < 64 ? a.ckv + (row * 512 + c * 8) * 2
-                                    : a.kpe + (row * 64 + (c - 64) * 8) * 2;
-        st[blk] = *reinterpret_cast<const u32x4*>(live ? src : dummy);
+        const int sw = ((lane & 7) ^ swz(r)) * 16;
+        const uint8_t* cbase = live ? a.ckv + row * 1024 + sw : dummy + sw;
+        const uint8_t* kbase = live ? a.kpe + row * 128 + sw : dummy + sw;
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb)
+          st[rh * 9 + cb] = *reinterpret_cast<const u32x4*>(cbase + cb * 128);
+        st[rh * 9 + 8] = *reinterpret_cast<const u32x4*>(kbase);
       }
     };
 
@@ -811,9 +860,15 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
         tmax = fmaxf(tmax, x);
       }
       tmax = wave_max_16(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float psum = 0.f;
       bf16x4 pb;
 #pragma unroll
@@ -822,12 +877,7 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
         psum += p;
         pb[i] = (__bf16)p;
       }
-      l_run = l_run * alpha + psum;
-      if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-      }
-      m_run = m_new;
+      l_run += psum;
 
       // PV: O^T[c][h] += V^T[c][t] P^T[t][h]
       const s16x4 pv = __builtin_bit_cast(s16x4, pb);
@@ -856,34 +906,34 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
     }
 
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
-    segment_epilogue<H, 1, TS, S::kThreads>(a, acc, m_run, l_run, b, slot, split_req, slot0,
-                                             nsplit, wave, lane, tid, smem, &s_last);
+    write_head_block<H, 1, TS>(a, acc, m_run, l_run, b, slot, 0, wave, lane, smem);
+    finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
   }
 }
 
 // ---------------------------------------------------------------- launchers
-template <int HG, int TS, int MB, int NSTAGE>
+template <int HG, int HB, int TS, int MB, int NSTAGE>
 static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
-  using S = DecodeShape<HG, TS, MB, NSTAGE>;
-  hipLaunchKernelGGL((mla_decode_bf16_kernel<HG, TS, MB, NSTAGE>), dim3(grid), dim3(S::kThreads),
-                     0, stream, a);
+  using S = RingShape<HG, HB, TS, MB, NSTAGE>;
+  hipLaunchKernelGGL((mla_decode_ring_kernel<HG, HB, TS, MB, NSTAGE>), dim3(grid),
+                     dim3(S::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-// Kernel shape per head count: <head groups, token-split waves, row groups per
-// wave per tile, ring stages>.
+// Ring-kernel shape per head count: <16-head blocks, blocks per wave,
+// token-split waves, row groups per wave per tile, ring stages>.
 // 16 heads: the register-staged kernel <waves, groups in flight per wave>
 #ifndef MLA_WAVE_H16
 #define MLA_WAVE_H16 4, 2
 #endif
 #ifndef MLA_CFG_H32
-#define MLA_CFG_H32 2, 2, 2, 2
+#define MLA_CFG_H32 2, 1, 2, 1, 4
 #endif
 #ifndef MLA_CFG_H64
-#define MLA_CFG_H64 4, 1, 2, 3
+#define MLA_CFG_H64 4, 1, 1, 2, 4
 #endif
 #ifndef MLA_CFG_H128
-#define MLA_CFG_H128 8, 1, 2, 3
+#define MLA_CFG_H128 8, 1, 1, 2, 4
 #endif
 
 template <int TS, int NBUF>
@@ -908,18 +958,18 @@ static int wave_occupancy_of() {
   return n < 1 ? 1 : n;
 }
 
-template <int HG, int TS, int MB, int NSTAGE>
+template <int HG, int HB, int TS, int MB, int NSTAGE>
 static DecodeConfig config_of() {
-  using S = DecodeShape<HG, TS, MB, NSTAGE>;
+  using S = RingShape<HG, HB, TS, MB, NSTAGE>;
   return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
 }
 
-template <int HG, int TS, int MB, int NSTAGE>
+template <int HG, int HB, int TS, int MB, int NSTAGE>
 static int occupancy_of() {
-  using S = DecodeShape<HG, TS, MB, NSTAGE>;
+  using S = RingShape<HG, HB, TS, MB, NSTAGE>;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&mla_decode_bf16_kernel<HG, TS, MB, NSTAGE>),
+          &n, reinterpret_cast<const void*>(&mla_decode_ring_kernel<HG, HB, TS, MB, NSTAGE>),
           S::kThreads, 0) != hipSuccess ||
       n < 1)
     n = (160 * 1024) / S::kLdsBytes;

@@ -12,6 +12,7 @@
 #include "planner.h"
 
 #include <algorithm>
+#include <limits>
 #include <cstdint>
 #include <queue>
 #include <utility>
@@ -83,11 +84,40 @@ int64_t assign(const std::vector<Piece>& pieces, int32_t workers, std::vector<in
   return worst;
 }
 
+// Reorder workers so that the workers serving the hs sub-requests of one
+// request get launch positions congruent modulo the number of L2 domains
+// (workgroups are dealt to XCDs round-robin), letting them share the request's
+// KV through one L2.  Workers are ordered by the first row they serve, then
+// dealt in chunks of hs: chunk c goes to domain c % X, consecutive positions
+// of that domain.  Only applied when the worker count divides evenly; it is a
+// placement heuristic and never affects results.
+void xcd_colocate(const std::vector<Piece>& pieces, const std::vector<int32_t>& owner, int32_t hs,
+                  int32_t xcds, int32_t used, std::vector<int32_t>* remap) {
+  if (xcds < 1 || used % (xcds * hs) != 0) return;
+  std::vector<int32_t> first_row((size_t)used, std::numeric_limits<int32_t>::max());
+  for (size_t i = 0; i < pieces.size(); ++i) {
+    const int32_t w = (*remap)[owner[i]];
+    first_row[w] = std::min(first_row[w], pieces[i].request);
+  }
+  std::vector<int32_t> order((size_t)used);
+  for (int32_t w = 0; w < used; ++w) order[w] = w;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return first_row[x] < first_row[y]; });
+  std::vector<int32_t> pos((size_t)used);
+  for (int32_t i = 0; i < used; ++i) {
+    const int32_t c = i / hs, j = i % hs;
+    pos[order[i]] = (c % xcds) + xcds * (hs * (c / xcds) + j);
+  }
+  for (auto& r : *remap)
+    if (r >= 0) r = pos[r];
+}
+
 }  // namespace
 
 int64_t max_segments(int32_t batch, const PlanParams& p) {
-  if (p.force_splits > 0) return (int64_t)batch * std::min(p.force_splits, p.max_splits);
-  return (int64_t)batch + 2 * (int64_t)p.num_workers;
+  const int64_t rows = (int64_t)batch * std::max(1, p.head_split);
+  if (p.force_splits > 0) return rows * std::min(p.force_splits, p.max_splits);
+  return rows + 2 * (int64_t)p.num_workers;
 }
 
 int64_t max_partials(int32_t batch, const PlanParams& p) { return max_segments(batch, p); }
@@ -95,10 +125,12 @@ int64_t max_partials(int32_t batch, const PlanParams& p) { return max_segments(b
 int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
                    const PlanParams& p, Plan* out) {
   if (!kv_indptr || !kv_last_page_len || !out || batch < 0 || p.num_workers <= 0 ||
-      p.granularity <= 0 || p.page_size <= 0 || p.num_heads <= 0 || p.max_splits < 1)
+      p.granularity <= 0 || p.page_size <= 0 || p.num_heads <= 0 || p.max_splits < 1 ||
+      p.head_split < 1)
     return -1;
   if (kv_indptr[0] != 0) return -1;
-  std::vector<int64_t> len((size_t)batch);
+  const int32_t hs = p.head_split;
+  std::vector<int64_t> len((size_t)batch * hs);
   int64_t max_len = 0;
   for (int32_t b = 0; b < batch; ++b) {
     const int64_t n = (int64_t)kv_indptr[b + 1] - kv_indptr[b];
@@ -113,6 +145,9 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
     if (len[b] > INT32_MAX) return -1;
     max_len = std::max(max_len, len[b]);
   }
+  // sub-requests g of request b are rows b * hs + g (lengths copied, last first)
+  for (int64_t r = (int64_t)batch * hs - 1; r >= 0; --r) len[r] = len[r / hs];
+  const int32_t rows = batch * hs;
 
   const int32_t gran = p.granularity;
   const int64_t seg_cap = max_segments(batch, p);
@@ -154,6 +189,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
   int32_t used = 0;
   for (int32_t w = 0; w < p.num_workers; ++w)
     if (count[w] > 0) remap[w] = used++;
+  if (hs > 1) xcd_colocate(best_pieces, best_owner, hs, p.xcd_count, used, &remap);
   out->batch = batch;
   out->num_workers = used;
   out->worker_ptr.assign((size_t)used + 1, 0);
@@ -165,8 +201,8 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
 
   // partial slots: consecutive per split request, in token order (cut_requests
   // emits the pieces of a request consecutively, in token order)
-  std::vector<int32_t> first_slot((size_t)batch, -1), first_piece((size_t)batch, -1);
-  std::vector<int32_t> split_index((size_t)batch, -1);
+  std::vector<int32_t> first_slot((size_t)rows, -1), first_piece((size_t)rows, -1);
+  std::vector<int32_t> split_index((size_t)rows, -1);
   out->combine.clear();
   int32_t slots = 0;
   for (size_t i = 0; i < best_pieces.size(); ++i) {

@@ -20,10 +20,13 @@ struct PlanParams {
   int32_t granularity = 64;  // chunk boundaries are multiples of this many tokens
   int32_t force_splits = 0;  // > 0: every request cut into this many chunks (at most)
   int32_t max_splits = 256;  // chunks per request at most (the merge keeps n * H floats in LDS)
+  int32_t head_split = 1;    // > 1: each request's heads run as this many sub-requests
+                             // (rows b * head_split + g of q/o viewed with H / head_split heads)
+  int32_t xcd_count = 8;     // workgroups are dealt round-robin to this many L2 domains
 };
 
 struct Segment {
-  int32_t request;
+  int32_t request;  // q/o row block (a sub-request when heads are split)
   int32_t begin;  // first logical token
   int32_t end;    // one past the last token
   int32_t slot;   // partial slot, or -1 when this segment is the whole request
@@ -47,7 +50,8 @@ struct Plan {
 int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t batch,
                    const PlanParams& params, Plan* out);
 
-// Upper bound of segments and partial slots for any plan of `batch` requests.
+// Upper bound of segments and partial slots for any plan of `batch` requests
+// (counting sub-requests when heads are split).
 int64_t max_segments(int32_t batch, const PlanParams& params);
 int64_t max_partials(int32_t batch, const PlanParams& params);
 

@@ -46,6 +46,8 @@ def _table(lengths, P):
 def _check_plan(plan, lengths, gran):
     seg, wp = plan.segments()
     info = plan.info()
+    hs = info["head_split"]
+    lengths = [L for L in lengths for _ in range(hs)]  # row r reads request r // hs
     assert wp[0] == 0 and wp[-1] == len(seg) and np.all(np.diff(wp) > 0)
     covered = {}
     for b, t0, t1, slot in seg:
@@ -160,3 +162,44 @@ def test_run_without_workspace_is_refused(lib):
     st = lib.mla_decode_run(plan._h, P(1), P(1), P(1), P(1), None, P(1), P(1), P(1),
                             ctypes.c_float(0.1), P(1), P(1), None)
     assert st == -5
+
+
+def test_head_split_automatic_choice(lib):
+    ip, lp = _table([4096] * 64, 64)
+    info = mla.Plan(ip, lp, 128, 64, num_cus=256).info()
+    assert info["head_split"] == 4 and info["kernel_heads"] == 32 and info["num_partials"] == 0
+    lengths = list(np.random.default_rng(4).integers(1, 2049, 768))
+    ip, lp = _table(lengths, 16)
+    info = mla.Plan(ip, lp, 64, 16, num_cus=256).info()
+    assert info["head_split"] == 1 and info["kernel_heads"] == 64
+    ip, lp = _table([100, 200], 16)
+    assert mla.Plan(ip, lp, 16, 16, num_cus=256).info()["head_split"] == 1
+
+
+@pytest.mark.parametrize("heads,hs", [(128, 1), (128, 2), (128, 4), (64, 2), (32, 2)])
+def test_head_split_explicit(lib, heads, hs):
+    lengths = [333, 4096, 17, 0, 1000]
+    ip, lp = _table(lengths, 32)
+    plan = mla.Plan(ip, lp, heads, 32, num_cus=64, head_split=hs)
+    info = plan.info()
+    assert info["head_split"] == hs and info["kernel_heads"] == heads // hs
+    _check_plan(plan, lengths, info["granularity"])
+
+
+def test_head_split_rows_share_an_xcd(lib):
+    ip, lp = _table([4096] * 64, 64)
+    plan = mla.Plan(ip, lp, 128, 64, num_cus=256)
+    seg, wp = plan.segments()
+    xcd_of_request = {}
+    for w in range(len(wp) - 1):
+        for s_ in seg[wp[w]:wp[w + 1]]:
+            xcd_of_request.setdefault(int(s_[0]) // 4, set()).add(w % 8)
+    assert len(xcd_of_request) == 64
+    assert all(len(x) == 1 for x in xcd_of_request.values())
+
+
+def test_bad_head_split_rejected(lib):
+    ip, lp = _table([10], 16)
+    for heads, hs in ((128, 3), (16, 2), (64, 8)):
+        with pytest.raises(mla.MlaError):
+            mla.Plan(ip, lp, heads, 16, num_cus=8, head_split=hs)

@@ -44,13 +44,14 @@ def dev(inp):
     return t
 
 
-def gpu_run(inp, t=None, force_splits=0):
+def gpu_run(inp, t=None, force_splits=0, head_split=0):
     import mla_paged_kv_decode_amd as mla
     t = t or dev(inp)
     o, lse = mla.decode(t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_indptr"],
                         t["kv_indices"], t["kv_last_page_len"], inp.sm_scale, inp.kv_dtype,
                         t["kv_scale"], kv_indptr_host=inp.kv_indptr,
-                        kv_last_page_len_host=inp.kv_last_page_len, force_splits=force_splits)
+                        kv_last_page_len_host=inp.kv_last_page_len, force_splits=force_splits,
+                        head_split=head_split)
     torch.cuda.synchronize()
     return o, lse
 
@@ -96,6 +97,18 @@ def test_ragged_lengths_all_shapes(heads, page):
     print("case heads=%d page=%d" % (heads, page), flush=True)
     o, lse = host(*gpu_run(inp))
     check(o, lse, *ref(inp))
+
+
+@pytest.mark.parametrize("heads,hs", [(128, 1), (128, 2), (128, 4), (64, 1), (64, 2),
+                                      (32, 2)])
+def test_head_split_matches_oracle(heads, hs):
+    inp = synth.make_inputs([700, 1, 4096, 65, 0, 1999], heads, 32, seed=300 + hs, poison=True,
+                            extra_pages=3)
+    print("case heads=%d head_split=%d" % (heads, hs), flush=True)
+    o, lse = host(*gpu_run(inp, head_split=hs))
+    check(o, lse, *ref(inp))
+    o2, lse2 = host(*gpu_run(inp, head_split=hs, force_splits=3))
+    check(o2, lse2, *ref(inp))
 
 
 def test_tiny_workload():
