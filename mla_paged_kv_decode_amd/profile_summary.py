@@ -26,8 +26,9 @@ import sqlite3
 
 # decode kernel template arguments -> the workload bench.py runs it on
 WORKLOAD_OF_KERNEL = {
-    "mla_decode_bf16_kernel<1, 4, 1, 2>": "mem_b64_h16_l4096_p64",
-    "mla_decode_bf16_kernel<8, 1, 2, 3>": "compute_b64_h128_l4096_p64",
+    "mla_decode_wave_kernel<4, 2>": "mem_b64_h16_l4096_p64",
+    "mla_decode_ring_kernel<2, 1, 2, 1, 4>": "compute_b64_h128_l4096_p64",
+    "mla_decode_ring_kernel<8, 1, 1, 2, 4>": "compute_b64_h128_l4096_p64",
 }
 
 
@@ -104,6 +105,8 @@ def main():
         alg = None
         if bench and bench["config"]["workload"] == workload:
             alg = bench["config"]["algorithmic_bytes"]
+        elif workload.startswith("compute_b64_h128_l4096"):
+            alg = 319865348  # batch 64, 128 heads, 4096 tokens: inputs + outputs once
         sec = bench.get("secondary") if bench else None
         lines = [
             "# `%s` on `%s`" % (kname, workload), "",

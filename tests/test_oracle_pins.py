@@ -429,3 +429,12 @@ def test_pins_catch_planted_mistake(name):
             oracle._SRC = os.path.join(os.path.dirname(oracle.__file__), "mla_oracle.c")
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+
+
+def test_bf16_token_record_is_1152_bytes():
+    # "FlashMLA Ampere v2", "What is added": the bf16 latent token takes 1152 bytes
+    # (512 ckv + 64 kpe values, 2 bytes each); the 8-bit record the pages describe is
+    # 644 bytes and their ideal speed-up 1152 / 644 = 1.79 ("Performance").
+    inp = synth.make_inputs([3], 16, 16, seed=1)
+    assert inp.kv_bytes_per_token() == 1152
+    assert round(1152 / 644, 2) == 1.79
