@@ -36,6 +36,11 @@ METRIC = "MLA decode: HBM GB/s at h_q=16, bf16 TFLOPS at h_q=128, % of roofline"
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", "kernels.hip")
+# other workloads measured in the same run (parity cases at full size)
+SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
+             "fp8_b64_h16_l8192_p64", "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64",
+             "int8_b64_h128_l8192_p64")
+KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8"}
 
 
 class Hip:
@@ -102,13 +107,17 @@ def device_inputs(inp, copies: int):
     def i32(a):
         return torch.from_numpy(a).to(d)
 
+    def kv(a):  # bf16 bits or 8-bit codes
+        return bf(a) if a.dtype == np.uint16 else torch.from_numpy(a).to(d)
+
     sets = []
-    base = dict(q_nope=bf(inp.q_nope), q_pe=bf(inp.q_pe), ckv=bf(inp.ckv), kpe=bf(inp.kpe),
+    base = dict(q_nope=bf(inp.q_nope), q_pe=bf(inp.q_pe), ckv=kv(inp.ckv), kpe=kv(inp.kpe),
+                kv_scale=None if inp.kv_scale is None else torch.from_numpy(inp.kv_scale).to(d),
                 kv_indptr=i32(inp.kv_indptr), kv_indices=i32(inp.kv_indices),
                 kv_last_page_len=i32(inp.kv_last_page_len))
     sets.append(base)
     for _ in range(copies - 1):
-        sets.append({k: v.clone() for k, v in base.items()})
+        sets.append({k: None if v is None else v.clone() for k, v in base.items()})
     return sets
 
 
@@ -132,7 +141,7 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     def step(i):
         s = sets[i % copies]
         o, lse = outs[i % copies]
-        plan.run(s["q_nope"], s["q_pe"], s["ckv"], s["kpe"], None, s["kv_indptr"],
+        plan.run(s["q_nope"], s["q_pe"], s["ckv"], s["kpe"], s["kv_scale"], s["kv_indptr"],
                  s["kv_indices"], s["kv_last_page_len"], inp.sm_scale, o, lse)
 
     for i in range(warmup):
@@ -161,6 +170,31 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
                 ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
                 kernel_ms=sum(kern) / len(kern), kernel_ms_min=min(kern), plan_ms=plan_ms,
                 plan=info)
+
+
+def workload_report(m: dict, peaks: dict) -> dict:
+    """Throughput of one measured workload against both roofs: HBM bytes for
+    the memory-bound head counts (h_q <= 64), bf16 MFMA flops for h_q = 128."""
+    inp = m["inp"]
+    k_s = m["kernel_ms"] * 1e-3
+    gbs, tfs = m["bytes"] / k_s / 1e9, m["flops"] / k_s / 1e12
+    mfma = inp.num_heads >= 128
+    r = {"workload": m["name"], "kv_dtype": KV_NAMES[inp.kv_dtype],
+         "value": round((m["flops"] / 1e12 if mfma else m["bytes"] / 1e9)
+                        / (m["ms_per_step"] * 1e-3), 2),
+         "unit": "TFLOP/s" if mfma else "GB/s", "ms_per_step": round(m["ms_per_step"], 5),
+         "kernel_ms": round(m["kernel_ms"], 5), "kernel_gbs": round(gbs, 1),
+         "kernel_tflops": round(tfs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+         "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "plan": m["plan"]}
+    if peaks:
+        r["frac_of_measured_read_peak"] = round(gbs / peaks["stream_read_gbs"], 4)
+        r["frac_of_measured_mfma_peak"] = round(tfs / peaks["mfma_bf16_tflops"], 4)
+    r["roofline"] = ({"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                      "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)} if mfma else
+                     {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)})
+    r["roofline"]["traffic"] = measured_traffic(m["name"])
+    return r
 
 
 def cpu_baseline(inp, target_s: float) -> dict:
@@ -199,8 +233,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mem_b64_h16_l4096_p64")
-    ap.add_argument("--secondary", default="compute_b64_h128_l4096_p64",
-                    help="second workload reported under 'secondary' ('none' to skip)")
+    ap.add_argument("--secondary", default=",".join(SECONDARY),
+                    help="comma-separated workloads also measured and reported under 'also' "
+                         "('none' to skip)")
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--head-split", type=int, default=0,
                     help="head split for the measured workloads (0 = the planner's choice)")
@@ -268,7 +303,7 @@ def main():
                    "kernel_sha": kernel_sha()},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "mla_decode_bf16_kernel",
+                     "traffic": traffic, "kernel": "mla_decode_stream_kernel<1, 0, 2>",
                      "kernel_ms": round(prim["kernel_ms"], 5),
                      "frac_of_measured_read_peak": (round(kern_gbs / peaks["stream_read_gbs"], 4)
                                                     if peaks else None)},
@@ -277,23 +312,12 @@ def main():
         "wall_ms_per_step": round(prim["wall_ms_per_step"], 5),
     }
     if args.secondary != "none":
-        sec = measure(args.secondary, args.steps, args.warmup, args.copies, hip, args.head_split)
-        tfs = sec["flops"] / (sec["ms_per_step"] * 1e-3) / 1e12
-        ktfs = sec["flops"] / (sec["kernel_ms"] * 1e-3) / 1e12
-        out["secondary"] = {
-            "workload": args.secondary, "value": round(tfs, 2), "unit": "TFLOP/s",
-            "ms_per_step": round(sec["ms_per_step"], 5),
-            "hbm_gbs": round(sec["bytes"] / (sec["ms_per_step"] * 1e-3) / 1e9, 2),
-            "roofline": {"bound": "mfma", "achieved": round(ktfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                         "unit": "TFLOP/s", "frac": round(ktfs / MFMA_BF16_PEAK_TFS, 4),
-                         "hbm_frac": round(sec["bytes"] / (sec["kernel_ms"] * 1e-3) / 1e9
-                                           / HBM_PEAK_GBS, 4),
-                         "traffic": measured_traffic(args.secondary),
-                         "kernel_ms": round(sec["kernel_ms"], 5),
-                         "frac_of_measured_mfma_peak": (
-                             round(ktfs / peaks["mfma_bf16_tflops"], 4) if peaks else None)},
-        }
-        del sec
+        out["also"] = []
+        for name in args.secondary.split(","):
+            sec = measure(name, args.steps, args.warmup, args.copies, hip, args.head_split)
+            out["also"].append(workload_report(sec, peaks))
+            del sec
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -217,8 +217,25 @@ class Plan:
             raise ValueError("ckv must be [pages, page_size, 512]")
         if kpe.dim() != 3 or kpe.shape[1] != self.page_size or kpe.shape[2] != D_KPE:
             raise ValueError("kpe must be [pages, page_size, 64]")
-        if self.kv_dtype == KV_BF16 and (ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16):
-            raise ValueError("bf16 cache expected")
+        if self.kv_dtype == KV_BF16:
+            if ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16:
+                raise ValueError("bf16 cache expected")
+            if kv_scale is not None:
+                raise ValueError("kv_scale must be None for a bf16 cache")
+        else:
+            codes = (torch.uint8, torch.float8_e4m3fn) if self.kv_dtype == KV_FP8_E4M3 \
+                else (torch.uint8, torch.int8)
+            if ckv.dtype not in codes or kpe.dtype not in codes:
+                raise ValueError("8-bit cache expected (one byte per value)")
+            if (kv_scale is None or kv_scale.dtype != torch.float32
+                    or tuple(kv_scale.shape) != tuple(ckv.shape[:2])):
+                raise ValueError("kv_scale must be float32 [pages, page_size]")
+        if kpe.shape[0] != ckv.shape[0]:
+            raise ValueError("ckv and kpe must hold the same pages")
+        for name, t in (("q_nope", q_nope), ("q_pe", q_pe), ("ckv", ckv), ("kpe", kpe),
+                        ("kv_scale", kv_scale), ("o", o), ("lse", lse)):
+            if t is not None and not t.is_contiguous():
+                raise ValueError(name + " must be contiguous")
         st = self._lib.mla_decode_run(
             self._h, _dptr(q_nope), _dptr(q_pe), _dptr(ckv), _dptr(kpe), _dptr(kv_scale),
             _dptr(kv_indptr), _dptr(kv_indices), _dptr(kv_last_page_len), float(sm_scale),

@@ -60,11 +60,12 @@ Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, 
 // the kernel that serves `kernel_heads` heads.  With an explicit
 // opts->num_cus (host-only planning) the per-CU count comes from the kernel's
 // LDS footprint; on a device it comes from the occupancy query.
-mla_status worker_count(const mla_plan_opts* opts, int32_t kernel_heads, int32_t* workers) {
+mla_status worker_count(const mla_plan_opts* opts, int32_t kernel_heads, int32_t kv_dtype,
+                        int32_t* workers) {
   int32_t cus = opts ? opts->num_cus : 0;
   if (cus < 0) return MLA_ERR_INVALID_ARG;
   mla_gpu::DecodeConfig cfg{};
-  if (mla_gpu::decode_config(kernel_heads, &cfg) != 0) return MLA_ERR_UNSUPPORTED;
+  if (mla_gpu::decode_config(kernel_heads, kv_dtype, &cfg) != 0) return MLA_ERR_UNSUPPORTED;
   int32_t per_cu = std::max(1, (160 * 1024) / cfg.lds_bytes);
   if (cus == 0) {
     int dev = 0;
@@ -72,7 +73,7 @@ mla_status worker_count(const mla_plan_opts* opts, int32_t kernel_heads, int32_t
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    per_cu = mla_gpu::decode_blocks_per_cu(kernel_heads);
+    per_cu = mla_gpu::decode_blocks_per_cu(kernel_heads, kv_dtype);
   }
   int32_t w = cus * per_cu;
   if (opts && opts->max_workers > 0) w = std::min(w, opts->max_workers);
@@ -87,27 +88,25 @@ int log2_exact(int32_t x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Head split for a batch: explicit (opts->head_split) or automatic: spread
-// the heads of each request over H / 32 workgroups when that many rows still
-// fit in one wave of 32-head workgroups, so that no request needs cutting.
-mla_status choose_head_split(int32_t batch, int32_t num_heads, const mla_plan_opts* opts,
+// Head split for a batch: explicit (opts->head_split) or automatic.  8-bit
+// caches are served by the 16-head kernel only, so their requests are always
+// split into 16-head rows (the rows of one request are placed on one XCD, so
+// the latent cache is read from HBM about once).  bf16 requests keep all heads
+// in one workgroup: on 64 x 128 heads x 4096 tokens that measured faster than
+// 32-head rows.
+mla_status choose_head_split(int32_t num_heads, int32_t kv_dtype, const mla_plan_opts* opts,
                              int32_t* head_split) {
   const int32_t req = opts ? opts->head_split : 0;
   if (req < 0) return MLA_ERR_INVALID_ARG;
+  mla_gpu::DecodeConfig cfg{};
   if (req > 0) {
-    if (num_heads % req != 0 || log2_exact(req) < 0 || !supported_heads(num_heads / req))
+    if (num_heads % req != 0 || log2_exact(req) < 0 ||
+        mla_gpu::decode_config(num_heads / req, kv_dtype, &cfg) != 0)
       return MLA_ERR_UNSUPPORTED;
     *head_split = req;
     return MLA_OK;
   }
-  *head_split = 1;
-  if (num_heads >= 64) {
-    int32_t w32 = 0;
-    mla_status st = worker_count(opts, 32, &w32);
-    if (st != MLA_OK) return st;
-    const int32_t hs = num_heads / 32;
-    if ((int64_t)batch * hs <= w32) *head_split = hs;
-  }
+  *head_split = kv_dtype == MLA_KV_BF16 ? 1 : num_heads / 16;
   return MLA_OK;
 }
 
@@ -156,15 +155,15 @@ const char* mla_last_error(void) { return g_last_error.c_str(); }
 size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_plan_opts* opts) {
   if (batch < 0 || !supported_heads(num_heads)) return 0;
   if (opts && (opts->force_splits < 0 || opts->head_split < 0)) return 0;
-  // bound over every head split the plan may choose
+  // bound over every head split and cache dtype the plan may choose
   size_t best = 0;
+  for (int32_t kvd = 0; kvd < 3; ++kvd)
   for (int32_t hs = 1; hs <= num_heads / 16; hs *= 2) {
     if (opts && opts->head_split > 0 && hs != opts->head_split) continue;
-    if (!supported_heads(num_heads / hs)) continue;
-    int32_t workers = 0;
-    if (worker_count(opts, num_heads / hs, &workers) != MLA_OK) return 0;
     mla_gpu::DecodeConfig cfg{};
-    if (mla_gpu::decode_config(num_heads / hs, &cfg) != 0) return 0;
+    if (mla_gpu::decode_config(num_heads / hs, kvd, &cfg) != 0) continue;
+    int32_t workers = 0;
+    if (worker_count(opts, num_heads / hs, kvd, &workers) != MLA_OK) return 0;
     const mla::PlanParams pp = plan_params(num_heads, hs, workers, cfg, opts);
     const int64_t nseg = mla::max_segments(batch, pp);
     const int64_t nparts = mla::max_partials(batch, pp);
@@ -182,12 +181,13 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   if (batch < 0 || !kv_indptr_host || (batch > 0 && !kv_last_page_len_host))
     return MLA_ERR_INVALID_ARG;
   if (!supported_heads(num_heads) || page_shift_of(page_size) < 0) return MLA_ERR_UNSUPPORTED;
-  if (kv_dtype != MLA_KV_BF16) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_INT8)
+    return MLA_ERR_UNSUPPORTED;
   if (opts && (opts->force_splits < 0 || opts->max_workers < 0)) return MLA_ERR_INVALID_ARG;
 
   if (opts && opts->head_split < 0) return MLA_ERR_INVALID_ARG;
   int32_t head_split = 1;
-  mla_status st = choose_head_split(batch, num_heads, opts, &head_split);
+  mla_status st = choose_head_split(num_heads, kv_dtype, opts, &head_split);
   if (st != MLA_OK) return st;
   const int32_t kernel_heads = num_heads / head_split;
 
@@ -200,12 +200,12 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   p->page_size = page_size;
   p->page_shift = page_shift_of(page_size);
   p->kv_dtype = kv_dtype;
-  if (mla_gpu::decode_config(kernel_heads, &p->cfg) != 0) {
+  if (mla_gpu::decode_config(kernel_heads, kv_dtype, &p->cfg) != 0) {
     delete p;
     return MLA_ERR_UNSUPPORTED;
   }
   int32_t workers = 0;
-  st = worker_count(opts, kernel_heads, &workers);
+  st = worker_count(opts, kernel_heads, kv_dtype, &workers);
   if (st != MLA_OK) {
     delete p;
     return st;
@@ -290,7 +290,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
   }
   if (p->plan.num_workers > 0) {
-    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, a, p->plan.num_workers, s);
+    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
   }
   if (p->ev_after) {

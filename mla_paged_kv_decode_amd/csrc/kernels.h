@@ -36,10 +36,13 @@ struct DecodeConfig {
   int32_t lds_bytes;  // LDS per workgroup (also bounds the split merge scratch)
 };
 
-int decode_config(int num_heads, DecodeConfig* cfg);
-// Workgroups of the decode kernel that fit on one CU (HIP occupancy query on
-// the current device; an LDS-based estimate if the query fails).
-int decode_blocks_per_cu(int num_heads);
-hipError_t launch_decode(int num_heads, const DecodeArgs& a, int grid, hipStream_t stream);
+// Kernel for `heads` heads per workgroup and a cache of `kv_dtype` (0 bf16,
+// 1 fp8 e4m3, 2 int8): returns -1 when no kernel serves the pair.
+int decode_config(int heads, int kv_dtype, DecodeConfig* cfg);
+// Workgroups of that kernel resident on one CU (HIP occupancy query on the
+// current device; an LDS-based estimate if the query fails).
+int decode_blocks_per_cu(int heads, int kv_dtype);
+hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
+                         hipStream_t stream);
 
 }  // namespace mla_gpu

@@ -45,6 +45,7 @@ namespace mla_gpu {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -232,13 +233,16 @@ constexpr int merge_bytes() {
   return TS > 1 ? HG * TS * 16 * kMergeStride * 4 + HG * TS * 16 * 8 : 0;
 }
 
+// HG here is the number of merge-slot columns: a call merges slot (ts, hg) ->
+// ts * HG + hg; `hblock` is the 16-head block of the output rows it writes.
 template <int H, int HG, int TS>
 __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&acc)[32],
                                                  float m_run, float l_run, int b, int slot,
-                                                 int hg, int ts, int lane, uint8_t* smem) {
+                                                 int hblock, int hg, int ts, int lane,
+                                                 uint8_t* smem) {
   constexpr int kWaves = HG * TS;  // merge slots: (ts, hg) -> ts * HG + hg
   const int qr = lane & 15;
-  const int head = hg * 16 + qr;
+  const int head = hblock * 16 + qr;
   const int mslot = ts * HG + hg;
   const float l_tot = wave_sum_16(l_run);
   if constexpr (TS == 1) {
@@ -315,7 +319,7 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
       const bool empty = !(L > 0.f);
       const float inv = empty ? 0.f : 1.f / L;
       const float lse_v = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
-      const int hd = hg * 16 + hh;
+      const int hd = hblock * 16 + hh;
       if (slot < 0) {
         bf16x8 v;
 #pragma unroll
@@ -692,43 +696,77 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
     // ---- epilogue -----------------------------------------------------------
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
-      write_head_block<H, HG, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, wh * HB + hb, ts,
-                                  lane, smem);
+      write_head_block<H, HG, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, wh * HB + hb,
+                                  wh * HB + hb, ts, lane, smem);
     finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Register-staged variant for 16 query heads (one head group).  The work is
-// memory bound (about 30 flop per byte of KV), so what matters is the number
-// of bytes in flight per CU and keeping the waves out of each other's way:
-//   * TS waves split a segment's 16-token groups round-robin (wave w takes
-//     groups w, w + TS, ...); each wave runs its own pipeline with no
-//     workgroup barrier until the end of the segment.
-//   * a group (16 rows x 1152 B) is fetched with 18 coalesced 16-byte loads
-//     per lane into registers, NBUF groups ahead, so the vector register file
-//     (not LDS) holds the data in flight: NBUF x 18 KiB per wave;
-//   * the group is then written to a wave-private 18 KiB LDS buffer (same
-//     swizzled layout as the LDS ring) and consumed by the QK and PV MFMAs;
-//   * Q^T (16 heads x 576) sits in LDS once per segment, [chunk][head], so the
-//     registers go to the groups in flight.
+// Register-staged kernel for 16 or 32 heads per workgroup (HB 16-head blocks),
+// with a bf16, fp8-e4m3 or int8 latent cache (KVT 0 / 1 / 2).  At these head
+// counts the work is memory bound, so what matters is the number of bytes in
+// flight per CU and keeping the waves out of each other's way:
+//   * 4 waves split a segment's 16-token groups round-robin (wave w takes
+//     groups w, w + 4, ...); each wave runs its own pipeline with no workgroup
+//     barrier until the end of the segment;
+//   * a group is fetched with coalesced 16-byte loads per lane into registers,
+//     two groups ahead, so the vector register file (not LDS) holds the data
+//     in flight;
+//   * the group is then written to a wave-private 18 KiB LDS buffer in the
+//     swizzled bf16 layout of the LDS ring (8-bit codes are converted exactly
+//     to bf16 on the way) and consumed by the QK and PV MFMAs;
+//   * Q^T (HB x 16 heads x 576) sits in LDS once per segment, [chunk][head].
+// 8-bit caches (FlashMLA Ampere v2, "What is added": FP8 e4m3 or INT8 with one
+// scale per token, dequantised in the kernel): codes become bf16 exactly; the
+// token's scale multiplies its score (after QK, in fp32) and its probability
+// (before P is rounded to bf16 for PV), which is the same as dequantising the
+// row first.
 // ---------------------------------------------------------------------------
-template <int TS, int NBUF>
-struct WaveShape {
-  static constexpr int kThreads = 64 * TS;
-  static constexpr int kBufBytes = 18 * 1024;       // one 16-row group per wave
-  static constexpr int kQBytes = 72 * 16 * 16;      // Q^T: [chunk][head] x 16 B
-  static constexpr int kQOffset = TS * kBufBytes;
-  static constexpr int kMergeBytes = merge_bytes<16, 1, TS>();
+template <int HB, int KVT, int NB>
+struct StreamShape {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kHeads = 16 * HB;
+  static constexpr int kBufBytes = 18 * 1024;       // one 16-row bf16 group per wave
+  static constexpr int kQBytes = HB * 72 * 16 * 16;  // Q^T: [block][chunk][head] x 16 B
+  static constexpr int kQOffset = kWaves * kBufBytes;
+  static constexpr int kMergeBytes = merge_bytes<16, 1, kWaves>();  // one head block at a time
   static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
                                                                     : kMergeBytes;
+  static constexpr int kLoads = KVT == 0 ? 18 : 9;  // 16-byte loads per lane per group
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-template <int TS, int NBUF>
-__global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeArgs a) {
-  using S = WaveShape<TS, NBUF>;
-  constexpr int H = 16;
+// 8 codes (two dwords) -> 8 bf16 values, exactly.
+template <int KVT>
+__device__ __forceinline__ u32x4 codes_to_bf16(unsigned lo, unsigned hi) {
+  u32x4 r;
+  if constexpr (KVT == 1) {  // OCP fp8 e4m3: hardware conversion, scale 1
+    r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false));
+    r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true));
+    r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false));
+    r[3] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, true));
+  } else {  // int8: |v| <= 128 is exact in bf16
+    const unsigned w[2] = {lo, hi};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned x = w[k >> 1] >> (16 * (k & 1));
+      bf16x2 v;
+      v[0] = (__bf16)(float)(signed char)(x & 0xFF);
+      v[1] = (__bf16)(float)(signed char)((x >> 8) & 0xFF);
+      r[k] = __builtin_bit_cast(unsigned, v);
+    }
+  }
+  return r;
+}
+
+template <int HB, int KVT, int NB>
+__global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs a) {
+  using S = StreamShape<HB, KVT, NB>;
+  constexpr int H = S::kHeads;
+  constexpr int TS = S::kWaves;
+  constexpr int NL = S::kLoads;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
   __shared__ int s_last;
 
@@ -739,8 +777,6 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
   const int page_mask = (1 << page_shift) - 1;
   uint8_t* wbuf = smem + wave * S::kBufBytes;
 
-  // loader: lane covers row (rh * 8 + lane / 8) of block (rh, cb), 16-byte
-  // chunk cb * 8 + ((lane & 7) ^ swz(row)); it writes LDS slot `lane` of the block
   const int ld_r_lo = lane >> 3;
   // QK operand: token row lane & 15, chunk 4 s + (lane >> 4)
   const int qr = lane & 15;
@@ -754,6 +790,24 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
   int tr_off[4];
 #pragma unroll
   for (int A = 0; A < 4; ++A) tr_off[A] = tr_base + (((2 * A) | (tr_q >> 1)) ^ swz(tr_r)) * 16;
+  // 8-bit layout: load u < 8 covers row (u >> 2) * 8 + lane / 8, bytes
+  // (u & 3) * 128 + (lane & 7) * 16 of ckv, i.e. bf16 chunks c, c + 1 with
+  // c = (u & 3) * 16 + 2 (lane & 7); load 8 covers row lane / 4, kpe bytes
+  // (lane & 3) * 16 (chunks 64 + 2 (lane & 3), + 1).  LDS byte offsets of the
+  // two converted chunks, apart from immediates:
+  int st8[2][2], st8k[2];
+  {
+    const int xr = lane >> 3;
+    const int base = ((lane >> 2) & 1) * 1024 + xr * 128;
+#pragma unroll
+    for (int rh = 0; rh < 2; ++rh)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) st8[rh][e] = base + (((2 * (lane & 3) + e) ^ xr ^ rh) * 16);
+    const int rk = lane >> 2;
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      st8k[e] = (rk >> 3) * kHalfGroupBytes + 8 * 1024 + ((rk & 7) * 8 + ((2 * (lane & 3) + e) ^ swz(rk))) * 16;
+  }
 
   const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
   const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
@@ -775,112 +829,164 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
     const int ngroups = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
     const int nmine = ngroups > wave ? (ngroups - 1 - wave) / TS + 1 : 0;
 
-    // Q^T for the request into LDS: item (chunk c, head h) at (c * 16 + h) * 16
+    // Q^T for the row block into LDS: item (block, chunk c, head h) at
+    // ((block * 72 + c) * 16 + h) * 16
     uint8_t* qlds = smem + S::kQOffset;
     lds_barrier();  // previous segment's merge / combine done with this LDS
-    for (int x = tid; x < 72 * 16; x += S::kThreads) {
-      const int c = x >> 4, h = x & 15;
+    for (int x = tid; x < HB * 72 * 16; x += S::kThreads) {
+      const int hb = x / (72 * 16);
+      const int c = (x >> 4) % 72, h = hb * 16 + (x & 15);
       const u32x4 v = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
                              : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
       *reinterpret_cast<u32x4*>(qlds + x * 16) = v;
     }
     lds_barrier();
-    const uint8_t* qbase = qlds + ((lane >> 4) * 16 + qr) * 16;  // + s * 1024 for step s
+    const uint8_t* qbase = qlds + ((lane >> 4) * 16 + qr) * 16;  // + (hb * 72 + s * 4) * 256
 
-    float m_run = -INFINITY;
-    float l_run = 0.f;
-    f32x4 acc[32];
+    float m_ref[HB], l_run[HB];
+    f32x4 acc[HB][32];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int hb = 0; hb < HB; ++hb) {
+      m_ref[hb] = -INFINITY;
+      l_run[hb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    // Fetch this wave's j-th group into registers.  Every call issues the same
-    // 18 loads, also past the last group (then from a fixed, valid address),
-    // so that the number of loads in flight is the same on every path and the
-    // compiler's vmcnt waits only cover the group being consumed.  A lane
-    // covers one row of each half group: rows lane / 8 and 8 + lane / 8, 16-byte
-    // chunk (lane & 7) ^ swz(row) of every 128-byte block of the row.
+    // Fetch this wave's j-th group into registers: NL 16-byte loads per lane
+    // (+ the four token scales of this lane's score rows for 8-bit caches).
+    // Every call issues the same loads, also past the last group (then from a
+    // fixed, valid address), so the number of loads in flight is the same on
+    // every path and the compiler's vmcnt waits only cover the group consumed.
     const uint8_t* dummy = reinterpret_cast<const uint8_t*>(a.q_nope + (size_t)b * H * 512);
-    auto fetch = [&](int j, u32x4 (&st)[18]) __attribute__((always_inline)) {
+    auto fetch = [&](int j, u32x4 (&st)[NL], f32x4& sc) __attribute__((always_inline)) {
       const bool live = j < nmine;
       const int gs = t0 + 16 * (wave + TS * j);
       const int page = live ? ld_const(a.kv_indices + pbeg + (gs >> page_shift)) : 0;
+      const size_t pbase = (size_t)page << page_shift;
+      if constexpr (KVT == 0) {
 #pragma unroll
-      for (int rh = 0; rh < 2; ++rh) {
-        const int r = rh * 8 + ld_r_lo;
-        const int tok = min(gs + r, t1 - 1);
-        const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
-        const int sw = ((lane & 7) ^ swz(r)) * 16;
-        const uint8_t* cbase = live ? a.ckv + row * 1024 + sw : dummy + sw;
-        const uint8_t* kbase = live ? a.kpe + row * 128 + sw : dummy + sw;
+        for (int rh = 0; rh < 2; ++rh) {
+          const int r = rh * 8 + ld_r_lo;
+          const size_t row = pbase + (min(gs + r, t1 - 1) & page_mask);
+          const int sw = ((lane & 7) ^ swz(r)) * 16;
+          const uint8_t* cbase = live ? a.ckv + row * 1024 + sw : dummy + sw;
+          const uint8_t* kbase = live ? a.kpe + row * 128 + sw : dummy + sw;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb)
-          st[rh * 9 + cb] = *reinterpret_cast<const u32x4*>(cbase + cb * 128);
-        st[rh * 9 + 8] = *reinterpret_cast<const u32x4*>(kbase);
+          for (int cb = 0; cb < 8; ++cb)
+            st[rh * 9 + cb] = *reinterpret_cast<const u32x4*>(cbase + cb * 128);
+          st[rh * 9 + 8] = *reinterpret_cast<const u32x4*>(kbase);
+        }
+      } else {
+#pragma unroll
+        for (int rh = 0; rh < 2; ++rh) {
+          const int r = rh * 8 + ld_r_lo;
+          const size_t row = pbase + (min(gs + r, t1 - 1) & page_mask);
+          const uint8_t* cbase = live ? a.ckv + row * 512 + (lane & 7) * 16 : dummy;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb)
+            st[rh * 4 + cb] = *reinterpret_cast<const u32x4*>(cbase + cb * 128);
+        }
+        const size_t rowk = pbase + (min(gs + (lane >> 2), t1 - 1) & page_mask);
+        st[8] = *reinterpret_cast<const u32x4*>(live ? a.kpe + rowk * 64 + (lane & 3) * 16 : dummy);
+        // scales of score rows 4 (lane >> 4) .. + 3 (16-byte aligned, same page)
+        const size_t rows = pbase + ((gs + 4 * (lane >> 4)) & page_mask);
+        sc = *reinterpret_cast<const f32x4*>(live ? reinterpret_cast<const uint8_t*>(a.kv_scale + rows)
+                                                  : dummy);
       }
     };
 
     // Consume group j from registers st: LDS write and refill (always, so the
     // memory queue looks the same on every path), then QK, online softmax and
     // PV if the group exists.
-    auto consume = [&](int j, u32x4 (&st)[18]) __attribute__((always_inline)) {
+    auto consume = [&](int j, u32x4 (&st)[NL], f32x4& sc) __attribute__((always_inline)) {
+      f32x4 sig = sc;
+      if constexpr (KVT == 0) {
 #pragma unroll
-      for (int blk = 0; blk < 18; ++blk)
-        *reinterpret_cast<u32x4*>(wbuf + blk * 1024 + lane * 16) = st[blk];
-      fetch(j + NBUF, st);  // registers free again: next group in flight
+        for (int blk = 0; blk < 18; ++blk)
+          *reinterpret_cast<u32x4*>(wbuf + blk * 1024 + lane * 16) = st[blk];
+      } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int rh = u >> 2, cb = u & 3;
+          *reinterpret_cast<u32x4*>(wbuf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][0]) =
+              codes_to_bf16<KVT>(st[u][0], st[u][1]);
+          *reinterpret_cast<u32x4*>(wbuf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][1]) =
+              codes_to_bf16<KVT>(st[u][2], st[u][3]);
+        }
+        *reinterpret_cast<u32x4*>(wbuf + st8k[0]) = codes_to_bf16<KVT>(st[8][0], st[8][1]);
+        *reinterpret_cast<u32x4*>(wbuf + st8k[1]) = codes_to_bf16<KVT>(st[8][2], st[8][3]);
+      }
+      fetch(j + NB, st, sc);  // registers free again: NB groups ahead in flight
       if (j >= nmine) return;
 
-      // QK: S^T[16 tokens][16 heads], two partial chains; K and Q^T from LDS
+      // QK: S^T[16 tokens][16 heads] per head block; K and Q^T from LDS
       const uint8_t* gbase = wbuf + qk_base;
-      f32x4 c0 = f32x4{0.f, 0.f, 0.f, 0.f}, c1 = f32x4{0.f, 0.f, 0.f, 0.f};
+      f32x4 sacc[HB];
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s0 = 0; s0 < 18; s0 += 6) {
-        bf16x8 kf[6], qf[6];
+        bf16x8 kf[6];
 #pragma unroll
         for (int u = 0; u < 6; ++u) {
           const int s = s0 + u;
           kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
               (const LDS_AS uint8_t*)(gbase + (s >> 1) * 1024 + ((s & 1) ? qk_off_odd : qk_off_even)));
-          qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>((const LDS_AS uint8_t*)(qbase + s * 1024));
         }
 #pragma unroll
-        for (int u = 0; u < 6; u += 2) {
-          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[u], c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u + 1], qf[u + 1], c1, 0, 0, 0);
+        for (int hb = 0; hb < HB; ++hb) {
+          bf16x8 qf[6];
+#pragma unroll
+          for (int u = 0; u < 6; ++u)
+            qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+                (const LDS_AS uint8_t*)(qbase + (hb * 72 + (s0 + u) * 4) * 256));
+#pragma unroll
+          for (int u = 0; u < 6; ++u)
+            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[u], sacc[hb], 0, 0, 0);
         }
       }
-      f32x4 sacc = c0 + c1;
 
-      // online softmax, log2 domain; rows past the segment end are masked
+      // online softmax, log2 domain, lazy rescale; rows past the end masked
       const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
-      float tmax = -INFINITY;
+      if constexpr (KVT != 0) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = (row0 + i < t1) ? sacc[i] * a.scale_log2 : -INFINITY;
-        sacc[i] = x;
-        tmax = fmaxf(tmax, x);
+        for (int i = 0; i < 4; ++i) sig[i] = (row0 + i < t1) ? sig[i] : 0.f;
       }
-      tmax = wave_max_16(tmax);
-      if (__builtin_amdgcn_ballot_w64(tmax > m_run + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 when m_run = -inf
-        l_run *= alpha;
+      s16x4 pv[HB];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-      bf16x4 pb;
+      for (int hb = 0; hb < HB; ++hb) {
+        float tmax = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sacc[i] - m_use);
-        psum += p;
-        pb[i] = (__bf16)p;
+        for (int i = 0; i < 4; ++i) {
+          const float raw = KVT != 0 ? sacc[hb][i] * sig[i] : sacc[hb][i];
+          const float x = (row0 + i < t1) ? raw * a.scale_log2 : -INFINITY;
+          sacc[hb][i] = x;
+          tmax = fmaxf(tmax, x);
+        }
+        tmax = wave_max_16(tmax);
+        if (__builtin_amdgcn_ballot_w64(tmax > m_ref[hb] + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_ref[hb], tmax);
+          const float alpha = __builtin_amdgcn_exp2f(m_ref[hb] - m_new);  // 0 when m_ref = -inf
+          l_run[hb] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) acc[hb][i] *= alpha;
+          m_ref[hb] = m_new;
+        }
+        const float m_use = m_ref[hb] == -INFINITY ? 0.f : m_ref[hb];
+        float psum = 0.f;
+        bf16x4 pb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = __builtin_amdgcn_exp2f(sacc[hb][i] - m_use);
+          psum += p;
+          pb[i] = (__bf16)(KVT != 0 ? p * sig[i] : p);  // V = scale x codes
+        }
+        l_run[hb] += psum;
+        pv[hb] = __builtin_bit_cast(s16x4, pb);
       }
-      l_run += psum;
 
       // PV: O^T[c][h] += V^T[c][t] P^T[t][h]
-      const s16x4 pv = __builtin_bit_cast(s16x4, pb);
 #pragma unroll
       for (int c8 = 0; c8 < 32; c8 += 8) {
         s16x4 vf[8];
@@ -892,21 +998,34 @@ __global__ void __launch_bounds__(64 * TS) mla_decode_wave_kernel(const DecodeAr
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          acc[c8 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[u], pv, acc[c8 + u], 0, 0, 0);
+#pragma unroll
+          for (int hb = 0; hb < HB; ++hb)
+            acc[hb][c8 + u] =
+                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[u], pv[hb], acc[hb][c8 + u], 0, 0, 0);
       }
     };
 
-    static_assert(NBUF == 2, "two register buffers, unrolled by hand");
-    u32x4 stA[18], stB[18];
-    fetch(0, stA);
-    fetch(1, stB);
-    for (int j = 0; j < nmine; j += 2) {
-      consume(j, stA);
-      consume(j + 1, stB);
+    if constexpr (NB == 2) {
+      u32x4 stA[NL], stB[NL];
+      f32x4 scA, scB;
+      fetch(0, stA, scA);
+      fetch(1, stB, scB);
+      for (int j = 0; j < nmine; j += 2) {
+        consume(j, stA, scA);
+        consume(j + 1, stB, scB);
+      }
+    } else {
+      u32x4 stA[NL];
+      f32x4 scA;
+      fetch(0, stA, scA);
+      for (int j = 0; j < nmine; ++j) consume(j, stA, scA);
     }
 
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
-    write_head_block<H, 1, TS>(a, acc, m_run, l_run, b, slot, 0, wave, lane, smem);
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      write_head_block<H, 1, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave, lane,
+                                 smem);
     finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
   }
 }
@@ -920,49 +1039,56 @@ static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t s
   return hipGetLastError();
 }
 
+template <int HG, int HB, int TS, int MB, int NSTAGE>
+static DecodeConfig config_of() {
+  using S = RingShape<HG, HB, TS, MB, NSTAGE>;
+  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
+}
+
+template <int HB, int KVT, int NB>
+static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
+  using S = StreamShape<HB, KVT, NB>;
+  hipLaunchKernelGGL((mla_decode_stream_kernel<HB, KVT, NB>), dim3(grid), dim3(S::kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int HB, int KVT, int NB>
+static DecodeConfig stream_config_of() {
+  using S = StreamShape<HB, KVT, NB>;
+  return DecodeConfig{S::kWaves, 16, S::kLdsBytes};
+}
+
+template <int HB, int KVT, int NB>
+static int stream_occupancy_of() {
+  using S = StreamShape<HB, KVT, NB>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&mla_decode_stream_kernel<HB, KVT, NB>), S::kThreads,
+          0) != hipSuccess ||
+      n < 1)
+    n = (160 * 1024) / S::kLdsBytes;
+  return n < 1 ? 1 : n;
+}
+
 // Ring-kernel shape per head count: <16-head blocks, blocks per wave,
 // token-split waves, row groups per wave per tile, ring stages>.
-// 16 heads: the register-staged kernel <waves, groups in flight per wave>
-#ifndef MLA_WAVE_H16
-#define MLA_WAVE_H16 4, 2
-#endif
-#ifndef MLA_CFG_H32
-#define MLA_CFG_H32 2, 1, 2, 1, 4
-#endif
 #ifndef MLA_CFG_H64
 #define MLA_CFG_H64 4, 1, 1, 2, 4
 #endif
 #ifndef MLA_CFG_H128
 #define MLA_CFG_H128 8, 1, 1, 2, 4
 #endif
-
-template <int TS, int NBUF>
-static hipError_t launch_wave_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_wave_kernel<TS, NBUF>), dim3(grid), dim3(64 * TS), 0, stream, a);
-  return hipGetLastError();
-}
-
-template <int TS, int NBUF>
-static DecodeConfig wave_config_of() {
-  return DecodeConfig{TS, 16, WaveShape<TS, NBUF>::kLdsBytes};
-}
-
-template <int TS, int NBUF>
-static int wave_occupancy_of() {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&mla_decode_wave_kernel<TS, NBUF>), 64 * TS, 0) !=
-          hipSuccess ||
-      n < 1)
-    n = (160 * 1024) / WaveShape<TS, NBUF>::kLdsBytes;
-  return n < 1 ? 1 : n;
-}
-
-template <int HG, int HB, int TS, int MB, int NSTAGE>
-static DecodeConfig config_of() {
-  using S = RingShape<HG, HB, TS, MB, NSTAGE>;
-  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
-}
+// 32-head bf16 rows: 0 = LDS ring <2, 1, 2, 1, 4>, 1 = register-staged
+// stream kernel with two head blocks per wave (needs more than the 512
+// registers of a lane, so it spills; kept for comparison).
+#ifndef MLA_H32_STREAM
+#define MLA_H32_STREAM 0
+#endif
+// groups staged in registers per wave for 32-head rows
+#ifndef MLA_H32_NB
+#define MLA_H32_NB 1
+#endif
 
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 static int occupancy_of() {
@@ -976,34 +1102,68 @@ static int occupancy_of() {
   return n < 1 ? 1 : n;
 }
 
-int decode_blocks_per_cu(int num_heads) {
-  switch (num_heads) {
-    case 16: return wave_occupancy_of<MLA_WAVE_H16>();
-    case 32: return occupancy_of<MLA_CFG_H32>();
-    case 64: return occupancy_of<MLA_CFG_H64>();
-    case 128: return occupancy_of<MLA_CFG_H128>();
-    default: return 1;
+// One switch describes the kernel chosen for (heads per workgroup, cache
+// dtype); `op` is 0 = config, 1 = occupancy, 2 = launch.
+static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const DecodeArgs* a,
+                    int grid, hipStream_t stream, hipError_t* err) {
+#define MLA_STREAM(...)                                                     \
+  do {                                                                      \
+    if (op == 0) *cfg = stream_config_of<__VA_ARGS__>();                    \
+    if (op == 1) return stream_occupancy_of<__VA_ARGS__>();                 \
+    if (op == 2) *err = launch_stream_cfg<__VA_ARGS__>(*a, grid, stream);   \
+    return 1;                                                               \
+  } while (0)
+#define MLA_RING(...)                                                       \
+  do {                                                                      \
+    if (op == 0) *cfg = config_of<__VA_ARGS__>();                           \
+    if (op == 1) return occupancy_of<__VA_ARGS__>();                        \
+    if (op == 2) *err = launch_decode_cfg<__VA_ARGS__>(*a, grid, stream);   \
+    return 1;                                                               \
+  } while (0)
+  if (kv_dtype == 0) {
+    switch (heads) {
+      case 16: MLA_STREAM(1, 0, 2);
+#if MLA_H32_STREAM
+      case 32: MLA_STREAM(2, 0, MLA_H32_NB);
+#else
+      case 32: MLA_RING(2, 1, 2, 1, 4);
+#endif
+      case 64: MLA_RING(MLA_CFG_H64);
+      case 128: MLA_RING(MLA_CFG_H128);
+      default: return 0;
+    }
   }
+  if (kv_dtype == 1) {
+    switch (heads) {
+      case 16: MLA_STREAM(1, 1, 2);
+      default: return 0;
+    }
+  }
+  if (kv_dtype == 2) {
+    switch (heads) {
+      case 16: MLA_STREAM(1, 2, 2);
+      default: return 0;
+    }
+  }
+  return 0;
+#undef MLA_STREAM
+#undef MLA_RING
 }
 
-int decode_config(int num_heads, DecodeConfig* cfg) {
-  switch (num_heads) {
-    case 16: *cfg = wave_config_of<MLA_WAVE_H16>(); return 0;
-    case 32: *cfg = config_of<MLA_CFG_H32>(); return 0;
-    case 64: *cfg = config_of<MLA_CFG_H64>(); return 0;
-    case 128: *cfg = config_of<MLA_CFG_H128>(); return 0;
-    default: return -1;
-  }
+int decode_config(int heads, int kv_dtype, DecodeConfig* cfg) {
+  return dispatch(heads, kv_dtype, 0, cfg, nullptr, 0, nullptr, nullptr) ? 0 : -1;
 }
 
-hipError_t launch_decode(int num_heads, const DecodeArgs& a, int grid, hipStream_t stream) {
-  switch (num_heads) {
-    case 16: return launch_wave_cfg<MLA_WAVE_H16>(a, grid, stream);
-    case 32: return launch_decode_cfg<MLA_CFG_H32>(a, grid, stream);
-    case 64: return launch_decode_cfg<MLA_CFG_H64>(a, grid, stream);
-    case 128: return launch_decode_cfg<MLA_CFG_H128>(a, grid, stream);
-    default: return hipErrorInvalidValue;
-  }
+int decode_blocks_per_cu(int heads, int kv_dtype) {
+  const int n = dispatch(heads, kv_dtype, 1, nullptr, nullptr, 0, nullptr, nullptr);
+  return n < 1 ? 1 : n;
+}
+
+hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
+                         hipStream_t stream) {
+  hipError_t err = hipErrorInvalidValue;
+  if (!dispatch(heads, kv_dtype, 2, nullptr, &a, grid, stream, &err)) return hipErrorInvalidValue;
+  return err;
 }
 
 }  // namespace mla_gpu

@@ -8,7 +8,9 @@ made by the same bench command (``--calib-copy-mib``): the copy kernel with the
 largest WRITE_SIZE is taken as the calibration dispatch, its expected read and
 write sizes are the calibration size.
 
-Writes, for each decode kernel found, ``profiles/<kernel>_<workload>.md`` and
+The bench command is expected to measure one workload (``--secondary none``);
+the decode kernel with the largest total time in the trace is the one
+summarised.  Writes ``profiles/<kernel>_<workload>.md`` and
 ``profiles/traffic_<workload>.json`` (HBM bytes per launch, keyed by the
 kernel-source hash printed by bench.py so that stale counters are not used).
 
@@ -23,14 +25,6 @@ import json
 import os
 import re
 import sqlite3
-
-# decode kernel template arguments -> the workload bench.py runs it on
-WORKLOAD_OF_KERNEL = {
-    "mla_decode_wave_kernel<4, 2>": "mem_b64_h16_l4096_p64",
-    "mla_decode_ring_kernel<2, 1, 2, 1, 4>": "compute_b64_h128_l4096_p64",
-    "mla_decode_ring_kernel<8, 1, 1, 2, 4>": "compute_b64_h128_l4096_p64",
-}
-
 
 def _db(d):
     p = os.path.join(d, "run_results.db")
@@ -93,21 +87,19 @@ def main():
     for name, calls, tot, avg, pct in stats:
         table.append("| `%s` | %d | %.2f | %.1f | %.1f |" % (short(name), calls, avg, tot, pct))
 
-    for kname, workload in WORKLOAD_OF_KERNEL.items():
+    workload = bench["config"]["workload"]
+    decode = [st for st in stats if "mla_decode_" in st[0]]
+    if decode:
+        kname = short(max(decode, key=lambda st: st[2])[0])
         full = [n for n in fetch if kname in n]
         if not full:
-            continue
+            raise SystemExit("no counters for " + kname)
         fk = fetch[full[0]]
         wk = write.get(full[0])
         avg_us = [s[3] for s in stats if kname in s[0]]
         fetch_b = fk["avg"] * f_scale * 1024.0
         write_b = (wk["avg"] * w_scale * 1024.0) if wk else 0.0
-        alg = None
-        if bench and bench["config"]["workload"] == workload:
-            alg = bench["config"]["algorithmic_bytes"]
-        elif workload.startswith("compute_b64_h128_l4096"):
-            alg = 319865348  # batch 64, 128 heads, 4096 tokens: inputs + outputs once
-        sec = bench.get("secondary") if bench else None
+        alg = bench["config"]["algorithmic_bytes"]
         lines = [
             "# `%s` on `%s`" % (kname, workload), "",
             "rocprofv3 summaries of `bench.py` runs on one MI355X (gfx950).", "",
@@ -129,9 +121,8 @@ def main():
             "| HBM bytes read (scaled) | %.0f |" % fetch_b,
             "| HBM bytes written (scaled) | %.0f |" % write_b,
         ]
-        if alg:
-            lines.append("| algorithmic bytes (inputs + outputs once) | %d |" % alg)
-            lines.append("| traffic / algorithmic | %.3f |" % ((fetch_b + write_b) / alg))
+        lines.append("| algorithmic bytes (inputs + outputs once) | %d |" % alg)
+        lines.append("| traffic / algorithmic | %.3f |" % ((fetch_b + write_b) / alg))
         lines.append("")
         lines.append("kernel source hash (bench.py `kernel_sha`): `%s`" % sha)
         with open(os.path.join(args.out, "%s_%s.md" % (re.sub(r"[^a-z0-9_]", "", kname.split("<")[0]),

@@ -165,15 +165,42 @@ def test_run_without_workspace_is_refused(lib):
 
 
 def test_head_split_automatic_choice(lib):
+    # bf16 keeps every head of a request in one workgroup
     ip, lp = _table([4096] * 64, 64)
     info = mla.Plan(ip, lp, 128, 64, num_cus=256).info()
-    assert info["head_split"] == 4 and info["kernel_heads"] == 32 and info["num_partials"] == 0
+    assert info["head_split"] == 1 and info["kernel_heads"] == 128
     lengths = list(np.random.default_rng(4).integers(1, 2049, 768))
     ip, lp = _table(lengths, 16)
     info = mla.Plan(ip, lp, 64, 16, num_cus=256).info()
     assert info["head_split"] == 1 and info["kernel_heads"] == 64
-    ip, lp = _table([100, 200], 16)
-    assert mla.Plan(ip, lp, 16, 16, num_cus=256).info()["head_split"] == 1
+    # 8-bit caches run 16-head rows
+    ip, lp = _table([8192] * 64, 64)
+    for heads in (16, 32, 64, 128):
+        for kvd in (mla.KV_FP8_E4M3, mla.KV_INT8):
+            info = mla.Plan(ip, lp, heads, 64, kvd, num_cus=256).info()
+            assert info["head_split"] == heads // 16 and info["kernel_heads"] == 16
+    plan = mla.Plan(ip, lp, 128, 64, mla.KV_FP8_E4M3, num_cus=256)
+    _check_plan(plan, [8192] * 64, plan.info()["granularity"])
+
+
+def test_8bit_rejects_wider_rows(lib):
+    ip, lp = _table([100], 16)
+    for hs in (1, 2, 4):
+        with pytest.raises(mla.MlaError) as e:
+            mla.Plan(ip, lp, 128, 16, mla.KV_INT8, num_cus=8, head_split=hs)
+        assert e.value.status == -2
+    with pytest.raises(mla.MlaError):
+        mla.Plan(ip, lp, 16, 16, 3, num_cus=8)
+
+
+def test_workspace_bound_covers_8bit_plans(lib):
+    lengths = list(np.random.default_rng(6).integers(1, 9000, 64))
+    ip, lp = _table(lengths, 64)
+    for heads in (16, 128):
+        n = mla.workspace_bytes(64, heads, num_cus=256)
+        info = mla.Plan(ip, lp, heads, 64, mla.KV_FP8_E4M3, num_cus=256).info()
+        need = info["num_partials"] * 16 * (512 + 1) * 4 + info["num_segments"] * 16
+        assert n >= need
 
 
 @pytest.mark.parametrize("heads,hs", [(128, 1), (128, 2), (128, 4), (64, 2), (32, 2)])
@@ -188,7 +215,7 @@ def test_head_split_explicit(lib, heads, hs):
 
 def test_head_split_rows_share_an_xcd(lib):
     ip, lp = _table([4096] * 64, 64)
-    plan = mla.Plan(ip, lp, 128, 64, num_cus=256)
+    plan = mla.Plan(ip, lp, 128, 64, num_cus=256, head_split=4)
     seg, wp = plan.segments()
     xcd_of_request = {}
     for w in range(len(wp) - 1):

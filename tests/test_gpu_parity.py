@@ -232,7 +232,9 @@ def test_graph_replay_matches_eager():
 
 
 @pytest.mark.parametrize("name", ["mem_b64_h16_l4096_p64", "compute_b64_h128_l4096_p64",
-                                  "varlen_b768_h64_l1to2048_p16"])
+                                  "varlen_b768_h64_l1to2048_p16", "fp8_b64_h16_l8192_p64",
+                                  "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64",
+                                  "int8_b64_h128_l8192_p64"])
 def test_full_workloads_sampled(name):
     inp = synth.make_workload(name, poison=True)
     print("workload", name, flush=True)
@@ -245,3 +247,72 @@ def test_full_workloads_sampled(name):
     # properties at every row: finite, |O| within the ckv range, LSE above the max score bound
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
     assert np.abs(o).max() < 8.0
+
+
+# ---- 8-bit latent caches: compared with the oracle on the dequantised values
+
+KV8 = [synth.KV_FP8_E4M3, synth.KV_INT8]
+
+
+@pytest.mark.parametrize("kv_dtype", KV8)
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("page", [16, 64])
+def test_8bit_ragged_lengths(kv_dtype, heads, page):
+    inp = synth.make_inputs(RAGGED, heads, page, kv_dtype, seed=400 + heads + page + kv_dtype,
+                            poison=True, extra_pages=5)
+    print("case kv_dtype=%d heads=%d page=%d" % (kv_dtype, heads, page), flush=True)
+    o, lse = host(*gpu_run(inp))
+    check(o, lse, *ref(inp))
+
+
+@pytest.mark.parametrize("kv_dtype", KV8)
+@pytest.mark.parametrize("heads,splits", [(16, 2), (16, 7), (128, 3)])
+def test_8bit_forced_splits(kv_dtype, heads, splits):
+    inp = synth.make_inputs([700, 64, 1, 1500, 0, 129], heads, 16, kv_dtype,
+                            seed=500 + splits + kv_dtype, poison=True)
+    print("case kv_dtype=%d heads=%d splits=%d" % (kv_dtype, heads, splits), flush=True)
+    o, lse = host(*gpu_run(inp, force_splits=splits))
+    check(o, lse, *ref(inp))
+
+
+@pytest.mark.parametrize("kv_dtype", KV8)
+def test_8bit_reruns_are_bit_identical(kv_dtype):
+    inp = synth.make_inputs([4096, 3000, 17, 1], 128, 64, kv_dtype, seed=600 + kv_dtype,
+                            poison=True)
+    t = dev(inp)
+    o0, l0 = gpu_run(inp, t)
+    for _ in range(3):
+        o1, l1 = gpu_run(inp, t)
+        assert torch.equal(o0.view(torch.int16), o1.view(torch.int16))
+        assert torch.equal(l0.view(torch.int32), l1.view(torch.int32))
+
+
+@pytest.mark.parametrize("kv_dtype", KV8)
+def test_8bit_quantisation_error_vs_bf16_source(kv_dtype):
+    """Diagnostic: the 8-bit result against the oracle on the bf16 source the
+    codes were made from (quantisation error, not kernel error).  Bounded
+    loosely; the values are printed."""
+    inp = synth.make_inputs([2048] * 4, 16, 64, kv_dtype, seed=700 + kv_dtype)
+    o, lse = host(*gpu_run(inp))
+    src = synth.MlaInputs(inp.batch, inp.num_heads, inp.page_size, synth.KV_BF16, inp.lengths,
+                          inp.q_nope, inp.q_pe, inp.ckv_src, inp.kpe_src, None, inp.kv_indptr,
+                          inp.kv_indices, inp.kv_last_page_len, inp.sm_scale)
+    o_src, lse_src = ref(src)
+    a, b = o.ravel(), o_src.ravel()
+    cos = 1.0 - float(a @ b) / (np.linalg.norm(a) * np.linalg.norm(b))
+    err = float(np.abs(a - b).max())
+    print("kv_dtype=%d vs bf16 source: cosine distance %.3g, max abs %.3g, max |dLSE| %.3g"
+          % (kv_dtype, cos, err, float(np.abs(lse - lse_src).max())), flush=True)
+    assert cos < 1e-2 and err < 0.5
+
+
+def test_8bit_needs_16_head_rows():
+    import mla_paged_kv_decode_amd as mla
+    ip = np.array([0, 1], np.int32)
+    lp = np.array([1], np.int32)
+    ws = torch.empty(mla.workspace_bytes(1, 128), dtype=torch.uint8, device="cuda")
+    plan = mla.Plan(ip, lp, 128, 16, synth.KV_FP8_E4M3, ws)
+    assert plan.info()["head_split"] == 8 and plan.info()["kernel_heads"] == 16
+    with pytest.raises(mla.MlaError) as e:
+        mla.Plan(ip, lp, 128, 16, synth.KV_INT8, ws, head_split=4)
+    assert e.value.status == -2
