@@ -2,8 +2,10 @@
 //
 // mla_decode_plan runs the split-KV planner on the host copies of the page
 // table and copies the work list (and zeroed arrival counters) into the
-// caller's workspace; mla_decode_run only launches the decode kernel, which
-// also merges split requests, so it is safe to capture in a HIP graph.
+// caller's workspace; mla_decode_run only launches kernels: the decode kernel
+// and, for kernels that leave split requests as partials, the combine kernel.
+// It allocates and synchronises nothing, so it is safe to capture in a HIP
+// graph.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -40,16 +42,18 @@ int page_shift_of(int32_t p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t segs, wptr, counters, plse, po, total, meta_bytes;
+  size_t segs, wptr, counters, clist, plse, po, total, meta_bytes;
 };
 
-// workspace: segments (32 B each) | worker_ptr | arrival counters | partial LSE | partial O
+// workspace: segments (32 B each) | worker_ptr | arrival counters | combine list
+// (16 B per split request) | partial LSE | partial O
 Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, int32_t heads) {
   Layout L;
   L.segs = 0;
   L.wptr = align256(L.segs + (size_t)nseg * 32);
   L.counters = align256(L.wptr + (size_t)(workers + 1) * 4);
-  L.meta_bytes = L.counters + (size_t)ncomb * 4;
+  L.clist = align256(L.counters + (size_t)ncomb * 4);
+  L.meta_bytes = L.clist + (size_t)ncomb * 16;
   L.plse = align256(L.meta_bytes);
   L.po = align256(L.plse + (size_t)nparts * heads * 4);
   L.total = align256(L.po + (size_t)nparts * heads * 512 * 4);
@@ -223,7 +227,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          kernel_heads);
 
-  // stage the work list: segments | worker_ptr | zeroed arrival counters
+  // stage the work list: segments | worker_ptr | zeroed arrival counters | combine list
   p->host_meta.assign(p->layout.meta_bytes, 0);
   for (size_t i = 0; i < pl.segments.size(); ++i) {
     const mla::Segment& g = pl.segments[i];
@@ -233,6 +237,8 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   }
   std::memcpy(p->host_meta.data() + p->layout.wptr, pl.worker_ptr.data(),
               pl.worker_ptr.size() * 4);
+  if (ncomb > 0)
+    std::memcpy(p->host_meta.data() + p->layout.clist, pl.combine.data(), (size_t)ncomb * 16);
 
   if (workspace) {
     if (workspace_bytes < p->layout.total) {
@@ -282,6 +288,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
   a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
   a.counters = reinterpret_cast<int32_t*>(ws + p->layout.counters);
+  a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.page_shift = p->page_shift;
   a.head_shift = log2_exact(p->head_split);
@@ -292,6 +299,11 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   if (p->plan.num_workers > 0) {
     hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
+    const int ncomb = (int)(p->plan.combine.size() / 4);
+    if (!p->cfg.fused_merge && ncomb > 0) {
+      e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, s);
+      if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
   }
   if (p->ev_after) {
     hipError_t e = hipEventRecord(p->ev_after, s);

@@ -24,6 +24,7 @@ struct DecodeArgs {
   float* part_o;              // [slots, H, 512]
   float* part_lse;            // [slots, H]
   int32_t* counters;          // arrival counter per split request (0 between launches)
+  const int4* clist;          // 4 ints per split request: row, first slot, chunks, 0
   float scale_log2;           // sm_scale * log2(e)
   int32_t page_shift;         // log2(page_size)
   int32_t head_shift;         // log2(head split): row b of q/o/lse (of kernel-width heads)
@@ -34,6 +35,8 @@ struct DecodeConfig {
   int32_t waves;  // waves per workgroup
   int32_t tile;   // tokens per KV tile = split granularity
   int32_t lds_bytes;  // LDS per workgroup (also bounds the split merge scratch)
+  int32_t fused_merge;  // 1: the decode kernel merges split requests itself (arrival
+                        // counters); 0: launch_combine does, after the decode kernel
 };
 
 // Kernel for `heads` heads per workgroup and a cache of `kv_dtype` (0 bf16,
@@ -44,5 +47,8 @@ int decode_config(int heads, int kv_dtype, DecodeConfig* cfg);
 int decode_blocks_per_cu(int heads, int kv_dtype);
 hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
                          hipStream_t stream);
+// Merge of the ncomb split requests listed in a.clist (for kernels with
+// fused_merge = 0): writes o and lse of those rows.
+hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, hipStream_t stream);
 
 }  // namespace mla_gpu

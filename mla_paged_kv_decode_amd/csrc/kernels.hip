@@ -1030,6 +1030,422 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
   }
 }
 
+// ---------------------------------------------------------------------------
+// Wide kernel for 128 query heads: 4 waves (one per SIMD, so each may hold up
+// to 512 registers), one 32-token tile at a time from an LDS ring.
+//   * QK is split across the waves by heads: wave w computes S^T for heads
+//     32 w .. 32 w + 31 with v_mfma_f32_32x32x16_bf16 (A = 32 token rows of
+//     the tile, B = Q^T of those heads, kept in registers for the segment), runs
+//     their online softmax and writes P^T, already in the PV operand layout,
+//     plus the heads' rescale factors to LDS;
+//   * after a barrier, PV is split by value channels: wave w accumulates O^T
+//     for channels 128 w .. 128 w + 127 of all 128 heads (256 accumulator
+//     registers) from V^T (transposing reads of the same tile) and every
+//     wave's P^T.
+// Each LDS byte read for QK feeds 32 heads and each V^T / P^T byte read for
+// PV feeds 64 flops, where a wave owning 16 heads and all 512 channels gets
+// 16 flops per byte in both, so LDS bandwidth no longer caps the MFMA rate.
+//
+// Token order inside the MFMA reduction: S^T lane l holds rows
+// 8 (r / 4) + 4 (l / 32) + r % 4 of head l % 32 (r = 0..15).  PV step ks
+// (16 tokens) takes r = 8 ks .. 8 ks + 7 of that lane as its B operand, i.e.
+// k = 8 g + j <-> token 16 ks + 8 (j / 4) + 4 g + j % 4 (g = l / 32); the V^T
+// A operand is gathered in the same token order by two transposing reads.
+// ---------------------------------------------------------------------------
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+
+// Multiply a 16-register MFMA accumulator held in AGPRs by s, in place, through
+// one temporary VGPR.  Written as assembly so that the (rarely executed)
+// rescale does not make the compiler move the accumulators into VGPRs, which
+// costs the registers that hold Q.  The leading s_nops cover the wait states
+// between an MFMA writing the AGPRs and v_accvgpr_read, the trailing one those
+// before a later MFMA reads them as its accumulator.
+__device__ __forceinline__ void scale_agpr16(f32x16& acc, float s) {
+  float t;
+  asm volatile(
+      "s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\t"
+#define MLA_SCALE_ONE(i)                                                      \
+  "v_accvgpr_read_b32 %16, %" #i "\n\tv_mul_f32 %16, %16, %17\n\t"          \
+  "v_accvgpr_write_b32 %" #i ", %16\n\t"
+      MLA_SCALE_ONE(0) MLA_SCALE_ONE(1) MLA_SCALE_ONE(2) MLA_SCALE_ONE(3)
+      MLA_SCALE_ONE(4) MLA_SCALE_ONE(5) MLA_SCALE_ONE(6) MLA_SCALE_ONE(7)
+      MLA_SCALE_ONE(8) MLA_SCALE_ONE(9) MLA_SCALE_ONE(10) MLA_SCALE_ONE(11)
+      MLA_SCALE_ONE(12) MLA_SCALE_ONE(13) MLA_SCALE_ONE(14) MLA_SCALE_ONE(15)
+#undef MLA_SCALE_ONE
+      "s_nop 4"
+      : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]), "+a"(acc[4]), "+a"(acc[5]),
+        "+a"(acc[6]), "+a"(acc[7]), "+a"(acc[8]), "+a"(acc[9]), "+a"(acc[10]), "+a"(acc[11]),
+        "+a"(acc[12]), "+a"(acc[13]), "+a"(acc[14]), "+a"(acc[15]), "=&v"(t)
+      : "v"(s));
+}
+
+// O^T += A B with the accumulator pinned to AGPRs.  As assembly, the
+// compiler cannot move the 256 accumulator registers of the wide kernel into
+// VGPRs (which then spills the Q operands, and every spill reload waits for
+// the whole KV prefetch on vmcnt).  A and B are consumed when the MFMA issues;
+// chained MFMAs on the same accumulator need no wait states, and every read of
+// the accumulators by other instructions is preceded by agpr_settle() or by
+// the wait states in scale_agpr16.
+__device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between the last MFMA writing AGPRs and VALU reads of them.
+__device__ __forceinline__ void agpr_settle() {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+}
+
+struct WideShape {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 256;
+  static constexpr int kHeads = 128;
+  static constexpr int kTile = 32;
+  static constexpr int kGroups = 2;
+  static constexpr int kStages = 4;
+  static constexpr int kStageBytes = kTile * kRowBytes;              // 36 KiB
+  static constexpr int kPOffset = kStages * kStageBytes;             // P^T [wave][ks][lane] x 16 B
+  static constexpr int kAlphaOffset = kPOffset + 4 * 2 * 64 * 16;    // [128] rescale factors
+  static constexpr int kFlagOffset = kAlphaOffset + 128 * 4;         // [4] rescale flags
+  static constexpr int kStatOffset = kFlagOffset + 16;               // [128] 1 / row sum
+  static constexpr int kLdsBytes = kStatOffset + 128 * 4;
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+__global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a) {
+  using S = WideShape;
+  constexpr int H = S::kHeads;
+  constexpr int T = S::kTile;
+  constexpr int NS = S::kStages;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int page_shift = a.page_shift;
+  const int page_mask = (1 << page_shift) - 1;
+  const int ld_r_lo = lane >> 3;
+
+  // QK A operand (ds_read_b128): token l32 of the tile, chunk 2 s + g.
+  int qk_off[4];
+  {
+    const int r = l32 & 15, half = r >> 3, rr = r & 7;
+    const int base = (l32 >> 4) * kGroupBytes + half * kHalfGroupBytes + rr * 128;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) qk_off[s4] = base + (((2 * s4 + g) ^ rr ^ half) * 16);
+  }
+  // PV A operand (ds_read_b64_tr_b16): source lane sl of 16-lane group G reads
+  // token 16 ks + 8 half + 4 (G >> 1) + sl / 4, channels
+  // 128 w + 32 cb + 16 (G & 1) + 4 (sl % 4) .. + 3.
+  int pv_off[2][2];  // [half][cb & 1]
+  {
+    const int G = lane >> 4, sl = lane & 15;
+    const int rr = 4 * (G >> 1) + (sl >> 2);
+    const int e = 2 * (G & 1) + ((sl >> 1) & 1);
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+      for (int c1 = 0; c1 < 2; ++c1)
+        pv_off[half][c1] = half * kHalfGroupBytes + rr * 128 + (((4 * c1 + e) ^ rr ^ half) * 16) +
+                           (sl & 1) * 8;
+  }
+  uint8_t* pbuf = smem + S::kPOffset;
+  float* alpha_s = reinterpret_cast<float*>(smem + S::kAlphaOffset);
+  int* flags = reinterpret_cast<int*>(smem + S::kFlagOffset);
+  float* stat = reinterpret_cast<float*>(smem + S::kStatOffset);
+
+  const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
+  const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
+
+  for (int si = seg_begin; si < seg_end; ++si) {
+    const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
+    const int b = ld_const(sgp + 0);
+    const int t0 = ld_const(sgp + 1);
+    const int send = ld_const(sgp + 2);
+    const int slot = ld_const(sgp + 3);
+    const int kvb = b >> a.head_shift;
+    const int pbeg = ld_const(a.kv_indptr + kvb);
+    const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
+    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
+    const int t1 = min(send, ldev);
+    const int ntiles = t1 > t0 ? (t1 - t0 + T - 1) / T : 0;
+
+    // Direct-to-LDS loads of tile k: wave w loads half group w (group w / 2,
+    // rows 8 (w % 2) .. + 7), 9 blocks of 1 KiB.  The page number of each
+    // group is one scalar load, prefetched one tile ahead.
+    const int last_group = t1 > 0 ? ((t1 - 1) >> 4) << 4 : 0;
+    const int my_group = wave >> 1, my_half = wave & 1;
+    int pg_next = 0;
+    auto tile_page = [&](int k) {
+      const int gs = min(t0 + k * T + 16 * my_group, last_group);
+      pg_next = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
+    };
+    auto issue_tile = [&](int k, int st) {
+      const int page = pg_next;
+      if (k + 1 < ntiles) tile_page(k + 1);
+      const int gs = min(t0 + k * T + 16 * my_group, last_group);
+      const int r = my_half * 8 + ld_r_lo;
+      const int tok = min(gs + r, t1 - 1);
+      const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
+      const int sw = ((lane & 7) ^ swz(r)) * 16;
+      const uint8_t* cbase = a.ckv + row * 1024 + sw;
+      const uint8_t* kbase = a.kpe + row * 128 + sw;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+          LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
+                           my_half * kHalfGroupBytes));
+#pragma unroll
+      for (int cb = 0; cb < 8; ++cb) dma16(cbase + cb * 128, dst + cb * 1024);
+      dma16(kbase, dst + 8 * 1024);
+    };
+
+    if (ntiles > 0) tile_page(0);
+    for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
+
+    // Q^T of heads 32 w .. 32 w + 31: k-step s holds dims 16 s + 8 g .. + 7.
+    bf16x8 qf[36];
+    {
+      const int head = 32 * wave + l32;
+      const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + head) * 512);
+      const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + head) * 64);
+#pragma unroll
+      for (int s = 0; s < 36; ++s) qf[s] = s < 32 ? qn[2 * s + g] : qp[2 * (s - 32) + g];
+    }
+    vm_wait_n<0>();
+
+    f32x16 acc[4][4];  // O^T [channel block cb][head block hb]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[cb][hb][i] = 0.f;
+    float m_ref = -INFINITY;  // head 32 w + l32, log2 domain
+    float l_run = 0.f;        // this lane's 16 tokens of that head
+
+    for (int it = 0; it < ntiles; ++it) {
+      const int st = it % NS;
+      {
+        const int later = min(NS - 2, ntiles - 1 - it);
+        if (later >= 2)
+          vm_wait_n<18>();
+        else if (later == 1)
+          vm_wait_n<9>();
+        else
+          vm_wait_n<0>();
+      }
+      lds_barrier();  // tile `it` landed for every wave; iteration it - 1 done everywhere
+      {
+        const int nxt = it + NS - 1;
+        if (nxt < ntiles) issue_tile(nxt, nxt % NS);
+      }
+      const uint8_t* stage = smem + st * S::kStageBytes;
+      const int tile_start = t0 + it * T;
+
+      // ---- QK: S^T[32 tokens][32 heads of this wave] ------------------------
+      f32x16 sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+      for (int s0 = 0; s0 < 36; s0 += 4) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)(stage + (s0 >> 2) * 1024 + qk_off[u]));
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], qf[s0 + u], sacc, 0, 0, 0);
+      }
+
+      // ---- online softmax of this wave's heads (log2 domain, lazy rescale) --
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float x = tok < t1 ? sacc[r] * a.scale_log2 : -INFINITY;
+        sacc[r] = x;
+        tmax = fmaxf(tmax, x);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_ref, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 when m_ref = -inf
+        l_run *= alpha;
+        m_ref = m_new;
+        if (lane < 32) alpha_s[32 * wave + lane] = alpha;
+        if (lane == 0) flags[wave] = 1;
+      } else if (lane == 0) {
+        flags[wave] = 0;
+      }
+      {
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float psum = 0.f;
+        bf16x8 p0, p1;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float e0 = __builtin_amdgcn_exp2f(sacc[r] - m_use);
+          const float e1 = __builtin_amdgcn_exp2f(sacc[8 + r] - m_use);
+          psum += e0 + e1;
+          p0[r] = (__bf16)e0;
+          p1[r] = (__bf16)e1;
+        }
+        l_run += psum;
+        *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + 0) * 64 + lane) * 16) = p0;
+        *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + 1) * 64 + lane) * 16) = p1;
+      }
+      lds_barrier();  // P^T and the rescale factors of every wave are in LDS
+
+      // ---- PV: O^T[128 w + c][h] += V^T[c][t] P^T[t][h] ---------------------
+      {
+        const u32x4 fl = *reinterpret_cast<const u32x4*>(flags);
+        const unsigned any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+        if (it > 0 && any != 0) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            if (__builtin_amdgcn_readfirstlane(fl[hb]) != 0) {
+              const float al = alpha_s[32 * hb + l32];
+#pragma unroll
+              for (int cb = 0; cb < 4; ++cb) scale_agpr16(acc[cb][hb], al);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        bf16x8 pb[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          pb[hb] = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)(pbuf + ((hb * 2 + ks) * 64 + lane) * 16));
+        const uint8_t* vbase = stage + ks * kGroupBytes + (2 * wave) * 1024;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          const uint8_t* vb = vbase + (cb >> 1) * 1024;
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_AS s16x4*)((LDS_AS uint8_t*)(vb + pv_off[0][cb & 1])));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_AS s16x4*)((LDS_AS uint8_t*)(vb + pv_off[1][cb & 1])));
+          const bf16x4 a0 = __builtin_bit_cast(bf16x4, v0);
+          const bf16x4 a1 = __builtin_bit_cast(bf16x4, v1);
+          bf16x8 vf;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            vf[i] = a0[i];
+            vf[4 + i] = a1[i];
+          }
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) mfma_agpr(acc[cb][hb], vf, pb[hb]);
+        }
+      }
+    }
+    lds_barrier();  // ring, P^T and flags free
+    agpr_settle();
+
+    // ---- epilogue: per-head sums from the QK owners, then O / l ------------
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    const bool empty = !(l_tot > 0.f);
+    const float lse_v = empty ? -INFINITY : (m_ref + __log2f(l_tot)) * kLn2;
+    if (lane < 32) stat[32 * wave + lane] = empty ? 0.f : 1.f / l_tot;
+    lds_barrier();
+    float inv[4];
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) inv[hb] = stat[32 * hb + l32];
+    if (slot < 0) {
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        uint16_t* op = a.o + ((size_t)b * H + 32 * hb + l32) * 512 + 128 * wave + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[cb][hb][4 * q + i] * inv[hb]);
+            *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * q) = v;
+          }
+      }
+      if (lane < 32) a.lse[(size_t)b * H + 32 * wave + lane] = lse_v;
+    } else {
+      // partial of a chunk: merged by the combine kernel after this launch
+      float* po = a.part_o + (size_t)slot * H * 512;
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) {
+        float* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = acc[cb][hb][4 * q + i] * inv[hb];
+            *reinterpret_cast<f32x4*>(prow + 32 * cb + 8 * q) = v;
+          }
+      }
+      if (lane < 32) a.part_lse[(size_t)slot * H + 32 * wave + lane] = lse_v;
+    }
+    lds_barrier();  // stat read by every wave before the next segment rewrites it
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of split requests as a launch of its own (after a decode kernel that
+// leaves partials): one thread per (split request, head, 8 columns), so the
+// merge runs on the whole GPU.  LSE = M + ln sum_i exp(LSE_i - M) and
+// O = sum_i exp(LSE_i - LSE) O_i, summed in chunk order i = 0, 1, ...  The 64
+// threads of a wave share one head, so its partial LSEs are one cache line.
+// ---------------------------------------------------------------------------
+template <int H>
+__global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
+  constexpr int kBlocksPerReq = H * 64 / 256;
+  const int req = blockIdx.x / kBlocksPerReq;
+  const int e = (blockIdx.x % kBlocksPerReq) * 256 + threadIdx.x;
+  const int hd = e >> 6;
+  const int col = (e & 63) * 8;
+  const int* cl = reinterpret_cast<const int*>(a.clist) + req * 4;
+  const int b = ld_const(cl + 0);
+  const int slot0 = ld_const(cl + 1);
+  const int n = ld_const(cl + 2);
+  const float* pl = a.part_lse + (size_t)slot0 * H + hd;
+  float M = -INFINITY;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, pl[i * H]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float sum = 0.f;
+  for (int i = 0; i < n; ++i) sum += __expf(pl[i * H] - Mu);
+  const bool empty = !(sum > 0.f);
+  const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
+  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
+  float o8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o8[j] = 0.f;
+  for (int i0 = 0; i0 < n; i0 += 4) {
+    f32x4 x[4][2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = min(i0 + v, n - 1);
+      x[v][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
+      x[v][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      if (i0 + v < n) {
+        const float w = empty ? 0.f : __expf(pl[(i0 + v) * H] - lse_v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o8[j] += w * x[v][0][j];
+          o8[4 + j] += w * x[v][1][j];
+        }
+      }
+    }
+  }
+  bf16x8 v;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
+  *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
+  if (col == 0) a.lse[(size_t)b * H + hd] = lse_v;
+}
+
 // ---------------------------------------------------------------- launchers
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
@@ -1039,10 +1455,29 @@ static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t s
   return hipGetLastError();
 }
 
+static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(mla_decode_wide_kernel, dim3(grid), dim3(WideShape::kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+static DecodeConfig wide_config() {
+  return DecodeConfig{WideShape::kWaves, WideShape::kTile, WideShape::kLdsBytes, 0};
+}
+
+static int wide_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&mla_decode_wide_kernel), WideShape::kThreads, 0) !=
+          hipSuccess ||
+      n < 1)
+    n = 1;
+  return n;
+}
+
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 static DecodeConfig config_of() {
   using S = RingShape<HG, HB, TS, MB, NSTAGE>;
-  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
+  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes, 1};
 }
 
 template <int HB, int KVT, int NB>
@@ -1056,7 +1491,7 @@ static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t s
 template <int HB, int KVT, int NB>
 static DecodeConfig stream_config_of() {
   using S = StreamShape<HB, KVT, NB>;
-  return DecodeConfig{S::kWaves, 16, S::kLdsBytes};
+  return DecodeConfig{S::kWaves, 16, S::kLdsBytes, 1};
 }
 
 template <int HB, int KVT, int NB>
@@ -1084,6 +1519,11 @@ static int stream_occupancy_of() {
 // registers of a lane, so it spills; kept for comparison).
 #ifndef MLA_H32_STREAM
 #define MLA_H32_STREAM 0
+#endif
+// 128-head bf16 rows: 1 = wide kernel (QK split by heads, PV by channels),
+// 0 = LDS ring with 8 waves of 16 heads.
+#ifndef MLA_H128_WIDE
+#define MLA_H128_WIDE 1
 #endif
 // groups staged in registers per wave for 32-head rows
 #ifndef MLA_H32_NB
@@ -1129,7 +1569,15 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
       case 32: MLA_RING(2, 1, 2, 1, 4);
 #endif
       case 64: MLA_RING(MLA_CFG_H64);
+#if MLA_H128_WIDE
+      case 128:
+        if (op == 0) *cfg = wide_config();
+        if (op == 1) return wide_occupancy();
+        if (op == 2) *err = launch_wide(*a, grid, stream);
+        return 1;
+#else
       case 128: MLA_RING(MLA_CFG_H128);
+#endif
       default: return 0;
     }
   }
@@ -1148,6 +1596,22 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   return 0;
 #undef MLA_STREAM
 #undef MLA_RING
+}
+
+hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, hipStream_t stream) {
+  if (ncomb <= 0) return hipSuccess;
+  switch (heads) {
+#define MLA_COMBINE(H)                                                                 \
+  case H:                                                                              \
+    hipLaunchKernelGGL(mla_combine_kernel<H>, dim3(ncomb * (H / 4)), dim3(256), 0, stream, a); \
+    return hipGetLastError();
+    MLA_COMBINE(16)
+    MLA_COMBINE(32)
+    MLA_COMBINE(64)
+    MLA_COMBINE(128)
+#undef MLA_COMBINE
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int decode_config(int heads, int kv_dtype, DecodeConfig* cfg) {

@@ -316,3 +316,41 @@ def test_8bit_needs_16_head_rows():
     with pytest.raises(mla.MlaError) as e:
         mla.Plan(ip, lp, 128, 16, synth.KV_INT8, ws, head_split=4)
     assert e.value.status == -2
+
+
+def _jump_inputs(lengths, heads, kv_dtype, seed, factor, jumps):
+    """Inputs whose running score maximum jumps part way through a request:
+    the kpe rows of request b from token t on (for (b, t) in jumps) are
+    multiplied by a power of two (exact in bf16) before any 8-bit
+    quantisation, so the q_pe . kpe part of the scores grows by that factor
+    while the values (ckv) keep their size.  The online softmax then has to
+    rescale its accumulators after the first tile."""
+    inp = synth.make_inputs(lengths, heads, 64, synth.KV_BF16, seed=seed)
+    P = inp.page_size
+    for b, t_from in jumps:
+        toks = np.arange(t_from, int(inp.lengths[b]))
+        pages = inp.kv_indices[inp.kv_indptr[b] + toks // P]
+        rows = toks % P
+        x = (inp.kpe[pages, rows].astype(np.uint32) << 16).view(np.float32) * np.float32(factor)
+        inp.kpe[pages, rows] = (x.view(np.uint32) >> 16).astype(np.uint16)
+    if kv_dtype != synth.KV_BF16:
+        ckv, kpe, scale = synth._quantize_tokens(inp.ckv, inp.kpe, kv_dtype)
+        inp = synth.MlaInputs(inp.batch, inp.num_heads, P, kv_dtype, inp.lengths, inp.q_nope,
+                              inp.q_pe, ckv, kpe, scale, inp.kv_indptr, inp.kv_indices,
+                              inp.kv_last_page_len, inp.sm_scale, inp.ckv, inp.kpe)
+    synth._poison(inp.ckv, inp.kpe, inp.kv_scale, kv_dtype, inp.kv_indptr, inp.kv_indices,
+                  inp.kv_last_page_len, P, inp.num_pages)
+    return inp
+
+
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8_E4M3])
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("factor", [16, 64])
+def test_score_jump_rescales(kv_dtype, heads, factor):
+    inp = _jump_inputs([2000, 700, 3000], heads, kv_dtype, 800 + heads + factor, factor,
+                       [(0, 1000), (2, 2500)])
+    print("case kv_dtype=%d heads=%d factor=%d" % (kv_dtype, heads, factor), flush=True)
+    o, lse = host(*gpu_run(inp))
+    check(o, lse, *ref(inp))
+    o2, lse2 = host(*gpu_run(inp, force_splits=3))
+    check(o2, lse2, *ref(inp))
