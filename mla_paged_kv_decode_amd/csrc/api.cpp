@@ -92,12 +92,11 @@ int log2_exact(int32_t x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Head split for a batch: explicit (opts->head_split) or automatic.  8-bit
-// caches are served by the 16-head kernel only, so their requests are always
-// split into 16-head rows (the rows of one request are placed on one XCD, so
-// the latent cache is read from HBM about once).  bf16 requests keep all heads
-// in one workgroup: on 64 x 128 heads x 4096 tokens that measured faster than
-// 32-head rows.
+// Head split for a batch: explicit (opts->head_split) or automatic.  Requests
+// keep all their heads in one workgroup where a kernel serves that width (bf16:
+// 16 to 128 heads; 8-bit: 16 and 128 heads); otherwise (8-bit with 32 or 64
+// heads) they are split into 16-head rows, placed on one XCD so that the
+// latent cache is read from HBM about once.
 mla_status choose_head_split(int32_t num_heads, int32_t kv_dtype, const mla_plan_opts* opts,
                              int32_t* head_split) {
   const int32_t req = opts ? opts->head_split : 0;
@@ -110,7 +109,7 @@ mla_status choose_head_split(int32_t num_heads, int32_t kv_dtype, const mla_plan
     *head_split = req;
     return MLA_OK;
   }
-  *head_split = kv_dtype == MLA_KV_BF16 ? 1 : num_heads / 16;
+  *head_split = mla_gpu::decode_config(num_heads, kv_dtype, &cfg) == 0 ? 1 : num_heads / 16;
   return MLA_OK;
 }
 

@@ -1096,15 +1096,31 @@ __device__ __forceinline__ void agpr_settle() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// LDS of the wide kernel.  bf16 cache: a ring of kStages bf16 tiles (36 KiB,
+// the swizzled 16-row group layout) filled by direct-to-LDS loads.  8-bit
+// cache: a ring of kStages code tiles (ckv codes [32][512], kpe codes
+// [32][64], the 32 scales; filled by direct-to-LDS loads) and two bf16 tiles:
+// the codes of tile k + 1 are converted (exactly) into one of them while tile
+// k is computed from the other.
+template <int KVT>
 struct WideShape {
   static constexpr int kWaves = 4;
   static constexpr int kThreads = 256;
   static constexpr int kHeads = 128;
   static constexpr int kTile = 32;
-  static constexpr int kGroups = 2;
-  static constexpr int kStages = 4;
-  static constexpr int kStageBytes = kTile * kRowBytes;              // 36 KiB
-  static constexpr int kPOffset = kStages * kStageBytes;             // P^T [wave][ks][lane] x 16 B
+  static constexpr int kStages = KVT == 0 ? 4 : 3;
+  // QK k-steps whose Q^T operands stay in registers (8-bit: the kpe steps live
+  // in LDS, to make room for the code conversion)
+  static constexpr int kQRegSteps = KVT == 0 ? 36 : 32;
+  static constexpr int kStageBytes = kTile * kRowBytes;              // 36 KiB bf16 tile
+  static constexpr int kCodeKpe = kTile * 512;                       // offsets in a code tile
+  static constexpr int kCodeScale = kCodeKpe + kTile * 64;
+  static constexpr int kCodeBytes = kCodeScale + 1024;               // 19 KiB
+  static constexpr int kBf16Offset = kStages * kCodeBytes;           // 8-bit: the two bf16 tiles
+  static constexpr int kRingBytes = KVT == 0 ? kStages * kStageBytes
+                                             : kBf16Offset + 2 * kStageBytes;
+  static constexpr int kQOffset = kRingBytes;                        // Q^T [wave][step][lane] x 16 B
+  static constexpr int kPOffset = kQOffset + 4 * (36 - kQRegSteps) * 1024;  // P^T [wave][ks][lane]
   static constexpr int kAlphaOffset = kPOffset + 4 * 2 * 64 * 16;    // [128] rescale factors
   static constexpr int kFlagOffset = kAlphaOffset + 128 * 4;         // [4] rescale flags
   static constexpr int kStatOffset = kFlagOffset + 16;               // [128] 1 / row sum
@@ -1112,8 +1128,9 @@ struct WideShape {
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
+template <int KVT>
 __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a) {
-  using S = WideShape;
+  using S = WideShape<KVT>;
   constexpr int H = S::kHeads;
   constexpr int T = S::kTile;
   constexpr int NS = S::kStages;
@@ -1172,47 +1189,142 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     const int t1 = min(send, ldev);
     const int ntiles = t1 > t0 ? (t1 - t0 + T - 1) / T : 0;
 
-    // Direct-to-LDS loads of tile k: wave w loads half group w (group w / 2,
-    // rows 8 (w % 2) .. + 7), 9 blocks of 1 KiB.  The page number of each
-    // group is one scalar load, prefetched one tile ahead.
+    // Page numbers of the two 16-row groups of a tile (a group past the end
+    // reuses the group of the last valid token): scalar loads, prefetched one
+    // tile ahead.
     const int last_group = t1 > 0 ? ((t1 - 1) >> 4) << 4 : 0;
-    const int my_group = wave >> 1, my_half = wave & 1;
-    int pg_next = 0;
-    auto tile_page = [&](int k) {
-      const int gs = min(t0 + k * T + 16 * my_group, last_group);
-      pg_next = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
-    };
-    auto issue_tile = [&](int k, int st) {
-      const int page = pg_next;
-      if (k + 1 < ntiles) tile_page(k + 1);
-      const int gs = min(t0 + k * T + 16 * my_group, last_group);
-      const int r = my_half * 8 + ld_r_lo;
-      const int tok = min(gs + r, t1 - 1);
-      const size_t row = ((size_t)page << page_shift) + (tok & page_mask);
-      const int sw = ((lane & 7) ^ swz(r)) * 16;
-      const uint8_t* cbase = a.ckv + row * 1024 + sw;
-      const uint8_t* kbase = a.kpe + row * 128 + sw;
-      const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-          LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
-                           my_half * kHalfGroupBytes));
+    int pg_next[2] = {0, 0};
+    auto tile_pages = [&](int k) {
+      const int kc = min(k, max(ntiles - 1, 0));
 #pragma unroll
-      for (int cb = 0; cb < 8; ++cb) dma16(cbase + cb * 128, dst + cb * 1024);
-      dma16(kbase, dst + 8 * 1024);
+      for (int gi = 0; gi < 2; ++gi) {
+        const int gs = min(t0 + kc * T + 16 * gi, last_group);
+        pg_next[gi] = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
+      }
     };
 
-    if (ntiles > 0) tile_page(0);
-    for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
+    // Direct-to-LDS loads of tile k into ring slot st.
+    //   bf16: wave w loads half group w (group w / 2, rows 8 (w % 2) .. + 7),
+    //   9 blocks of 1 KiB in the swizzled layout.
+    //   8-bit: wave w issues loads d = 5 w .. 5 w + 4 of 20: ckv code rows 2d,
+    //   2d + 1 (d < 16), kpe code rows 16 (d - 16) .. + 15 (d = 16, 17), the 32
+    //   scales (d = 18 and again d = 19, so that every wave issues 5 loads).
+    //   Past the last tile, the last tile is loaded again (its data lands in
+    //   a slot no one reads), which keeps the loads in flight, and so every
+    //   vmcnt wait, the same in every iteration.
+    auto issue_tile = [&](int k, int st) {
+      const int pg[2] = {pg_next[0], pg_next[1]};
+      tile_pages(k + 1);
+      const int kc = min(k, ntiles - 1);
+      if constexpr (KVT == 0) {
+        const int my_group = wave >> 1, my_half = wave & 1;
+        const int gs = min(t0 + kc * T + 16 * my_group, last_group);
+        const int r = my_half * 8 + ld_r_lo;
+        const int tok = min(gs + r, t1 - 1);
+        const size_t row = ((size_t)pg[my_group] << page_shift) + (tok & page_mask);
+        const int sw = ((lane & 7) ^ swz(r)) * 16;
+        const uint8_t* cbase = a.ckv + row * 1024 + sw;
+        const uint8_t* kbase = a.kpe + row * 128 + sw;
+        const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+            LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
+                             my_half * kHalfGroupBytes));
+#pragma unroll
+        for (int cb = 0; cb < 8; ++cb) dma16(cbase + cb * 128, dst + cb * 1024);
+        dma16(kbase, dst + 8 * 1024);
+      } else {
+        const int tile0 = t0 + kc * T;
+        const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + st * S::kCodeBytes));
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+          const int d = 5 * wave + u;  // wave-uniform
+          int t, off;
+          uint32_t dst;
+          if (d < 16) {
+            t = 2 * d + (lane >> 5);
+            off = (lane & 31) * 16;
+            dst = dst0 + d * 1024;
+          } else if (d < 18) {
+            t = 16 * (d - 16) + (lane >> 2);
+            off = (lane & 3) * 16;
+            dst = dst0 + S::kCodeKpe + (d - 16) * 1024;
+          } else {
+            t = 4 * min(lane, 7);  // lanes 8.. load again what lane 7 loads
+            off = 0;
+            dst = dst0 + S::kCodeScale;
+          }
+          // a 16-byte read of scales covers 4 tokens: keep it inside the page
+          const int tok = min(tile0 + t, d < 18 ? t1 - 1 : (t1 - 1) & ~3);
+          const int gpage = t < 16 ? pg[0] : pg[1];
+          const size_t row = ((size_t)gpage << page_shift) + (tok & page_mask);
+          const uint8_t* src =
+              d < 16 ? a.ckv + row * 512 + off
+                     : (d < 18 ? a.kpe + row * 64 + off
+                               : reinterpret_cast<const uint8_t*>(a.kv_scale + row));
+          dma16(src, __builtin_amdgcn_readfirstlane(dst));
+        }
+      }
+    };
+
+    // 8-bit: convert the codes of the tile in code slot cs to the bf16 tile
+    // layout at dst (exact; the token scales are applied to S and P).
+    auto convert_tile = [&](int cs, uint8_t* dst) {
+      const uint8_t* cod = smem + cs * S::kCodeBytes;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {  // ckv: 1024 pieces of 16 codes
+        const int p = i * 256 + tid;
+        const int t = p >> 5, u = p & 31, r = t & 15;
+        const u32x4 c = *reinterpret_cast<const u32x4*>(cod + t * 512 + u * 16);
+        uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + (u >> 2) * 1024 +
+                       (r & 7) * 128;
+        *reinterpret_cast<u32x4*>(row + ((((2 * u) & 7) ^ swz(r)) * 16)) =
+            codes_to_bf16<KVT>(c[0], c[1]);
+        *reinterpret_cast<u32x4*>(row + ((((2 * u + 1) & 7) ^ swz(r)) * 16)) =
+            codes_to_bf16<KVT>(c[2], c[3]);
+      }
+      if (wave < 2) {  // kpe: 128 pieces
+        const int t = tid >> 2, u = tid & 3, r = t & 15;
+        const u32x4 c = *reinterpret_cast<const u32x4*>(cod + S::kCodeKpe + t * 64 + u * 16);
+        uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + 8 * 1024 +
+                       (r & 7) * 128;
+        *reinterpret_cast<u32x4*>(row + (((2 * u) ^ swz(r)) * 16)) = codes_to_bf16<KVT>(c[0], c[1]);
+        *reinterpret_cast<u32x4*>(row + (((2 * u + 1) ^ swz(r)) * 16)) =
+            codes_to_bf16<KVT>(c[2], c[3]);
+      }
+    };
+
+    if (ntiles > 0) tile_pages(0);
+    if constexpr (KVT == 0) {
+      for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
+    } else {
+      if (ntiles > 0)
+        for (int k = 0; k < NS - 1; ++k) issue_tile(k, k);
+    }
 
     // Q^T of heads 32 w .. 32 w + 31: k-step s holds dims 16 s + 8 g .. + 7.
-    bf16x8 qf[36];
+    constexpr int QR = S::kQRegSteps;
+    bf16x8 qf[QR];
+    uint8_t* const qlds = smem + S::kQOffset + wave * (36 - QR) * 1024 + lane * 16;
     {
       const int head = 32 * wave + l32;
       const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + head) * 512);
       const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + head) * 64);
 #pragma unroll
-      for (int s = 0; s < 36; ++s) qf[s] = s < 32 ? qn[2 * s + g] : qp[2 * (s - 32) + g];
+      for (int s = 0; s < 36; ++s) {
+        const bf16x8 v = s < 32 ? qn[2 * s + g] : qp[2 * (s - 32) + g];
+        if (s < QR)
+          qf[s < QR ? s : 0] = v;
+        else
+          *reinterpret_cast<bf16x8*>(qlds + (s - QR) * 1024) = v;
+      }
     }
     vm_wait_n<0>();
+    if constexpr (KVT != 0) {
+      if (ntiles > 0) {
+        lds_barrier();  // code tile 0 of every wave
+        convert_tile(0, smem + S::kBf16Offset);
+      }
+    }
 
     f32x16 acc[4][4];  // O^T [channel block cb][head block hb]
 #pragma unroll
@@ -1225,8 +1337,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     float l_run = 0.f;        // this lane's 16 tokens of that head
 
     for (int it = 0; it < ntiles; ++it) {
-      const int st = it % NS;
-      {
+      const uint8_t* stage;
+      if constexpr (KVT == 0) {
         const int later = min(NS - 2, ntiles - 1 - it);
         if (later >= 2)
           vm_wait_n<18>();
@@ -1234,13 +1346,20 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           vm_wait_n<9>();
         else
           vm_wait_n<0>();
-      }
-      lds_barrier();  // tile `it` landed for every wave; iteration it - 1 done everywhere
-      {
+        lds_barrier();  // tile `it` landed for every wave; iteration it - 1 done everywhere
         const int nxt = it + NS - 1;
         if (nxt < ntiles) issue_tile(nxt, nxt % NS);
+        stage = smem + (it % NS) * S::kStageBytes;
+      } else {
+        // code tile it + 1 landed (tiles it + 2 .. it + NS - 2 may be in
+        // flight); bf16 tile `it` converted; iteration it - 1 done everywhere
+        vm_wait_n<5 * (NS - 3)>();
+        lds_barrier();
+        issue_tile(it + NS - 1, (it + NS - 1) % NS);
+        if (it + 1 < ntiles)
+          convert_tile((it + 1) % NS, smem + S::kBf16Offset + ((it + 1) & 1) * S::kStageBytes);
+        stage = smem + S::kBf16Offset + (it & 1) * S::kStageBytes;
       }
-      const uint8_t* stage = smem + st * S::kStageBytes;
       const int tile_start = t0 + it * T;
 
       // ---- QK: S^T[32 tokens][32 heads of this wave] ------------------------
@@ -1255,16 +1374,40 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
               (const LDS_AS uint8_t*)(stage + (s0 >> 2) * 1024 + qk_off[u]));
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], qf[s0 + u], sacc, 0, 0, 0);
+        for (int u = 0; u < 4; ++u) {
+          const int s = s0 + u;
+          const bf16x8 qv = s < QR ? qf[s < QR ? s : 0]
+                                   : *reinterpret_cast<const LDS_AS bf16x8*>(
+                                         (const LDS_AS uint8_t*)(qlds + (s - QR) * 1024));
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], qv, sacc, 0, 0, 0);
+        }
       }
 
       // ---- online softmax of this wave's heads (log2 domain, lazy rescale) --
+      // 8-bit: the token scale multiplies the score (after QK, in fp32) and the
+      // probability (before P is rounded to bf16 for PV), the same as
+      // dequantising the row first.
+      f32x16 sig;
+      if constexpr (KVT != 0) {
+        const float* sc = reinterpret_cast<const float*>(smem + (it % NS) * S::kCodeBytes +
+                                                         S::kCodeScale);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sc + 8 * j + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // rows past the end may hold any scale (NaN padding included)
+            const int tok = tile_start + 8 * j + 4 * g + i;
+            sig[4 * j + i] = tok < t1 ? v[i] : 0.f;
+          }
+        }
+      }
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float x = tok < t1 ? sacc[r] * a.scale_log2 : -INFINITY;
+        const float raw = KVT != 0 ? sacc[r] * sig[r] : sacc[r];
+        const float x = tok < t1 ? raw * a.scale_log2 : -INFINITY;
         sacc[r] = x;
         tmax = fmaxf(tmax, x);
       }
@@ -1288,8 +1431,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           const float e0 = __builtin_amdgcn_exp2f(sacc[r] - m_use);
           const float e1 = __builtin_amdgcn_exp2f(sacc[8 + r] - m_use);
           psum += e0 + e1;
-          p0[r] = (__bf16)e0;
-          p1[r] = (__bf16)e1;
+          p0[r] = (__bf16)(KVT != 0 ? e0 * sig[r] : e0);
+          p1[r] = (__bf16)(KVT != 0 ? e1 * sig[8 + r] : e1);
         }
         l_run += psum;
         *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + 0) * 64 + lane) * 16) = p0;
@@ -1340,6 +1483,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         }
       }
     }
+    if constexpr (KVT != 0) vm_wait_n<0>();  // the trailing re-loads have landed
     lds_barrier();  // ring, P^T and flags free
     agpr_settle();
 
@@ -1455,20 +1599,24 @@ static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t s
   return hipGetLastError();
 }
 
+template <int KVT>
 static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(mla_decode_wide_kernel, dim3(grid), dim3(WideShape::kThreads), 0, stream, a);
+  hipLaunchKernelGGL((mla_decode_wide_kernel<KVT>), dim3(grid), dim3(WideShape<KVT>::kThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
+template <int KVT>
 static DecodeConfig wide_config() {
-  return DecodeConfig{WideShape::kWaves, WideShape::kTile, WideShape::kLdsBytes, 0};
+  return DecodeConfig{WideShape<KVT>::kWaves, WideShape<KVT>::kTile, WideShape<KVT>::kLdsBytes, 0};
 }
 
+template <int KVT>
 static int wide_occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&mla_decode_wide_kernel), WideShape::kThreads, 0) !=
-          hipSuccess ||
+          &n, reinterpret_cast<const void*>(&mla_decode_wide_kernel<KVT>),
+          WideShape<KVT>::kThreads, 0) != hipSuccess ||
       n < 1)
     n = 1;
   return n;
@@ -1553,6 +1701,13 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
     if (op == 2) *err = launch_stream_cfg<__VA_ARGS__>(*a, grid, stream);   \
     return 1;                                                               \
   } while (0)
+#define MLA_WIDE(K)                                                         \
+  do {                                                                      \
+    if (op == 0) *cfg = wide_config<K>();                                   \
+    if (op == 1) return wide_occupancy<K>();                                \
+    if (op == 2) *err = launch_wide<K>(*a, grid, stream);                   \
+    return 1;                                                               \
+  } while (0)
 #define MLA_RING(...)                                                       \
   do {                                                                      \
     if (op == 0) *cfg = config_of<__VA_ARGS__>();                           \
@@ -1570,11 +1725,7 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
 #endif
       case 64: MLA_RING(MLA_CFG_H64);
 #if MLA_H128_WIDE
-      case 128:
-        if (op == 0) *cfg = wide_config();
-        if (op == 1) return wide_occupancy();
-        if (op == 2) *err = launch_wide(*a, grid, stream);
-        return 1;
+      case 128: MLA_WIDE(0);
 #else
       case 128: MLA_RING(MLA_CFG_H128);
 #endif
@@ -1584,17 +1735,20 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   if (kv_dtype == 1) {
     switch (heads) {
       case 16: MLA_STREAM(1, 1, 2);
+      case 128: MLA_WIDE(1);
       default: return 0;
     }
   }
   if (kv_dtype == 2) {
     switch (heads) {
       case 16: MLA_STREAM(1, 2, 2);
+      case 128: MLA_WIDE(2);
       default: return 0;
     }
   }
   return 0;
 #undef MLA_STREAM
+#undef MLA_WIDE
 #undef MLA_RING
 }
 

@@ -173,22 +173,26 @@ def test_head_split_automatic_choice(lib):
     ip, lp = _table(lengths, 16)
     info = mla.Plan(ip, lp, 64, 16, num_cus=256).info()
     assert info["head_split"] == 1 and info["kernel_heads"] == 64
-    # 8-bit caches run 16-head rows
+    # 8-bit caches: 16 and 128 heads in one workgroup, 32 and 64 as 16-head rows
     ip, lp = _table([8192] * 64, 64)
     for heads in (16, 32, 64, 128):
         for kvd in (mla.KV_FP8_E4M3, mla.KV_INT8):
             info = mla.Plan(ip, lp, heads, 64, kvd, num_cus=256).info()
-            assert info["head_split"] == heads // 16 and info["kernel_heads"] == 16
-    plan = mla.Plan(ip, lp, 128, 64, mla.KV_FP8_E4M3, num_cus=256)
+            hs = 1 if heads in (16, 128) else heads // 16
+            assert info["head_split"] == hs and info["kernel_heads"] == heads // hs
+    plan = mla.Plan(ip, lp, 64, 64, mla.KV_FP8_E4M3, num_cus=256)
     _check_plan(plan, [8192] * 64, plan.info()["granularity"])
 
 
-def test_8bit_rejects_wider_rows(lib):
+def test_8bit_rejects_unserved_rows(lib):
     ip, lp = _table([100], 16)
-    for hs in (1, 2, 4):
+    for hs in (2, 4):  # 64- and 32-head rows have no 8-bit kernel
         with pytest.raises(mla.MlaError) as e:
             mla.Plan(ip, lp, 128, 16, mla.KV_INT8, num_cus=8, head_split=hs)
         assert e.value.status == -2
+    for hs in (1, 8):
+        assert mla.Plan(ip, lp, 128, 16, mla.KV_INT8, num_cus=8, head_split=hs).info()[
+            "head_split"] == hs
     with pytest.raises(mla.MlaError):
         mla.Plan(ip, lp, 16, 16, 3, num_cus=8)
 

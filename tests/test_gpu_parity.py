@@ -306,16 +306,26 @@ def test_8bit_quantisation_error_vs_bf16_source(kv_dtype):
     assert cos < 1e-2 and err < 0.5
 
 
-def test_8bit_needs_16_head_rows():
+def test_8bit_row_widths():
     import mla_paged_kv_decode_amd as mla
     ip = np.array([0, 1], np.int32)
     lp = np.array([1], np.int32)
     ws = torch.empty(mla.workspace_bytes(1, 128), dtype=torch.uint8, device="cuda")
     plan = mla.Plan(ip, lp, 128, 16, synth.KV_FP8_E4M3, ws)
-    assert plan.info()["head_split"] == 8 and plan.info()["kernel_heads"] == 16
+    assert plan.info()["head_split"] == 1 and plan.info()["kernel_heads"] == 128
+    plan = mla.Plan(ip, lp, 64, 16, synth.KV_FP8_E4M3, ws)
+    assert plan.info()["head_split"] == 4 and plan.info()["kernel_heads"] == 16
     with pytest.raises(mla.MlaError) as e:
         mla.Plan(ip, lp, 128, 16, synth.KV_INT8, ws, head_split=4)
     assert e.value.status == -2
+
+
+@pytest.mark.parametrize("kv_dtype", KV8)
+def test_8bit_128_heads_as_16_head_rows(kv_dtype):
+    inp = synth.make_inputs([700, 1, 4096, 65, 0, 1999], 128, 32, kv_dtype, seed=900 + kv_dtype,
+                            poison=True, extra_pages=3)
+    o, lse = host(*gpu_run(inp, head_split=8))
+    check(o, lse, *ref(inp))
 
 
 def _jump_inputs(lengths, heads, kv_dtype, seed, factor, jumps):
