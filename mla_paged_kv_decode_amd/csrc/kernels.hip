@@ -43,6 +43,12 @@
 
 namespace mla_gpu {
 
+// 16-head kernel: 1 = the last chunk of a split request merges it, 0 = the
+// separate combine launch does
+#ifndef MLA_STREAM_FUSED_MERGE
+#define MLA_STREAM_FUSED_MERGE 1
+#endif
+
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -1005,20 +1011,15 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       }
     };
 
-    if constexpr (NB == 2) {
-      u32x4 stA[NL], stB[NL];
-      f32x4 scA, scB;
-      fetch(0, stA, scA);
-      fetch(1, stB, scB);
-      for (int j = 0; j < nmine; j += 2) {
-        consume(j, stA, scA);
-        consume(j + 1, stB, scB);
+    {
+      u32x4 st[NB][NL];
+      f32x4 sc[NB];
+#pragma unroll
+      for (int u = 0; u < NB; ++u) fetch(u, st[u], sc[u]);
+      for (int j = 0; j < nmine; j += NB) {
+#pragma unroll
+        for (int u = 0; u < NB; ++u) consume(j + u, st[u], sc[u]);
       }
-    } else {
-      u32x4 stA[NL];
-      f32x4 scA;
-      fetch(0, stA, scA);
-      for (int j = 0; j < nmine; ++j) consume(j, stA, scA);
     }
 
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
@@ -1026,7 +1027,8 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     for (int hb = 0; hb < HB; ++hb)
       write_head_block<H, 1, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave, lane,
                                  smem);
-    finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
+    if constexpr (MLA_STREAM_FUSED_MERGE)
+      finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
   }
 }
 
@@ -1639,7 +1641,7 @@ static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t s
 template <int HB, int KVT, int NB>
 static DecodeConfig stream_config_of() {
   using S = StreamShape<HB, KVT, NB>;
-  return DecodeConfig{S::kWaves, 16, S::kLdsBytes, 1};
+  return DecodeConfig{S::kWaves, 16, S::kLdsBytes, MLA_STREAM_FUSED_MERGE};
 }
 
 template <int HB, int KVT, int NB>
@@ -1672,6 +1674,11 @@ static int stream_occupancy_of() {
 // 0 = LDS ring with 8 waves of 16 heads.
 #ifndef MLA_H128_WIDE
 #define MLA_H128_WIDE 1
+#endif
+// groups staged in registers per wave for 16-head 8-bit rows (a group is
+// half the bytes of a bf16 one)
+#ifndef MLA_H16_NB8
+#define MLA_H16_NB8 2
 #endif
 // groups staged in registers per wave for 32-head rows
 #ifndef MLA_H32_NB
@@ -1734,14 +1741,14 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   }
   if (kv_dtype == 1) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 1, 2);
+      case 16: MLA_STREAM(1, 1, MLA_H16_NB8);
       case 128: MLA_WIDE(1);
       default: return 0;
     }
   }
   if (kv_dtype == 2) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 2, 2);
+      case 16: MLA_STREAM(1, 2, MLA_H16_NB8);
       case 128: MLA_WIDE(2);
       default: return 0;
     }

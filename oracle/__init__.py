@@ -76,6 +76,10 @@ def _load():
     lib.mla_oracle_partial.restype = ctypes.c_int
     lib.mla_oracle_combine.argtypes = [i32, P, P, P, P]
     lib.mla_oracle_combine.restype = None
+    lib.mla_oracle_quantize.argtypes = [i32, i32, P, P, P, P, P]
+    lib.mla_oracle_quantize.restype = ctypes.c_int
+    lib.oracle_enc_e4m3fn.argtypes = [ctypes.c_float]
+    lib.oracle_enc_e4m3fn.restype = ctypes.c_uint8
     _lib = lib
     return lib
 
@@ -181,3 +185,28 @@ def combine(lse_parts, o_parts):
     lse = np.zeros((1,), np.float64)
     _load().mla_oracle_combine(int(lp.size), _ptr(lp), _ptr(op), _ptr(o), _ptr(lse))
     return o, float(lse[0])
+
+
+def enc_e4m3fn(v: float) -> int:
+    """e4m3fn code of a binary32 value: nearest, ties to even, saturated."""
+    return int(_load().oracle_enc_e4m3fn(float(v)))
+
+
+def quantize(ckv_new: np.ndarray, kpe_new: np.ndarray, kv_dtype: int):
+    """Quantise new tokens for an 8-bit cache (see ``mla_oracle_quantize``):
+    bf16 bits [n, 512] and [n, 64] -> (ckv codes uint8 [n, 512], kpe codes
+    uint8 [n, 64], scales float32 [n])."""
+    ckv_new = np.ascontiguousarray(ckv_new, np.uint16)
+    kpe_new = np.ascontiguousarray(kpe_new, np.uint16)
+    n = ckv_new.shape[0]
+    assert ckv_new.shape == (n, D_CKV) and kpe_new.shape == (n, D_KPE)
+    cc = np.zeros((n, D_CKV), np.uint8)
+    kc = np.zeros((n, D_KPE), np.uint8)
+    sc = np.zeros(n, np.float32)
+    P = ctypes.c_void_p
+    st = _load().mla_oracle_quantize(n, int(kv_dtype), ckv_new.ctypes.data_as(P),
+                                     kpe_new.ctypes.data_as(P), cc.ctypes.data_as(P),
+                                     kc.ctypes.data_as(P), sc.ctypes.data_as(P))
+    if st != 0:
+        raise ValueError("unsupported kv_dtype for quantisation")
+    return cc, kc, sc

@@ -332,3 +332,86 @@ void mla_oracle_combine(int32_t n, const double* lse_parts, const double* o_part
   }
   *lse_out = lse;
 }
+
+/*
+ * Cache append with quantisation on write (the cache-write part of the fused
+ * prologue in FlashMLA PR 233, "What is added": an 8-bit latent cache, FP8
+ * e4m3 or INT8, with one scale per token).  For each new token j the 576
+ * values (512 ckv, then 64 kpe) are bf16; for an 8-bit cache
+ *   amax  = max_i |x_i|                          (exact in binary32)
+ *   scale = amax / qmax in binary32 (qmax = 448 for e4m3, 127 for int8);
+ *           scale = 1 for an all-zero token
+ *   v_i   = x_i / scale in binary32
+ *   code_i = the e4m3 value nearest to v_i, ties to even mantissa, saturated
+ *           to +-448 (never NaN); or round-to-nearest-even integer of v_i
+ *           clamped to [-127, 127]
+ * The divisions are the IEEE binary32 ones (the rounding of the reading that
+ * both sides compute them in binary32).  The encoder below works from the
+ * format definition in the header: it finds the binade of |v| with frexp and
+ * rounds the scaled value to the 3-bit mantissa grid with nearbyint (default
+ * rounding mode: to nearest, ties to even).
+ */
+static uint8_t encode_e4m3fn(float v) {
+  const int neg = signbit(v) ? 1 : 0;
+  const double a = fabs((double)v);
+  int code;
+  if (a >= 448.0) {
+    code = 0x7E;
+  } else if (a < ldexp(1.0, -6)) {
+    code = (int)nearbyint(a / ldexp(1.0, -9)); /* subnormal grid m/8 * 2^-6; 8 is 2^-6 */
+  } else {
+    int k;
+    int E;
+    double r;
+    (void)frexp(a, &k); /* a = f 2^k, f in [0.5, 1) */
+    E = k - 1;          /* a in [2^E, 2^(E+1)) */
+    r = nearbyint(a / ldexp(1.0, E - 3)); /* 8 .. 16 */
+    if (r >= 16.0) {
+      r = 8.0;
+      E += 1;
+    }
+    code = ((E + 7) << 3) | ((int)r - 8); /* a < 448 keeps this at or below 0x7E */
+  }
+  return (uint8_t)(code | (neg << 7));
+}
+
+int mla_oracle_quantize(int32_t n, int32_t kv_dtype, const uint16_t* ckv_new,
+                        const uint16_t* kpe_new, uint8_t* ckv_codes, uint8_t* kpe_codes,
+                        float* scales) {
+  int32_t j;
+  int i;
+  if (kv_dtype != ORC_FP8_E4M3 && kv_dtype != ORC_INT8) return -1;
+  for (j = 0; j < n; ++j) {
+    float x[D_CKV + D_KPE];
+    float amax = 0.0f, scale;
+    const float qmax = kv_dtype == ORC_FP8_E4M3 ? 448.0f : 127.0f;
+    for (i = 0; i < D_CKV + D_KPE; ++i) {
+      const uint16_t bits = i < D_CKV ? ckv_new[(int64_t)j * D_CKV + i]
+                                      : kpe_new[(int64_t)j * D_KPE + i - D_CKV];
+      x[i] = (float)oracle_dec_bf16(bits);
+      if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+    }
+    scale = amax > 0.0f ? amax / qmax : 1.0f;
+    scales[j] = scale;
+    for (i = 0; i < D_CKV + D_KPE; ++i) {
+      const float v = x[i] / scale;
+      uint8_t c;
+      if (kv_dtype == ORC_FP8_E4M3) {
+        c = encode_e4m3fn(v);
+      } else {
+        float r = nearbyintf(v);
+        if (r > 127.0f) r = 127.0f;
+        if (r < -127.0f) r = -127.0f;
+        c = (uint8_t)(int8_t)r;
+      }
+      if (i < D_CKV)
+        ckv_codes[(int64_t)j * D_CKV + i] = c;
+      else
+        kpe_codes[(int64_t)j * D_KPE + i - D_CKV] = c;
+    }
+  }
+  return 0;
+}
+
+/* the encoder on its own, for its pins */
+uint8_t oracle_enc_e4m3fn(float v) { return encode_e4m3fn(v); }

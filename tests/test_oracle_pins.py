@@ -365,6 +365,105 @@ def test_row_selection_matches_full_and_thread_count():
 
 
 # ----------------------------------------------------- planted-mistake check
+# ---- quantisation on cache append (oracle.quantize / oracle.enc_e4m3fn) ----
+# The reading: scale = max|x| / 448 (e4m3) or / 127 (int8) in binary32 (1 for an
+# all-zero token), code = nearest representable value of x / scale (binary32
+# division), ties to even, saturated; "FlashMLA Ampere v2", "What is added"
+# (8-bit cache with one scale per token).
+
+def _e4m3_values():
+    return [(c, oracle.dec_e4m3fn(c)) for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+def test_encode_e4m3fn_round_trips_every_code():
+    for c, v in _e4m3_values():
+        assert oracle.enc_e4m3fn(v) == c, (hex(c), v)
+
+
+def test_encode_e4m3fn_ties_go_to_even_mantissa():
+    pos = sorted(v for c, v in _e4m3_values() if c < 0x80)
+    for lo, hi in zip(pos, pos[1:]):
+        mid = (lo + hi) / 2  # exact in binary32 for e4m3 neighbours
+        c = oracle.enc_e4m3fn(mid)
+        assert c % 2 == 0 and oracle.dec_e4m3fn(c) in (lo, hi), (lo, hi, hex(c))
+        below = np.nextafter(np.float32(mid), np.float32(0))
+        above = np.nextafter(np.float32(mid), np.float32(1000))
+        assert oracle.dec_e4m3fn(oracle.enc_e4m3fn(float(below))) == lo
+        assert oracle.dec_e4m3fn(oracle.enc_e4m3fn(float(above))) == hi
+
+
+def test_encode_e4m3fn_matches_library_rounding():
+    # library special case: torch's float32 -> float8_e4m3fn conversion (round to
+    # nearest even) on values inside the finite range
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(17)
+    v = np.concatenate([rng.uniform(-448, 448, 4000), rng.normal(0, 1, 4000) * 2.0 ** rng.integers(-12, 8, 4000),
+                        [v for _, v in _e4m3_values()]]).astype(np.float32)
+    v = v[np.abs(v) <= 448]
+    ref = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([oracle.enc_e4m3fn(float(x)) for x in v], np.uint8)
+    assert np.array_equal(got, ref)
+
+
+def test_encode_e4m3fn_saturates():
+    for v in (448.0, 449.0, 463.9, 464.0, 480.0, 1e6, 3.0e38):
+        assert oracle.enc_e4m3fn(v) == 0x7E and oracle.enc_e4m3fn(-v) == 0xFE
+
+
+def _bf16(x):
+    x = np.asarray(x, np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)  # exact for bf16-representable x
+
+
+def test_quantize_scale_and_codes_definition():
+    rng = np.random.default_rng(3)
+    n = 40
+    xf = (rng.normal(0, 1, (n, 576)) * 2.0 ** rng.integers(-20, 10, (n, 1))).astype(np.float32)
+    xb = _bf16(xf)
+    x = (xb.astype(np.uint32) << 16).view(np.float32)
+    for kvd, qmax in ((oracle.KV_FP8_E4M3, 448.0), (oracle.KV_INT8, 127.0)):
+        cc, kc, sc = oracle.quantize(xb[:, :512], xb[:, 512:], kvd)
+        codes = np.concatenate([cc, kc], axis=1)
+        amax = np.abs(x).max(axis=1)
+        assert np.array_equal(sc, (amax / np.float32(qmax)).astype(np.float32))
+        dec = oracle.dec_e4m3fn if kvd == oracle.KV_FP8_E4M3 else oracle.dec_int8
+        for j in range(n):
+            v = x[j] / sc[j]  # binary32, as the definition
+            back = np.array([dec(c) for c in codes[j]])
+            if kvd == oracle.KV_INT8:
+                assert np.array_equal(back, np.clip(np.rint(v), -127, 127))
+            else:
+                # nearest representable: no e4m3 value is strictly closer
+                grid = np.array(sorted(v2 for _, v2 in _e4m3_values()))
+                err = np.abs(back - v)
+                best = np.abs(grid[None, :] - v[:, None]).min(axis=1)
+                assert np.all(err <= best)
+            # the largest magnitude maps to the end of the range
+            assert np.abs(back).max() == qmax
+
+
+def test_quantize_all_zero_token():
+    z = np.zeros((2, 576), np.uint16)
+    z[1, 7] = 0x8000  # -0.0
+    for kvd in (oracle.KV_FP8_E4M3, oracle.KV_INT8):
+        cc, kc, sc = oracle.quantize(z[:, :512], z[:, 512:], kvd)
+        assert np.all(sc == 1.0)
+        assert all(c in (0, 0x80) for c in np.concatenate([cc.ravel(), kc.ravel()]))
+
+
+def test_quantize_error_bound():
+    # |dec(code) * scale - x| <= half a grid step at |x / scale| times the scale
+    rng = np.random.default_rng(8)
+    xb = _bf16(rng.normal(0, 1, (16, 576)).astype(np.float32))
+    x = (xb.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    cc, kc, sc = oracle.quantize(xb[:, :512], xb[:, 512:], oracle.KV_FP8_E4M3)
+    codes = np.concatenate([cc, kc], axis=1)
+    back = np.vectorize(oracle.dec_e4m3fn)(codes) * sc[:, None].astype(np.float64)
+    v = np.abs(x / sc[:, None])
+    step = np.where(v < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(v, 2.0 ** -6))) - 3))
+    assert np.all(np.abs(back - x) <= 0.5 * step * sc[:, None] * (1 + 1e-6))
+
+
 PIN_SUITE = [
     lambda: test_brute_force_tiny(BRUTE_CASES[0]),
     lambda: test_brute_force_tiny(BRUTE_CASES[4]),
@@ -377,6 +476,10 @@ PIN_SUITE = [
     test_decode_e4m3fn_all_codes,
     test_decode_int8_all_codes,
     test_last_page_len_bounds_the_tokens,
+    test_encode_e4m3fn_round_trips_every_code,
+    test_encode_e4m3fn_ties_go_to_even_mantissa,
+    test_encode_e4m3fn_saturates,
+    test_quantize_scale_and_codes_definition,
 ]
 
 MUTANTS = {
@@ -394,6 +497,12 @@ MUTANTS = {
     "value_from_wrong_head": ("(int64_t)b * in->num_heads + h) * D_CKV;",
                               "(int64_t)b * in->num_heads + 0) * D_CKV;"),
     "unnormalised": ("double p = exp(s[t] - m) / Z;", "double p = exp(s[t] - m);"),
+    "encode_ties_up": ("r = nearbyint(a / ldexp(1.0, E - 3)); /* 8 .. 16 */",
+                       "r = floor(a / ldexp(1.0, E - 3) + 0.5);"),
+    "encode_no_saturation": ("if (a >= 448.0) {", "if (a >= 1e30) {"),
+    "encode_exponent": ("code = ((E + 7) << 3) | ((int)r - 8);", "code = ((E + 8) << 3) | ((int)r - 8);"),
+    "quant_scale_int8": ("kv_dtype == ORC_FP8_E4M3 ? 448.0f : 127.0f;", "kv_dtype == ORC_FP8_E4M3 ? 448.0f : 128.0f;"),
+    "quant_truncate": ("float r = nearbyintf(v);", "float r = truncf(v);"),
 }
 
 
