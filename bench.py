@@ -197,6 +197,51 @@ def workload_report(m: dict, peaks: dict) -> dict:
     return r
 
 
+def measure_append(kv_dtype: int, n: int, steps: int, warmup: int, hip: Hip) -> dict:
+    """mla_cache_append of n new tokens (bf16 in, kv_dtype cache out) into a
+    cache of n slots, rows in a seeded random order.  Algorithmic bytes per
+    token: 1152 read, 1152 (bf16) or 576 codes + 4 scale (8-bit) written, and
+    the 8-byte slot."""
+    import numpy as np
+    import torch
+    import mla_paged_kv_decode_amd as mla
+    rng = np.random.default_rng(11)
+    P = 64
+    pages = n // P
+    new_c = torch.randn((n, 512), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    new_k = torch.randn((n, 64), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+    slots = torch.from_numpy(rng.permutation(n).astype(np.int64)).cuda()
+    if kv_dtype == mla.KV_BF16:
+        ckv = torch.empty((pages, P, 512), dtype=torch.bfloat16, device="cuda")
+        kpe = torch.empty((pages, P, 64), dtype=torch.bfloat16, device="cuda")
+        sc = None
+        wbytes = 1152
+    else:
+        ckv = torch.empty((pages, P, 512), dtype=torch.uint8, device="cuda")
+        kpe = torch.empty((pages, P, 64), dtype=torch.uint8, device="cuda")
+        sc = torch.empty((pages, P), dtype=torch.float32, device="cuda")
+        wbytes = 580
+    for _ in range(warmup):
+        mla.cache_append(new_c, new_k, slots, ckv, kpe, kv_dtype, sc)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    start, stop = hip.event(), hip.event()
+    hip.lib.hipEventRecord(start, ctypes.c_void_p(stream))
+    for _ in range(steps):
+        mla.cache_append(new_c, new_k, slots, ckv, kpe, kv_dtype, sc)
+    hip.lib.hipEventRecord(stop, ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    ms = hip.elapsed_ms(start, stop) / steps
+    hip.destroy(start)
+    hip.destroy(stop)
+    nbytes = n * (1152 + wbytes + 8)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "append_%s_n%d" % (KV_NAMES[kv_dtype], n), "tokens": n,
+            "value": round(gbs, 2), "unit": "GB/s", "ms_per_step": round(ms, 5),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
+
+
 def cpu_baseline(inp, target_s: float) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     the first n (request, head) rows, doubling n until the run takes at least
@@ -241,6 +286,8 @@ def main():
                     help="head split for the measured workloads (0 = the planner's choice)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true",
+                    help="skip the cache-append measurement")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured stream-read / MFMA peak kernels")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -318,6 +365,9 @@ def main():
             out["also"].append(workload_report(sec, peaks))
             del sec
             torch.cuda.empty_cache()
+    if not args.no_append:
+        out["append"] = [measure_append(k, 262144, args.steps, args.warmup, hip)
+                         for k in (0, 1, 2)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

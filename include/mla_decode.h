@@ -33,6 +33,7 @@
  *     from mla_last_error().
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).
  *   - qo_len is 1 (decode): q_nope is [batch, H, 512].
+ *   - A cache "row" is one token slot: row = page * page_size + position.
  */
 #ifndef MLA_DECODE_H
 #define MLA_DECODE_H
@@ -169,6 +170,30 @@ const char* mla_last_error(void);
  */
 mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[12]);
 mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* worker_ptr);
+
+/*
+ * mla_cache_append writes n new latent tokens into the paged cache, quantising
+ * them when the cache is 8-bit (FlashMLA PR 233, "What is added": an FP8 e4m3
+ * or INT8 latent cache with one fp32 scale per token; the layer's prologue
+ * writes the cache before the decode reads it).
+ *   ckv_new  device bf16 [n, 512]; kpe_new device bf16 [n, 64]
+ *   slots    device int64 [n]: destination row page * page_size + position of
+ *            the cache viewed as [pages * page_size, ...]; a negative entry
+ *            skips that token.  Destinations must be distinct and inside the
+ *            cache (not checked on the device).
+ *   ckv, kpe device cache [pages, page_size, 512] and [.., 64] of kv_dtype
+ *   kv_scale device fp32 [pages, page_size] for 8-bit caches, NULL for bf16
+ * bf16: the rows are copied.  8-bit, per token over its 576 values (ckv then
+ * kpe): amax = max |x|; scale = amax / 448 (fp8) or amax / 127 (int8) in
+ * binary32, 1 for an all-zero token; code = the representable value nearest
+ * to x / scale (binary32 division), ties to even, saturated to +-448 / +-127.
+ * Errors: MLA_ERR_INVALID_ARG for n < 0, a null pointer (n > 0) or kv_scale
+ * not matching kv_dtype; MLA_ERR_UNSUPPORTED for another kv_dtype.  One kernel
+ * launch on stream; nothing is allocated or synchronised.
+ */
+mla_status mla_cache_append(const void* ckv_new, const void* kpe_new, const int64_t* slots,
+                            int32_t n, mla_kv_dtype kv_dtype, void* ckv, void* kpe,
+                            float* kv_scale, void* stream);
 
 #ifdef __cplusplus
 }

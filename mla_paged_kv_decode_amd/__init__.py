@@ -35,6 +35,7 @@ EXPORTED_SYMBOLS = (
     "mla_decode_plan_info",
     "mla_decode_plan_segments",
     "mla_decode_plan_set_events",
+    "mla_cache_append",
     "mla_peak_stream_read",
     "mla_peak_mfma_bf16",
 )
@@ -86,6 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_plan_segments.restype = ctypes.c_int
     lib.mla_decode_plan_set_events.argtypes = [P, P, P]
     lib.mla_decode_plan_set_events.restype = ctypes.c_int
+    lib.mla_cache_append.argtypes = [P, P, P, i32, i32, P, P, P, P]
+    lib.mla_cache_append.restype = ctypes.c_int
     lib.mla_peak_stream_read.argtypes = [P, sz, P, i32, ctypes.POINTER(ctypes.c_float), P]
     lib.mla_peak_stream_read.restype = ctypes.c_int
     lib.mla_peak_mfma_bf16.argtypes = [P, i32, ctypes.POINTER(ctypes.c_float), P]
@@ -242,6 +245,38 @@ class Plan:
             _dptr(o), _dptr(lse), _stream_ptr(stream))
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_run")
+
+
+def cache_append(ckv_new, kpe_new, slots, ckv, kpe, kv_dtype: int = KV_BF16, kv_scale=None,
+                 stream=None) -> None:
+    """``mla_cache_append``: write new tokens (bf16 ckv_new [n, 512], kpe_new
+    [n, 64]) into cache rows ``slots`` (int64 [n], page * page_size + position;
+    negative = skip), quantising them for an 8-bit cache."""
+    import torch
+    n = int(ckv_new.shape[0])
+    if ckv_new.dtype != torch.bfloat16 or kpe_new.dtype != torch.bfloat16:
+        raise ValueError("new tokens must be bfloat16")
+    if tuple(ckv_new.shape) != (n, D_CKV) or tuple(kpe_new.shape) != (n, D_KPE):
+        raise ValueError("ckv_new must be [n, 512] and kpe_new [n, 64]")
+    if slots.dtype != torch.int64 or tuple(slots.shape) != (n,):
+        raise ValueError("slots must be int64 [n]")
+    if ckv.dim() != 3 or ckv.shape[2] != D_CKV or kpe.dim() != 3 or kpe.shape[2] != D_KPE \
+            or tuple(ckv.shape[:2]) != tuple(kpe.shape[:2]):
+        raise ValueError("ckv / kpe must be [pages, page_size, 512 / 64]")
+    if kv_dtype == KV_BF16:
+        if ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16 or kv_scale is not None:
+            raise ValueError("bf16 cache expected, without kv_scale")
+    else:
+        if ckv.element_size() != 1 or kpe.element_size() != 1:
+            raise ValueError("8-bit cache expected")
+        if kv_scale is None or kv_scale.dtype != torch.float32 \
+                or tuple(kv_scale.shape) != tuple(ckv.shape[:2]):
+            raise ValueError("kv_scale must be float32 [pages, page_size]")
+    st = load_library().mla_cache_append(_dptr(ckv_new), _dptr(kpe_new), _dptr(slots), n,
+                                         int(kv_dtype), _dptr(ckv), _dptr(kpe), _dptr(kv_scale),
+                                         _stream_ptr(stream))
+    if st != MLA_OK:
+        raise MlaError(st, "mla_cache_append")
 
 
 def peak_stream_read_gbs(nbytes: int = 4 << 30, iters: int = 20, stream=None) -> float:

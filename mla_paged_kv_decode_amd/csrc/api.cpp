@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "../../include/mla_decode.h"
+#include "append.h"
 #include "kernels.h"
 #include "planner.h"
 
@@ -346,6 +347,23 @@ mla_status mla_decode_plan_segments(mla_plan_t p, int32_t* seg, int32_t* worker_
     seg[4 * i + 3] = p->plan.segments[i].slot;
   }
   std::memcpy(worker_ptr, p->plan.worker_ptr.data(), p->plan.worker_ptr.size() * 4);
+  return MLA_OK;
+}
+
+mla_status mla_cache_append(const void* ckv_new, const void* kpe_new, const int64_t* slots,
+                            int32_t n, mla_kv_dtype kv_dtype, void* ckv, void* kpe,
+                            float* kv_scale, void* stream) {
+  if (n < 0) return MLA_ERR_INVALID_ARG;
+  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_INT8)
+    return MLA_ERR_UNSUPPORTED;
+  if (n == 0) return MLA_OK;
+  if (!ckv_new || !kpe_new || !slots || !ckv || !kpe) return MLA_ERR_INVALID_ARG;
+  if ((kv_dtype == MLA_KV_BF16) != (kv_scale == nullptr)) return MLA_ERR_INVALID_ARG;
+  hipError_t e = mla_gpu::launch_cache_append(
+      kv_dtype, static_cast<const uint16_t*>(ckv_new), static_cast<const uint16_t*>(kpe_new),
+      slots, n, static_cast<uint8_t*>(ckv), static_cast<uint8_t*>(kpe), kv_scale,
+      static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "cache append launch");
   return MLA_OK;
 }
 

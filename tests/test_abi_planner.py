@@ -234,3 +234,14 @@ def test_bad_head_split_rejected(lib):
     for heads, hs in ((128, 3), (16, 2), (64, 8)):
         with pytest.raises(mla.MlaError):
             mla.Plan(ip, lp, heads, 16, num_cus=8, head_split=hs)
+
+
+def test_cache_append_rejects_bad_arguments(lib):
+    # every check happens before any HIP call, so this runs without a GPU
+    Pp = ctypes.c_void_p
+    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), -1, 0, Pp(1), Pp(1), None, None) == -1
+    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 3, Pp(1), Pp(1), None, None) == -2
+    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 1, Pp(1), Pp(1), None, None) == -1
+    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 0, Pp(1), Pp(1), Pp(1), None) == -1
+    assert lib.mla_cache_append(None, None, Pp(1), 4, 0, Pp(1), Pp(1), None, None) == -1
+    assert lib.mla_cache_append(None, None, None, 0, 1, None, None, None, None) == 0
