@@ -5,8 +5,9 @@ arithmetic, and neither the GPU path nor the oracle is imported here.  Both
 sides receive the same host arrays from it.
 
 Recipe (the inputs the pages describe, made concrete):
-  * q_nope [B, H, 512], q_pe [B, H, 64], ckv [pages, P, 512], kpe [pages, P, 64]
-    are N(0, 1) draws rounded to bf16 (round-to-nearest-even).  Gaussian rather
+  * q_nope [B * qo_len, H, 512], q_pe [B * qo_len, H, 64], ckv [pages, P, 512],
+    kpe [pages, P, 64] are N(0, 1) draws rounded to bf16 (round-to-nearest-even);
+    qo_len = 1 for plain decode, more for several new tokens per request.  Gaussian rather
     than zero inputs, as flashinfer PR 844's review notes that zero
     initialisation inflates measured throughput.
   * Each request b has L_b tokens in n_b = ceil(L_b / P) pages; the last page
@@ -50,8 +51,8 @@ class MlaInputs:
     page_size: int
     kv_dtype: int
     lengths: np.ndarray           # int64 [B]
-    q_nope: np.ndarray            # uint16 (bf16 bits) [B, H, 512]
-    q_pe: np.ndarray              # uint16 (bf16 bits) [B, H, 64]
+    q_nope: np.ndarray            # uint16 (bf16 bits) [B * qo_len, H, 512]
+    q_pe: np.ndarray              # uint16 (bf16 bits) [B * qo_len, H, 64]
     ckv: np.ndarray               # uint16 [pages, P, 512] (bf16) or uint8 codes
     kpe: np.ndarray               # uint16 [pages, P, 64] (bf16) or uint8 codes
     kv_scale: Optional[np.ndarray]  # float32 [pages, P] for 8-bit caches, else None
@@ -61,6 +62,7 @@ class MlaInputs:
     sm_scale: float
     ckv_src: Optional[np.ndarray] = None  # bf16 source of an 8-bit cache
     kpe_src: Optional[np.ndarray] = None
+    qo_len: int = 1               # queries per request (the last qo_len positions)
 
     @property
     def num_pages(self) -> int:
@@ -76,16 +78,23 @@ class MlaInputs:
         quoted on the "Benchmarking MLA" page: q_nope + q_pe + the KV rows the
         requests cover + kv_indptr + kv_indices + kv_last_page_len, plus o
         (bf16) and lse (fp32)."""
-        B, H = self.batch, self.num_heads
-        q = B * H * (D_CKV + D_KPE) * 2
+        NQ, H = self.batch * self.qo_len, self.num_heads
+        q = NQ * H * (D_CKV + D_KPE) * 2
         kv = int(self.lengths.sum()) * self.kv_bytes_per_token()
         meta = 4 * (self.kv_indptr.size + self.kv_indices.size + self.kv_last_page_len.size)
-        out = B * H * D_CKV * 2 + B * H * 4
+        out = NQ * H * D_CKV * 2 + NQ * H * 4
         return q + kv + meta + out
 
+    def visible_tokens(self) -> int:
+        """Sum over the queries of the tokens each may attend to (causal, with
+        the qo_len queries at the end of their request)."""
+        q = self.qo_len
+        return int(sum(max(0, int(L) - (q - 1 - i)) for L in self.lengths for i in range(q)))
+
     def flops(self) -> int:
-        """2 * H * L * (576 + 512) per request: QK over 576 dims, PV over 512."""
-        return int(2 * self.num_heads * int(self.lengths.sum()) * (D_CKV + D_KPE + D_CKV))
+        """2 * H * (576 + 512) per visible (query, token) pair: QK over 576
+        dims, PV over 512."""
+        return int(2 * self.num_heads * self.visible_tokens() * (D_CKV + D_KPE + D_CKV))
 
 
 def _rngs(seed: int, n: int):
@@ -148,15 +157,15 @@ def page_table(lengths, page_size: int, rng: np.random.Generator, extra_pages: i
 
 def make_inputs(lengths, num_heads: int, page_size: int, kv_dtype: int = KV_BF16, seed: int = 0,
                 poison: bool = False, extra_pages: int = 0,
-                sm_scale: float = SM_SCALE_192) -> MlaInputs:
+                sm_scale: float = SM_SCALE_192, qo_len: int = 1) -> MlaInputs:
     lengths = np.asarray(lengths, np.int64)
     B = int(lengths.size)
     H = int(num_heads)
     P = int(page_size)
     r_qn, r_qp, r_ckv, r_kpe, r_perm = _rngs(seed, 5)
     indptr, indices, last, pages = page_table(lengths, P, r_perm, extra_pages)
-    q_nope = _normal_bf16(r_qn, (B, H, D_CKV))
-    q_pe = _normal_bf16(r_qp, (B, H, D_KPE))
+    q_nope = _normal_bf16(r_qn, (B * qo_len, H, D_CKV))
+    q_pe = _normal_bf16(r_qp, (B * qo_len, H, D_KPE))
     ckv = _normal_bf16(r_ckv, (pages, P, D_CKV))
     kpe = _normal_bf16(r_kpe, (pages, P, D_KPE))
     ckv_src = kpe_src = None
@@ -167,7 +176,7 @@ def make_inputs(lengths, num_heads: int, page_size: int, kv_dtype: int = KV_BF16
     if poison:
         _poison(ckv, kpe, kv_scale, kv_dtype, indptr, indices, last, P, pages)
     return MlaInputs(B, H, P, int(kv_dtype), lengths, q_nope, q_pe, ckv, kpe, kv_scale,
-                     indptr, indices, last, float(sm_scale), ckv_src, kpe_src)
+                     indptr, indices, last, float(sm_scale), ckv_src, kpe_src, int(qo_len))
 
 
 def _poison(ckv, kpe, kv_scale, kv_dtype, indptr, indices, last, P, pages):

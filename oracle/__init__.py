@@ -68,11 +68,11 @@ def _load():
     lib.oracle_dec_int8.restype = f64
     lib.oracle_kv_len.argtypes = [P, P, i32, i32]
     lib.oracle_kv_len.restype = i64
-    lib.mla_oracle_decode.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, P, i64, P, P,
-                                      i32]
+    lib.mla_oracle_decode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, P, i64,
+                                      P, P, i32]
     lib.mla_oracle_decode.restype = ctypes.c_int
-    lib.mla_oracle_partial.argtypes = [i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, i32, i32, i64,
-                                       i64, P, P]
+    lib.mla_oracle_partial.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, i32, i32,
+                                       i32, i64, i64, P, P]
     lib.mla_oracle_partial.restype = ctypes.c_int
     lib.mla_oracle_combine.argtypes = [i32, P, P, P, P]
     lib.mla_oracle_combine.restype = None
@@ -119,17 +119,23 @@ def _kv_arrays(kv_dtype, ckv, kpe):
 
 
 def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_scale: float,
-           page_size: int, kv_dtype: int = KV_BF16, kv_scale=None, rows=None, threads: int = 0):
+           page_size: int, kv_dtype: int = KV_BF16, kv_scale=None, rows=None, threads: int = 0,
+           qo_len: int = 1):
     """fp64 decode.  Inputs are host numpy arrays: bf16 tensors as uint16 bit
     patterns, 8-bit caches as uint8 codes with an fp32 ``kv_scale[pages, P]``.
+    With qo_len > 1 the queries are [B * qo_len, H, *] and query i of request b
+    sees its first L_b - (qo_len - 1 - i) tokens (causal, queries at the end).
 
-    Returns (o, lse): o is float64 [B, H, 512] (or [len(rows), 512] when a list
-    of flattened b*H + h rows is given) and lse float64 [B, H] (or [len(rows)]).
+    Returns (o, lse): o is float64 [B * qo_len, H, 512] (or [len(rows), 512]
+    when a list of flattened (b * qo_len + i) * H + h rows is given) and lse
+    float64 [B * qo_len, H] (or [len(rows)]).
     """
     qn = _c(q_nope, np.uint16)
     qp = _c(q_pe, np.uint16)
-    B, H = qn.shape[0], qn.shape[1]
-    assert qn.shape == (B, H, D_CKV) and qp.shape == (B, H, D_KPE)
+    NQ, H = qn.shape[0], qn.shape[1]
+    assert qo_len >= 1 and NQ % qo_len == 0
+    B = NQ // qo_len
+    assert qn.shape == (NQ, H, D_CKV) and qp.shape == (NQ, H, D_KPE)
     ck, kp = _kv_arrays(kv_dtype, ckv, kpe)
     sc = _c(kv_scale, np.float32)
     ip = _c(kv_indptr, np.int32)
@@ -138,15 +144,16 @@ def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_s
     if threads <= 0:
         threads = os.cpu_count() or 1
     if rows is None:
-        o = np.zeros((B, H, D_CKV), np.float64)
-        lse = np.zeros((B, H), np.float64)
+        o = np.zeros((NQ, H, D_CKV), np.float64)
+        lse = np.zeros((NQ, H), np.float64)
         rr, nr = None, 0
     else:
         rr = _c(rows, np.int32)
         nr = rr.size
         o = np.zeros((nr, D_CKV), np.float64)
         lse = np.zeros((nr,), np.float64)
-    st = _load().mla_oracle_decode(B, H, int(page_size), int(kv_dtype), _ptr(qn), _ptr(qp),
+    st = _load().mla_oracle_decode(B, int(qo_len), H, int(page_size), int(kv_dtype), _ptr(qn),
+                                    _ptr(qp),
                                     _ptr(ck), _ptr(kp), _ptr(sc), _ptr(ip), _ptr(ix), _ptr(lp),
                                     float(sm_scale), _ptr(rr), nr, _ptr(o), _ptr(lse), int(threads))
     if st != 0:
@@ -156,11 +163,12 @@ def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_s
 
 def partial(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_scale: float,
             page_size: int, b: int, h: int, t0: int, t1: int, kv_dtype: int = KV_BF16,
-            kv_scale=None):
-    """Partial (O_i [512], LSE_i) of head h of request b over tokens [t0, t1)."""
+            kv_scale=None, qo_len: int = 1, qi: int = 0):
+    """Partial (O_i [512], LSE_i) of head h of query qi of request b over tokens
+    [t0, t1), tokens past the query's causal limit excluded."""
     qn = _c(q_nope, np.uint16)
     qp = _c(q_pe, np.uint16)
-    B, H = qn.shape[0], qn.shape[1]
+    B, H = qn.shape[0] // qo_len, qn.shape[1]
     ck, kp = _kv_arrays(kv_dtype, ckv, kpe)
     sc = _c(kv_scale, np.float32)
     ip = _c(kv_indptr, np.int32)
@@ -168,10 +176,10 @@ def partial(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_
     lp = _c(kv_last_page_len, np.int32)
     o = np.zeros((D_CKV,), np.float64)
     lse = np.zeros((1,), np.float64)
-    st = _load().mla_oracle_partial(B, H, int(page_size), int(kv_dtype), _ptr(qn), _ptr(qp),
-                                     _ptr(ck), _ptr(kp), _ptr(sc), _ptr(ip), _ptr(ix), _ptr(lp),
-                                     float(sm_scale), int(b), int(h), int(t0), int(t1), _ptr(o),
-                                     _ptr(lse))
+    st = _load().mla_oracle_partial(B, int(qo_len), H, int(page_size), int(kv_dtype), _ptr(qn),
+                                     _ptr(qp), _ptr(ck), _ptr(kp), _ptr(sc), _ptr(ip), _ptr(ix),
+                                     _ptr(lp), float(sm_scale), int(b), int(qi), int(h), int(t0),
+                                     int(t1), _ptr(o), _ptr(lse))
     if st != 0:
         raise RuntimeError("mla_oracle_partial: bad range")
     return o, float(lse[0])

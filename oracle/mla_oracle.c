@@ -29,6 +29,15 @@
  *   O    = sum_t (exp(s_t - m) / Z) * K_t   (512 values)
  *   An empty request (L_b = 0) gives O = 0 and LSE = -inf.
  *
+ * Several queries per request (qo_len > 1, e.g. speculative tokens): the
+ * query tensors are [batch * qo_len, H, *] ("perf: MLA decode kernel
+ * implemented by CuTe targeted to SM80", the test's tensor shapes), query i
+ * of request b is row b * qo_len + i, and the sums above run over its
+ * visible tokens t < L_b - (qo_len - 1 - i) only: the queries are the last
+ * qo_len positions of the sequence, the causal mask with Q at the end of the
+ * score matrix ("FlashMLA SM100", the forward kernel notes on N_Q != N_K).
+ * A query with no visible token gets O = 0 and LSE = -inf.
+ *
  * The softmax is taken in two plain passes (max first, then sums), in logical
  * token order, in fp64, with no online rescaling, no blocking and no
  * reordering.  The split-KV merge (one partial (O_i, LSE_i) per token chunk,
@@ -84,9 +93,9 @@ int64_t oracle_kv_len(const int32_t* kv_indptr, const int32_t* kv_last_page_len,
 }
 
 typedef struct {
-  int32_t batch, num_heads, page_size, kv_dtype;
-  const uint16_t* q_nope; /* bf16 bits [B, H, 512] */
-  const uint16_t* q_pe;   /* bf16 bits [B, H, 64] */
+  int32_t batch, qo_len, num_heads, page_size, kv_dtype;
+  const uint16_t* q_nope; /* bf16 bits [B * qo_len, H, 512] */
+  const uint16_t* q_pe;   /* bf16 bits [B * qo_len, H, 64] */
   const void* ckv;        /* [pages, P, 512] bf16 bits or 8-bit codes */
   const void* kpe;        /* [pages, P, 64]  bf16 bits or 8-bit codes */
   const float* kv_scale;  /* [pages, P] or NULL for bf16 */
@@ -123,15 +132,30 @@ static void load_token(const oracle_inputs* in, int32_t b, int64_t t, double* K,
 }
 
 /*
- * Attention of head h of request b over the logical token range [t0, t1)
- * (t1 <= L_b).  Writes the normalised output (512) and the log-sum-exp.
- * An empty range gives O = 0, LSE = -inf.  Returns 0, or -1 on allocation
- * failure.
+ * Tokens that query i (0 <= i < qo_len) of request b may attend to: the
+ * first V = L_b - (qo_len - 1 - i) tokens (none if that is not positive).
+ * The qo_len queries of a request are its last qo_len positions, so the
+ * causal mask is aligned to the bottom-right corner of the score matrix (the
+ * "Q at the end" causal mask for N_Q != N_K that the FlashMLA SM100 release
+ * notes name).  With qo_len = 1 every query sees all L_b tokens.
  */
-static int attend_range(const oracle_inputs* in, int32_t b, int32_t h, int64_t t0, int64_t t1,
-                        double* o, double* lse) {
-  const uint16_t* qn = in->q_nope + ((int64_t)b * in->num_heads + h) * D_CKV;
-  const uint16_t* qp = in->q_pe + ((int64_t)b * in->num_heads + h) * D_KPE;
+static int64_t visible_len(const oracle_inputs* in, int32_t b, int32_t qi) {
+  int64_t v = oracle_kv_len(in->kv_indptr, in->kv_last_page_len, in->page_size, b) -
+              (int64_t)(in->qo_len - 1 - qi);
+  return v > 0 ? v : 0;
+}
+
+/*
+ * Attention of head h of query i of request b over the logical token range
+ * [t0, t1) (t1 <= L_b).  The query vector is row b * qo_len + i of q_nope /
+ * q_pe.  Writes the normalised output (512) and the log-sum-exp.  An empty
+ * range gives O = 0, LSE = -inf.  Returns 0, or -1 on allocation failure.
+ */
+static int attend_range(const oracle_inputs* in, int32_t b, int32_t qi, int32_t h, int64_t t0,
+                        int64_t t1, double* o, double* lse) {
+  const int64_t qrow = (int64_t)b * in->qo_len + qi;
+  const uint16_t* qn = in->q_nope + (qrow * in->num_heads + h) * D_CKV;
+  const uint16_t* qp = in->q_pe + (qrow * in->num_heads + h) * D_KPE;
   double q[D_CKV + D_KPE];
   double K[D_CKV], R[D_KPE];
   int64_t n = t1 - t0, t;
@@ -177,7 +201,7 @@ static int attend_range(const oracle_inputs* in, int32_t b, int32_t h, int64_t t
 
 typedef struct {
   const oracle_inputs* in;
-  const int32_t* rows; /* flattened b*H + h, or NULL for all */
+  const int32_t* rows; /* flattened (b * qo_len + i) * H + h, or NULL for all */
   int64_t n_rows;
   double* o;
   double* lse;
@@ -190,23 +214,29 @@ static void* worker(void* p) {
   int64_t r;
   for (r = w->begin; r < w->end; ++r) {
     int64_t flat = w->rows ? (int64_t)w->rows[r] : r;
-    int32_t b = (int32_t)(flat / w->in->num_heads);
+    int64_t qrow = flat / w->in->num_heads;
     int32_t h = (int32_t)(flat % w->in->num_heads);
-    int64_t L = oracle_kv_len(w->in->kv_indptr, w->in->kv_last_page_len, w->in->page_size, b);
-    if (attend_range(w->in, b, h, 0, L, w->o + r * D_CKV, w->lse + r) != 0) w->status = -1;
+    int32_t b = (int32_t)(qrow / w->in->qo_len);
+    int32_t qi = (int32_t)(qrow % w->in->qo_len);
+    int64_t V = visible_len(w->in, b, qi);
+    if (attend_range(w->in, b, qi, h, 0, V, w->o + r * D_CKV, w->lse + r) != 0) w->status = -1;
   }
   return NULL;
 }
 
 /*
- * Full decode (or a selected list of (b, h) rows).
- *   rows == NULL: all B*H rows; o_out is [B*H, 512], lse_out [B*H].
- *   rows != NULL: n_rows entries of b*H + h; o_out is [n_rows, 512].
+ * Full decode (or a selected list of query rows) of qo_len queries per
+ * request (qo_len = 1: one new token per request).
+ *   rows == NULL: all B*qo_len*H rows; o_out is [B*qo_len*H, 512], lse_out
+ *                 [B*qo_len*H].
+ *   rows != NULL: n_rows entries of (b * qo_len + i) * H + h; o_out is
+ *                 [n_rows, 512].
  * Rows are distributed over num_threads threads in contiguous blocks; each
  * row's arithmetic is independent of the thread count.
  * Returns 0 on success, -1 on bad arguments or allocation failure.
  */
-int mla_oracle_decode(int32_t batch, int32_t num_heads, int32_t page_size, int32_t kv_dtype,
+int mla_oracle_decode(int32_t batch, int32_t qo_len, int32_t num_heads, int32_t page_size,
+                      int32_t kv_dtype,
                       const uint16_t* q_nope, const uint16_t* q_pe, const void* ckv, const void* kpe,
                       const float* kv_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
                       const int32_t* kv_last_page_len, double sm_scale, const int32_t* rows,
@@ -217,10 +247,12 @@ int mla_oracle_decode(int32_t batch, int32_t num_heads, int32_t page_size, int32
   worker_arg* args;
   int status = 0;
 
-  if (batch < 0 || num_heads <= 0 || page_size <= 0 || !o_out || !lse_out) return -1;
+  if (batch < 0 || qo_len < 1 || num_heads <= 0 || page_size <= 0 || !o_out || !lse_out)
+    return -1;
   if (kv_dtype != ORC_BF16 && kv_dtype != ORC_FP8_E4M3 && kv_dtype != ORC_INT8) return -1;
   if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
   in.batch = batch;
+  in.qo_len = qo_len;
   in.num_heads = num_heads;
   in.page_size = page_size;
   in.kv_dtype = kv_dtype;
@@ -234,7 +266,7 @@ int mla_oracle_decode(int32_t batch, int32_t num_heads, int32_t page_size, int32
   in.kv_last_page_len = kv_last_page_len;
   in.sm_scale = sm_scale;
 
-  total = rows ? n_rows : (int64_t)batch * num_heads;
+  total = rows ? n_rows : (int64_t)batch * qo_len * num_heads;
   if (total == 0) return 0;
   if (num_threads < 1) num_threads = 1;
   if (num_threads > total) num_threads = (int32_t)total;
@@ -273,22 +305,26 @@ int mla_oracle_decode(int32_t batch, int32_t num_heads, int32_t page_size, int32
 }
 
 /*
- * Attention of one (b, h) over the logical token range [t0, t1) only, giving
- * the partial (O_i, LSE_i) of a split-KV chunk.  Returns -1 if the range is
- * outside [0, L_b].
+ * Attention of one (b, i, h) over the logical token range [t0, t1) only,
+ * giving the partial (O_i, LSE_i) of a split-KV chunk; tokens past the
+ * query's causal limit (visible_len) carry no weight.  Returns -1 if the
+ * range is outside [0, L_b].
  */
-int mla_oracle_partial(int32_t batch, int32_t num_heads, int32_t page_size, int32_t kv_dtype,
+int mla_oracle_partial(int32_t batch, int32_t qo_len, int32_t num_heads, int32_t page_size,
+                       int32_t kv_dtype,
                        const uint16_t* q_nope, const uint16_t* q_pe, const void* ckv, const void* kpe,
                        const float* kv_scale, const int32_t* kv_indptr, const int32_t* kv_indices,
-                       const int32_t* kv_last_page_len, double sm_scale, int32_t b, int32_t h,
-                       int64_t t0, int64_t t1, double* o_out, double* lse_out) {
+                       const int32_t* kv_last_page_len, double sm_scale, int32_t b, int32_t qi,
+                       int32_t h, int64_t t0, int64_t t1, double* o_out, double* lse_out) {
   oracle_inputs in;
-  int64_t L;
-  if (b < 0 || b >= batch || h < 0 || h >= num_heads) return -1;
+  int64_t L, V;
+  if (b < 0 || b >= batch || qo_len < 1 || qi < 0 || qi >= qo_len || h < 0 || h >= num_heads)
+    return -1;
   if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
   L = oracle_kv_len(kv_indptr, kv_last_page_len, page_size, b);
   if (t0 < 0 || t1 < t0 || t1 > L) return -1;
   in.batch = batch;
+  in.qo_len = qo_len;
   in.num_heads = num_heads;
   in.page_size = page_size;
   in.kv_dtype = kv_dtype;
@@ -301,7 +337,8 @@ int mla_oracle_partial(int32_t batch, int32_t num_heads, int32_t page_size, int3
   in.kv_indices = kv_indices;
   in.kv_last_page_len = kv_last_page_len;
   in.sm_scale = sm_scale;
-  return attend_range(&in, b, h, t0, t1, o_out, lse_out);
+  V = visible_len(&in, b, qi);
+  return attend_range(&in, b, qi, h, t0, t1 < V ? t1 : (t0 > V ? t0 : V), o_out, lse_out);
 }
 
 /*

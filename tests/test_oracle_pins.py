@@ -73,34 +73,40 @@ def _token_rows(inp, b):
 
 
 def brute_force(inp):
-    B, H = inp.batch, inp.num_heads
+    """Exact-rational scores, exp without max-shift, fsum.  With qo_len = q
+    queries per request, query i (row b * q + i) sees the first L_b - (q - 1 - i)
+    tokens: the queries are the request's last q positions ("FlashMLA SM100",
+    forward kernel notes: causal mask with Q at the end of the matrix)."""
+    B, H, Q = inp.batch, inp.num_heads, inp.qo_len
     qn = _dec_tensor(inp.q_nope, synth.KV_BF16)
     qp = _dec_tensor(inp.q_pe, synth.KV_BF16)
-    O = np.zeros((B, H, 512))
-    LSE = np.zeros((B, H))
+    O = np.zeros((B * Q, H, 512))
+    LSE = np.zeros((B * Q, H))
     smf = Fraction(inp.sm_scale)
     for b in range(B):
         K, R = _token_rows(inp, b)
-        L = K.shape[0]
-        if L == 0:
-            LSE[b, :] = -np.inf
-            continue
-        Kf = [[Fraction(float(x)) for x in np.concatenate([K[t], R[t]])] for t in range(L)]
-        for h in range(H):
-            q = [Fraction(float(x)) for x in np.concatenate([qn[b, h], qp[b, h]])]
-            s = [float(smf * sum(a * c for a, c in zip(q, Kf[t]))) for t in range(L)]
-            w = [math.exp(x) for x in s]
-            Z = math.fsum(w)
-            LSE[b, h] = math.log(Z)
-            for i in range(512):
-                O[b, h, i] = math.fsum(w[t] * K[t, i] for t in range(L)) / Z
+        Kf = [[Fraction(float(x)) for x in np.concatenate([K[t], R[t]])] for t in range(K.shape[0])]
+        for qi in range(Q):
+            row = b * Q + qi
+            V = max(0, K.shape[0] - (Q - 1 - qi))
+            if V == 0:
+                LSE[row, :] = -np.inf
+                continue
+            for h in range(H):
+                q = [Fraction(float(x)) for x in np.concatenate([qn[row, h], qp[row, h]])]
+                s = [float(smf * sum(a * c for a, c in zip(q, Kf[t]))) for t in range(V)]
+                w = [math.exp(x) for x in s]
+                Z = math.fsum(w)
+                LSE[row, h] = math.log(Z)
+                for i in range(512):
+                    O[row, h, i] = math.fsum(w[t] * K[t, i] for t in range(V)) / Z
     return O, LSE
 
 
 def run_oracle(inp, rows=None, threads=4):
     return oracle.decode(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.kv_indptr, inp.kv_indices,
                          inp.kv_last_page_len, inp.sm_scale, inp.page_size, inp.kv_dtype,
-                         inp.kv_scale, rows=rows, threads=threads)
+                         inp.kv_scale, rows=rows, threads=threads, qo_len=inp.qo_len)
 
 
 def _bf16(x):
@@ -166,6 +172,82 @@ def test_brute_force_tiny(case):
     O, LSE = brute_force(inp)
     _close(o, O)
     _close(lse, LSE)
+
+
+# --------------------------------------------- several queries per request
+# (lengths, H, P, kv_dtype, seed, qo_len): short requests (L_b < qo_len) leave
+# the first queries with nothing visible; an empty request leaves all of them.
+CAUSAL_CASES = [
+    ([5, 1, 13], 2, 4, synth.KV_BF16, 21, 3),
+    ([9, 0, 4], 2, 2, synth.KV_FP8_E4M3, 22, 2),
+    ([17, 6], 2, 16, synth.KV_INT8, 23, 4),
+]
+
+
+@pytest.mark.parametrize("case", CAUSAL_CASES)
+def test_brute_force_causal_queries(case):
+    lengths, H, P, kvd, seed, q = case
+    inp = synth.make_inputs(lengths, H, P, kvd, seed=seed, poison=True, extra_pages=2, qo_len=q)
+    o, lse = run_oracle(inp)
+    O, LSE = brute_force(inp)
+    _close(o, O)
+    _close(lse, LSE)
+
+
+def _truncated(inp, b, V):
+    """Request b alone with a page table cut to its first V tokens (built here)."""
+    P = inp.page_size
+    one = synth.make_inputs([1], inp.num_heads, P, inp.kv_dtype, seed=0)
+    one.ckv, one.kpe, one.kv_scale = inp.ckv, inp.kpe, inp.kv_scale
+    n = (V + P - 1) // P
+    pages = inp.kv_indices[inp.kv_indptr[b]:inp.kv_indptr[b] + n]
+    one.kv_indptr = np.array([0, n], np.int32)
+    one.kv_indices = pages.copy()
+    one.kv_last_page_len = np.array([V - (n - 1) * P if n else 1], np.int32)
+    one.lengths = np.array([V], np.int64)
+    return one
+
+
+@pytest.mark.parametrize("kvd", [synth.KV_BF16, synth.KV_FP8_E4M3])
+def test_causal_query_is_decode_of_its_prefix(kvd):
+    # query i of q sees exactly what a one-query decode of the request cut to
+    # L_b - (q - 1 - i) tokens sees; the last query sees the whole request
+    q = 4
+    inp = synth.make_inputs([37, 50], 3, 16, kvd, seed=24, poison=True, qo_len=q)
+    o, lse = run_oracle(inp)
+    for b in range(2):
+        L = int(inp.lengths[b])
+        for qi in range(q):
+            one = _truncated(inp, b, L - (q - 1 - qi))
+            one.q_nope = inp.q_nope[b * q + qi:b * q + qi + 1]
+            one.q_pe = inp.q_pe[b * q + qi:b * q + qi + 1]
+            o1, l1 = run_oracle(one)
+            assert np.array_equal(o1[0], o[b * q + qi]) and np.array_equal(l1[0], lse[b * q + qi])
+    # the mask matters: query 0 over the whole request is a different result
+    whole = _truncated(inp, 0, 37)
+    whole.q_nope, whole.q_pe = inp.q_nope[0:1], inp.q_pe[0:1]
+    assert not np.array_equal(run_oracle(whole)[1][0], lse[0])
+
+
+def test_causal_split_partials_combine_to_unsplit():
+    q, L = 3, 70
+    inp = synth.make_inputs([L], 2, 16, synth.KV_BF16, seed=25, qo_len=q)
+    o, lse = run_oracle(inp)
+    args = (inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.kv_indptr, inp.kv_indices,
+            inp.kv_last_page_len, inp.sm_scale, inp.page_size)
+    # cuts inside the masked tail: the last chunk is fully masked for query 0
+    for bounds in ([0, 32, 68, 70], [0, 69, 70], [0, 16, 48, 64, 70]):
+        for qi in range(q):
+            for h in range(2):
+                parts = [oracle.partial(*args, 0, h, bounds[i], bounds[i + 1], qo_len=q, qi=qi)
+                         for i in range(len(bounds) - 1)]
+                oc, lc = oracle.combine(np.array([p[1] for p in parts]),
+                                        np.stack([p[0] for p in parts]))
+                _close(oc, o[qi, h], 1e-12)
+                assert abs(lc - lse[qi, h]) <= 1e-12 * abs(lse[qi, h])
+    # a chunk past the causal limit is empty
+    _, l_empty = oracle.partial(*args, 0, 0, 68, 70, qo_len=q, qi=0)
+    assert l_empty == -np.inf
 
 
 # ----------------------------------------------------------- library special
@@ -480,6 +562,8 @@ PIN_SUITE = [
     test_encode_e4m3fn_ties_go_to_even_mantissa,
     test_encode_e4m3fn_saturates,
     test_quantize_scale_and_codes_definition,
+    lambda: test_brute_force_causal_queries(CAUSAL_CASES[0]),
+    lambda: test_causal_query_is_decode_of_its_prefix(synth.KV_BF16),
 ]
 
 MUTANTS = {
@@ -494,8 +578,8 @@ MUTANTS = {
     "int8_unsigned": ("return (double)(int8_t)code;", "return (double)code;"),
     "kpe_unscaled": ("oracle_dec_int8(k[i])) * sigma;", "oracle_dec_int8(k[i]));"),
     "combine_weight": ("double w = exp(lse_parts[i] - lse);", "double w = exp(lse_parts[i] - M);"),
-    "value_from_wrong_head": ("(int64_t)b * in->num_heads + h) * D_CKV;",
-                              "(int64_t)b * in->num_heads + 0) * D_CKV;"),
+    "value_from_wrong_head": ("(qrow * in->num_heads + h) * D_CKV;",
+                              "(qrow * in->num_heads + 0) * D_CKV;"),
     "unnormalised": ("double p = exp(s[t] - m) / Z;", "double p = exp(s[t] - m);"),
     "encode_ties_up": ("r = nearbyint(a / ldexp(1.0, E - 3)); /* 8 .. 16 */",
                        "r = floor(a / ldexp(1.0, E - 3) + 0.5);"),
@@ -503,6 +587,11 @@ MUTANTS = {
     "encode_exponent": ("code = ((E + 7) << 3) | ((int)r - 8);", "code = ((E + 8) << 3) | ((int)r - 8);"),
     "quant_scale_int8": ("kv_dtype == ORC_FP8_E4M3 ? 448.0f : 127.0f;", "kv_dtype == ORC_FP8_E4M3 ? 448.0f : 128.0f;"),
     "quant_truncate": ("float r = nearbyintf(v);", "float r = truncf(v);"),
+    "causal_off_by_one": ("(int64_t)(in->qo_len - 1 - qi);", "(int64_t)(in->qo_len - qi);"),
+    "causal_reversed": ("(int64_t)(in->qo_len - 1 - qi);", "(int64_t)(qi);"),
+    "causal_none": ("(int64_t)(in->qo_len - 1 - qi);", "(int64_t)0;"),
+    "query_row_ignores_index": ("const int64_t qrow = (int64_t)b * in->qo_len + qi;",
+                                "const int64_t qrow = (int64_t)b * in->qo_len;"),
 }
 
 
