@@ -39,7 +39,7 @@ KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", "kernels.hip"
 # other workloads measured in the same run (parity cases at full size)
 SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
              "fp8_b64_h16_l8192_p64", "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64",
-             "int8_b64_h128_l8192_p64")
+             "int8_b64_h128_l8192_p64", "mtp_b64_h16_q2_l4096_p64", "mtp_b64_h128_q2_l4096_p64")
 KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8"}
 
 
@@ -128,15 +128,15 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
 
     inp = synth.make_workload(name)
     sets = device_inputs(inp, copies)
-    B, H = inp.batch, inp.num_heads
-    ws = torch.empty(mla.workspace_bytes(B, H, head_split=head_split), dtype=torch.uint8,
+    B, H, Q = inp.batch, inp.num_heads, inp.qo_len
+    ws = torch.empty(mla.workspace_bytes(B, H, head_split=head_split, qo_len=Q), dtype=torch.uint8,
                      device="cuda")
     t0 = time.perf_counter()
     plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, inp.page_size, inp.kv_dtype, ws,
-                    head_split=head_split)
+                    head_split=head_split, qo_len=Q)
     plan_ms = (time.perf_counter() - t0) * 1e3
-    outs = [(torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda"),
-             torch.empty((B, H), dtype=torch.float32, device="cuda")) for _ in range(copies)]
+    outs = [(torch.empty((B * Q, H, 512), dtype=torch.bfloat16, device="cuda"),
+             torch.empty((B * Q, H), dtype=torch.float32, device="cuda")) for _ in range(copies)]
 
     def step(i):
         s = sets[i % copies]
@@ -174,12 +174,13 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
 
 def workload_report(m: dict, peaks: dict) -> dict:
     """Throughput of one measured workload against both roofs: HBM bytes for
-    the memory-bound head counts (h_q <= 64), bf16 MFMA flops for h_q = 128."""
+    the memory-bound shapes (at most 64 query vectors per request), bf16 MFMA
+    flops from 128 (h_q = 128, or h_q x qo_len >= 128)."""
     inp = m["inp"]
     k_s = m["kernel_ms"] * 1e-3
     gbs, tfs = m["bytes"] / k_s / 1e9, m["flops"] / k_s / 1e12
-    mfma = inp.num_heads >= 128
-    r = {"workload": m["name"], "kv_dtype": KV_NAMES[inp.kv_dtype],
+    mfma = inp.num_heads * inp.qo_len >= 128
+    r = {"workload": m["name"], "kv_dtype": KV_NAMES[inp.kv_dtype], "qo_len": inp.qo_len,
          "value": round((m["flops"] / 1e12 if mfma else m["bytes"] / 1e9)
                         / (m["ms_per_step"] * 1e-3), 2),
          "unit": "TFLOP/s" if mfma else "GB/s", "ms_per_step": round(m["ms_per_step"], 5),

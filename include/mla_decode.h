@@ -32,7 +32,17 @@
  *     is reported as MLA_ERR_HIP and the text of the last error is available
  *     from mla_last_error().
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).
- *   - qo_len is 1 (decode): q_nope is [batch, H, 512].
+ *   - qo_len (mla_plan_opts.qo_len, default 1) queries per request: q_nope is
+ *     [batch * qo_len, H, 512], q_pe [batch * qo_len, H, 64], o
+ *     [batch * qo_len, H, 512], lse [batch * qo_len, H]; row b * qo_len + i is
+ *     query i of request b.  The queries are the request's last qo_len
+ *     positions: query i attends to the first L_b - (qo_len - 1 - i) tokens
+ *     (the causal mask with Q at the end of the score matrix, for
+ *     N_Q != N_K, of FlashMLA PR 76's forward kernel notes); a query with
+ *     no visible token gets o = 0, lse = -inf.  All qo_len * H query vectors
+ *     of a request share its latent stream, so they are folded into the
+ *     kernel's head dimension (flashinfer issue 700 notes that fusing the
+ *     query length with the heads raises the work per KV byte).
  *   - A cache "row" is one token slot: row = page * page_size + position.
  */
 #ifndef MLA_DECODE_H
@@ -65,14 +75,19 @@ typedef struct {
   int32_t num_cus;      /* compute units to balance over; 0 = query the current device */
   int32_t force_splits; /* > 0: cut every request into this many near-equal chunks (testing) */
   int32_t max_workers;  /* > 0: cap on the number of workgroups; 0 = library default */
-  int32_t head_split;   /* 0 = automatic; n >= 1: run each request's heads as n groups of
-                           num_heads / n heads sharing the request's latent cache (n = 1:
-                           all heads in one workgroup).  num_heads / n must be supported. */
+  int32_t head_split;   /* 0 = automatic; n >= 1: run each request's qo_len * num_heads query
+                           vectors as n groups of qo_len * num_heads / n sharing the
+                           request's latent cache (n = 1: all in one workgroup).  The group
+                           width must be one the kernels serve: 16, 32, 64 or 128 (bf16),
+                           16 or 128 (8-bit caches). */
+  int32_t qo_len;       /* queries per request, 1..64; 0 means 1 */
 } mla_plan_opts;
 
 typedef struct mla_plan_s* mla_plan_t;
 
-/* Supported shapes: num_heads in {16, 32, 64, 128}; page_size in {16, 32, 64}. */
+/* Supported shapes: num_heads in {16, 32, 64, 128}; page_size in {16, 32, 64};
+   qo_len in 1..64.  The automatic group width is the largest served width that
+   divides qo_len * num_heads. */
 
 /*
  * Upper bound, in bytes, of the device workspace that mla_decode_plan needs
@@ -84,11 +99,11 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
 
 /*
  * Build the split-KV schedule for one batch (the balanced scheduler; runs on
- * the host, launches no kernel).  When few requests carry many heads (batch x
- * num_heads / 32 no more than the workgroups of one wave), the heads of a
- * request are spread over several workgroups instead of cutting its tokens,
- * which needs no partial results; those workgroups are placed on one XCD so
- * that the request's latent cache is fetched from HBM once.
+ * the host, launches no kernel).  A request whose qo_len * num_heads query
+ * vectors are wider than one workgroup serves (see head_split) runs as
+ * several rows of the served width; the workgroups of those rows are placed
+ * on one XCD so that the request's latent cache is fetched from HBM about
+ * once.
  *   kv_indptr_host        [batch + 1] int32, host: page-list offsets, non-decreasing, from 0.
  *   kv_last_page_len_host [batch] int32, host: valid slots of each request's last page,
  *                          in [1, page_size] when the request has pages (ignored otherwise).
@@ -118,7 +133,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
  * synchronises and never reads device memory from the host, so it may be
  * captured in a HIP graph and replayed while the page-table lengths are
  * unchanged.
- *   q_nope  device bf16 [batch, H, 512]      q_pe device bf16 [batch, H, 64]
+ *   q_nope  device bf16 [batch * qo_len, H, 512]   q_pe device bf16 [batch * qo_len, H, 64]
  *   ckv     device [pages, P, 512]           kpe  device [pages, P, 64]
  *           (bf16, or 8-bit codes per the plan's kv_dtype)
  *   kv_scale device fp32 [pages, P] for 8-bit caches, NULL for bf16
@@ -127,8 +142,8 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
  *           reads past a request's device-side length; kv_indices entries must
  *           be valid page numbers (not checked on the device).
  *   sm_scale softmax scale applied to the whole 576-wide score
- *   o       device bf16 [batch, H, 512] (written)
- *   lse     device fp32 [batch, H] (written)
+ *   o       device bf16 [batch * qo_len, H, 512] (written)
+ *   lse     device fp32 [batch * qo_len, H] (written)
  * Results are bit-identical across runs of the same plan and inputs.
  * Errors: MLA_ERR_INVALID_ARG (null pointers, kv_scale inconsistent with the
  * dtype), MLA_ERR_NOT_UPLOADED, MLA_ERR_HIP (launch failure).
@@ -160,15 +175,17 @@ const char* mla_last_error(void);
  *   info[0] batch, [1] num_heads, [2] page_size, [3] kv_dtype, [4] num_workers
  *   (grid size), [5] num_segments, [6] num_partials (split partial slots),
  *   [7] num_split_requests, [8] split granularity in tokens, [9] waves per
- *   workgroup, [10] head split, [11] heads per workgroup.  With a head split
- *   n > 1, segment requests count head groups: row r covers heads
- *   (r % n) * num_heads / n .. of request r / n.
+ *   workgroup, [10] head split, [11] query vectors per workgroup, [12]
+ *   qo_len.  With a head split n > 1, segment requests count groups: row r
+ *   covers query vectors (r % n) * W .. (r % n) * W + W - 1 (W = info[11]) of
+ *   request r / n, where query vector j is head j % num_heads of query
+ *   j / num_heads.
  * mla_decode_plan_segments copies the work list: seg[4*i..4*i+3] =
  * {request, token_begin, token_end, partial_slot (-1 = writes o/lse directly)}
  * for i < num_segments, and worker_ptr[w], worker_ptr[w+1] delimit the
  * segments of workgroup w (worker_ptr has num_workers + 1 entries).
  */
-mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[12]);
+mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[13]);
 mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* worker_ptr);
 
 /*

@@ -55,7 +55,8 @@ class MlaError(RuntimeError):
 
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
-                ("max_workers", ctypes.c_int32), ("head_split", ctypes.c_int32)]
+                ("max_workers", ctypes.c_int32), ("head_split", ctypes.c_int32),
+                ("qo_len", ctypes.c_int32)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -97,8 +98,9 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-def _opts(num_cus=0, force_splits=0, max_workers=0, head_split=0) -> PlanOpts:
-    return PlanOpts(int(num_cus), int(force_splits), int(max_workers), int(head_split))
+def _opts(num_cus=0, force_splits=0, max_workers=0, head_split=0, qo_len=1) -> PlanOpts:
+    return PlanOpts(int(num_cus), int(force_splits), int(max_workers), int(head_split),
+                    int(qo_len))
 
 
 def _host_i32(x) -> np.ndarray:
@@ -125,8 +127,8 @@ def _stream_ptr(stream) -> Optional[int]:
 
 
 def workspace_bytes(batch: int, num_heads: int, num_cus: int = 0, force_splits: int = 0,
-                    max_workers: int = 0, head_split: int = 0) -> int:
-    o = _opts(num_cus, force_splits, max_workers, head_split)
+                    max_workers: int = 0, head_split: int = 0, qo_len: int = 1) -> int:
+    o = _opts(num_cus, force_splits, max_workers, head_split, qo_len)
     n = load_library().mla_decode_workspace_bytes(int(batch), int(num_heads), ctypes.byref(o))
     if n == 0:
         raise MlaError(-2, "mla_decode_workspace_bytes")
@@ -138,12 +140,14 @@ class Plan:
 
     ``workspace`` is a device uint8 tensor of at least ``workspace_bytes``;
     ``None`` makes a host-only plan that can be inspected but not run.
+    ``qo_len`` queries per request: q and o are [batch * qo_len, H, ...], with
+    the causal mask aligned to the end of each request.
     """
 
     def __init__(self, kv_indptr, kv_last_page_len, num_heads: int, page_size: int,
                  kv_dtype: int = KV_BF16, workspace=None, num_cus: int = 0,
                  force_splits: int = 0, max_workers: int = 0, head_split: int = 0,
-                 stream=None):
+                 stream=None, qo_len: int = 1):
         lib = load_library()
         self._lib = lib
         ip = _host_i32(kv_indptr)
@@ -152,8 +156,9 @@ class Plan:
         self.num_heads = int(num_heads)
         self.page_size = int(page_size)
         self.kv_dtype = int(kv_dtype)
+        self.qo_len = int(qo_len)
         self.workspace = workspace
-        o = _opts(num_cus, force_splits, max_workers, head_split)
+        o = _opts(num_cus, force_splits, max_workers, head_split, qo_len)
         h = ctypes.c_void_p()
         ws_ptr, ws_n, sp = None, 0, None
         if workspace is not None:
@@ -174,13 +179,13 @@ class Plan:
             self._h = None
 
     def info(self) -> dict:
-        buf = np.zeros(12, np.int32)
+        buf = np.zeros(13, np.int32)
         st = self._lib.mla_decode_plan_info(self._h, buf.ctypes.data_as(ctypes.c_void_p))
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_plan_info")
         keys = ("batch", "num_heads", "page_size", "kv_dtype", "num_workers", "num_segments",
                 "num_partials", "num_split_requests", "granularity", "waves", "head_split",
-                "kernel_heads")
+                "kernel_heads", "qo_len")
         return {k: int(v) for k, v in zip(keys, buf)}
 
     def segments(self):
@@ -203,15 +208,15 @@ class Plan:
             sm_scale: float, o, lse, stream=None) -> None:
         """``mla_decode_run`` on device tensors (o and lse are written)."""
         import torch
-        B, H = self.batch, self.num_heads
+        B, H = self.batch * self.qo_len, self.num_heads
         if q_nope.dtype != torch.bfloat16 or q_pe.dtype != torch.bfloat16:
             raise ValueError("q_nope / q_pe must be bfloat16")
         if tuple(q_nope.shape) != (B, H, D_CKV) or tuple(q_pe.shape) != (B, H, D_KPE):
             raise ValueError("q_nope / q_pe shape mismatch with the plan")
         if tuple(o.shape) != (B, H, D_CKV) or o.dtype != torch.bfloat16:
-            raise ValueError("o must be bfloat16 [B, H, 512]")
+            raise ValueError("o must be bfloat16 [B * qo_len, H, 512]")
         if tuple(lse.shape) != (B, H) or lse.dtype != torch.float32:
-            raise ValueError("lse must be float32 [B, H]")
+            raise ValueError("lse must be float32 [B * qo_len, H]")
         for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
                         ("kv_last_page_len", kv_last_page_len)):
             if t.dtype != torch.int32:
@@ -308,19 +313,23 @@ def peak_mfma_bf16_tflops(iters: int = 10, stream=None) -> float:
 def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_scale: float,
            kv_dtype: int = KV_BF16, kv_scale=None, kv_indptr_host=None,
            kv_last_page_len_host=None, force_splits: int = 0, head_split: int = 0,
-           stream=None):
+           stream=None, qo_len: int = 1):
     """One-shot plan + run.  Returns (o, lse) as new device tensors."""
     import torch
-    B, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    NQ, H = int(q_nope.shape[0]), int(q_nope.shape[1])
+    B = int(kv_indptr.shape[0]) - 1
+    if NQ != B * qo_len:
+        raise ValueError("q_nope must hold batch * qo_len query rows")
     P = int(ckv.shape[1])
     ip_h = kv_indptr if kv_indptr_host is None else kv_indptr_host
     lp_h = kv_last_page_len if kv_last_page_len_host is None else kv_last_page_len_host
-    ws = torch.empty(workspace_bytes(B, H, force_splits=force_splits, head_split=head_split),
+    ws = torch.empty(workspace_bytes(B, H, force_splits=force_splits, head_split=head_split,
+                                     qo_len=qo_len),
                      dtype=torch.uint8, device=q_nope.device)
     plan = Plan(ip_h, lp_h, H, P, kv_dtype, ws, force_splits=force_splits, head_split=head_split,
-                stream=stream)
-    o = torch.empty((B, H, D_CKV), dtype=torch.bfloat16, device=q_nope.device)
-    lse = torch.empty((B, H), dtype=torch.float32, device=q_nope.device)
+                stream=stream, qo_len=qo_len)
+    o = torch.empty((NQ, H, D_CKV), dtype=torch.bfloat16, device=q_nope.device)
+    lse = torch.empty((NQ, H), dtype=torch.float32, device=q_nope.device)
     plan.run(q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len, sm_scale,
              o, lse, stream)
     return o, lse

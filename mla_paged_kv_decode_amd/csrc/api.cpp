@@ -93,31 +93,46 @@ int log2_exact(int32_t x) {
   return (1 << s) == x ? s : -1;
 }
 
-// Head split for a batch: explicit (opts->head_split) or automatic.  Requests
-// keep all their heads in one workgroup where a kernel serves that width (bf16:
-// 16 to 128 heads; 8-bit: 16 and 128 heads); otherwise (8-bit with 32 or 64
-// heads) they are split into 16-head rows, placed on one XCD so that the
-// latent cache is read from HBM about once.
-mla_status choose_head_split(int32_t num_heads, int32_t kv_dtype, const mla_plan_opts* opts,
-                             int32_t* head_split) {
+constexpr int32_t kMaxQoLen = 64;
+
+// Queries per request from the options (0 = 1); -1 if out of range.
+int32_t qo_len_of(const mla_plan_opts* opts) {
+  const int32_t q = opts ? opts->qo_len : 0;
+  if (q < 0 || q > kMaxQoLen) return -1;
+  return q == 0 ? 1 : q;
+}
+
+// Head split for a batch: explicit (opts->head_split) or automatic.  The
+// qo_len * num_heads query vectors of a request share its latent stream; they
+// run as head_split rows of the largest width a kernel serves that divides
+// them (bf16: 16 to 128; 8-bit: 16 and 128), so that a request takes as few
+// passes over its cache as possible.  Rows of one request are placed on one
+// XCD by the planner, so that the latent cache is read from HBM about once.
+mla_status choose_head_split(int32_t num_heads, int32_t qo_len, int32_t kv_dtype,
+                             const mla_plan_opts* opts, int32_t* head_split) {
   const int32_t req = opts ? opts->head_split : 0;
   if (req < 0) return MLA_ERR_INVALID_ARG;
+  const int32_t nq = num_heads * qo_len;
   mla_gpu::DecodeConfig cfg{};
   if (req > 0) {
-    if (num_heads % req != 0 || log2_exact(req) < 0 ||
-        mla_gpu::decode_config(num_heads / req, kv_dtype, &cfg) != 0)
+    if (nq % req != 0 || mla_gpu::decode_config(nq / req, kv_dtype, &cfg) != 0)
       return MLA_ERR_UNSUPPORTED;
     *head_split = req;
     return MLA_OK;
   }
-  *head_split = mla_gpu::decode_config(num_heads, kv_dtype, &cfg) == 0 ? 1 : num_heads / 16;
-  return MLA_OK;
+  for (int32_t w = 128; w >= 16; w /= 2) {
+    if (nq % w == 0 && mla_gpu::decode_config(w, kv_dtype, &cfg) == 0) {
+      *head_split = nq / w;
+      return MLA_OK;
+    }
+  }
+  return MLA_ERR_UNSUPPORTED;
 }
 
-mla::PlanParams plan_params(int32_t num_heads, int32_t head_split, int32_t workers,
+mla::PlanParams plan_params(int32_t num_queries, int32_t head_split, int32_t workers,
                             const mla_gpu::DecodeConfig& cfg, const mla_plan_opts* opts) {
   mla::PlanParams pp;
-  pp.num_heads = num_heads / head_split;
+  pp.num_heads = num_queries / head_split;
   pp.num_workers = workers;
   pp.granularity = cfg.tile;
   pp.force_splits = opts ? opts->force_splits : 0;
@@ -131,7 +146,7 @@ mla::PlanParams plan_params(int32_t num_heads, int32_t head_split, int32_t worke
 
 struct mla_plan_s {
   int32_t batch = 0, heads = 0, page_size = 0, page_shift = 0, kv_dtype = 0;
-  int32_t head_split = 1, kernel_heads = 0;
+  int32_t qo_len = 1, head_split = 1, kernel_heads = 0;
   mla_gpu::DecodeConfig cfg{};
   mla::Plan plan;
   Layout layout{};
@@ -159,16 +174,21 @@ const char* mla_last_error(void) { return g_last_error.c_str(); }
 size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_plan_opts* opts) {
   if (batch < 0 || !supported_heads(num_heads)) return 0;
   if (opts && (opts->force_splits < 0 || opts->head_split < 0)) return 0;
-  // bound over every head split and cache dtype the plan may choose
+  const int32_t qo_len = qo_len_of(opts);
+  if (qo_len < 1) return 0;
+  const int32_t nq = num_heads * qo_len;
+  // bound over every row width and cache dtype the plan may choose
   size_t best = 0;
   for (int32_t kvd = 0; kvd < 3; ++kvd)
-  for (int32_t hs = 1; hs <= num_heads / 16; hs *= 2) {
+  for (int32_t w = 16; w <= 128; w *= 2) {
+    if (nq % w != 0) continue;
+    const int32_t hs = nq / w;
     if (opts && opts->head_split > 0 && hs != opts->head_split) continue;
     mla_gpu::DecodeConfig cfg{};
-    if (mla_gpu::decode_config(num_heads / hs, kvd, &cfg) != 0) continue;
+    if (mla_gpu::decode_config(w, kvd, &cfg) != 0) continue;
     int32_t workers = 0;
-    if (worker_count(opts, num_heads / hs, kvd, &workers) != MLA_OK) return 0;
-    const mla::PlanParams pp = plan_params(num_heads, hs, workers, cfg, opts);
+    if (worker_count(opts, w, kvd, &workers) != MLA_OK) return 0;
+    const mla::PlanParams pp = plan_params(nq, hs, workers, cfg, opts);
     const int64_t nseg = mla::max_segments(batch, pp);
     const int64_t nparts = mla::max_partials(batch, pp);
     best = std::max(best, layout_for(nseg, workers, (int64_t)batch * hs, nparts, pp.num_heads).total);
@@ -190,15 +210,19 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   if (opts && (opts->force_splits < 0 || opts->max_workers < 0)) return MLA_ERR_INVALID_ARG;
 
   if (opts && opts->head_split < 0) return MLA_ERR_INVALID_ARG;
+  const int32_t qo_len = qo_len_of(opts);
+  if (qo_len < 1) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)batch * qo_len * num_heads / 16 > INT32_MAX) return MLA_ERR_INVALID_ARG;  // rows
   int32_t head_split = 1;
-  mla_status st = choose_head_split(num_heads, kv_dtype, opts, &head_split);
+  mla_status st = choose_head_split(num_heads, qo_len, kv_dtype, opts, &head_split);
   if (st != MLA_OK) return st;
-  const int32_t kernel_heads = num_heads / head_split;
+  const int32_t kernel_heads = num_heads * qo_len / head_split;
 
   mla_plan_s* p = new (std::nothrow) mla_plan_s();
   if (!p) return MLA_ERR_INVALID_ARG;
   p->batch = batch;
   p->heads = num_heads;
+  p->qo_len = qo_len;
   p->head_split = head_split;
   p->kernel_heads = kernel_heads;
   p->page_size = page_size;
@@ -214,7 +238,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
     delete p;
     return st;
   }
-  mla::PlanParams pp = plan_params(num_heads, head_split, workers, p->cfg, opts);
+  mla::PlanParams pp = plan_params(num_heads * qo_len, head_split, workers, p->cfg, opts);
   pp.page_size = page_size;
   static const int32_t kZero = 0;
   if (mla::build_plan(kv_indptr_host, batch > 0 ? kv_last_page_len_host : &kZero, batch, pp,
@@ -232,7 +256,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   for (size_t i = 0; i < pl.segments.size(); ++i) {
     const mla::Segment& g = pl.segments[i];
     const int32_t v[8] = {g.request, g.begin, g.end, g.slot, g.split_request, g.first_slot,
-                          g.num_splits, 0};
+                          g.num_splits, g.request / head_split};
     std::memcpy(p->host_meta.data() + p->layout.segs + i * 32, v, 32);
   }
   std::memcpy(p->host_meta.data() + p->layout.wptr, pl.worker_ptr.data(),
@@ -291,7 +315,9 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.page_shift = p->page_shift;
-  a.head_shift = log2_exact(p->head_split);
+  a.rows_per_req = p->head_split;
+  a.qo_len = p->qo_len;
+  a.head_log2 = log2_exact(p->heads);
   if (p->ev_before) {
     hipError_t e = hipEventRecord(p->ev_before, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
@@ -321,7 +347,7 @@ mla_status mla_decode_plan_set_events(mla_plan_t p, void* before, void* after) {
   return MLA_OK;
 }
 
-mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[12]) {
+mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[13]) {
   if (!p || !info) return MLA_ERR_INVALID_ARG;
   info[0] = p->batch;
   info[1] = p->heads;
@@ -335,6 +361,7 @@ mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[12]) {
   info[9] = p->cfg.waves;
   info[10] = p->head_split;
   info[11] = p->kernel_heads;
+  info[12] = p->qo_len;
   return MLA_OK;
 }
 

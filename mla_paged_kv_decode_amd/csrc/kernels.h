@@ -16,8 +16,8 @@ struct DecodeArgs {
   const int32_t* kv_indptr;
   const int32_t* kv_indices;
   const int32_t* kv_last_page_len;
-  const int4* segs;           // 8 ints each: request, begin, end, slot, split index,
-                              // first slot, number of chunks, 0
+  const int4* segs;           // 8 ints each: row, begin, end, slot, split index,
+                              // first slot, number of chunks, request (row / rows_per_req)
   const int32_t* worker_ptr;  // grid + 1
   uint16_t* o;                // bf16 [B, H, 512]
   float* lse;                 // [B, H]
@@ -27,8 +27,12 @@ struct DecodeArgs {
   const int4* clist;          // 4 ints per split request: row, first slot, chunks, 0
   float scale_log2;           // sm_scale * log2(e)
   int32_t page_shift;         // log2(page_size)
-  int32_t head_shift;         // log2(head split): row b of q/o/lse (of kernel-width heads)
-                              // reads the latent cache of request b >> head_shift
+  int32_t rows_per_req;       // kernel rows per request: row b of q/o/lse (kernel-width
+                              // groups of query vectors) reads the latent cache of request
+                              // b / rows_per_req
+  int32_t qo_len;             // queries per request: query vector j of a request is head
+  int32_t head_log2;          // j & (2^head_log2 - 1) of query j >> head_log2, and sees the
+                              // first L_b - (qo_len - 1 - (j >> head_log2)) tokens
 };
 
 struct DecodeConfig {

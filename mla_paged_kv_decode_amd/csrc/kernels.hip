@@ -116,6 +116,19 @@ __device__ __forceinline__ T ld_const(const T* p) {
   return *(const __attribute__((address_space(4))) T*)(p);
 }
 
+// Token limit of one query column with several queries per request: column
+// `col` of kernel row b (width W) is query vector j = (b - kvb R) W + col of
+// request kvb, i.e. head j % H of query i = j / H, and the qo_len queries are
+// the request's last positions, so query i sees tokens t < ldev - (qo_len -
+// 1 - i) (the causal mask with Q at the end of the score matrix).  With
+// qo_len = 1 the limit is ldev.
+template <int W>
+__device__ __forceinline__ int causal_limit(const DecodeArgs& a, int b, int kvb, int col,
+                                            int ldev) {
+  const int j = (b - kvb * a.rows_per_req) * W + col;
+  return ldev - (a.qo_len - 1 - (j >> a.head_log2));
+}
+
 // 16-byte direct global -> LDS load: lane i's 16 bytes land at
 // lds_base + 16 * i.  Issued as inline assembly so that the compiler does not
 // treat every later LDS read as dependent on the in-flight copy (which makes it
@@ -463,11 +476,16 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
     const int split_req = ld_const(sgp + 4);
     const int slot0 = ld_const(sgp + 5);
     const int nsplit = ld_const(sgp + 6);
-    const int kvb = b >> a.head_shift;  // request whose latent cache this segment reads
+    const int kvb = ld_const(sgp + 7);  // request whose latent cache this segment reads
     const int pbeg = ld_const(a.kv_indptr + kvb);
     const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
     const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
     const int t1 = min(send, ldev);
+    // score rows at or past tlim[hb] are masked (end of chunk, or causal limit)
+    int tlim[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      tlim[hb] = min(t1, causal_limit<H>(a, b, kvb, (wh * HB + hb) * 16 + (lane & 15), ldev));
     const int ntiles = t1 > t0 ? (t1 - t0 + T - 1) / T : 0;
 
     // Page numbers of the row groups of tile k (one scalar load per group;
@@ -608,7 +626,7 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
           const int row0 = tile_start + (ts * MB + mb) * 16 + 4 * (lane >> 4);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = (row0 + i < t1) ? sacc[hb][mb][i] * a.scale_log2 : -INFINITY;
+            const float x = (row0 + i < tlim[hb]) ? sacc[hb][mb][i] * a.scale_log2 : -INFINITY;
             sacc[hb][mb][i] = x;
             tmax = fmaxf(tmax, x);
           }
@@ -827,11 +845,16 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     const int split_req = ld_const(sgp + 4);
     const int slot0 = ld_const(sgp + 5);
     const int nsplit = ld_const(sgp + 6);
-    const int kvb = b >> a.head_shift;  // request whose latent cache this segment reads
+    const int kvb = ld_const(sgp + 7);  // request whose latent cache this segment reads
     const int pbeg = ld_const(a.kv_indptr + kvb);
     const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
     const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
     const int t1 = min(send, ldev);
+    // score rows at or past tlim[hb] are masked (end of chunk, or causal limit)
+    int tlim[HB];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb)
+      tlim[hb] = min(t1, causal_limit<H>(a, b, kvb, hb * 16 + (lane & 15), ldev));
     const int ngroups = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
     const int nmine = ngroups > wave ? (ngroups - 1 - wave) / TS + 1 : 0;
 
@@ -966,7 +989,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float raw = KVT != 0 ? sacc[hb][i] * sig[i] : sacc[hb][i];
-          const float x = (row0 + i < t1) ? raw * a.scale_log2 : -INFINITY;
+          const float x = (row0 + i < tlim[hb]) ? raw * a.scale_log2 : -INFINITY;
           sacc[hb][i] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -1126,11 +1149,12 @@ struct WideShape {
   static constexpr int kAlphaOffset = kPOffset + 4 * 2 * 64 * 16;    // [128] rescale factors
   static constexpr int kFlagOffset = kAlphaOffset + 128 * 4;         // [4] rescale flags
   static constexpr int kStatOffset = kFlagOffset + 16;               // [128] 1 / row sum
-  static constexpr int kLdsBytes = kStatOffset + 128 * 4;
+  static constexpr int kLimitOffset = kStatOffset + 128 * 4;         // [128] token limit per head
+  static constexpr int kLdsBytes = kLimitOffset + 128 * 4;
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
-template <int KVT>
+template <int KVT, bool CAUSAL>
 __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a) {
   using S = WideShape<KVT>;
   constexpr int H = S::kHeads;
@@ -1174,6 +1198,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
   float* alpha_s = reinterpret_cast<float*>(smem + S::kAlphaOffset);
   int* flags = reinterpret_cast<int*>(smem + S::kFlagOffset);
   float* stat = reinterpret_cast<float*>(smem + S::kStatOffset);
+  int* limit_s = reinterpret_cast<int*>(smem + S::kLimitOffset);
 
   const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
   const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
@@ -1184,11 +1209,19 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     const int t0 = ld_const(sgp + 1);
     const int send = ld_const(sgp + 2);
     const int slot = ld_const(sgp + 3);
-    const int kvb = b >> a.head_shift;
+    const int kvb = ld_const(sgp + 7);
     const int pbeg = ld_const(a.kv_indptr + kvb);
     const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
     const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
     const int t1 = min(send, ldev);
+    // CAUSAL (several queries per request): score rows of this lane's QK
+    // head at or past its causal limit are masked too.  The limit is kept in
+    // LDS (each wave reads only its own entries) rather than in a register,
+    // which the 8-bit kernel does not have to spare.
+    if constexpr (CAUSAL) {
+      if (lane < 32)
+        limit_s[32 * wave + l32] = min(t1, causal_limit<H>(a, b, kvb, 32 * wave + l32, ldev));
+    }
     const int ntiles = t1 > t0 ? (t1 - t0 + T - 1) / T : 0;
 
     // Page numbers of the two 16-row groups of a tile (a group past the end
@@ -1404,12 +1437,13 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           }
         }
       }
+      const int tlim = CAUSAL ? limit_s[32 * wave + l32] : t1;
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
         const float raw = KVT != 0 ? sacc[r] * sig[r] : sacc[r];
-        const float x = tok < t1 ? raw * a.scale_log2 : -INFINITY;
+        const float x = tok < tlim ? raw * a.scale_log2 : -INFINITY;
         sacc[r] = x;
         tmax = fmaxf(tmax, x);
       }
@@ -1603,8 +1637,12 @@ static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t s
 
 template <int KVT>
 static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((mla_decode_wide_kernel<KVT>), dim3(grid), dim3(WideShape<KVT>::kThreads), 0,
-                     stream, a);
+  if (a.qo_len > 1)
+    hipLaunchKernelGGL((mla_decode_wide_kernel<KVT, true>), dim3(grid),
+                       dim3(WideShape<KVT>::kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((mla_decode_wide_kernel<KVT, false>), dim3(grid),
+                       dim3(WideShape<KVT>::kThreads), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1617,7 +1655,7 @@ template <int KVT>
 static int wide_occupancy() {
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&mla_decode_wide_kernel<KVT>),
+          &n, reinterpret_cast<const void*>(&mla_decode_wide_kernel<KVT, false>),
           WideShape<KVT>::kThreads, 0) != hipSuccess ||
       n < 1)
     n = 1;

@@ -219,6 +219,11 @@ WORKLOADS = {
                                    seed=5),
     "int8_b64_h128_l8192_p64": dict(batch=64, heads=128, kv_len=8192, page=64, kv_dtype=KV_INT8,
                                     seed=5),
+    # two queries per request (one speculative / next-token-prediction token)
+    "mtp_b64_h16_q2_l4096_p64": dict(batch=64, heads=16, kv_len=4096, page=64, kv_dtype=KV_BF16,
+                                     seed=6, qo_len=2),
+    "mtp_b64_h128_q2_l4096_p64": dict(batch=64, heads=128, kv_len=4096, page=64,
+                                      kv_dtype=KV_BF16, seed=6, qo_len=2),
 }
 
 
@@ -234,4 +239,4 @@ def workload_lengths(name: str) -> np.ndarray:
 def make_workload(name: str, poison: bool = False) -> MlaInputs:
     w = WORKLOADS[name]
     return make_inputs(workload_lengths(name), w["heads"], w["page"], w["kv_dtype"], w["seed"],
-                       poison=poison)
+                       poison=poison, qo_len=w.get("qo_len", 1))

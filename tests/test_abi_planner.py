@@ -236,6 +236,40 @@ def test_bad_head_split_rejected(lib):
             mla.Plan(ip, lp, heads, 16, num_cus=8, head_split=hs)
 
 
+@pytest.mark.parametrize("heads,q,kvd,width", [
+    (16, 1, mla.KV_BF16, 16), (16, 2, mla.KV_BF16, 32), (16, 3, mla.KV_BF16, 16),
+    (16, 4, mla.KV_BF16, 64), (16, 8, mla.KV_BF16, 128), (16, 16, mla.KV_BF16, 128),
+    (128, 2, mla.KV_BF16, 128), (32, 3, mla.KV_BF16, 32), (16, 2, mla.KV_FP8_E4M3, 16),
+    (64, 2, mla.KV_INT8, 128), (16, 6, mla.KV_INT8, 16), (128, 4, mla.KV_FP8_E4M3, 128)])
+def test_multiquery_rows(lib, heads, q, kvd, width):
+    # the qo_len * heads query vectors of a request run as rows of the largest
+    # served width that divides them, each row reading the request's cache
+    lengths = [333, 4096, 17, 0, 1000, 2]
+    ip, lp = _table(lengths, 32)
+    plan = mla.Plan(ip, lp, heads, 32, kvd, num_cus=64, qo_len=q)
+    info = plan.info()
+    assert info["qo_len"] == q and info["kernel_heads"] == width
+    assert info["head_split"] == heads * q // width
+    _check_plan(plan, lengths, info["granularity"])
+    n = mla.workspace_bytes(len(lengths), heads, num_cus=64, qo_len=q)
+    need = info["num_partials"] * width * (512 + 1) * 4 + info["num_segments"] * 32
+    assert n >= need
+
+
+def test_multiquery_bad_qo_len_rejected(lib):
+    ip, lp = _table([10, 20], 16)
+    for q in (-1, 65):
+        with pytest.raises(mla.MlaError) as e:
+            mla.Plan(ip, lp, 16, 16, num_cus=8, qo_len=q)
+        assert e.value.status == -1
+    with pytest.raises(mla.MlaError):
+        mla.workspace_bytes(2, 16, num_cus=8, qo_len=65)
+    assert mla.Plan(ip, lp, 16, 16, num_cus=8, qo_len=0).info()["qo_len"] == 1
+    # a head split that does not divide the query vectors
+    with pytest.raises(mla.MlaError):
+        mla.Plan(ip, lp, 16, 16, num_cus=8, qo_len=3, head_split=2)
+
+
 def test_cache_append_rejects_bad_arguments(lib):
     # every check happens before any HIP call, so this runs without a GPU
     Pp = ctypes.c_void_p
