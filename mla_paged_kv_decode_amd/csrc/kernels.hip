@@ -180,51 +180,111 @@ __device__ __forceinline__ float wave_sum_16(float v) {
   return v;
 }
 
-// Merge the n partials (slots slot0 .. slot0 + n - 1, in that order) of
+// Merge of the n partials (slots slot0 .. slot0 + n - 1, in that order) of
 // request b: LSE = M + ln sum_i exp(LSE_i - M), O = sum_i exp(LSE_i - LSE) O_i.
-// `wbuf` is LDS scratch of n * H floats.  Every load of a phase is issued
-// before any result is used, so the merge costs a few memory round trips.
+// Thread items are (head, 8 columns).  Up to kBatch partials, the loads of
+// kPass items of a thread (their heads' partial LSEs and the O slices) are all
+// issued before any is used, so a pass takes one memory round trip and needs
+// no LDS or barrier; more partials take a pass over the LSEs and then the O
+// slices kBatch partials at a time.  The arithmetic per item is the same
+// either way.
 template <int H, int NT>
 __device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int slot0, int n,
-                                                int tid, float* wbuf) {
-  // 1. the n * H partial LSEs (consecutive slots are contiguous)
+                                                int tid) {
+  constexpr int kItems = H * 64;  // (head, 8 columns)
+  constexpr int K = (kItems + NT - 1) / NT;
+  constexpr int kBatch = 4;
+  constexpr int kPass = K < 2 ? K : 2;  // 72 registers of loads in flight per pass
   const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + (size_t)slot0 * H);
-  for (int x = tid; x < n * H; x += NT) wbuf[x] = load_coherent1(rl, (uint32_t)(x * 4));
-  lds_barrier();
-  // 2. per head: merged LSE and the weights exp(LSE_i - LSE), in place
-  for (int hd = tid; hd < H; hd += NT) {
+  const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + (size_t)slot0 * H * 512);
+  auto finish = [&](int e, float lse_v, const float (&o8)[8]) __attribute__((always_inline)) {
+    const int hd = e >> 6, col = (e & 63) * 8;
+    bf16x8 v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
+    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
+    if ((e & 63) == 0) a.lse[(size_t)b * H + hd] = lse_v;
+  };
+  if (n <= kBatch) {
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += kPass) {
+    float lv[kPass][kBatch];
+    f32x4 x[kPass][kBatch][2];
+#pragma unroll
+    for (int k = 0; k < kPass; ++k) {
+      const int e = min(tid + (k0 + k) * NT, kItems - 1);
+      const int hd = e >> 6, col = (e & 63) * 8;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int i = min(u, n - 1);
+        lv[k][u] = load_coherent1(rl, (uint32_t)((i * H + hd) * 4));
+        const uint32_t off = (uint32_t)(((i * H + hd) * 512 + col) * 4);
+        x[k][u][0] = load_coherent4(ro, off);
+        x[k][u][1] = load_coherent4(ro, off + 16);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPass; ++k) {
+      const int e = tid + (k0 + k) * NT;
+      if (k0 + k >= K || e >= kItems) break;
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (u < n) M = fmaxf(M, lv[k][u]);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float sum = 0.f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (u < n) sum += __expf(lv[k][u] - Mu);
+      const bool empty = !(sum > 0.f);
+      const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
+      float o8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) o8[j] = 0.f;
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (u < n) {
+          const float w = empty ? 0.f : __expf(lv[k][u] - lse_v);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            o8[j] += w * x[k][u][0][j];
+            o8[4 + j] += w * x[k][u][1][j];
+          }
+        }
+      }
+      finish(e, lse_v, o8);
+    }
+    }
+    return;
+  }
+  for (int e = tid; e < kItems; e += NT) {
+    const int hd = e >> 6, col = (e & 63) * 8;
     float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, wbuf[i * H + hd]);
+    for (int i = 0; i < n; ++i) M = fmaxf(M, load_coherent1(rl, (uint32_t)((i * H + hd) * 4)));
     const float Mu = M == -INFINITY ? 0.f : M;
     float sum = 0.f;
-    for (int i = 0; i < n; ++i) sum += __expf(wbuf[i * H + hd] - Mu);
+    for (int i = 0; i < n; ++i)
+      sum += __expf(load_coherent1(rl, (uint32_t)((i * H + hd) * 4)) - Mu);
     const bool empty = !(sum > 0.f);
     const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
-    for (int i = 0; i < n; ++i) wbuf[i * H + hd] = empty ? 0.f : __expf(wbuf[i * H + hd] - lse_v);
-    a.lse[(size_t)b * H + hd] = lse_v;
-  }
-  lds_barrier();
-  // 3. O, item = (head, 8 columns); splits in groups of 4 with all loads in flight
-  const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + (size_t)slot0 * H * 512);
-  for (int e = tid; e < H * 64; e += NT) {
-    const int hd = e >> 6;
-    const int col = (e & 63) * 8;
     float o8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o8[j] = 0.f;
-    for (int i0 = 0; i0 < n; i0 += 4) {
-      f32x4 x[4][2];
+    for (int i0 = 0; i0 < n; i0 += kBatch) {
+      float lv[kBatch];
+      f32x4 x[kBatch][2];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kBatch; ++u) {
         const int i = min(i0 + u, n - 1);
+        lv[u] = load_coherent1(rl, (uint32_t)((i * H + hd) * 4));
         const uint32_t off = (uint32_t)(((i * H + hd) * 512 + col) * 4);
         x[u][0] = load_coherent4(ro, off);
         x[u][1] = load_coherent4(ro, off + 16);
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kBatch; ++u) {
         if (i0 + u < n) {
-          const float w = wbuf[(i0 + u) * H + hd];
+          const float w = empty ? 0.f : __expf(lv[u] - lse_v);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             o8[j] += w * x[u][0][j];
@@ -233,10 +293,7 @@ __device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int 
         }
       }
     }
-    bf16x8 v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
-    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
+    finish(e, lse_v, o8);
   }
 }
 
@@ -384,8 +441,7 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int s
       *s_last = last;
     }
     lds_barrier();
-    if (*s_last) combine_request<H, NT>(a, b, slot0, nsplit, tid,
-                                                reinterpret_cast<float*>(smem));
+    if (*s_last) combine_request<H, NT>(a, b, slot0, nsplit, tid);
     lds_barrier();  // merge scratch free before the next segment's loads
   }
 }
