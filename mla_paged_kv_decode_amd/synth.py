@@ -20,7 +20,9 @@ Recipe (the inputs the pages describe, made concrete):
   * 8-bit caches (FlashMLA PR 233, "What is added"): one fp32 scale per token
     over all 576 latent values, scale = max|x| / 448 (fp8 e4m3) or / 127
     (int8), codes = round-to-nearest-even of x / scale, saturated; a token
-    whose values are all zero gets scale 1.
+    whose values are all zero gets scale 1.  The 644-byte record of the same
+    page (8-bit ckv, bf16 kpe, fp32 scale) quantises ckv alone, with the scale
+    from its 512 values.
   * sm_scale = fp32(1 / sqrt(192)).
 
 Random streams: numpy PCG64 generators spawned from one SeedSequence(seed),
@@ -37,6 +39,8 @@ import torch
 
 D_CKV, D_KPE = 512, 64
 KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
+# 644-byte token record: 8-bit ckv codes + bf16 kpe + fp32 scale (ckv only)
+KV_FP8_KPE16, KV_INT8_KPE16 = 3, 4
 KV_DTYPE_NAMES = {KV_BF16: "bf16", KV_FP8_E4M3: "fp8_e4m3", KV_INT8: "int8"}
 
 BF16_NAN = 0x7FC0
@@ -71,6 +75,8 @@ class MlaInputs:
     def kv_bytes_per_token(self) -> int:
         if self.kv_dtype == KV_BF16:
             return 2 * (D_CKV + D_KPE)
+        if self.kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16):
+            return D_CKV + 2 * D_KPE + 4  # 644
         return D_CKV + D_KPE + 4
 
     def algorithmic_bytes(self) -> int:
@@ -117,23 +123,29 @@ def _bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
 
 
 def _quantize_tokens(ckv_bits: np.ndarray, kpe_bits: np.ndarray, kv_dtype: int):
-    """Per-token 8-bit codes and fp32 scales of a bf16 source (input recipe)."""
+    """Per-token 8-bit codes and fp32 scales of a bf16 source (input recipe).
+    The 644-byte layouts quantise ckv only (amax over its 512 values) and keep
+    kpe as the bf16 source."""
     pages, P = ckv_bits.shape[0], ckv_bits.shape[1]
+    kpe16 = kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16)
+    fp8 = kv_dtype in (KV_FP8_E4M3, KV_FP8_KPE16)
     ckv_codes = np.empty(ckv_bits.shape, np.uint8)
-    kpe_codes = np.empty(kpe_bits.shape, np.uint8)
+    kpe_codes = kpe_bits.copy() if kpe16 else np.empty(kpe_bits.shape, np.uint8)
     scale = np.empty((pages, P), np.float32)
     step = max(1, (1 << 22) // (P * (D_CKV + D_KPE)))
-    qmax = np.float32(448.0 if kv_dtype == KV_FP8_E4M3 else 127.0)
+    qmax = np.float32(448.0 if fp8 else 127.0)
     for p0 in range(0, pages, step):
         p1 = min(pages, p0 + step)
         c = _bf16_bits_to_f32(ckv_bits[p0:p1])
         k = _bf16_bits_to_f32(kpe_bits[p0:p1])
-        amax = np.maximum(np.abs(c).max(axis=-1), np.abs(k).max(axis=-1))
+        amax = np.abs(c).max(axis=-1)
+        if not kpe16:
+            amax = np.maximum(amax, np.abs(k).max(axis=-1))
         s = np.where(amax > 0, amax / qmax, np.float32(1.0)).astype(np.float32)
         scale[p0:p1] = s
-        for src, dst in ((c, ckv_codes), (k, kpe_codes)):
+        for src, dst in ((c, ckv_codes),) + ((() if kpe16 else ((k, kpe_codes),))):
             y = np.clip(src / s[..., None], -qmax, qmax).astype(np.float32)
-            if kv_dtype == KV_FP8_E4M3:
+            if fp8:
                 codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn)
                 dst[p0:p1] = codes.view(torch.uint8).numpy()
             else:
@@ -191,12 +203,14 @@ def _poison(ckv, kpe, kv_scale, kv_dtype, indptr, indices, last, P, pages):
     if kv_dtype == KV_BF16:
         ckv[slot_dead] = BF16_NAN
         kpe[slot_dead] = BF16_NAN
-    elif kv_dtype == KV_FP8_E4M3:
+        return
+    kv_scale[slot_dead] = np.nan
+    if kv_dtype in (KV_FP8_E4M3, KV_FP8_KPE16):
         ckv[slot_dead] = FP8_E4M3_NAN
+    if kv_dtype == KV_FP8_E4M3:
         kpe[slot_dead] = FP8_E4M3_NAN
-        kv_scale[slot_dead] = np.nan
-    else:
-        kv_scale[slot_dead] = np.nan
+    if kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16):
+        kpe[slot_dead] = BF16_NAN
 
 
 # Named workloads (sizes as the pages' regimes: a tiny correctness case, the

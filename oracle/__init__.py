@@ -32,6 +32,8 @@ _SRC = os.path.join(_HERE, "mla_oracle.c")
 _LIB = os.path.join(_HERE, "libmla_oracle.so")
 
 KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
+# 644-byte record: 8-bit ckv codes, bf16 kpe, fp32 scale on ckv only
+KV_FP8_KPE16, KV_INT8_KPE16 = 3, 4
 D_CKV, D_KPE = 512, 64
 
 _lib = None
@@ -115,6 +117,8 @@ def kv_len(kv_indptr, kv_last_page_len, page_size: int, b: int) -> int:
 def _kv_arrays(kv_dtype, ckv, kpe):
     if kv_dtype == KV_BF16:
         return _c(ckv, np.uint16), _c(kpe, np.uint16)
+    if kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16):
+        return _c(ckv, np.uint8), _c(kpe, np.uint16)
     return _c(ckv, np.uint8), _c(kpe, np.uint8)
 
 
@@ -203,7 +207,8 @@ def enc_e4m3fn(v: float) -> int:
 def quantize(ckv_new: np.ndarray, kpe_new: np.ndarray, kv_dtype: int):
     """Quantise new tokens for an 8-bit cache (see ``mla_oracle_quantize``):
     bf16 bits [n, 512] and [n, 64] -> (ckv codes uint8 [n, 512], kpe codes
-    uint8 [n, 64], scales float32 [n])."""
+    uint8 [n, 64], scales float32 [n]).  For the 644-byte layouts only ckv is
+    quantised and the kpe element is the bf16 input, unchanged."""
     ckv_new = np.ascontiguousarray(ckv_new, np.uint16)
     kpe_new = np.ascontiguousarray(kpe_new, np.uint16)
     n = ckv_new.shape[0]
@@ -217,4 +222,6 @@ def quantize(ckv_new: np.ndarray, kpe_new: np.ndarray, kv_dtype: int):
                                      kc.ctypes.data_as(P), sc.ctypes.data_as(P))
     if st != 0:
         raise ValueError("unsupported kv_dtype for quantisation")
+    if kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16):
+        return cc, kpe_new.copy(), sc
     return cc, kc, sc

@@ -60,7 +60,19 @@
 #define D_CKV 512
 #define D_KPE 64
 
-enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1, ORC_INT8 = 2 };
+/*
+ * Cache layouts.  BF16: ckv and kpe bf16.  FP8_E4M3 / INT8: ckv and kpe both
+ * 8-bit codes, one fp32 scale per token over all 576 values (580 B / token).
+ * FP8_KPE16 / INT8_KPE16: the 644-byte token record of "FlashMLA Ampere v2"
+ * ("What is added", 644 instead of 1152 bytes per token), read as 512 8-bit
+ * ckv codes + 64 bf16 kpe values + one fp32 scale that applies to ckv only
+ * (512 + 128 + 4 = 644).
+ */
+enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1, ORC_INT8 = 2, ORC_FP8_KPE16 = 3, ORC_INT8_KPE16 = 4 };
+
+static int ckv_fp8(int32_t kv_dtype) { return kv_dtype == ORC_FP8_E4M3 || kv_dtype == ORC_FP8_KPE16; }
+static int kpe_bf16(int32_t kv_dtype) { return kv_dtype == ORC_BF16 || kv_dtype >= ORC_FP8_KPE16; }
+static int valid_dtype(int32_t kv_dtype) { return kv_dtype >= ORC_BF16 && kv_dtype <= ORC_INT8_KPE16; }
 
 double oracle_dec_bf16(uint16_t bits) {
   uint32_t w = ((uint32_t)bits) << 16;
@@ -123,11 +135,16 @@ static void load_token(const oracle_inputs* in, int32_t b, int64_t t, double* K,
   sigma = (double)in->kv_scale[row];
   {
     const uint8_t* c = (const uint8_t*)in->ckv + row * D_CKV;
-    const uint8_t* k = (const uint8_t*)in->kpe + row * D_KPE;
     for (i = 0; i < D_CKV; ++i)
-      K[i] = (in->kv_dtype == ORC_FP8_E4M3 ? oracle_dec_e4m3fn(c[i]) : oracle_dec_int8(c[i])) * sigma;
+      K[i] = (ckv_fp8(in->kv_dtype) ? oracle_dec_e4m3fn(c[i]) : oracle_dec_int8(c[i])) * sigma;
+  }
+  if (kpe_bf16(in->kv_dtype)) {
+    const uint16_t* k = (const uint16_t*)in->kpe + row * D_KPE;
+    for (i = 0; i < D_KPE; ++i) R[i] = oracle_dec_bf16(k[i]);
+  } else {
+    const uint8_t* k = (const uint8_t*)in->kpe + row * D_KPE;
     for (i = 0; i < D_KPE; ++i)
-      R[i] = (in->kv_dtype == ORC_FP8_E4M3 ? oracle_dec_e4m3fn(k[i]) : oracle_dec_int8(k[i])) * sigma;
+      R[i] = (ckv_fp8(in->kv_dtype) ? oracle_dec_e4m3fn(k[i]) : oracle_dec_int8(k[i])) * sigma;
   }
 }
 
@@ -249,7 +266,7 @@ int mla_oracle_decode(int32_t batch, int32_t qo_len, int32_t num_heads, int32_t 
 
   if (batch < 0 || qo_len < 1 || num_heads <= 0 || page_size <= 0 || !o_out || !lse_out)
     return -1;
-  if (kv_dtype != ORC_BF16 && kv_dtype != ORC_FP8_E4M3 && kv_dtype != ORC_INT8) return -1;
+  if (!valid_dtype(kv_dtype)) return -1;
   if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
   in.batch = batch;
   in.qo_len = qo_len;
@@ -320,7 +337,7 @@ int mla_oracle_partial(int32_t batch, int32_t qo_len, int32_t num_heads, int32_t
   int64_t L, V;
   if (b < 0 || b >= batch || qo_len < 1 || qi < 0 || qi >= qo_len || h < 0 || h >= num_heads)
     return -1;
-  if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
+  if (!valid_dtype(kv_dtype) || (kv_dtype != ORC_BF16 && !kv_scale)) return -1;
   L = oracle_kv_len(kv_indptr, kv_last_page_len, page_size, b);
   if (t0 < 0 || t1 < t0 || t1 > L) return -1;
   in.batch = batch;
@@ -383,7 +400,9 @@ void mla_oracle_combine(int32_t n, const double* lse_parts, const double* o_part
  *           to +-448 (never NaN); or round-to-nearest-even integer of v_i
  *           clamped to [-127, 127]
  * The divisions are the IEEE binary32 ones (the rounding of the reading that
- * both sides compute them in binary32).  The encoder below works from the
+ * both sides compute them in binary32).  For the 644-byte layouts (FP8_KPE16,
+ * INT8_KPE16) only the 512 ckv values are quantised: amax runs over them
+ * alone and kpe stays bf16 (kpe_codes is not written and may be NULL).  The encoder below works from the
  * format definition in the header: it finds the binade of |v| with frexp and
  * rounds the scaled value to the 3-bit mantissa grid with nearbyint (default
  * rounding mode: to nearest, ties to even).
@@ -417,12 +436,13 @@ int mla_oracle_quantize(int32_t n, int32_t kv_dtype, const uint16_t* ckv_new,
                         float* scales) {
   int32_t j;
   int i;
-  if (kv_dtype != ORC_FP8_E4M3 && kv_dtype != ORC_INT8) return -1;
+  if (!valid_dtype(kv_dtype) || kv_dtype == ORC_BF16) return -1;
   for (j = 0; j < n; ++j) {
     float x[D_CKV + D_KPE];
     float amax = 0.0f, scale;
-    const float qmax = kv_dtype == ORC_FP8_E4M3 ? 448.0f : 127.0f;
-    for (i = 0; i < D_CKV + D_KPE; ++i) {
+    const float qmax = ckv_fp8(kv_dtype) ? 448.0f : 127.0f;
+    const int nq = kpe_bf16(kv_dtype) ? D_CKV : D_CKV + D_KPE; /* values quantised */
+    for (i = 0; i < nq; ++i) {
       const uint16_t bits = i < D_CKV ? ckv_new[(int64_t)j * D_CKV + i]
                                       : kpe_new[(int64_t)j * D_KPE + i - D_CKV];
       x[i] = (float)oracle_dec_bf16(bits);
@@ -430,10 +450,10 @@ int mla_oracle_quantize(int32_t n, int32_t kv_dtype, const uint16_t* ckv_new,
     }
     scale = amax > 0.0f ? amax / qmax : 1.0f;
     scales[j] = scale;
-    for (i = 0; i < D_CKV + D_KPE; ++i) {
+    for (i = 0; i < nq; ++i) {
       const float v = x[i] / scale;
       uint8_t c;
-      if (kv_dtype == ORC_FP8_E4M3) {
+      if (ckv_fp8(kv_dtype)) {
         c = encode_e4m3fn(v);
       } else {
         float r = nearbyintf(v);

@@ -40,7 +40,7 @@ SM = synth.SM_SCALE_192
 # ----------------------------------------------------------------- helpers
 def _dec_tensor(codes, kv_dtype):
     """Decode with library conversions (not the oracle's decoders)."""
-    if kv_dtype == synth.KV_BF16:
+    if kv_dtype == synth.KV_BF16 or codes.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(codes).view(np.int16)).view(
             torch.bfloat16).to(torch.float64).numpy()
     if kv_dtype == synth.KV_FP8_E4M3:
@@ -62,13 +62,18 @@ def _tokens(inp, b):
 
 
 def _token_rows(inp, b):
-    ck = _dec_tensor(inp.ckv, inp.kv_dtype)
-    kp = _dec_tensor(inp.kpe, inp.kv_dtype)
+    # 644-byte layouts ("FlashMLA Ampere v2", "What is added": 644 bytes per
+    # token = 512 8-bit ckv + 128 bf16 kpe + 4 scale): the scale is ckv's only
+    code_dt = {synth.KV_FP8_KPE16: synth.KV_FP8_E4M3,
+               synth.KV_INT8_KPE16: synth.KV_INT8}.get(inp.kv_dtype, inp.kv_dtype)
+    kpe16 = inp.kv_dtype in (synth.KV_FP8_KPE16, synth.KV_INT8_KPE16)
+    ck = _dec_tensor(inp.ckv, code_dt)
+    kp = _dec_tensor(inp.kpe, synth.KV_BF16 if kpe16 else code_dt)
     K, R = [], []
     for pg, s in _tokens(inp, b):
         sig = 1.0 if inp.kv_scale is None else float(inp.kv_scale[pg, s])
         K.append(ck[pg, s] * sig)
-        R.append(kp[pg, s] * sig)
+        R.append(kp[pg, s] * (1.0 if kpe16 else sig))
     return np.array(K).reshape(-1, 512), np.array(R).reshape(-1, 64)
 
 
@@ -161,6 +166,8 @@ BRUTE_CASES = [
     ([40, 17], 2, 16, synth.KV_BF16, 14),
     ([6, 11], 2, 4, synth.KV_FP8_E4M3, 15),
     ([10, 3], 2, 4, synth.KV_INT8, 16),
+    ([7, 12], 2, 4, synth.KV_FP8_KPE16, 17),
+    ([9, 2], 2, 4, synth.KV_INT8_KPE16, 18),
 ]
 
 
@@ -524,6 +531,28 @@ def test_quantize_scale_and_codes_definition():
             assert np.abs(back).max() == qmax
 
 
+@pytest.mark.parametrize("kvd", [synth.KV_FP8_KPE16, synth.KV_INT8_KPE16])
+def test_quantize_644_record_scales_ckv_only(kvd):
+    # "FlashMLA Ampere v2", "What is added": 644 bytes per token = 512 8-bit
+    # ckv codes + 64 bf16 kpe + one fp32 scale, so kpe is not quantised and
+    # the scale is set by ckv alone; a kpe value far above every ckv value
+    # must not change the scale or the codes
+    rng = np.random.default_rng(77)
+    c = rng.normal(0, 1, (5, 512)).astype(np.float32)
+    k = rng.normal(0, 1, (5, 64)).astype(np.float32)
+    k[:, 3] = 1e4
+    cb, kb = _bf16(c), _bf16(k)
+    cc, kc, sc = oracle.quantize(cb, kb, kvd)
+    assert np.array_equal(kc, kb)
+    qmax = np.float32(448.0 if kvd == synth.KV_FP8_KPE16 else 127.0)
+    cf = (cb.astype(np.uint32) << 16).view(np.float32)
+    amax = np.abs(cf).max(axis=1)
+    assert np.array_equal(sc, (amax / qmax).astype(np.float32))
+    full = synth.KV_FP8_E4M3 if kvd == synth.KV_FP8_KPE16 else synth.KV_INT8
+    cc2, _, sc2 = oracle.quantize(cb, np.zeros_like(kb), full)  # kpe of zeros: same amax
+    assert np.array_equal(cc, cc2) and np.array_equal(sc, sc2)
+
+
 def test_quantize_all_zero_token():
     z = np.zeros((2, 576), np.uint16)
     z[1, 7] = 0x8000  # -0.0
@@ -563,6 +592,9 @@ PIN_SUITE = [
     test_encode_e4m3fn_saturates,
     test_quantize_scale_and_codes_definition,
     lambda: test_brute_force_causal_queries(CAUSAL_CASES[0]),
+    lambda: test_brute_force_tiny(BRUTE_CASES[6]),
+    lambda: test_brute_force_tiny(BRUTE_CASES[7]),
+    lambda: test_quantize_644_record_scales_ckv_only(synth.KV_FP8_KPE16),
     lambda: test_causal_query_is_decode_of_its_prefix(synth.KV_BF16),
 ]
 
@@ -585,13 +617,17 @@ MUTANTS = {
                        "r = floor(a / ldexp(1.0, E - 3) + 0.5);"),
     "encode_no_saturation": ("if (a >= 448.0) {", "if (a >= 1e30) {"),
     "encode_exponent": ("code = ((E + 7) << 3) | ((int)r - 8);", "code = ((E + 8) << 3) | ((int)r - 8);"),
-    "quant_scale_int8": ("kv_dtype == ORC_FP8_E4M3 ? 448.0f : 127.0f;", "kv_dtype == ORC_FP8_E4M3 ? 448.0f : 128.0f;"),
+    "quant_scale_int8": ("ckv_fp8(kv_dtype) ? 448.0f : 127.0f;", "ckv_fp8(kv_dtype) ? 448.0f : 128.0f;"),
     "quant_truncate": ("float r = nearbyintf(v);", "float r = truncf(v);"),
     "causal_off_by_one": ("(int64_t)(in->qo_len - 1 - qi);", "(int64_t)(in->qo_len - qi);"),
     "causal_reversed": ("(int64_t)(in->qo_len - 1 - qi);", "(int64_t)(qi);"),
     "causal_none": ("(int64_t)(in->qo_len - 1 - qi);", "(int64_t)0;"),
     "query_row_ignores_index": ("const int64_t qrow = (int64_t)b * in->qo_len + qi;",
                                 "const int64_t qrow = (int64_t)b * in->qo_len;"),
+    "kpe16_scaled": ("row * D_KPE;\n    for (i = 0; i < D_KPE; ++i) R[i] = oracle_dec_bf16(k[i]);\n  } else",
+                     "row * D_KPE;\n    for (i = 0; i < D_KPE; ++i) R[i] = oracle_dec_bf16(k[i]) * sigma;\n  } else"),
+    "kpe16_amax_over_kpe": ("const int nq = kpe_bf16(kv_dtype) ? D_CKV : D_CKV + D_KPE;",
+                            "const int nq = D_CKV + D_KPE;"),
 }
 
 
