@@ -39,8 +39,11 @@ KERNEL_SRC = os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", "kernels.hip"
 # other workloads measured in the same run (parity cases at full size)
 SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
              "fp8_b64_h16_l8192_p64", "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64",
-             "int8_b64_h128_l8192_p64", "mtp_b64_h16_q2_l4096_p64", "mtp_b64_h128_q2_l4096_p64")
-KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8"}
+             "int8_b64_h128_l8192_p64", "fp8ckv_bf16kpe_b64_h16_l8192_p64",
+             "fp8ckv_bf16kpe_b64_h128_l8192_p64", "int8ckv_bf16kpe_b64_h16_l8192_p64",
+             "int8ckv_bf16kpe_b64_h128_l8192_p64", "mtp_b64_h16_q2_l4096_p64",
+             "mtp_b64_h128_q2_l4096_p64")
+KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8", 3: "fp8_e4m3_ckv_bf16_kpe", 4: "int8_ckv_bf16_kpe"}
 
 
 class Hip:
@@ -201,8 +204,8 @@ def workload_report(m: dict, peaks: dict) -> dict:
 def measure_append(kv_dtype: int, n: int, steps: int, warmup: int, hip: Hip) -> dict:
     """mla_cache_append of n new tokens (bf16 in, kv_dtype cache out) into a
     cache of n slots, rows in a seeded random order.  Algorithmic bytes per
-    token: 1152 read, 1152 (bf16) or 576 codes + 4 scale (8-bit) written, and
-    the 8-byte slot."""
+    token: 1152 read, 1152 (bf16), 576 codes + 4 scale (8-bit) or 512 codes +
+    128 kpe + 4 scale (644-byte record) written, and the 8-byte slot."""
     import numpy as np
     import torch
     import mla_paged_kv_decode_amd as mla
@@ -218,10 +221,12 @@ def measure_append(kv_dtype: int, n: int, steps: int, warmup: int, hip: Hip) -> 
         sc = None
         wbytes = 1152
     else:
+        kpe16 = kv_dtype in (mla.KV_FP8_E4M3_KPE_BF16, mla.KV_INT8_KPE_BF16)
         ckv = torch.empty((pages, P, 512), dtype=torch.uint8, device="cuda")
-        kpe = torch.empty((pages, P, 64), dtype=torch.uint8, device="cuda")
+        kpe = torch.empty((pages, P, 64), dtype=torch.bfloat16 if kpe16 else torch.uint8,
+                          device="cuda")
         sc = torch.empty((pages, P), dtype=torch.float32, device="cuda")
-        wbytes = 580
+        wbytes = 644 if kpe16 else 580
     for _ in range(warmup):
         mla.cache_append(new_c, new_k, slots, ckv, kpe, kv_dtype, sc)
     torch.cuda.synchronize()
@@ -368,7 +373,7 @@ def main():
             torch.cuda.empty_cache()
     if not args.no_append:
         out["append"] = [measure_append(k, 262144, args.steps, args.warmup, hip)
-                         for k in (0, 1, 2)]
+                         for k in (0, 1, 2, 3)]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -66,8 +66,15 @@ typedef enum {
 
 typedef enum {
   MLA_KV_BF16 = 0,      /* ckv/kpe are bf16; kv_scale must be NULL */
-  MLA_KV_FP8_E4M3 = 1,  /* ckv/kpe are OCP fp8 e4m3 codes; kv_scale [pages, P] fp32 */
-  MLA_KV_INT8 = 2       /* ckv/kpe are int8 codes; kv_scale [pages, P] fp32 */
+  MLA_KV_FP8_E4M3 = 1,  /* ckv/kpe are OCP fp8 e4m3 codes; kv_scale [pages, P] fp32
+                           scales both (580 bytes per token) */
+  MLA_KV_INT8 = 2,      /* ckv/kpe are int8 codes; kv_scale [pages, P] fp32 scales both */
+  /* The 644-byte token record of FlashMLA PR 233 ("What is added": 644
+     instead of 1152 bytes per token): 512 one-byte ckv codes, 64 bf16 kpe
+     values and one fp32 scale, which applies to ckv only.  ckv [pages, P, 512]
+     codes, kpe [pages, P, 64] bf16, kv_scale [pages, P] fp32. */
+  MLA_KV_FP8_E4M3_KPE_BF16 = 3,
+  MLA_KV_INT8_KPE_BF16 = 4
 } mla_kv_dtype;
 
 /* Scheduling options; zero-initialise for defaults. */
@@ -86,6 +93,7 @@ typedef struct {
 typedef struct mla_plan_s* mla_plan_t;
 
 /* Supported shapes: num_heads in {16, 32, 64, 128}; page_size in {16, 32, 64};
+   every kv_dtype (8-bit caches run 16- and 128-wide rows);
    qo_len in 1..64.  The automatic group width is the largest served width that
    divides qo_len * num_heads. */
 
@@ -204,6 +212,8 @@ mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* work
  * kpe): amax = max |x|; scale = amax / 448 (fp8) or amax / 127 (int8) in
  * binary32, 1 for an all-zero token; code = the representable value nearest
  * to x / scale (binary32 division), ties to even, saturated to +-448 / +-127.
+ * The 644-byte layouts quantise the 512 ckv values the same way (amax over
+ * them alone) and copy kpe as bf16 (kpe is then [pages, P, 64] bf16).
  * Errors: MLA_ERR_INVALID_ARG for n < 0, a null pointer (n > 0) or kv_scale
  * not matching kv_dtype; MLA_ERR_UNSUPPORTED for another kv_dtype.  One kernel
  * launch on stream; nothing is allocated or synchronised.

@@ -23,6 +23,9 @@ LIB_PATH = os.path.join(_HERE, "libmla_decode.so")
 
 MLA_OK = 0
 KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
+# the 644-byte record: 8-bit ckv codes, bf16 kpe, fp32 scale on ckv only
+KV_FP8_E4M3_KPE_BF16, KV_INT8_KPE_BF16 = 3, 4
+_KPE_BF16 = (KV_FP8_E4M3_KPE_BF16, KV_INT8_KPE_BF16)
 D_CKV, D_KPE = 512, 64
 
 EXPORTED_SYMBOLS = (
@@ -231,10 +234,12 @@ class Plan:
             if kv_scale is not None:
                 raise ValueError("kv_scale must be None for a bf16 cache")
         else:
-            codes = (torch.uint8, torch.float8_e4m3fn) if self.kv_dtype == KV_FP8_E4M3 \
-                else (torch.uint8, torch.int8)
-            if ckv.dtype not in codes or kpe.dtype not in codes:
-                raise ValueError("8-bit cache expected (one byte per value)")
+            codes = (torch.uint8, torch.float8_e4m3fn) \
+                if self.kv_dtype in (KV_FP8_E4M3, KV_FP8_E4M3_KPE_BF16) else (torch.uint8, torch.int8)
+            kpe_ok = kpe.dtype == torch.bfloat16 if self.kv_dtype in _KPE_BF16 else kpe.dtype in codes
+            if ckv.dtype not in codes or not kpe_ok:
+                raise ValueError("8-bit cache expected (one byte per ckv value; kpe one byte, "
+                                 "or bf16 for the 644-byte layouts)")
             if (kv_scale is None or kv_scale.dtype != torch.float32
                     or tuple(kv_scale.shape) != tuple(ckv.shape[:2])):
                 raise ValueError("kv_scale must be float32 [pages, page_size]")
@@ -272,8 +277,9 @@ def cache_append(ckv_new, kpe_new, slots, ckv, kpe, kv_dtype: int = KV_BF16, kv_
         if ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16 or kv_scale is not None:
             raise ValueError("bf16 cache expected, without kv_scale")
     else:
-        if ckv.element_size() != 1 or kpe.element_size() != 1:
-            raise ValueError("8-bit cache expected")
+        kpe_size = 2 if kv_dtype in _KPE_BF16 else 1
+        if ckv.element_size() != 1 or kpe.element_size() != kpe_size:
+            raise ValueError("8-bit cache expected (bf16 kpe for the 644-byte layouts)")
         if kv_scale is None or kv_scale.dtype != torch.float32 \
                 or tuple(kv_scale.shape) != tuple(ckv.shape[:2]):
             raise ValueError("kv_scale must be float32 [pages, page_size]")

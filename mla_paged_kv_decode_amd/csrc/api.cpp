@@ -179,7 +179,7 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
   const int32_t nq = num_heads * qo_len;
   // bound over every row width and cache dtype the plan may choose
   size_t best = 0;
-  for (int32_t kvd = 0; kvd < 3; ++kvd)
+  for (int32_t kvd = 0; kvd <= MLA_KV_INT8_KPE_BF16; ++kvd)
   for (int32_t w = 16; w <= 128; w *= 2) {
     if (nq % w != 0) continue;
     const int32_t hs = nq / w;
@@ -205,8 +205,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   if (batch < 0 || !kv_indptr_host || (batch > 0 && !kv_last_page_len_host))
     return MLA_ERR_INVALID_ARG;
   if (!supported_heads(num_heads) || page_shift_of(page_size) < 0) return MLA_ERR_UNSUPPORTED;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_INT8)
-    return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_INT8_KPE_BF16) return MLA_ERR_UNSUPPORTED;
   if (opts && (opts->force_splits < 0 || opts->max_workers < 0)) return MLA_ERR_INVALID_ARG;
 
   if (opts && opts->head_split < 0) return MLA_ERR_INVALID_ARG;
@@ -381,8 +380,7 @@ mla_status mla_cache_append(const void* ckv_new, const void* kpe_new, const int6
                             int32_t n, mla_kv_dtype kv_dtype, void* ckv, void* kpe,
                             float* kv_scale, void* stream) {
   if (n < 0) return MLA_ERR_INVALID_ARG;
-  if (kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP8_E4M3 && kv_dtype != MLA_KV_INT8)
-    return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_INT8_KPE_BF16) return MLA_ERR_UNSUPPORTED;
   if (n == 0) return MLA_OK;
   if (!ckv_new || !kpe_new || !slots || !ckv || !kpe) return MLA_ERR_INVALID_ARG;
   if ((kv_dtype == MLA_KV_BF16) != (kv_scale == nullptr)) return MLA_ERR_INVALID_ARG;

@@ -9,7 +9,9 @@
 //   code_i = nearest representable value of x_i / scale (binary32 division),
 //           ties to even, saturated at +-448 / +-127
 // One wave per token: lane l holds ckv values 8l .. 8l + 7 and kpe value l,
-// the max is a wave reduction, and each lane stores its 8 + 1 codes.
+// the max is a wave reduction, and each lane stores its 8 + 1 codes.  The
+// 644-byte record (same page: 8-bit ckv, bf16 kpe, one scale per token) takes
+// amax over the 512 ckv values only and stores kpe unchanged (KVT 3 / 4).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -75,25 +77,31 @@ __global__ void __launch_bounds__(256)
       x[2 * i] = bf16_to_float(c[i] & 0xFFFFu);
       x[2 * i + 1] = bf16_to_float(c[i] >> 16);
     }
+    constexpr bool kpe16 = KVT >= 3;
+    constexpr bool fp8 = KVT == 1 || KVT == 3;
+    constexpr int nq = kpe16 ? 8 : 9;  // values of this lane that are quantised
     x[8] = bf16_to_float(k);
     float amax = 0.f;
 #pragma unroll
-    for (int i = 0; i < 9; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    for (int i = 0; i < nq; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    const float qmax = KVT == 1 ? 448.f : 127.f;
+    const float qmax = fp8 ? 448.f : 127.f;
     const float scale = amax > 0.f ? amax / qmax : 1.f;  // correctly rounded division
     unsigned codes[9];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
+    for (int i = 0; i < nq; ++i) {
       const float v = x[i] / scale;
-      codes[i] = KVT == 1 ? encode_e4m3fn(v) : encode_int8(v);
+      codes[i] = fp8 ? encode_e4m3fn(v) : encode_int8(v);
     }
     u32x2 w;
     w[0] = codes[0] | (codes[1] << 8) | (codes[2] << 16) | (codes[3] << 24);
     w[1] = codes[4] | (codes[5] << 8) | (codes[6] << 16) | (codes[7] << 24);
     *reinterpret_cast<u32x2*>(ckv + slot * 512 + lane * 8) = w;
-    kpe[slot * 64 + lane] = (uint8_t)codes[8];
+    if constexpr (kpe16)
+      *reinterpret_cast<uint16_t*>(kpe + slot * 128 + lane * 2) = (uint16_t)k;
+    else
+      kpe[slot * 64 + lane] = (uint8_t)codes[8];
     if (lane == 0) kv_scale[slot] = scale;
   }
 }
@@ -116,6 +124,14 @@ hipError_t launch_cache_append(int kv_dtype, const uint16_t* ckv_new, const uint
       break;
     case 2:
       hipLaunchKernelGGL(mla_cache_append_kernel<2>, grid, block, 0, stream, ckv_new, kpe_new,
+                         slots, n, ckv, kpe, kv_scale);
+      break;
+    case 3:
+      hipLaunchKernelGGL(mla_cache_append_kernel<3>, grid, block, 0, stream, ckv_new, kpe_new,
+                         slots, n, ckv, kpe, kv_scale);
+      break;
+    case 4:
+      hipLaunchKernelGGL(mla_cache_append_kernel<4>, grid, block, 0, stream, ckv_new, kpe_new,
                          slots, n, ckv, kpe, kv_scale);
       break;
     default:

@@ -43,8 +43,9 @@ struct DecodeConfig {
                         // counters); 0: launch_combine does, after the decode kernel
 };
 
-// Kernel for `heads` heads per workgroup and a cache of `kv_dtype` (0 bf16,
-// 1 fp8 e4m3, 2 int8): returns -1 when no kernel serves the pair.
+// Kernel for `heads` heads per workgroup and a cache of `kv_dtype` (mla_kv_dtype:
+// 0 bf16, 1 / 2 fp8 / int8, 3 / 4 fp8 / int8 ckv with bf16 kpe): returns -1 when
+// no kernel serves the pair.
 int decode_config(int heads, int kv_dtype, DecodeConfig* cfg);
 // Workgroups of that kernel resident on one CU (HIP occupancy query on the
 // current device; an LDS-based estimate if the query fails).

@@ -784,7 +784,8 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
 
 // ---------------------------------------------------------------------------
 // Register-staged kernel for 16 or 32 heads per workgroup (HB 16-head blocks),
-// with a bf16, fp8-e4m3 or int8 latent cache (KVT 0 / 1 / 2).  At these head
+// with a bf16, fp8-e4m3 or int8 latent cache (KVT 0 / 1 / 2), or the 644-byte
+// record with fp8 / int8 ckv and bf16 kpe (KVT 3 / 4).  At these head
 // counts the work is memory bound, so what matters is the number of bytes in
 // flight per CU and keeping the waves out of each other's way:
 //   * 4 waves split a segment's 16-token groups round-robin (wave w takes
@@ -801,7 +802,9 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
 // scale per token, dequantised in the kernel): codes become bf16 exactly; the
 // token's scale multiplies its score (after QK, in fp32) and its probability
 // (before P is rounded to bf16 for PV), which is the same as dequantising the
-// row first.
+// row first.  With a bf16 kpe (644-byte record, the scale belongs to ckv
+// only), the scale multiplies the accumulator after the 512 ckv dimensions
+// and before the 64 kpe dimensions are added.
 // ---------------------------------------------------------------------------
 template <int HB, int KVT, int NB>
 struct StreamShape {
@@ -814,15 +817,19 @@ struct StreamShape {
   static constexpr int kMergeBytes = merge_bytes<16, 1, kWaves>();  // one head block at a time
   static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
                                                                     : kMergeBytes;
-  static constexpr int kLoads = KVT == 0 ? 18 : 9;  // 16-byte loads per lane per group
+  // 16-byte loads per lane per group: bf16 18; 8-bit ckv 8 + kpe 1 (8-bit) or 2 (bf16)
+  static constexpr int kLoads = KVT == 0 ? 18 : (KVT >= 3 ? 10 : 9);
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
+// Cache layouts (KVT): 0 bf16; 1 / 2 fp8 e4m3 / int8 ckv and kpe with one
+// scale per token (580 B); 3 / 4 fp8 e4m3 / int8 ckv, bf16 kpe, one scale per
+// token for ckv (the 644-byte record).
 // 8 codes (two dwords) -> 8 bf16 values, exactly.
 template <int KVT>
 __device__ __forceinline__ u32x4 codes_to_bf16(unsigned lo, unsigned hi) {
   u32x4 r;
-  if constexpr (KVT == 1) {  // OCP fp8 e4m3: hardware conversion, scale 1
+  if constexpr (KVT == 1 || KVT == 3) {  // OCP fp8 e4m3: hardware conversion, scale 1
     r[0] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, false));
     r[1] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.f, true));
     r[2] = __builtin_bit_cast(unsigned, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.f, false));
@@ -972,8 +979,18 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
           for (int cb = 0; cb < 4; ++cb)
             st[rh * 4 + cb] = *reinterpret_cast<const u32x4*>(cbase + cb * 128);
         }
-        const size_t rowk = pbase + (min(gs + (lane >> 2), t1 - 1) & page_mask);
-        st[8] = *reinterpret_cast<const u32x4*>(live ? a.kpe + rowk * 64 + (lane & 3) * 16 : dummy);
+        if constexpr (KVT >= 3) {  // bf16 kpe rows, as in the bf16 layout
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh) {
+            const int r = rh * 8 + ld_r_lo;
+            const size_t row = pbase + (min(gs + r, t1 - 1) & page_mask);
+            const int sw = ((lane & 7) ^ swz(r)) * 16;
+            st[8 + rh] = *reinterpret_cast<const u32x4*>(live ? a.kpe + row * 128 + sw : dummy + sw);
+          }
+        } else {
+          const size_t rowk = pbase + (min(gs + (lane >> 2), t1 - 1) & page_mask);
+          st[8] = *reinterpret_cast<const u32x4*>(live ? a.kpe + rowk * 64 + (lane & 3) * 16 : dummy);
+        }
         // scales of score rows 4 (lane >> 4) .. + 3 (16-byte aligned, same page)
         const size_t rows = pbase + ((gs + 4 * (lane >> 4)) & page_mask);
         sc = *reinterpret_cast<const f32x4*>(live ? reinterpret_cast<const uint8_t*>(a.kv_scale + rows)
@@ -999,11 +1016,24 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
           *reinterpret_cast<u32x4*>(wbuf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][1]) =
               codes_to_bf16<KVT>(st[u][2], st[u][3]);
         }
-        *reinterpret_cast<u32x4*>(wbuf + st8k[0]) = codes_to_bf16<KVT>(st[8][0], st[8][1]);
-        *reinterpret_cast<u32x4*>(wbuf + st8k[1]) = codes_to_bf16<KVT>(st[8][2], st[8][3]);
+        if constexpr (KVT >= 3) {
+#pragma unroll
+          for (int rh = 0; rh < 2; ++rh)
+            *reinterpret_cast<u32x4*>(wbuf + (rh * 9 + 8) * 1024 + lane * 16) = st[8 + rh];
+        } else {
+          *reinterpret_cast<u32x4*>(wbuf + st8k[0]) = codes_to_bf16<KVT>(st[8][0], st[8][1]);
+          *reinterpret_cast<u32x4*>(wbuf + st8k[1]) = codes_to_bf16<KVT>(st[8][2], st[8][3]);
+        }
       }
       fetch(j + NB, st, sc);  // registers free again: NB groups ahead in flight
       if (j >= nmine) return;
+
+      // scales of rows past the end are zeroed (NaN padding may sit there)
+      const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
+      if constexpr (KVT != 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sig[i] = (row0 + i < t1) ? sig[i] : 0.f;
+      }
 
       // QK: S^T[16 tokens][16 heads] per head block; K and Q^T from LDS
       const uint8_t* gbase = wbuf + qk_base;
@@ -1027,24 +1057,23 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
             qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
                 (const LDS_AS uint8_t*)(qbase + (hb * 72 + (s0 + u) * 4) * 256));
 #pragma unroll
-          for (int u = 0; u < 6; ++u)
+          for (int u = 0; u < 6; ++u) {
+            // 644-byte record: the scale is ckv's, applied before the kpe steps
+            if constexpr (KVT >= 3)
+              if (s0 + u == 16) sacc[hb] = sacc[hb] * sig;
             sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[u], sacc[hb], 0, 0, 0);
+          }
         }
       }
 
       // online softmax, log2 domain, lazy rescale; rows past the end masked
-      const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
-      if constexpr (KVT != 0) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sig[i] = (row0 + i < t1) ? sig[i] : 0.f;
-      }
       s16x4 pv[HB];
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float raw = KVT != 0 ? sacc[hb][i] * sig[i] : sacc[hb][i];
+          const float raw = (KVT == 1 || KVT == 2) ? sacc[hb][i] * sig[i] : sacc[hb][i];
           const float x = (row0 + i < tlim[hb]) ? raw * a.scale_log2 : -INFINITY;
           sacc[hb][i] = x;
           tmax = fmaxf(tmax, x);
@@ -1182,7 +1211,9 @@ __device__ __forceinline__ void agpr_settle() {
 // cache: a ring of kStages code tiles (ckv codes [32][512], kpe codes
 // [32][64], the 32 scales; filled by direct-to-LDS loads) and two bf16 tiles:
 // the codes of tile k + 1 are converted (exactly) into one of them while tile
-// k is computed from the other.
+// k is computed from the other.  644-byte record (KVT 3 / 4): the code tile
+// holds bf16 kpe rows [32][64] (copied, not converted) and only the 128 bytes
+// of scales.
 template <int KVT>
 struct WideShape {
   static constexpr int kWaves = 4;
@@ -1194,9 +1225,11 @@ struct WideShape {
   // in LDS, to make room for the code conversion)
   static constexpr int kQRegSteps = KVT == 0 ? 36 : 32;
   static constexpr int kStageBytes = kTile * kRowBytes;              // 36 KiB bf16 tile
+  static constexpr bool kKpe16 = KVT >= 3;
   static constexpr int kCodeKpe = kTile * 512;                       // offsets in a code tile
-  static constexpr int kCodeScale = kCodeKpe + kTile * 64;
-  static constexpr int kCodeBytes = kCodeScale + 1024;               // 19 KiB
+  static constexpr int kCodeScale = kCodeKpe + kTile * 64 * (kKpe16 ? 2 : 1);
+  static constexpr int kCodeBytes = kCodeScale + (kKpe16 ? 128 : 1024);  // 19 / 20.1 KiB
+  static constexpr int kDmaPerWave = KVT == 0 ? 9 : (kKpe16 ? 6 : 5);  // loads per tile
   static constexpr int kBf16Offset = kStages * kCodeBytes;           // 8-bit: the two bf16 tiles
   static constexpr int kRingBytes = KVT == 0 ? kStages * kStageBytes
                                              : kBf16Offset + 2 * kStageBytes;
@@ -1300,6 +1333,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     //   8-bit: wave w issues loads d = 5 w .. 5 w + 4 of 20: ckv code rows 2d,
     //   2d + 1 (d < 16), kpe code rows 16 (d - 16) .. + 15 (d = 16, 17), the 32
     //   scales (d = 18 and again d = 19, so that every wave issues 5 loads).
+    //   644-byte record: d = 6 w .. 6 w + 5 of 24: ckv as above, bf16 kpe rows
+    //   8 (d - 16) .. + 7 (d = 16 .. 19), the 32 scales by lanes 0..7 (d >= 20).
     //   Past the last tile, the last tile is loaded again (its data lands in
     //   a slot no one reads), which keeps the loads in flight, and so every
     //   vmcnt wait, the same in every iteration.
@@ -1327,15 +1362,19 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + st * S::kCodeBytes));
 #pragma unroll
-        for (int u = 0; u < 5; ++u) {
-          const int d = 5 * wave + u;  // wave-uniform
+        for (int u = 0; u < S::kDmaPerWave; ++u) {
+          const int d = S::kDmaPerWave * wave + u;  // wave-uniform
           int t, off;
           uint32_t dst;
           if (d < 16) {
             t = 2 * d + (lane >> 5);
             off = (lane & 31) * 16;
             dst = dst0 + d * 1024;
-          } else if (d < 18) {
+          } else if (S::kKpe16 && d < 20) {
+            t = 8 * (d - 16) + (lane >> 3);
+            off = (lane & 7) * 16;
+            dst = dst0 + S::kCodeKpe + (d - 16) * 1024;
+          } else if (!S::kKpe16 && d < 18) {
             t = 16 * (d - 16) + (lane >> 2);
             off = (lane & 3) * 16;
             dst = dst0 + S::kCodeKpe + (d - 16) * 1024;
@@ -1344,15 +1383,20 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             off = 0;
             dst = dst0 + S::kCodeScale;
           }
+          const int dscale = S::kKpe16 ? 20 : 18;  // first scale load
           // a 16-byte read of scales covers 4 tokens: keep it inside the page
-          const int tok = min(tile0 + t, d < 18 ? t1 - 1 : (t1 - 1) & ~3);
+          const int tok = min(tile0 + t, d < dscale ? t1 - 1 : (t1 - 1) & ~3);
           const int gpage = t < 16 ? pg[0] : pg[1];
           const size_t row = ((size_t)gpage << page_shift) + (tok & page_mask);
           const uint8_t* src =
               d < 16 ? a.ckv + row * 512 + off
-                     : (d < 18 ? a.kpe + row * 64 + off
-                               : reinterpret_cast<const uint8_t*>(a.kv_scale + row));
-          dma16(src, __builtin_amdgcn_readfirstlane(dst));
+                     : (d < dscale ? a.kpe + row * (S::kKpe16 ? 128 : 64) + off
+                                   : reinterpret_cast<const uint8_t*>(a.kv_scale + row));
+          if (S::kKpe16 && d >= dscale) {
+            if (lane < 8) dma16(src, __builtin_amdgcn_readfirstlane(dst));  // 128 bytes
+          } else {
+            dma16(src, __builtin_amdgcn_readfirstlane(dst));
+          }
         }
       }
     };
@@ -1373,7 +1417,13 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         *reinterpret_cast<u32x4*>(row + ((((2 * u + 1) & 7) ^ swz(r)) * 16)) =
             codes_to_bf16<KVT>(c[2], c[3]);
       }
-      if (wave < 2) {  // kpe: 128 pieces
+      if constexpr (S::kKpe16) {  // bf16 kpe: 256 pieces of 8 values, copied
+        const int t = tid >> 3, u = tid & 7, r = t & 15;
+        const u32x4 c = *reinterpret_cast<const u32x4*>(cod + S::kCodeKpe + t * 128 + u * 16);
+        uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + 8 * 1024 +
+                       (r & 7) * 128;
+        *reinterpret_cast<u32x4*>(row + ((u ^ swz(r)) * 16)) = c;
+      } else if (wave < 2) {  // kpe: 128 pieces
         const int t = tid >> 2, u = tid & 3, r = t & 15;
         const u32x4 c = *reinterpret_cast<const u32x4*>(cod + S::kCodeKpe + t * 64 + u * 16);
         uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + 8 * 1024 +
@@ -1444,7 +1494,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       } else {
         // code tile it + 1 landed (tiles it + 2 .. it + NS - 2 may be in
         // flight); bf16 tile `it` converted; iteration it - 1 done everywhere
-        vm_wait_n<5 * (NS - 3)>();
+        vm_wait_n<S::kDmaPerWave * (NS - 3)>();
         lds_barrier();
         issue_tile(it + NS - 1, (it + NS - 1) % NS);
         if (it + 1 < ntiles)
@@ -1453,12 +1503,37 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       }
       const int tile_start = t0 + it * T;
 
+      // 8-bit: the token scales of this lane's score rows (rows past the end may
+      // hold any scale, NaN padding included: zeroed)
+      f32x16 sig;
+      auto load_sig = [&]() __attribute__((always_inline)) {
+        const float* sc = reinterpret_cast<const float*>(smem + (it % NS) * S::kCodeBytes +
+                                                         S::kCodeScale);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(sc + 8 * j + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = tile_start + 8 * j + 4 * g + i;
+            sig[4 * j + i] = tok < t1 ? v[i] : 0.f;
+          }
+        }
+      };
+
       // ---- QK: S^T[32 tokens][32 heads of this wave] ------------------------
       f32x16 sacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
 #pragma unroll
       for (int s0 = 0; s0 < 36; s0 += 4) {
+        if constexpr (S::kKpe16) {
+          // 644-byte record: the scale is ckv's, applied before the kpe steps
+          if (s0 == 32) {
+            load_sig();
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] *= sig[r];
+          }
+        }
         bf16x8 kf[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u)
@@ -1478,27 +1553,13 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       // 8-bit: the token scale multiplies the score (after QK, in fp32) and the
       // probability (before P is rounded to bf16 for PV), the same as
       // dequantising the row first.
-      f32x16 sig;
-      if constexpr (KVT != 0) {
-        const float* sc = reinterpret_cast<const float*>(smem + (it % NS) * S::kCodeBytes +
-                                                         S::kCodeScale);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(sc + 8 * j + 4 * g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // rows past the end may hold any scale (NaN padding included)
-            const int tok = tile_start + 8 * j + 4 * g + i;
-            sig[4 * j + i] = tok < t1 ? v[i] : 0.f;
-          }
-        }
-      }
+      if constexpr (KVT == 1 || KVT == 2) load_sig();
       const int tlim = CAUSAL ? limit_s[32 * wave + l32] : t1;
       float tmax = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float raw = KVT != 0 ? sacc[r] * sig[r] : sacc[r];
+        const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
         const float x = tok < tlim ? raw * a.scale_log2 : -INFINITY;
         sacc[r] = x;
         tmax = fmaxf(tmax, x);
@@ -1844,6 +1905,20 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
     switch (heads) {
       case 16: MLA_STREAM(1, 2, MLA_H16_NB8);
       case 128: MLA_WIDE(2);
+      default: return 0;
+    }
+  }
+  if (kv_dtype == 3) {
+    switch (heads) {
+      case 16: MLA_STREAM(1, 3, MLA_H16_NB8);
+      case 128: MLA_WIDE(3);
+      default: return 0;
+    }
+  }
+  if (kv_dtype == 4) {
+    switch (heads) {
+      case 16: MLA_STREAM(1, 4, MLA_H16_NB8);
+      case 128: MLA_WIDE(4);
       default: return 0;
     }
   }

@@ -233,6 +233,15 @@ WORKLOADS = {
                                    seed=5),
     "int8_b64_h128_l8192_p64": dict(batch=64, heads=128, kv_len=8192, page=64, kv_dtype=KV_INT8,
                                     seed=5),
+    # the 644-byte record (8-bit ckv, bf16 kpe, fp32 scale on ckv)
+    "fp8ckv_bf16kpe_b64_h16_l8192_p64": dict(batch=64, heads=16, kv_len=8192, page=64,
+                                             kv_dtype=KV_FP8_KPE16, seed=5),
+    "fp8ckv_bf16kpe_b64_h128_l8192_p64": dict(batch=64, heads=128, kv_len=8192, page=64,
+                                              kv_dtype=KV_FP8_KPE16, seed=5),
+    "int8ckv_bf16kpe_b64_h16_l8192_p64": dict(batch=64, heads=16, kv_len=8192, page=64,
+                                              kv_dtype=KV_INT8_KPE16, seed=5),
+    "int8ckv_bf16kpe_b64_h128_l8192_p64": dict(batch=64, heads=128, kv_len=8192, page=64,
+                                               kv_dtype=KV_INT8_KPE16, seed=5),
     # two queries per request (one speculative / next-token-prediction token)
     "mtp_b64_h16_q2_l4096_p64": dict(batch=64, heads=16, kv_len=4096, page=64, kv_dtype=KV_BF16,
                                      seed=6, qo_len=2),

@@ -23,7 +23,10 @@ def dev(inp):
         t["kv_scale"] = None
     else:
         t["ckv"] = torch.from_numpy(inp.ckv).to(d)
-        t["kpe"] = torch.from_numpy(inp.kpe).to(d)
+        if inp.kpe.dtype == np.uint16:  # bf16 kpe of the 644-byte record
+            t["kpe"] = torch.from_numpy(inp.kpe.view(np.int16)).view(torch.bfloat16).to(d)
+        else:
+            t["kpe"] = torch.from_numpy(inp.kpe).to(d)
         t["kv_scale"] = torch.from_numpy(inp.kv_scale).to(d)
     for k in ("kv_indptr", "kv_indices", "kv_last_page_len"):
         t[k] = torch.from_numpy(getattr(inp, k)).to(d)

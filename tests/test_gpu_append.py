@@ -42,6 +42,7 @@ def _dev_bf16(bits):
 
 def _cache(pages, P, kv_dtype, seed):
     rng = np.random.default_rng(seed)
+    kpe16 = kv_dtype in (synth.KV_FP8_KPE16, synth.KV_INT8_KPE16)
     if kv_dtype == synth.KV_BF16:
         ckv = torch.from_numpy(rng.integers(0, 65536, (pages, P, 512)).astype(np.uint16).view(
             np.int16)).view(torch.bfloat16).cuda()
@@ -49,7 +50,11 @@ def _cache(pages, P, kv_dtype, seed):
             np.int16)).view(torch.bfloat16).cuda()
         return ckv, kpe, None
     ckv = torch.from_numpy(rng.integers(0, 256, (pages, P, 512)).astype(np.uint8)).cuda()
-    kpe = torch.from_numpy(rng.integers(0, 256, (pages, P, 64)).astype(np.uint8)).cuda()
+    if kpe16:
+        kpe = torch.from_numpy(rng.integers(0, 65536, (pages, P, 64)).astype(np.uint16).view(
+            np.int16)).view(torch.bfloat16).cuda()
+    else:
+        kpe = torch.from_numpy(rng.integers(0, 256, (pages, P, 64)).astype(np.uint8)).cuda()
     sc = torch.from_numpy(rng.normal(0, 1, (pages, P)).astype(np.float32)).cuda()
     return ckv, kpe, sc
 
@@ -59,7 +64,8 @@ def _as_u(t):
         else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8_E4M3, synth.KV_INT8])
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8_E4M3, synth.KV_INT8,
+                                      synth.KV_FP8_KPE16, synth.KV_INT8_KPE16])
 @pytest.mark.parametrize("n,wide", [(1, False), (37, False), (1000, True), (4099, False)])
 def test_append_matches_oracle(kv_dtype, n, wide):
     import mla_paged_kv_decode_amd as mla
@@ -94,7 +100,8 @@ def test_append_matches_oracle(kv_dtype, n, wide):
     assert np.array_equal(got_k, exp_k)
 
 
-@pytest.mark.parametrize("kv_dtype", [synth.KV_FP8_E4M3, synth.KV_INT8])
+@pytest.mark.parametrize("kv_dtype", [synth.KV_FP8_E4M3, synth.KV_INT8, synth.KV_FP8_KPE16,
+                                      synth.KV_INT8_KPE16])
 def test_append_then_decode(kv_dtype):
     """A cache built token by token with mla_cache_append decodes like the
     oracle on the oracle's quantisation of the same tokens."""
@@ -111,19 +118,21 @@ def test_append_then_decode(kv_dtype):
             toks_k.append(src.kpe[page, t % P])
     rows = np.array(rows, np.int64)
     tc, tk = np.stack(toks_c), np.stack(toks_k)
+    kpe16 = kv_dtype in (synth.KV_FP8_KPE16, synth.KV_INT8_KPE16)
     ckv = torch.zeros((pages, P, 512), dtype=torch.uint8, device="cuda")
-    kpe = torch.zeros((pages, P, 64), dtype=torch.uint8, device="cuda")
+    kpe = torch.zeros((pages, P, 64), dtype=torch.bfloat16 if kpe16 else torch.uint8,
+                      device="cuda")
     sc = torch.ones((pages, P), dtype=torch.float32, device="cuda")
     mla.cache_append(_dev_bf16(tc), _dev_bf16(tk), torch.from_numpy(rows).cuda(), ckv, kpe,
                      kv_dtype, sc)
     torch.cuda.synchronize()
     cc, kc, s = oracle.quantize(tc, tk, kv_dtype)
     ref_ckv = np.zeros((pages * P, 512), np.uint8)
-    ref_kpe = np.zeros((pages * P, 64), np.uint8)
+    ref_kpe = np.zeros((pages * P, 64), np.uint16 if kpe16 else np.uint8)
     ref_sc = np.ones(pages * P, np.float32)
     ref_ckv[rows], ref_kpe[rows], ref_sc[rows] = cc, kc, s
     assert np.array_equal(ckv.cpu().numpy().reshape(-1, 512), ref_ckv)
-    assert np.array_equal(kpe.cpu().numpy().reshape(-1, 64), ref_kpe)
+    assert np.array_equal(_as_u(kpe).reshape(-1, 64), ref_kpe)
     assert np.array_equal(sc.cpu().numpy().reshape(-1), ref_sc)
     q8 = synth.MlaInputs(src.batch, src.num_heads, P, kv_dtype, src.lengths, src.q_nope, src.q_pe,
                          ref_ckv.reshape(pages, P, 512), ref_kpe.reshape(pages, P, 64),

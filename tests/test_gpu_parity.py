@@ -174,7 +174,8 @@ def test_graph_replay_matches_eager():
 @pytest.mark.parametrize("name", ["mem_b64_h16_l4096_p64", "compute_b64_h128_l4096_p64",
                                   "varlen_b768_h64_l1to2048_p16", "fp8_b64_h16_l8192_p64",
                                   "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64",
-                                  "int8_b64_h128_l8192_p64"])
+                                  "int8_b64_h128_l8192_p64", "fp8ckv_bf16kpe_b64_h16_l8192_p64",
+                                  "int8ckv_bf16kpe_b64_h128_l8192_p64"])
 def test_full_workloads_sampled(name):
     inp = synth.make_workload(name, poison=True)
     print("workload", name, flush=True)
@@ -191,7 +192,7 @@ def test_full_workloads_sampled(name):
 
 # ---- 8-bit latent caches: compared with the oracle on the dequantised values
 
-KV8 = [synth.KV_FP8_E4M3, synth.KV_INT8]
+KV8 = [synth.KV_FP8_E4M3, synth.KV_INT8, synth.KV_FP8_KPE16, synth.KV_INT8_KPE16]
 
 
 @pytest.mark.parametrize("kv_dtype", KV8)
@@ -293,7 +294,7 @@ def _jump_inputs(lengths, heads, kv_dtype, seed, factor, jumps):
     return inp
 
 
-@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8_E4M3])
+@pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8_E4M3, synth.KV_INT8_KPE16])
 @pytest.mark.parametrize("heads", [16, 32, 64, 128])
 @pytest.mark.parametrize("factor", [16, 64])
 def test_score_jump_rescales(kv_dtype, heads, factor):
