@@ -42,7 +42,7 @@ SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
              "int8_b64_h128_l8192_p64", "fp8ckv_bf16kpe_b64_h16_l8192_p64",
              "fp8ckv_bf16kpe_b64_h128_l8192_p64", "int8ckv_bf16kpe_b64_h16_l8192_p64",
              "int8ckv_bf16kpe_b64_h128_l8192_p64", "mtp_b64_h16_q2_l4096_p64",
-             "mtp_b64_h128_q2_l4096_p64")
+             "mtp_b64_h128_q2_l4096_p64", "mem_b64_h16_l4096_p32", "mem_b64_h16_l4096_p16")
 KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8", 3: "fp8_e4m3_ckv_bf16_kpe", 4: "int8_ckv_bf16_kpe"}
 
 
@@ -124,7 +124,8 @@ def device_inputs(inp, copies: int):
     return sets
 
 
-def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_split: int = 0) -> dict:
+def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_split: int = 0,
+            l2_domains: int = 0) -> dict:
     import torch
     import mla_paged_kv_decode_amd as mla
     from mla_paged_kv_decode_amd import synth
@@ -136,7 +137,7 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
                      device="cuda")
     t0 = time.perf_counter()
     plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, inp.page_size, inp.kv_dtype, ws,
-                    head_split=head_split, qo_len=Q)
+                    head_split=head_split, qo_len=Q, l2_domains=l2_domains)
     plan_ms = (time.perf_counter() - t0) * 1e3
     outs = [(torch.empty((B * Q, H, 512), dtype=torch.bfloat16, device="cuda"),
              torch.empty((B * Q, H), dtype=torch.float32, device="cuda")) for _ in range(copies)]
@@ -290,6 +291,9 @@ def main():
     ap.add_argument("--copies", type=int, default=2)
     ap.add_argument("--head-split", type=int, default=0,
                     help="head split for the measured workloads (0 = the planner's choice)")
+    ap.add_argument("--l2-domains", type=int, default=0,
+                    help="L2 domains for placing the rows of one request (0 = the "
+                         "library default of 8 XCDs, 1 = no placement)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true",
@@ -330,7 +334,7 @@ def main():
         torch.cuda.empty_cache()
 
     prim = measure(args.workload, args.steps, args.warmup, args.copies, hip,
-                   args.head_split if synth_heads(args.workload) >= 64 else 0)
+                   args.head_split if synth_heads(args.workload) >= 64 else 0, args.l2_domains)
     inp = prim["inp"]
     gbs = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
     kern_gbs = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
@@ -367,7 +371,8 @@ def main():
     if args.secondary != "none":
         out["also"] = []
         for name in args.secondary.split(","):
-            sec = measure(name, args.steps, args.warmup, args.copies, hip, args.head_split)
+            sec = measure(name, args.steps, args.warmup, args.copies, hip, args.head_split,
+                          args.l2_domains)
             out["also"].append(workload_report(sec, peaks))
             del sec
             torch.cuda.empty_cache()

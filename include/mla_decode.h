@@ -88,6 +88,10 @@ typedef struct {
                            width must be one the kernels serve: 16, 32, 64 or 128 (bf16),
                            16 or 128 (8-bit caches). */
   int32_t qo_len;       /* queries per request, 1..64; 0 means 1 */
+  int32_t l2_domains;   /* L2 domains (XCDs) that workgroups are dealt to round-robin in
+                           launch order; the rows of one request are placed in one of them
+                           so that they share its latent cache through one L2.  0 = 8 (a
+                           whole MI355X); 1 = no placement (e.g. a one-XCD partition). */
 } mla_plan_opts;
 
 typedef struct mla_plan_s* mla_plan_t;

@@ -59,7 +59,7 @@ class MlaError(RuntimeError):
 class PlanOpts(ctypes.Structure):
     _fields_ = [("num_cus", ctypes.c_int32), ("force_splits", ctypes.c_int32),
                 ("max_workers", ctypes.c_int32), ("head_split", ctypes.c_int32),
-                ("qo_len", ctypes.c_int32)]
+                ("qo_len", ctypes.c_int32), ("l2_domains", ctypes.c_int32)]
 
 
 def load_library(path: str = LIB_PATH):
@@ -101,9 +101,10 @@ def load_library(path: str = LIB_PATH):
     return lib
 
 
-def _opts(num_cus=0, force_splits=0, max_workers=0, head_split=0, qo_len=1) -> PlanOpts:
+def _opts(num_cus=0, force_splits=0, max_workers=0, head_split=0, qo_len=1,
+          l2_domains=0) -> PlanOpts:
     return PlanOpts(int(num_cus), int(force_splits), int(max_workers), int(head_split),
-                    int(qo_len))
+                    int(qo_len), int(l2_domains))
 
 
 def _host_i32(x) -> np.ndarray:
@@ -150,7 +151,7 @@ class Plan:
     def __init__(self, kv_indptr, kv_last_page_len, num_heads: int, page_size: int,
                  kv_dtype: int = KV_BF16, workspace=None, num_cus: int = 0,
                  force_splits: int = 0, max_workers: int = 0, head_split: int = 0,
-                 stream=None, qo_len: int = 1):
+                 stream=None, qo_len: int = 1, l2_domains: int = 0):
         lib = load_library()
         self._lib = lib
         ip = _host_i32(kv_indptr)
@@ -161,7 +162,7 @@ class Plan:
         self.kv_dtype = int(kv_dtype)
         self.qo_len = int(qo_len)
         self.workspace = workspace
-        o = _opts(num_cus, force_splits, max_workers, head_split, qo_len)
+        o = _opts(num_cus, force_splits, max_workers, head_split, qo_len, l2_domains)
         h = ctypes.c_void_p()
         ws_ptr, ws_n, sp = None, 0, None
         if workspace is not None:

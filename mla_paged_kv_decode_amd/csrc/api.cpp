@@ -137,6 +137,7 @@ mla::PlanParams plan_params(int32_t num_queries, int32_t head_split, int32_t wor
   pp.granularity = cfg.tile;
   pp.force_splits = opts ? opts->force_splits : 0;
   pp.head_split = head_split;
+  if (opts && opts->l2_domains > 0) pp.xcd_count = opts->l2_domains;
   // the merge of a split request keeps one float per (chunk, head) in LDS
   pp.max_splits = std::min<int32_t>(256, cfg.lds_bytes / (4 * pp.num_heads));
   return pp;
@@ -206,7 +207,8 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
     return MLA_ERR_INVALID_ARG;
   if (!supported_heads(num_heads) || page_shift_of(page_size) < 0) return MLA_ERR_UNSUPPORTED;
   if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_INT8_KPE_BF16) return MLA_ERR_UNSUPPORTED;
-  if (opts && (opts->force_splits < 0 || opts->max_workers < 0)) return MLA_ERR_INVALID_ARG;
+  if (opts && (opts->force_splits < 0 || opts->max_workers < 0 || opts->l2_domains < 0))
+    return MLA_ERR_INVALID_ARG;
 
   if (opts && opts->head_split < 0) return MLA_ERR_INVALID_ARG;
   const int32_t qo_len = qo_len_of(opts);

@@ -84,16 +84,19 @@ int64_t assign(const std::vector<Piece>& pieces, int32_t workers, std::vector<in
   return worst;
 }
 
-// Reorder workers so that the workers serving the hs sub-requests of one
-// request get launch positions congruent modulo the number of L2 domains
-// (workgroups are dealt to XCDs round-robin), letting them share the request's
-// KV through one L2.  Workers are ordered by the first row they serve, then
-// dealt in chunks of hs: chunk c goes to domain c % X, consecutive positions
-// of that domain.  Only applied when the worker count divides evenly; it is a
-// placement heuristic and never affects results.
-void xcd_colocate(const std::vector<Piece>& pieces, const std::vector<int32_t>& owner, int32_t hs,
+// Reorder workers so that the workers serving the hs rows of one request
+// (the row groups that share its latent cache, with all their chunks) get
+// launch positions congruent modulo the number of L2 domains: workgroups are
+// dealt to XCDs round-robin in launch order, so they then share one L2.
+// Workers are sorted by the first row they serve and the domains are filled
+// one after the other (domain d takes sorted workers d * per .. d * per + per - 1,
+// per = used / xcds, at positions d, d + xcds, d + 2 xcds, ...), so a request
+// is split over two domains only where it straddles such a boundary.  Only
+// applied when the worker count divides evenly; it is a placement heuristic and
+// never affects results.
+void xcd_colocate(const std::vector<Piece>& pieces, const std::vector<int32_t>& owner,
                   int32_t xcds, int32_t used, std::vector<int32_t>* remap) {
-  if (xcds < 1 || used % (xcds * hs) != 0) return;
+  if (xcds < 2 || used % xcds != 0) return;
   std::vector<int32_t> first_row((size_t)used, std::numeric_limits<int32_t>::max());
   for (size_t i = 0; i < pieces.size(); ++i) {
     const int32_t w = (*remap)[owner[i]];
@@ -103,11 +106,9 @@ void xcd_colocate(const std::vector<Piece>& pieces, const std::vector<int32_t>& 
   for (int32_t w = 0; w < used; ++w) order[w] = w;
   std::stable_sort(order.begin(), order.end(),
                    [&](int32_t x, int32_t y) { return first_row[x] < first_row[y]; });
+  const int32_t per = used / xcds;
   std::vector<int32_t> pos((size_t)used);
-  for (int32_t i = 0; i < used; ++i) {
-    const int32_t c = i / hs, j = i % hs;
-    pos[order[i]] = (c % xcds) + xcds * (hs * (c / xcds) + j);
-  }
+  for (int32_t i = 0; i < used; ++i) pos[order[i]] = (i / per) + xcds * (i % per);
   for (auto& r : *remap)
     if (r >= 0) r = pos[r];
 }
@@ -189,7 +190,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
   int32_t used = 0;
   for (int32_t w = 0; w < p.num_workers; ++w)
     if (count[w] > 0) remap[w] = used++;
-  if (hs > 1) xcd_colocate(best_pieces, best_owner, hs, p.xcd_count, used, &remap);
+  if (hs > 1) xcd_colocate(best_pieces, best_owner, p.xcd_count, used, &remap);
   out->batch = batch;
   out->num_workers = used;
   out->worker_ptr.assign((size_t)used + 1, 0);

@@ -221,6 +221,11 @@ WORKLOADS = {
     "tiny_b4_h16_l256_p16": dict(batch=4, heads=16, kv_len=256, page=16, kv_dtype=KV_BF16, seed=1),
     "mem_b64_h16_l4096_p64": dict(batch=64, heads=16, kv_len=4096, page=64, kv_dtype=KV_BF16,
                                   seed=2),
+    # the memory-bound shape with the other page sizes of the same page
+    "mem_b64_h16_l4096_p32": dict(batch=64, heads=16, kv_len=4096, page=32, kv_dtype=KV_BF16,
+                                  seed=2),
+    "mem_b64_h16_l4096_p16": dict(batch=64, heads=16, kv_len=4096, page=16, kv_dtype=KV_BF16,
+                                  seed=2),
     "compute_b64_h128_l4096_p64": dict(batch=64, heads=128, kv_len=4096, page=64,
                                        kv_dtype=KV_BF16, seed=3),
     "varlen_b768_h64_l1to2048_p16": dict(batch=768, heads=64, kv_len=(1, 2048), page=16,

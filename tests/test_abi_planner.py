@@ -229,6 +229,31 @@ def test_head_split_rows_share_an_xcd(lib):
     assert all(len(x) == 1 for x in xcd_of_request.values())
 
 
+@pytest.mark.parametrize("heads,q,kvd", [(128, 2, mla.KV_BF16), (64, 1, mla.KV_FP8_E4M3),
+                                         (16, 4, mla.KV_INT8)])
+def test_rows_of_a_request_share_an_xcd_with_token_splits(lib, heads, q, kvd):
+    # rows of one request (several per request, each also cut into token
+    # chunks) get launch positions congruent mod 8, i.e. one L2 domain
+    ip, lp = _table([4096] * 64, 64)
+    plan = mla.Plan(ip, lp, heads, 64, kvd, num_cus=256, qo_len=q)
+    hs = plan.info()["head_split"]
+    assert hs > 1
+    seg, wp = plan.segments()
+    assert len(seg) >= 64 * hs  # (128 heads x 2 queries: rows also cut into chunks)
+    xcd = {}
+    for w in range(len(wp) - 1):
+        for s_ in seg[wp[w]:wp[w + 1]]:
+            xcd.setdefault(int(s_[0]) // hs, set()).add(w % 8)
+    # (each workgroup serves one request here, and the domains hold whole requests)
+    assert len(xcd) == 64 and all(len(x) == 1 for x in xcd.values())
+    # l2_domains = 1 turns the placement off (same segments, other order)
+    flat = mla.Plan(ip, lp, heads, 64, kvd, num_cus=256, qo_len=q, l2_domains=1)
+    seg1, _ = flat.segments()
+    assert sorted(map(tuple, seg1.tolist())) == sorted(map(tuple, seg.tolist()))
+    with pytest.raises(mla.MlaError):
+        mla.Plan(ip, lp, heads, 64, kvd, num_cus=256, qo_len=q, l2_domains=-1)
+
+
 def test_bad_head_split_rejected(lib):
     ip, lp = _table([10], 16)
     for heads, hs in ((128, 3), (16, 2), (64, 8)):
