@@ -41,6 +41,9 @@ D_CKV, D_KPE = 512, 64
 KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
 # 644-byte token record: 8-bit ckv codes + bf16 kpe + fp32 scale (ckv only)
 KV_FP8_KPE16, KV_INT8_KPE16 = 3, 4
+# fp16 cache with fp16 queries
+KV_FP16 = 5
+FP16_NAN = 0x7E00
 KV_DTYPE_NAMES = {KV_BF16: "bf16", KV_FP8_E4M3: "fp8_e4m3", KV_INT8: "int8"}
 
 BF16_NAN = 0x7FC0
@@ -55,8 +58,8 @@ class MlaInputs:
     page_size: int
     kv_dtype: int
     lengths: np.ndarray           # int64 [B]
-    q_nope: np.ndarray            # uint16 (bf16 bits) [B * qo_len, H, 512]
-    q_pe: np.ndarray              # uint16 (bf16 bits) [B * qo_len, H, 64]
+    q_nope: np.ndarray            # uint16 (bf16 bits; fp16 for KV_FP16) [B * qo_len, H, 512]
+    q_pe: np.ndarray              # uint16 (bf16 bits; fp16 for KV_FP16) [B * qo_len, H, 64]
     ckv: np.ndarray               # uint16 [pages, P, 512] (bf16) or uint8 codes
     kpe: np.ndarray               # uint16 [pages, P, 64] (bf16) or uint8 codes
     kv_scale: Optional[np.ndarray]  # float32 [pages, P] for 8-bit caches, else None
@@ -73,7 +76,7 @@ class MlaInputs:
         return int(self.ckv.shape[0])
 
     def kv_bytes_per_token(self) -> int:
-        if self.kv_dtype == KV_BF16:
+        if self.kv_dtype in (KV_BF16, KV_FP16):
             return 2 * (D_CKV + D_KPE)
         if self.kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16):
             return D_CKV + 2 * D_KPE + 4  # 644
@@ -107,14 +110,19 @@ def _rngs(seed: int, n: int):
     return [np.random.Generator(np.random.PCG64(s)) for s in np.random.SeedSequence(seed).spawn(n)]
 
 
-def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24) -> np.ndarray:
-    """N(0,1) draws rounded to bf16, returned as uint16 bit patterns."""
+def _normal_bf16(rng: np.random.Generator, shape, chunk: int = 1 << 24,
+                 fp16: bool = False) -> np.ndarray:
+    """N(0,1) draws rounded to bf16 (or fp16), returned as uint16 bit patterns."""
     n = int(np.prod(shape))
     out = np.empty(n, np.uint16)
     for s in range(0, n, chunk):
         e = min(n, s + chunk)
         f = rng.standard_normal(e - s, dtype=np.float32)
-        out[s:e] = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        if fp16:
+            out[s:e] = f.astype(np.float16).view(np.uint16)
+        else:
+            out[s:e] = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(
+                np.uint16)
     return out.reshape(shape)
 
 
@@ -176,13 +184,14 @@ def make_inputs(lengths, num_heads: int, page_size: int, kv_dtype: int = KV_BF16
     P = int(page_size)
     r_qn, r_qp, r_ckv, r_kpe, r_perm = _rngs(seed, 5)
     indptr, indices, last, pages = page_table(lengths, P, r_perm, extra_pages)
-    q_nope = _normal_bf16(r_qn, (B * qo_len, H, D_CKV))
-    q_pe = _normal_bf16(r_qp, (B * qo_len, H, D_KPE))
-    ckv = _normal_bf16(r_ckv, (pages, P, D_CKV))
-    kpe = _normal_bf16(r_kpe, (pages, P, D_KPE))
+    f16 = kv_dtype == KV_FP16
+    q_nope = _normal_bf16(r_qn, (B * qo_len, H, D_CKV), fp16=f16)
+    q_pe = _normal_bf16(r_qp, (B * qo_len, H, D_KPE), fp16=f16)
+    ckv = _normal_bf16(r_ckv, (pages, P, D_CKV), fp16=f16)
+    kpe = _normal_bf16(r_kpe, (pages, P, D_KPE), fp16=f16)
     ckv_src = kpe_src = None
     kv_scale = None
-    if kv_dtype != KV_BF16:
+    if kv_dtype not in (KV_BF16, KV_FP16):
         ckv_src, kpe_src = ckv, kpe
         ckv, kpe, kv_scale = _quantize_tokens(ckv_src, kpe_src, kv_dtype)
     if poison:
@@ -200,9 +209,10 @@ def _poison(ckv, kpe, kv_scale, kv_dtype, indptr, indices, last, P, pages):
         if indptr[b + 1] > indptr[b]:
             lp = int(indices[indptr[b + 1] - 1])
             slot_dead[lp, int(last[b]):] = True
-    if kv_dtype == KV_BF16:
-        ckv[slot_dead] = BF16_NAN
-        kpe[slot_dead] = BF16_NAN
+    if kv_dtype in (KV_BF16, KV_FP16):
+        nan = BF16_NAN if kv_dtype == KV_BF16 else FP16_NAN
+        ckv[slot_dead] = nan
+        kpe[slot_dead] = nan
         return
     kv_scale[slot_dead] = np.nan
     if kv_dtype in (KV_FP8_E4M3, KV_FP8_KPE16):

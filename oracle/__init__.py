@@ -34,6 +34,8 @@ _LIB = os.path.join(_HERE, "libmla_oracle.so")
 KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
 # 644-byte record: 8-bit ckv codes, bf16 kpe, fp32 scale on ckv only
 KV_FP8_KPE16, KV_INT8_KPE16 = 3, 4
+# fp16 cache, with fp16 queries
+KV_FP16 = 5
 D_CKV, D_KPE = 512, 64
 
 _lib = None
@@ -68,6 +70,8 @@ def _load():
     lib.oracle_dec_e4m3fn.restype = f64
     lib.oracle_dec_int8.argtypes = [ctypes.c_uint8]
     lib.oracle_dec_int8.restype = f64
+    lib.oracle_dec_fp16.argtypes = [ctypes.c_uint16]
+    lib.oracle_dec_fp16.restype = f64
     lib.oracle_kv_len.argtypes = [P, P, i32, i32]
     lib.oracle_kv_len.restype = i64
     lib.mla_oracle_decode.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P, P, P, f64, P, i64,
@@ -104,6 +108,10 @@ def dec_e4m3fn(code: int) -> float:
     return _load().oracle_dec_e4m3fn(int(code) & 0xFF)
 
 
+def dec_fp16(bits: int) -> float:
+    return _load().oracle_dec_fp16(int(bits))
+
+
 def dec_int8(code: int) -> float:
     return _load().oracle_dec_int8(int(code) & 0xFF)
 
@@ -115,7 +123,7 @@ def kv_len(kv_indptr, kv_last_page_len, page_size: int, b: int) -> int:
 
 
 def _kv_arrays(kv_dtype, ckv, kpe):
-    if kv_dtype == KV_BF16:
+    if kv_dtype in (KV_BF16, KV_FP16):
         return _c(ckv, np.uint16), _c(kpe, np.uint16)
     if kv_dtype in (KV_FP8_KPE16, KV_INT8_KPE16):
         return _c(ckv, np.uint8), _c(kpe, np.uint16)
@@ -126,7 +134,8 @@ def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_s
            page_size: int, kv_dtype: int = KV_BF16, kv_scale=None, rows=None, threads: int = 0,
            qo_len: int = 1):
     """fp64 decode.  Inputs are host numpy arrays: bf16 tensors as uint16 bit
-    patterns, 8-bit caches as uint8 codes with an fp32 ``kv_scale[pages, P]``.
+    patterns (fp16 ones for kv_dtype KV_FP16, queries included), 8-bit caches
+    as uint8 codes with an fp32 ``kv_scale[pages, P]``.
     With qo_len > 1 the queries are [B * qo_len, H, *] and query i of request b
     sees its first L_b - (qo_len - 1 - i) tokens (causal, queries at the end).
 

@@ -66,13 +66,23 @@
  * FP8_KPE16 / INT8_KPE16: the 644-byte token record of "FlashMLA Ampere v2"
  * ("What is added", 644 instead of 1152 bytes per token), read as 512 8-bit
  * ckv codes + 64 bf16 kpe values + one fp32 scale that applies to ckv only
- * (512 + 128 + 4 = 644).
+ * (512 + 128 + 4 = 644).  FP16: ckv and kpe fp16, and the queries are fp16 too
+ * (the same page's v2 kernel takes bf16 or fp16 inputs).
  */
-enum { ORC_BF16 = 0, ORC_FP8_E4M3 = 1, ORC_INT8 = 2, ORC_FP8_KPE16 = 3, ORC_INT8_KPE16 = 4 };
+enum {
+  ORC_BF16 = 0,
+  ORC_FP8_E4M3 = 1,
+  ORC_INT8 = 2,
+  ORC_FP8_KPE16 = 3,
+  ORC_INT8_KPE16 = 4,
+  ORC_FP16 = 5
+};
 
 static int ckv_fp8(int32_t kv_dtype) { return kv_dtype == ORC_FP8_E4M3 || kv_dtype == ORC_FP8_KPE16; }
-static int kpe_bf16(int32_t kv_dtype) { return kv_dtype == ORC_BF16 || kv_dtype >= ORC_FP8_KPE16; }
-static int valid_dtype(int32_t kv_dtype) { return kv_dtype >= ORC_BF16 && kv_dtype <= ORC_INT8_KPE16; }
+static int kpe_bf16(int32_t kv_dtype) {
+  return kv_dtype == ORC_BF16 || kv_dtype == ORC_FP8_KPE16 || kv_dtype == ORC_INT8_KPE16;
+}
+static int valid_dtype(int32_t kv_dtype) { return kv_dtype >= ORC_BF16 && kv_dtype <= ORC_FP16; }
 
 double oracle_dec_bf16(uint16_t bits) {
   uint32_t w = ((uint32_t)bits) << 16;
@@ -95,6 +105,26 @@ double oracle_dec_e4m3fn(uint8_t code) {
 }
 
 double oracle_dec_int8(uint8_t code) { return (double)(int8_t)code; }
+
+/* IEEE binary16: 1 sign, 5 exponent (bias 15), 10 mantissa bits; exponent 0 is
+   subnormal (m / 1024 * 2^-14); exponent 31 is infinity (m = 0) or NaN. */
+double oracle_dec_fp16(uint16_t bits) {
+  int sign = (bits >> 15) & 1;
+  int e = (bits >> 10) & 31;
+  int m = bits & 1023;
+  double v;
+  if (e == 31) return m ? NAN : (sign ? -INFINITY : INFINITY);
+  if (e == 0)
+    v = ldexp((double)m / 1024.0, -14);
+  else
+    v = ldexp(1.0 + (double)m / 1024.0, e - 15);
+  return sign ? -v : v;
+}
+
+/* The 16-bit element type of q (and of a 16-bit cache) for a layout. */
+static double dec16(int32_t kv_dtype, uint16_t bits) {
+  return kv_dtype == ORC_FP16 ? oracle_dec_fp16(bits) : oracle_dec_bf16(bits);
+}
 
 /* Number of tokens of request b. */
 int64_t oracle_kv_len(const int32_t* kv_indptr, const int32_t* kv_last_page_len, int32_t page_size,
@@ -125,11 +155,11 @@ static void load_token(const oracle_inputs* in, int32_t b, int64_t t, double* K,
   int64_t row = page * P + slot;
   double sigma = 1.0;
   int i;
-  if (in->kv_dtype == ORC_BF16) {
+  if (in->kv_dtype == ORC_BF16 || in->kv_dtype == ORC_FP16) {
     const uint16_t* c = (const uint16_t*)in->ckv + row * D_CKV;
     const uint16_t* k = (const uint16_t*)in->kpe + row * D_KPE;
-    for (i = 0; i < D_CKV; ++i) K[i] = oracle_dec_bf16(c[i]);
-    for (i = 0; i < D_KPE; ++i) R[i] = oracle_dec_bf16(k[i]);
+    for (i = 0; i < D_CKV; ++i) K[i] = dec16(in->kv_dtype, c[i]);
+    for (i = 0; i < D_KPE; ++i) R[i] = dec16(in->kv_dtype, k[i]);
     return;
   }
   sigma = (double)in->kv_scale[row];
@@ -185,8 +215,8 @@ static int attend_range(const oracle_inputs* in, int32_t b, int32_t qi, int32_t 
     *lse = -INFINITY;
     return 0;
   }
-  for (i = 0; i < D_CKV; ++i) q[i] = oracle_dec_bf16(qn[i]);
-  for (i = 0; i < D_KPE; ++i) q[D_CKV + i] = oracle_dec_bf16(qp[i]);
+  for (i = 0; i < D_CKV; ++i) q[i] = dec16(in->kv_dtype, qn[i]);
+  for (i = 0; i < D_KPE; ++i) q[D_CKV + i] = dec16(in->kv_dtype, qp[i]);
 
   s = (double*)malloc((size_t)n * sizeof(double));
   if (!s) return -1;
@@ -267,7 +297,7 @@ int mla_oracle_decode(int32_t batch, int32_t qo_len, int32_t num_heads, int32_t 
   if (batch < 0 || qo_len < 1 || num_heads <= 0 || page_size <= 0 || !o_out || !lse_out)
     return -1;
   if (!valid_dtype(kv_dtype)) return -1;
-  if (kv_dtype != ORC_BF16 && !kv_scale) return -1;
+  if (kv_dtype != ORC_BF16 && kv_dtype != ORC_FP16 && !kv_scale) return -1;
   in.batch = batch;
   in.qo_len = qo_len;
   in.num_heads = num_heads;
@@ -337,7 +367,8 @@ int mla_oracle_partial(int32_t batch, int32_t qo_len, int32_t num_heads, int32_t
   int64_t L, V;
   if (b < 0 || b >= batch || qo_len < 1 || qi < 0 || qi >= qo_len || h < 0 || h >= num_heads)
     return -1;
-  if (!valid_dtype(kv_dtype) || (kv_dtype != ORC_BF16 && !kv_scale)) return -1;
+  if (!valid_dtype(kv_dtype) || (kv_dtype != ORC_BF16 && kv_dtype != ORC_FP16 && !kv_scale))
+    return -1;
   L = oracle_kv_len(kv_indptr, kv_last_page_len, page_size, b);
   if (t0 < 0 || t1 < t0 || t1 > L) return -1;
   in.batch = batch;
@@ -436,7 +467,7 @@ int mla_oracle_quantize(int32_t n, int32_t kv_dtype, const uint16_t* ckv_new,
                         float* scales) {
   int32_t j;
   int i;
-  if (!valid_dtype(kv_dtype) || kv_dtype == ORC_BF16) return -1;
+  if (!valid_dtype(kv_dtype) || kv_dtype == ORC_BF16 || kv_dtype == ORC_FP16) return -1;
   for (j = 0; j < n; ++j) {
     float x[D_CKV + D_KPE];
     float amax = 0.0f, scale;

@@ -40,6 +40,8 @@ SM = synth.SM_SCALE_192
 # ----------------------------------------------------------------- helpers
 def _dec_tensor(codes, kv_dtype):
     """Decode with library conversions (not the oracle's decoders)."""
+    if kv_dtype == synth.KV_FP16:
+        return np.ascontiguousarray(codes).view(np.float16).astype(np.float64)
     if kv_dtype == synth.KV_BF16 or codes.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(codes).view(np.int16)).view(
             torch.bfloat16).to(torch.float64).numpy()
@@ -83,8 +85,9 @@ def brute_force(inp):
     tokens: the queries are the request's last q positions ("FlashMLA SM100",
     forward kernel notes: causal mask with Q at the end of the matrix)."""
     B, H, Q = inp.batch, inp.num_heads, inp.qo_len
-    qn = _dec_tensor(inp.q_nope, synth.KV_BF16)
-    qp = _dec_tensor(inp.q_pe, synth.KV_BF16)
+    q16 = synth.KV_FP16 if inp.kv_dtype == synth.KV_FP16 else synth.KV_BF16
+    qn = _dec_tensor(inp.q_nope, q16)
+    qp = _dec_tensor(inp.q_pe, q16)
     O = np.zeros((B * Q, H, 512))
     LSE = np.zeros((B * Q, H))
     smf = Fraction(inp.sm_scale)
@@ -152,6 +155,15 @@ def test_decode_e4m3fn_all_codes():
     assert oracle.dec_e4m3fn(0x01) == 2.0 ** -9
 
 
+def test_decode_fp16_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = codes.view(np.float16).astype(np.float64)
+    for c in range(65536):
+        v = oracle.dec_fp16(c)
+        assert (math.isnan(v) and math.isnan(ref[c])) or v == ref[c], c
+    assert oracle.dec_fp16(0x7BFF) == 65504.0 and oracle.dec_fp16(0x0001) == 2.0 ** -24
+
+
 def test_decode_int8_all_codes():
     for c in range(256):
         assert oracle.dec_int8(c) == float(np.array([c], np.uint8).view(np.int8)[0])
@@ -168,6 +180,7 @@ BRUTE_CASES = [
     ([10, 3], 2, 4, synth.KV_INT8, 16),
     ([7, 12], 2, 4, synth.KV_FP8_KPE16, 17),
     ([9, 2], 2, 4, synth.KV_INT8_KPE16, 18),
+    ([8, 0, 13], 3, 4, synth.KV_FP16, 19),
 ]
 
 
@@ -593,6 +606,8 @@ PIN_SUITE = [
     test_quantize_scale_and_codes_definition,
     lambda: test_brute_force_causal_queries(CAUSAL_CASES[0]),
     lambda: test_brute_force_tiny(BRUTE_CASES[6]),
+    lambda: test_brute_force_tiny(BRUTE_CASES[8]),
+    test_decode_fp16_all_codes,
     lambda: test_brute_force_tiny(BRUTE_CASES[7]),
     lambda: test_quantize_644_record_scales_ckv_only(synth.KV_FP8_KPE16),
     lambda: test_causal_query_is_decode_of_its_prefix(synth.KV_BF16),
@@ -628,6 +643,9 @@ MUTANTS = {
                      "row * D_KPE;\n    for (i = 0; i < D_KPE; ++i) R[i] = oracle_dec_bf16(k[i]) * sigma;\n  } else"),
     "kpe16_amax_over_kpe": ("const int nq = kpe_bf16(kv_dtype) ? D_CKV : D_CKV + D_KPE;",
                             "const int nq = D_CKV + D_KPE;"),
+    "fp16_bias": ("ldexp(1.0 + (double)m / 1024.0, e - 15)", "ldexp(1.0 + (double)m / 1024.0, e - 16)"),
+    "fp16_queries_as_bf16": ("for (i = 0; i < D_CKV; ++i) q[i] = dec16(in->kv_dtype, qn[i]);",
+                             "for (i = 0; i < D_CKV; ++i) q[i] = oracle_dec_bf16(qn[i]);"),
 }
 
 
