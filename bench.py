@@ -42,8 +42,10 @@ SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
              "int8_b64_h128_l8192_p64", "fp8ckv_bf16kpe_b64_h16_l8192_p64",
              "fp8ckv_bf16kpe_b64_h128_l8192_p64", "int8ckv_bf16kpe_b64_h16_l8192_p64",
              "int8ckv_bf16kpe_b64_h128_l8192_p64", "mtp_b64_h16_q2_l4096_p64",
-             "mtp_b64_h128_q2_l4096_p64", "mem_b64_h16_l4096_p32", "mem_b64_h16_l4096_p16")
-KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8", 3: "fp8_e4m3_ckv_bf16_kpe", 4: "int8_ckv_bf16_kpe"}
+             "mtp_b64_h128_q2_l4096_p64", "mem_b64_h16_l4096_p32", "mem_b64_h16_l4096_p16",
+             "fp16_b64_h16_l4096_p64", "fp16_b64_h128_l4096_p64")
+KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8", 3: "fp8_e4m3_ckv_bf16_kpe", 4: "int8_ckv_bf16_kpe",
+            5: "fp16"}
 
 
 class Hip:
@@ -104,8 +106,10 @@ def device_inputs(inp, copies: int):
     import torch
     d = "cuda"
 
+    t16 = torch.float16 if inp.kv_dtype == 5 else torch.bfloat16  # fp16 inputs
+
     def bf(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(d)
+        return torch.from_numpy(a.view(np.int16)).view(t16).to(d)
 
     def i32(a):
         return torch.from_numpy(a).to(d)
@@ -139,7 +143,8 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, inp.page_size, inp.kv_dtype, ws,
                     head_split=head_split, qo_len=Q, l2_domains=l2_domains)
     plan_ms = (time.perf_counter() - t0) * 1e3
-    outs = [(torch.empty((B * Q, H, 512), dtype=torch.bfloat16, device="cuda"),
+    t16 = torch.float16 if inp.kv_dtype == 5 else torch.bfloat16  # fp16 inputs: fp16 output
+    outs = [(torch.empty((B * Q, H, 512), dtype=t16, device="cuda"),
              torch.empty((B * Q, H), dtype=torch.float32, device="cuda")) for _ in range(copies)]
 
     def step(i):

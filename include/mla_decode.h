@@ -74,7 +74,10 @@ typedef enum {
      values and one fp32 scale, which applies to ckv only.  ckv [pages, P, 512]
      codes, kpe [pages, P, 64] bf16, kv_scale [pages, P] fp32. */
   MLA_KV_FP8_E4M3_KPE_BF16 = 3,
-  MLA_KV_INT8_KPE_BF16 = 4
+  MLA_KV_INT8_KPE_BF16 = 4,
+  /* fp16 inputs (FlashMLA PR 233: the v2 kernel takes bf16 or fp16): ckv/kpe fp16,
+     and q_nope, q_pe and o are fp16 too; kv_scale must be NULL. */
+  MLA_KV_FP16 = 5
 } mla_kv_dtype;
 
 /* Scheduling options; zero-initialise for defaults. */
@@ -146,6 +149,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
  * captured in a HIP graph and replayed while the page-table lengths are
  * unchanged.
  *   q_nope  device bf16 [batch * qo_len, H, 512]   q_pe device bf16 [batch * qo_len, H, 64]
+ *           (fp16 for MLA_KV_FP16, as are ckv, kpe and o)
  *   ckv     device [pages, P, 512]           kpe  device [pages, P, 64]
  *           (bf16, or 8-bit codes per the plan's kv_dtype)
  *   kv_scale device fp32 [pages, P] for 8-bit caches, NULL for bf16
@@ -205,17 +209,18 @@ mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* work
  * them when the cache is 8-bit (FlashMLA PR 233, "What is added": an FP8 e4m3
  * or INT8 latent cache with one fp32 scale per token; the layer's prologue
  * writes the cache before the decode reads it).
- *   ckv_new  device bf16 [n, 512]; kpe_new device bf16 [n, 64]
+ *   ckv_new  device bf16 [n, 512]; kpe_new device bf16 [n, 64] (fp16 for MLA_KV_FP16)
  *   slots    device int64 [n]: destination row page * page_size + position of
  *            the cache viewed as [pages * page_size, ...]; a negative entry
  *            skips that token.  Destinations must be distinct and inside the
  *            cache (not checked on the device).
  *   ckv, kpe device cache [pages, page_size, 512] and [.., 64] of kv_dtype
- *   kv_scale device fp32 [pages, page_size] for 8-bit caches, NULL for bf16
- * bf16: the rows are copied.  8-bit, per token over its 576 values (ckv then
- * kpe): amax = max |x|; scale = amax / 448 (fp8) or amax / 127 (int8) in
- * binary32, 1 for an all-zero token; code = the representable value nearest
- * to x / scale (binary32 division), ties to even, saturated to +-448 / +-127.
+ *   kv_scale device fp32 [pages, page_size] for 8-bit caches, NULL for bf16 / fp16
+ * bf16 and fp16 caches: the rows are copied (ckv_new / kpe_new are then fp16 for
+ * an fp16 cache).  8-bit, per token over its 576 values (ckv then kpe):
+ * amax = max |x|; scale = amax / 448 (fp8) or amax / 127 (int8) in binary32,
+ * 1 for an all-zero token; code = the representable value nearest to
+ * x / scale (binary32 division), ties to even, saturated to +-448 / +-127.
  * The 644-byte layouts quantise the 512 ckv values the same way (amax over
  * them alone) and copy kpe as bf16 (kpe is then [pages, P, 64] bf16).
  * Errors: MLA_ERR_INVALID_ARG for n < 0, a null pointer (n > 0) or kv_scale

@@ -26,6 +26,8 @@ KV_BF16, KV_FP8_E4M3, KV_INT8 = 0, 1, 2
 # the 644-byte record: 8-bit ckv codes, bf16 kpe, fp32 scale on ckv only
 KV_FP8_E4M3_KPE_BF16, KV_INT8_KPE_BF16 = 3, 4
 _KPE_BF16 = (KV_FP8_E4M3_KPE_BF16, KV_INT8_KPE_BF16)
+# fp16 inputs: fp16 cache, queries and output
+KV_FP16 = 5
 D_CKV, D_KPE = 512, 64
 
 EXPORTED_SYMBOLS = (
@@ -213,12 +215,13 @@ class Plan:
         """``mla_decode_run`` on device tensors (o and lse are written)."""
         import torch
         B, H = self.batch * self.qo_len, self.num_heads
-        if q_nope.dtype != torch.bfloat16 or q_pe.dtype != torch.bfloat16:
-            raise ValueError("q_nope / q_pe must be bfloat16")
+        t16 = torch.float16 if self.kv_dtype == KV_FP16 else torch.bfloat16
+        if q_nope.dtype != t16 or q_pe.dtype != t16:
+            raise ValueError("q_nope / q_pe must be %s" % t16)
         if tuple(q_nope.shape) != (B, H, D_CKV) or tuple(q_pe.shape) != (B, H, D_KPE):
             raise ValueError("q_nope / q_pe shape mismatch with the plan")
-        if tuple(o.shape) != (B, H, D_CKV) or o.dtype != torch.bfloat16:
-            raise ValueError("o must be bfloat16 [B * qo_len, H, 512]")
+        if tuple(o.shape) != (B, H, D_CKV) or o.dtype != t16:
+            raise ValueError("o must be %s [B * qo_len, H, 512]" % t16)
         if tuple(lse.shape) != (B, H) or lse.dtype != torch.float32:
             raise ValueError("lse must be float32 [B * qo_len, H]")
         for name, t in (("kv_indptr", kv_indptr), ("kv_indices", kv_indices),
@@ -229,11 +232,11 @@ class Plan:
             raise ValueError("ckv must be [pages, page_size, 512]")
         if kpe.dim() != 3 or kpe.shape[1] != self.page_size or kpe.shape[2] != D_KPE:
             raise ValueError("kpe must be [pages, page_size, 64]")
-        if self.kv_dtype == KV_BF16:
-            if ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16:
-                raise ValueError("bf16 cache expected")
+        if self.kv_dtype in (KV_BF16, KV_FP16):
+            if ckv.dtype != t16 or kpe.dtype != t16:
+                raise ValueError("%s cache expected" % t16)
             if kv_scale is not None:
-                raise ValueError("kv_scale must be None for a bf16 cache")
+                raise ValueError("kv_scale must be None for a 16-bit cache")
         else:
             codes = (torch.uint8, torch.float8_e4m3fn) \
                 if self.kv_dtype in (KV_FP8_E4M3, KV_FP8_E4M3_KPE_BF16) else (torch.uint8, torch.int8)
@@ -265,8 +268,9 @@ def cache_append(ckv_new, kpe_new, slots, ckv, kpe, kv_dtype: int = KV_BF16, kv_
     negative = skip), quantising them for an 8-bit cache."""
     import torch
     n = int(ckv_new.shape[0])
-    if ckv_new.dtype != torch.bfloat16 or kpe_new.dtype != torch.bfloat16:
-        raise ValueError("new tokens must be bfloat16")
+    t16 = torch.float16 if kv_dtype == KV_FP16 else torch.bfloat16
+    if ckv_new.dtype != t16 or kpe_new.dtype != t16:
+        raise ValueError("new tokens must be %s" % t16)
     if tuple(ckv_new.shape) != (n, D_CKV) or tuple(kpe_new.shape) != (n, D_KPE):
         raise ValueError("ckv_new must be [n, 512] and kpe_new [n, 64]")
     if slots.dtype != torch.int64 or tuple(slots.shape) != (n,):
@@ -274,9 +278,9 @@ def cache_append(ckv_new, kpe_new, slots, ckv, kpe, kv_dtype: int = KV_BF16, kv_
     if ckv.dim() != 3 or ckv.shape[2] != D_CKV or kpe.dim() != 3 or kpe.shape[2] != D_KPE \
             or tuple(ckv.shape[:2]) != tuple(kpe.shape[:2]):
         raise ValueError("ckv / kpe must be [pages, page_size, 512 / 64]")
-    if kv_dtype == KV_BF16:
-        if ckv.dtype != torch.bfloat16 or kpe.dtype != torch.bfloat16 or kv_scale is not None:
-            raise ValueError("bf16 cache expected, without kv_scale")
+    if kv_dtype in (KV_BF16, KV_FP16):
+        if ckv.dtype != t16 or kpe.dtype != t16 or kv_scale is not None:
+            raise ValueError("%s cache expected, without kv_scale" % t16)
     else:
         kpe_size = 2 if kv_dtype in _KPE_BF16 else 1
         if ckv.element_size() != 1 or kpe.element_size() != kpe_size:
@@ -335,7 +339,7 @@ def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_s
                      dtype=torch.uint8, device=q_nope.device)
     plan = Plan(ip_h, lp_h, H, P, kv_dtype, ws, force_splits=force_splits, head_split=head_split,
                 stream=stream, qo_len=qo_len)
-    o = torch.empty((NQ, H, D_CKV), dtype=torch.bfloat16, device=q_nope.device)
+    o = torch.empty((NQ, H, D_CKV), dtype=q_nope.dtype, device=q_nope.device)
     lse = torch.empty((NQ, H), dtype=torch.float32, device=q_nope.device)
     plan.run(q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len, sm_scale,
              o, lse, stream)

@@ -180,7 +180,7 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
   const int32_t nq = num_heads * qo_len;
   // bound over every row width and cache dtype the plan may choose
   size_t best = 0;
-  for (int32_t kvd = 0; kvd <= MLA_KV_INT8_KPE_BF16; ++kvd)
+  for (int32_t kvd = 0; kvd <= MLA_KV_FP16; ++kvd)
   for (int32_t w = 16; w <= 128; w *= 2) {
     if (nq % w != 0) continue;
     const int32_t hs = nq / w;
@@ -206,7 +206,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   if (batch < 0 || !kv_indptr_host || (batch > 0 && !kv_last_page_len_host))
     return MLA_ERR_INVALID_ARG;
   if (!supported_heads(num_heads) || page_shift_of(page_size) < 0) return MLA_ERR_UNSUPPORTED;
-  if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_INT8_KPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_FP16) return MLA_ERR_UNSUPPORTED;
   if (opts && (opts->force_splits < 0 || opts->max_workers < 0 || opts->l2_domains < 0))
     return MLA_ERR_INVALID_ARG;
 
@@ -292,7 +292,8 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   if (!q_nope || !q_pe || !ckv || !kpe || !kv_indptr || !kv_indices || !kv_last_page_len || !o ||
       !lse)
     return MLA_ERR_INVALID_ARG;
-  if ((p->kv_dtype == MLA_KV_BF16) != (kv_scale == nullptr)) return MLA_ERR_INVALID_ARG;
+  const bool scaled = p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP16;
+  if (scaled != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
   if (!(sm_scale == sm_scale)) return MLA_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = p->workspace;
@@ -315,6 +316,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.counters = reinterpret_cast<int32_t*>(ws + p->layout.counters);
   a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.o_fp16 = p->kv_dtype == MLA_KV_FP16 ? 1 : 0;
   a.page_shift = p->page_shift;
   a.rows_per_req = p->head_split;
   a.qo_len = p->qo_len;
@@ -382,10 +384,11 @@ mla_status mla_cache_append(const void* ckv_new, const void* kpe_new, const int6
                             int32_t n, mla_kv_dtype kv_dtype, void* ckv, void* kpe,
                             float* kv_scale, void* stream) {
   if (n < 0) return MLA_ERR_INVALID_ARG;
-  if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_INT8_KPE_BF16) return MLA_ERR_UNSUPPORTED;
+  if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_FP16) return MLA_ERR_UNSUPPORTED;
   if (n == 0) return MLA_OK;
   if (!ckv_new || !kpe_new || !slots || !ckv || !kpe) return MLA_ERR_INVALID_ARG;
-  if ((kv_dtype == MLA_KV_BF16) != (kv_scale == nullptr)) return MLA_ERR_INVALID_ARG;
+  const bool scaled = kv_dtype != MLA_KV_BF16 && kv_dtype != MLA_KV_FP16;
+  if (scaled != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
   hipError_t e = mla_gpu::launch_cache_append(
       kv_dtype, static_cast<const uint16_t*>(ckv_new), static_cast<const uint16_t*>(kpe_new),
       slots, n, static_cast<uint8_t*>(ckv), static_cast<uint8_t*>(kpe), kv_scale,

@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256)
   if (slot < 0) return;  // padding token, whole wave
   const u32x4 c = *reinterpret_cast<const u32x4*>(ckv_new + (size_t)j * 512 + lane * 8);
   const unsigned k = kpe_new[(size_t)j * 64 + lane];
-  if constexpr (KVT == 0) {
+  if constexpr (KVT == 0 || KVT == 5) {  // 16-bit cache: copy
     *reinterpret_cast<u32x4*>(ckv + slot * 1024 + lane * 16) = c;
     *reinterpret_cast<uint16_t*>(kpe + slot * 128 + lane * 2) = (uint16_t)k;
   } else {
@@ -77,7 +77,7 @@ __global__ void __launch_bounds__(256)
       x[2 * i] = bf16_to_float(c[i] & 0xFFFFu);
       x[2 * i + 1] = bf16_to_float(c[i] >> 16);
     }
-    constexpr bool kpe16 = KVT >= 3;
+    constexpr bool kpe16 = KVT == 3 || KVT == 4;  // 644-byte record
     constexpr bool fp8 = KVT == 1 || KVT == 3;
     constexpr int nq = kpe16 ? 8 : 9;  // values of this lane that are quantised
     x[8] = bf16_to_float(k);
@@ -132,6 +132,10 @@ hipError_t launch_cache_append(int kv_dtype, const uint16_t* ckv_new, const uint
       break;
     case 4:
       hipLaunchKernelGGL(mla_cache_append_kernel<4>, grid, block, 0, stream, ckv_new, kpe_new,
+                         slots, n, ckv, kpe, kv_scale);
+      break;
+    case 5:
+      hipLaunchKernelGGL(mla_cache_append_kernel<5>, grid, block, 0, stream, ckv_new, kpe_new,
                          slots, n, ckv, kpe, kv_scale);
       break;
     default:

@@ -26,6 +26,7 @@ struct DecodeArgs {
   int32_t* counters;          // arrival counter per split request (0 between launches)
   const int4* clist;          // 4 ints per split request: row, first slot, chunks, 0
   float scale_log2;           // sm_scale * log2(e)
+  int32_t o_fp16;             // 1: o is fp16 (fp16 cache and queries), 0: bf16
   int32_t page_shift;         // log2(page_size)
   int32_t rows_per_req;       // kernel rows per request: row b of q/o/lse (kernel-width
                               // groups of query vectors) reads the latent cache of request
@@ -44,7 +45,7 @@ struct DecodeConfig {
 };
 
 // Kernel for `heads` heads per workgroup and a cache of `kv_dtype` (mla_kv_dtype:
-// 0 bf16, 1 / 2 fp8 / int8, 3 / 4 fp8 / int8 ckv with bf16 kpe): returns -1 when
+// 0 bf16, 1 / 2 fp8 / int8, 3 / 4 fp8 / int8 ckv with bf16 kpe, 5 fp16): returns -1 when
 // no kernel serves the pair.
 int decode_config(int heads, int kv_dtype, DecodeConfig* cfg);
 // Workgroups of that kernel resident on one CU (HIP occupancy query on the

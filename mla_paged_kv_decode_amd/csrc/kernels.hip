@@ -56,6 +56,45 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// The 16-bit element type of q, of a 16-bit cache, of P and of O is bf16, or
+// fp16 with an fp16 cache (cache layout 5; "FlashMLA Ampere v2" takes bf16 or
+// fp16 inputs).  Values travel in bf16-typed registers either way; these
+// pick the conversion and the MFMA for the type (F16 = fp16).
+template <bool F16>
+__device__ __forceinline__ __bf16 to16(float x) {
+  if constexpr (F16)
+    return __builtin_bit_cast(__bf16, (_Float16)x);
+  else
+    return (__bf16)x;
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x4 mma_16x16x16(const s16x4& a, const s16x4& b, const f32x4& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                 __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+template <bool F16>
+__device__ __forceinline__ f32x16 mma_32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -141,6 +180,20 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same for lanes 0..7 only (128 bytes at lds_base).  The exec mask is set
+// and restored inside the one asm statement, so the compiler sees no divergent
+// region (a register spilled and reloaded under a partial exec mask would keep
+// stale values in the other lanes).
+__device__ __forceinline__ void dma16_lanes8(const void* src, uint32_t lds_base) {
+  uint64_t saved;
+  asm volatile(
+      "s_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xff\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b64 exec, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory", "m0");
+}
+
 // Device-coherent access to the split partials.  Partials are written and
 // read with the sc1 cache policy (coherent at device scope, as for agent-scope
 // atomic loads and stores), so a workgroup on another XCD sees them without a
@@ -188,7 +241,7 @@ __device__ __forceinline__ float wave_sum_16(float v) {
 // no LDS or barrier; more partials take a pass over the LSEs and then the O
 // slices kBatch partials at a time.  The arithmetic per item is the same
 // either way.
-template <int H, int NT>
+template <int H, int NT, bool F16>
 __device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int slot0, int n,
                                                 int tid) {
   constexpr int kItems = H * 64;  // (head, 8 columns)
@@ -201,7 +254,7 @@ __device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int 
     const int hd = e >> 6, col = (e & 63) * 8;
     bf16x8 v;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
+    for (int j = 0; j < 8; ++j) v[j] = to16<F16>(o8[j]);
     *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
     if ((e & 63) == 0) a.lse[(size_t)b * H + hd] = lse_v;
   };
@@ -311,7 +364,7 @@ constexpr int merge_bytes() {
 
 // HG here is the number of merge-slot columns: a call merges slot (ts, hg) ->
 // ts * HG + hg; `hblock` is the 16-head block of the output rows it writes.
-template <int H, int HG, int TS>
+template <int H, int HG, int TS, bool F16 = false>
 __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&acc)[32],
                                                  float m_run, float l_run, int b, int slot,
                                                  int hblock, int hg, int ts, int lane,
@@ -332,7 +385,7 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
       for (int cb = 0; cb < 32; ++cb) {
         bf16x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[cb][i] * inv);
+        for (int i = 0; i < 4; ++i) v[i] = to16<F16>(acc[cb][i] * inv);
         *reinterpret_cast<bf16x4*>(op + cb * 16 + 4 * (lane >> 4)) = v;
       }
       if (lane < 16) a.lse[orow] = lse_v;
@@ -399,7 +452,7 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
       if (slot < 0) {
         bf16x8 v;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = (__bf16)(o8[i] * inv);
+        for (int i = 0; i < 8; ++i) v[i] = to16<F16>(o8[i] * inv);
         *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
         if (ts == 0 && (e % (kCols / 8)) == 0) a.lse[(size_t)b * H + hd] = lse_v;
       } else {
@@ -422,7 +475,7 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
 
 // After every head block of a segment is written: the workgroup completing
 // the last chunk of a split request merges the request's partials.
-template <int H, int NT>
+template <int H, int NT, bool F16 = false>
 __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int slot, int split_req,
                                                int slot0, int nsplit, int tid, uint8_t* smem,
                                                int* s_last) {
@@ -441,7 +494,7 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int s
       *s_last = last;
     }
     lds_barrier();
-    if (*s_last) combine_request<H, NT>(a, b, slot0, nsplit, tid);
+    if (*s_last) combine_request<H, NT, F16>(a, b, slot0, nsplit, tid);
     lds_barrier();  // merge scratch free before the next segment's loads
   }
 }
@@ -818,7 +871,8 @@ struct StreamShape {
   static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
                                                                     : kMergeBytes;
   // 16-byte loads per lane per group: bf16 18; 8-bit ckv 8 + kpe 1 (8-bit) or 2 (bf16)
-  static constexpr int kLoads = KVT == 0 ? 18 : (KVT >= 3 ? 10 : 9);
+  static constexpr bool kCache16 = KVT == 0 || KVT == 5;  // bf16 or fp16 cache
+  static constexpr int kLoads = kCache16 ? 18 : (KVT == 3 || KVT == 4 ? 10 : 9);
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
@@ -852,6 +906,8 @@ template <int HB, int KVT, int NB>
 __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs a) {
   using S = StreamShape<HB, KVT, NB>;
   constexpr int H = S::kHeads;
+  constexpr bool kC16 = S::kCache16;
+  constexpr bool kF16 = KVT == 5;  // fp16 q, cache, P and O
   constexpr int TS = S::kWaves;
   constexpr int NL = S::kLoads;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
@@ -956,7 +1012,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       const int gs = t0 + 16 * (wave + TS * j);
       const int page = live ? ld_const(a.kv_indices + pbeg + (gs >> page_shift)) : 0;
       const size_t pbase = (size_t)page << page_shift;
-      if constexpr (KVT == 0) {
+      if constexpr (kC16) {
 #pragma unroll
         for (int rh = 0; rh < 2; ++rh) {
           const int r = rh * 8 + ld_r_lo;
@@ -979,7 +1035,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
           for (int cb = 0; cb < 4; ++cb)
             st[rh * 4 + cb] = *reinterpret_cast<const u32x4*>(cbase + cb * 128);
         }
-        if constexpr (KVT >= 3) {  // bf16 kpe rows, as in the bf16 layout
+        if constexpr (KVT == 3 || KVT == 4) {  // bf16 kpe rows, as in the bf16 layout
 #pragma unroll
           for (int rh = 0; rh < 2; ++rh) {
             const int r = rh * 8 + ld_r_lo;
@@ -1003,7 +1059,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     // PV if the group exists.
     auto consume = [&](int j, u32x4 (&st)[NL], f32x4& sc) __attribute__((always_inline)) {
       f32x4 sig = sc;
-      if constexpr (KVT == 0) {
+      if constexpr (kC16) {
 #pragma unroll
         for (int blk = 0; blk < 18; ++blk)
           *reinterpret_cast<u32x4*>(wbuf + blk * 1024 + lane * 16) = st[blk];
@@ -1016,7 +1072,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
           *reinterpret_cast<u32x4*>(wbuf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][1]) =
               codes_to_bf16<KVT>(st[u][2], st[u][3]);
         }
-        if constexpr (KVT >= 3) {
+        if constexpr (KVT == 3 || KVT == 4) {
 #pragma unroll
           for (int rh = 0; rh < 2; ++rh)
             *reinterpret_cast<u32x4*>(wbuf + (rh * 9 + 8) * 1024 + lane * 16) = st[8 + rh];
@@ -1030,7 +1086,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
 
       // scales of rows past the end are zeroed (NaN padding may sit there)
       const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
-      if constexpr (KVT != 0) {
+      if constexpr (!kC16) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sig[i] = (row0 + i < t1) ? sig[i] : 0.f;
       }
@@ -1059,9 +1115,9 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
 #pragma unroll
           for (int u = 0; u < 6; ++u) {
             // 644-byte record: the scale is ckv's, applied before the kpe steps
-            if constexpr (KVT >= 3)
+            if constexpr (KVT == 3 || KVT == 4)
               if (s0 + u == 16) sacc[hb] = sacc[hb] * sig;
-            sacc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[u], qf[u], sacc[hb], 0, 0, 0);
+            sacc[hb] = mma_16x16x32<kF16>(kf[u], qf[u], sacc[hb]);
           }
         }
       }
@@ -1094,7 +1150,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
         for (int i = 0; i < 4; ++i) {
           const float p = __builtin_amdgcn_exp2f(sacc[hb][i] - m_use);
           psum += p;
-          pb[i] = (__bf16)(KVT != 0 ? p * sig[i] : p);  // V = scale x codes
+          pb[i] = to16<kF16>(kC16 ? p : p * sig[i]);  // 8-bit: V = scale x codes
         }
         l_run[hb] += psum;
         pv[hb] = __builtin_bit_cast(s16x4, pb);
@@ -1115,7 +1171,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb)
             acc[hb][c8 + u] =
-                __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf[u], pv[hb], acc[hb][c8 + u], 0, 0, 0);
+                mma_16x16x16<kF16>(vf[u], pv[hb], acc[hb][c8 + u]);
       }
     };
 
@@ -1133,10 +1189,11 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb)
-      write_head_block<H, 1, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave, lane,
+      write_head_block<H, 1, TS, kF16>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave, lane,
                                  smem);
     if constexpr (MLA_STREAM_FUSED_MERGE)
-      finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
+      finish_segment<H, S::kThreads, kF16>(a, b, slot, split_req, slot0, nsplit, tid, smem,
+                                           &s_last);
   }
 }
 
@@ -1162,7 +1219,6 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
 // k = 8 g + j <-> token 16 ks + 8 (j / 4) + 4 g + j % 4 (g = l / 32); the V^T
 // A operand is gathered in the same token order by two transposing reads.
 // ---------------------------------------------------------------------------
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 
 // Multiply a 16-register MFMA accumulator held in AGPRs by s, in place, through
@@ -1194,11 +1250,20 @@ __device__ __forceinline__ void scale_agpr16(f32x16& acc, float s) {
 // compiler cannot move the 256 accumulator registers of the wide kernel into
 // VGPRs (which then spills the Q operands, and every spill reload waits for
 // the whole KV prefetch on vmcnt).  A and B are consumed when the MFMA issues;
-// chained MFMAs on the same accumulator need no wait states, and every read of
-// the accumulators by other instructions is preceded by agpr_settle() or by
-// the wait states in scale_agpr16.
+// chained MFMAs on the same accumulator need no wait states.  The compiler
+// does not know the latency of an MFMA written as assembly, so nothing may
+// read these accumulators (a v_accvgpr_read, also one the compiler would add
+// to move a block between registers) until enough wait states have passed:
+// agpr_settle() precedes the epilogue and scale_agpr16 has its own wait
+// states; inside the loop the kernel relies on the accumulators staying where
+// they are, which holds while the loop is spill-free (a CPU test scans the
+// compiled kernels for a read of an accumulator too soon after such an MFMA).
+template <bool F16 = false>
 __device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  if constexpr (F16)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
 // Wait states between the last MFMA writing AGPRs and VALU reads of them.
@@ -1220,18 +1285,19 @@ struct WideShape {
   static constexpr int kThreads = 256;
   static constexpr int kHeads = 128;
   static constexpr int kTile = 32;
-  static constexpr int kStages = KVT == 0 ? 4 : 3;
+  static constexpr bool kCache16 = KVT == 0 || KVT == 5;  // bf16 or fp16 cache
+  static constexpr int kStages = kCache16 ? 4 : 3;
   // QK k-steps whose Q^T operands stay in registers (8-bit: the kpe steps live
   // in LDS, to make room for the code conversion)
-  static constexpr int kQRegSteps = KVT == 0 ? 36 : 32;
+  static constexpr int kQRegSteps = kCache16 ? 36 : 32;
   static constexpr int kStageBytes = kTile * kRowBytes;              // 36 KiB bf16 tile
-  static constexpr bool kKpe16 = KVT >= 3;
+  static constexpr bool kKpe16 = KVT == 3 || KVT == 4;  // 644-byte record
   static constexpr int kCodeKpe = kTile * 512;                       // offsets in a code tile
   static constexpr int kCodeScale = kCodeKpe + kTile * 64 * (kKpe16 ? 2 : 1);
   static constexpr int kCodeBytes = kCodeScale + (kKpe16 ? 128 : 1024);  // 19 / 20.1 KiB
-  static constexpr int kDmaPerWave = KVT == 0 ? 9 : (kKpe16 ? 6 : 5);  // loads per tile
+  static constexpr int kDmaPerWave = kCache16 ? 9 : (kKpe16 ? 6 : 5);  // loads per tile
   static constexpr int kBf16Offset = kStages * kCodeBytes;           // 8-bit: the two bf16 tiles
-  static constexpr int kRingBytes = KVT == 0 ? kStages * kStageBytes
+  static constexpr int kRingBytes = kCache16 ? kStages * kStageBytes
                                              : kBf16Offset + 2 * kStageBytes;
   static constexpr int kQOffset = kRingBytes;                        // Q^T [wave][step][lane] x 16 B
   static constexpr int kPOffset = kQOffset + 4 * (36 - kQRegSteps) * 1024;  // P^T [wave][ks][lane]
@@ -1247,6 +1313,8 @@ template <int KVT, bool CAUSAL>
 __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a) {
   using S = WideShape<KVT>;
   constexpr int H = S::kHeads;
+  constexpr bool kC16 = S::kCache16;
+  constexpr bool kF16 = KVT == 5;  // fp16 q, cache, P and O
   constexpr int T = S::kTile;
   constexpr int NS = S::kStages;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
@@ -1342,7 +1410,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       const int pg[2] = {pg_next[0], pg_next[1]};
       tile_pages(k + 1);
       const int kc = min(k, ntiles - 1);
-      if constexpr (KVT == 0) {
+      if constexpr (kC16) {
         const int my_group = wave >> 1, my_half = wave & 1;
         const int gs = min(t0 + kc * T + 16 * my_group, last_group);
         const int r = my_half * 8 + ld_r_lo;
@@ -1392,11 +1460,10 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
               d < 16 ? a.ckv + row * 512 + off
                      : (d < dscale ? a.kpe + row * (S::kKpe16 ? 128 : 64) + off
                                    : reinterpret_cast<const uint8_t*>(a.kv_scale + row));
-          if (S::kKpe16 && d >= dscale) {
-            if (lane < 8) dma16(src, __builtin_amdgcn_readfirstlane(dst));  // 128 bytes
-          } else {
+          if (S::kKpe16 && d >= dscale)
+            dma16_lanes8(src, __builtin_amdgcn_readfirstlane(dst));  // 128 bytes
+          else
             dma16(src, __builtin_amdgcn_readfirstlane(dst));
-          }
         }
       }
     };
@@ -1435,7 +1502,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     };
 
     if (ntiles > 0) tile_pages(0);
-    if constexpr (KVT == 0) {
+    if constexpr (kC16) {
       for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
     } else {
       if (ntiles > 0)
@@ -1460,7 +1527,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       }
     }
     vm_wait_n<0>();
-    if constexpr (KVT != 0) {
+    if constexpr (!kC16) {
       if (ntiles > 0) {
         lds_barrier();  // code tile 0 of every wave
         convert_tile(0, smem + S::kBf16Offset);
@@ -1479,7 +1546,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 
     for (int it = 0; it < ntiles; ++it) {
       const uint8_t* stage;
-      if constexpr (KVT == 0) {
+      if constexpr (kC16) {
         const int later = min(NS - 2, ntiles - 1 - it);
         if (later >= 2)
           vm_wait_n<18>();
@@ -1545,7 +1612,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           const bf16x8 qv = s < QR ? qf[s < QR ? s : 0]
                                    : *reinterpret_cast<const LDS_AS bf16x8*>(
                                          (const LDS_AS uint8_t*)(qlds + (s - QR) * 1024));
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], qv, sacc, 0, 0, 0);
+          sacc = mma_32x32x16<kF16>(kf[u], qv, sacc);
         }
       }
 
@@ -1554,6 +1621,12 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       // probability (before P is rounded to bf16 for PV), the same as
       // dequantising the row first.
       if constexpr (KVT == 1 || KVT == 2) load_sig();
+      if constexpr (S::kKpe16) {
+        // read the scales again rather than keep them live through the kpe
+        // steps (the compiler barrier stops it from reusing the first read)
+        asm volatile("" ::: "memory");
+        load_sig();
+      }
       const int tlim = CAUSAL ? limit_s[32 * wave + l32] : t1;
       float tmax = -INFINITY;
 #pragma unroll
@@ -1584,8 +1657,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           const float e0 = __builtin_amdgcn_exp2f(sacc[r] - m_use);
           const float e1 = __builtin_amdgcn_exp2f(sacc[8 + r] - m_use);
           psum += e0 + e1;
-          p0[r] = (__bf16)(KVT != 0 ? e0 * sig[r] : e0);
-          p1[r] = (__bf16)(KVT != 0 ? e1 * sig[8 + r] : e1);
+          p0[r] = to16<kF16>(kC16 ? e0 : e0 * sig[r]);
+          p1[r] = to16<kF16>(kC16 ? e1 : e1 * sig[8 + r]);
         }
         l_run += psum;
         *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + 0) * 64 + lane) * 16) = p0;
@@ -1632,11 +1705,11 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             vf[4 + i] = a1[i];
           }
 #pragma unroll
-          for (int hb = 0; hb < 4; ++hb) mfma_agpr(acc[cb][hb], vf, pb[hb]);
+          for (int hb = 0; hb < 4; ++hb) mfma_agpr<kF16>(acc[cb][hb], vf, pb[hb]);
         }
       }
     }
-    if constexpr (KVT != 0) vm_wait_n<0>();  // the trailing re-loads have landed
+    if constexpr (!kC16) vm_wait_n<0>();  // the trailing re-loads have landed
     lds_barrier();  // ring, P^T and flags free
     agpr_settle();
 
@@ -1659,7 +1732,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           for (int q = 0; q < 4; ++q) {
             bf16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[cb][hb][4 * q + i] * inv[hb]);
+            for (int i = 0; i < 4; ++i) v[i] = to16<kF16>(acc[cb][hb][4 * q + i] * inv[hb]);
             *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * q) = v;
           }
       }
@@ -1738,7 +1811,7 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   }
   bf16x8 v;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) v[j] = (__bf16)o8[j];
+  for (int j = 0; j < 8; ++j) v[j] = a.o_fp16 ? to16<true>(o8[j]) : to16<false>(o8[j]);
   *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
   if (col == 0) a.lse[(size_t)b * H + hd] = lse_v;
 }
@@ -1919,6 +1992,13 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
     switch (heads) {
       case 16: MLA_STREAM(1, 4, MLA_H16_NB8);
       case 128: MLA_WIDE(4);
+      default: return 0;
+    }
+  }
+  if (kv_dtype == 5) {  // fp16: 32- and 64-wide requests run as 16-wide rows
+    switch (heads) {
+      case 16: MLA_STREAM(1, 5, 2);
+      case 128: MLA_WIDE(5);
       default: return 0;
     }
   }

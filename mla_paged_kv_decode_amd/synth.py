@@ -257,6 +257,11 @@ WORKLOADS = {
                                               kv_dtype=KV_INT8_KPE16, seed=5),
     "int8ckv_bf16kpe_b64_h128_l8192_p64": dict(batch=64, heads=128, kv_len=8192, page=64,
                                                kv_dtype=KV_INT8_KPE16, seed=5),
+    # fp16 inputs (cache, queries and output)
+    "fp16_b64_h16_l4096_p64": dict(batch=64, heads=16, kv_len=4096, page=64, kv_dtype=KV_FP16,
+                                   seed=2),
+    "fp16_b64_h128_l4096_p64": dict(batch=64, heads=128, kv_len=4096, page=64,
+                                    kv_dtype=KV_FP16, seed=3),
     # two queries per request (one speculative / next-token-prediction token)
     "mtp_b64_h16_q2_l4096_p64": dict(batch=64, heads=16, kv_len=4096, page=64, kv_dtype=KV_BF16,
                                      seed=6, qo_len=2),

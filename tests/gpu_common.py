@@ -15,11 +15,12 @@ COS_TOL, ABS_TOL, LSE_TOL = 1e-4, 2e-2, 1e-3
 def dev(inp):
     d = "cuda"
     t = {}
-    t["q_nope"] = torch.from_numpy(inp.q_nope.view(np.int16)).view(torch.bfloat16).to(d)
-    t["q_pe"] = torch.from_numpy(inp.q_pe.view(np.int16)).view(torch.bfloat16).to(d)
-    if inp.kv_dtype == synth.KV_BF16:
-        t["ckv"] = torch.from_numpy(inp.ckv.view(np.int16)).view(torch.bfloat16).to(d)
-        t["kpe"] = torch.from_numpy(inp.kpe.view(np.int16)).view(torch.bfloat16).to(d)
+    t16 = torch.float16 if inp.kv_dtype == synth.KV_FP16 else torch.bfloat16
+    t["q_nope"] = torch.from_numpy(inp.q_nope.view(np.int16)).view(t16).to(d)
+    t["q_pe"] = torch.from_numpy(inp.q_pe.view(np.int16)).view(t16).to(d)
+    if inp.kv_dtype in (synth.KV_BF16, synth.KV_FP16):
+        t["ckv"] = torch.from_numpy(inp.ckv.view(np.int16)).view(t16).to(d)
+        t["kpe"] = torch.from_numpy(inp.kpe.view(np.int16)).view(t16).to(d)
         t["kv_scale"] = None
     else:
         t["ckv"] = torch.from_numpy(inp.ckv).to(d)

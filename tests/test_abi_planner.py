@@ -194,7 +194,7 @@ def test_8bit_rejects_unserved_rows(lib):
         assert mla.Plan(ip, lp, 128, 16, mla.KV_INT8, num_cus=8, head_split=hs).info()[
             "head_split"] == hs
     with pytest.raises(mla.MlaError):
-        mla.Plan(ip, lp, 16, 16, 5, num_cus=8)
+        mla.Plan(ip, lp, 16, 16, 6, num_cus=8)
 
 
 def test_workspace_bound_covers_8bit_plans(lib):
@@ -267,6 +267,7 @@ def test_bad_head_split_rejected(lib):
     (128, 2, mla.KV_BF16, 128), (32, 3, mla.KV_BF16, 32), (16, 2, mla.KV_FP8_E4M3, 16),
     (16, 1, mla.KV_FP8_E4M3_KPE_BF16, 16), (128, 1, mla.KV_INT8_KPE_BF16, 128),
     (64, 1, mla.KV_FP8_E4M3_KPE_BF16, 16), (64, 2, mla.KV_INT8_KPE_BF16, 128),
+    (16, 1, mla.KV_FP16, 16), (32, 1, mla.KV_FP16, 16), (128, 1, mla.KV_FP16, 128),
     (64, 2, mla.KV_INT8, 128), (16, 6, mla.KV_INT8, 16), (128, 4, mla.KV_FP8_E4M3, 128)])
 def test_multiquery_rows(lib, heads, q, kvd, width):
     # the qo_len * heads query vectors of a request run as rows of the largest
@@ -301,7 +302,8 @@ def test_cache_append_rejects_bad_arguments(lib):
     # every check happens before any HIP call, so this runs without a GPU
     Pp = ctypes.c_void_p
     assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), -1, 0, Pp(1), Pp(1), None, None) == -1
-    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 5, Pp(1), Pp(1), None, None) == -2
+    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 6, Pp(1), Pp(1), None, None) == -2
+    assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 5, Pp(1), Pp(1), Pp(1), None) == -1
     assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, -1, Pp(1), Pp(1), None, None) == -2
     assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 3, Pp(1), Pp(1), None, None) == -1
     assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 1, Pp(1), Pp(1), None, None) == -1

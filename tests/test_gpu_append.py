@@ -36,18 +36,20 @@ def _tokens(n, seed, wide=False):
     return bits
 
 
-def _dev_bf16(bits):
-    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+def _dev_bf16(bits, fp16=False):
+    return torch.from_numpy(bits.view(np.int16)).view(
+        torch.float16 if fp16 else torch.bfloat16).cuda()
 
 
 def _cache(pages, P, kv_dtype, seed):
     rng = np.random.default_rng(seed)
     kpe16 = kv_dtype in (synth.KV_FP8_KPE16, synth.KV_INT8_KPE16)
-    if kv_dtype == synth.KV_BF16:
+    if kv_dtype in (synth.KV_BF16, synth.KV_FP16):
+        t16 = torch.float16 if kv_dtype == synth.KV_FP16 else torch.bfloat16
         ckv = torch.from_numpy(rng.integers(0, 65536, (pages, P, 512)).astype(np.uint16).view(
-            np.int16)).view(torch.bfloat16).cuda()
+            np.int16)).view(t16).cuda()
         kpe = torch.from_numpy(rng.integers(0, 65536, (pages, P, 64)).astype(np.uint16).view(
-            np.int16)).view(torch.bfloat16).cuda()
+            np.int16)).view(t16).cuda()
         return ckv, kpe, None
     ckv = torch.from_numpy(rng.integers(0, 256, (pages, P, 512)).astype(np.uint8)).cuda()
     if kpe16:
@@ -60,12 +62,12 @@ def _cache(pages, P, kv_dtype, seed):
 
 
 def _as_u(t):
-    return t.view(torch.int16).cpu().numpy().view(np.uint16) if t.dtype == torch.bfloat16 \
-        else t.cpu().numpy()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16) \
+        if t.dtype in (torch.bfloat16, torch.float16) else t.cpu().numpy()
 
 
 @pytest.mark.parametrize("kv_dtype", [synth.KV_BF16, synth.KV_FP8_E4M3, synth.KV_INT8,
-                                      synth.KV_FP8_KPE16, synth.KV_INT8_KPE16])
+                                      synth.KV_FP8_KPE16, synth.KV_INT8_KPE16, synth.KV_FP16])
 @pytest.mark.parametrize("n,wide", [(1, False), (37, False), (1000, True), (4099, False)])
 def test_append_matches_oracle(kv_dtype, n, wide):
     import mla_paged_kv_decode_amd as mla
@@ -77,7 +79,8 @@ def test_append_matches_oracle(kv_dtype, n, wide):
     ckv, kpe, sc = _cache(pages, P, kv_dtype, seed=n)
     before = [_as_u(ckv).copy(), _as_u(kpe).copy(), None if sc is None else sc.cpu().numpy()]
     print("case kv_dtype=%d n=%d" % (kv_dtype, n), flush=True)
-    mla.cache_append(_dev_bf16(bits[:, :512].copy()), _dev_bf16(bits[:, 512:].copy()),
+    f16 = kv_dtype == synth.KV_FP16  # a copy: any 16-bit pattern
+    mla.cache_append(_dev_bf16(bits[:, :512].copy(), f16), _dev_bf16(bits[:, 512:].copy(), f16),
                      torch.from_numpy(slots).cuda(), ckv, kpe, kv_dtype, sc)
     torch.cuda.synchronize()
     got_c = _as_u(ckv).reshape(pages * P, 512)
@@ -85,7 +88,7 @@ def test_append_matches_oracle(kv_dtype, n, wide):
     exp_c = before[0].reshape(pages * P, 512).copy()
     exp_k = before[1].reshape(pages * P, 64).copy()
     live = slots >= 0
-    if kv_dtype == synth.KV_BF16:
+    if kv_dtype in (synth.KV_BF16, synth.KV_FP16):
         exp_c[slots[live]] = bits[live, :512]
         exp_k[slots[live]] = bits[live, 512:]
     else:

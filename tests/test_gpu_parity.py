@@ -305,3 +305,38 @@ def test_score_jump_rescales(kv_dtype, heads, factor):
     check(o, lse, *ref(inp))
     o2, lse2 = host(*gpu_run(inp, force_splits=3))
     check(o2, lse2, *ref(inp))
+
+
+# ---- fp16 inputs (fp16 cache, queries and output) ---------------------------
+
+
+@pytest.mark.parametrize("heads", [16, 32, 64, 128])
+@pytest.mark.parametrize("page", [16, 64])
+def test_fp16_ragged_lengths(heads, page):
+    inp = synth.make_inputs(RAGGED, heads, page, synth.KV_FP16, seed=1100 + heads + page,
+                            poison=True, extra_pages=5)
+    print("case fp16 heads=%d page=%d" % (heads, page), flush=True)
+    o, lse = gpu_run(inp)
+    assert o.dtype == torch.float16
+    check(*host(o, lse), *ref(inp))
+
+
+@pytest.mark.parametrize("heads,splits", [(16, 3), (128, 2), (64, 5)])
+def test_fp16_forced_splits_and_queries(heads, splits):
+    inp = synth.make_inputs([700, 64, 1, 1500, 0, 129], heads, 16, synth.KV_FP16,
+                            seed=1200 + splits, poison=True, qo_len=2)
+    print("case fp16 heads=%d splits=%d qo_len=2" % (heads, splits), flush=True)
+    o, lse = host(*gpu_run(inp, force_splits=splits))
+    check(o, lse, *ref(inp))
+
+
+@pytest.mark.parametrize("name", ["fp16_b64_h16_l4096_p64", "fp16_b64_h128_l4096_p64"])
+def test_fp16_full_workloads_sampled(name):
+    inp = synth.make_workload(name, poison=True)
+    print("workload", name, flush=True)
+    o, lse = host(*gpu_run(inp))
+    B, H = inp.batch, inp.num_heads
+    rng = np.random.default_rng(6)
+    rows = np.unique(np.concatenate([rng.choice(B * H, 96, replace=False), [0, B * H - 1]]))
+    o_ref, lse_ref = ref(inp, rows=rows.astype(np.int32))
+    check(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)

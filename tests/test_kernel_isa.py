@@ -1,0 +1,119 @@
+"""CPU checks of the compiled gfx950 decode kernels (device assembly from hipcc).
+
+The 128-head kernel issues its PV MFMAs as inline assembly with the
+accumulators pinned to AGPRs.  The compiler does not know the latency of an
+MFMA it did not emit, so it inserts no wait states before a later read of
+those AGPRs; a read it adds on its own (a copy of an accumulator block
+between registers, which happens when the loop runs short of registers)
+would then see the value from before the MFMA.  This test compiles the
+kernels and fails if any v_accvgpr_read / v_accvgpr_mov of an AGPR written by
+such an MFMA comes before 18 wait states have passed (the 32x32 MFMA needs
+fewer; 18 leaves room), counting s_nop N as N + 1 and stopping at control
+flow.
+"""
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HIPCC = "/opt/rocm/bin/hipcc"
+WAIT_STATES = 18
+
+
+@pytest.fixture(scope="module")
+def device_asm():
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc missing")
+    tmp = tempfile.mkdtemp()
+    try:
+        out = os.path.join(tmp, "kernels.s")
+        cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-S", "--cuda-device-only",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Wno-unused-command-line-argument", "-Wno-inline-asm",
+               "-I", os.path.join(ROOT, "include"),
+               "-I", os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc"),
+               os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", "kernels.hip"), "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True)
+        yield open(out).read()
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+
+
+def _functions(asm):
+    """(name, instruction list) per kernel; instructions carry an in-asm flag."""
+    funcs = {}
+    name = None
+    in_asm = False
+    for line in asm.split("\n"):
+        m = re.match(r"^(_Z\S+):", line)
+        if m:
+            name = m.group(1)
+            funcs[name] = []
+            in_asm = False
+            continue
+        if name is None:
+            continue
+        t = line.strip()
+        if t.startswith(";;#ASMSTART"):
+            in_asm = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            in_asm = False
+            continue
+        if t == "s_endpgm":
+            funcs[name].append((t, in_asm))
+            name = None
+            continue
+        if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
+            continue
+        funcs[name].append((t, in_asm))
+    return funcs
+
+
+def _early_agpr_reads(instrs):
+    bad = []
+    for k, (t, asm) in enumerate(instrs):
+        m = re.match(r"v_mfma_f32_32x32x16_\w+ a\[(\d+):(\d+)\]", t)
+        if not (m and asm):
+            continue
+        lo, hi = int(m.group(1)), int(m.group(2))
+        ws = 0
+        for t2, _ in instrs[k + 1:]:
+            if ws >= WAIT_STATES or re.match(r"s_(cbranch|branch|setpc|swappc|endpgm)", t2):
+                break
+            r = re.match(r"v_accvgpr_(?:read_b32|mov_b32) \S+, a(\d+)", t2)
+            if r and lo <= int(r.group(1)) <= hi:
+                bad.append((t, t2, ws))
+                break
+            n = re.match(r"s_nop (\d+)", t2)
+            ws += int(n.group(1)) + 1 if n else 1
+    return bad
+
+
+def test_compiled_kernels_present(device_asm):
+    funcs = _functions(device_asm)
+    wide = [f for f in funcs if "mla_decode_wide_kernel" in f]
+    assert len(wide) == 12  # 6 cache layouts x causal / not
+    assert any("mla_decode_stream_kernel" in f for f in funcs)
+
+
+def test_no_accumulator_read_before_asm_mfma_completes(device_asm):
+    funcs = _functions(device_asm)
+    bad = {f: _early_agpr_reads(ins) for f, ins in funcs.items() if "mla_" in f}
+    bad = {f: b for f, b in bad.items() if b}
+    assert not bad, bad
+
+
+def test_scanner_flags_a_planted_early_read():
+    # the check itself: an AGPR read right after an asm MFMA is found, one after
+    # enough s_nop wait states is not
+    early = [("v_mfma_f32_32x32x16_bf16 a[16:31], v[0:3], v[4:7], a[16:31]", True),
+             ("s_add_i32 s1, s1, 1", False), ("v_accvgpr_read_b32 v0, a16", False)]
+    late = [early[0], ("s_nop 7", True), ("s_nop 7", True), ("s_nop 3", True), early[2]]
+    other = [early[0], ("v_accvgpr_read_b32 v0, a32", False)]
+    assert _early_agpr_reads(early) and not _early_agpr_reads(late)
+    assert not _early_agpr_reads(other)
