@@ -1252,16 +1252,24 @@ __device__ __forceinline__ void scale_agpr16(f32x16& acc, float s) {
 // the whole KV prefetch on vmcnt).  A and B are consumed when the MFMA issues;
 // chained MFMAs on the same accumulator need no wait states.  The compiler
 // does not know the latency of an MFMA written as assembly, so nothing may
-// read these accumulators (a v_accvgpr_read, also one the compiler would add
-// to move a block between registers) until enough wait states have passed:
-// agpr_settle() precedes the epilogue and scale_agpr16 has its own wait
-// states; inside the loop the kernel relies on the accumulators staying where
-// they are, which holds while the loop is spill-free (a CPU test scans the
-// compiled kernels for a read of an accumulator too soon after such an MFMA).
-template <bool F16 = false>
+// read or write these accumulators (a v_accvgpr_read, also one the compiler
+// adds on its own to copy or spill a block, which it may place on any path
+// leaving the tile loop) until enough wait states have passed.  The last MFMA
+// of each tile therefore carries 32 wait states in the same statement
+// (SETTLE), so no instruction can be placed between it and them; within a
+// tile's MFMA sequence the loop stays spill-free, and a CPU test scans every
+// path of the compiled kernels for an accumulator access too soon after such
+// an MFMA.
+template <bool F16 = false, bool SETTLE = false>
 __device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
-  if constexpr (F16)
+  if constexpr (F16 && SETTLE)
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc) : "v"(a), "v"(b));
+  else if constexpr (F16)
     asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  else if constexpr (SETTLE)
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+                 : "+a"(acc) : "v"(a), "v"(b));
   else
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
@@ -1591,6 +1599,18 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       f32x16 sacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      // K operands of the 4 k-steps of group g (1 KiB block g of the tile);
+      // group g + 1 is read while the MFMAs of group g issue (not in the
+      // 644-byte variant, whose loop has no 16 registers to spare)
+      constexpr bool kPrefetchK = !S::kKpe16;
+      auto read_k = [&](int g, bf16x8 (&kf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)(stage + g * 1024 + qk_off[u]));
+      };
+      bf16x8 kcur[4];
+      if constexpr (kPrefetchK) read_k(0, kcur);
 #pragma unroll
       for (int s0 = 0; s0 < 36; s0 += 4) {
         if constexpr (S::kKpe16) {
@@ -1601,18 +1621,20 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             for (int r = 0; r < 16; ++r) sacc[r] *= sig[r];
           }
         }
-        bf16x8 kf[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
-              (const LDS_AS uint8_t*)(stage + (s0 >> 2) * 1024 + qk_off[u]));
+        if constexpr (!kPrefetchK) read_k(s0 >> 2, kcur);
+        bf16x8 knext[4];
+        if (kPrefetchK && s0 + 4 < 36) read_k((s0 >> 2) + 1, knext);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int s = s0 + u;
           const bf16x8 qv = s < QR ? qf[s < QR ? s : 0]
                                    : *reinterpret_cast<const LDS_AS bf16x8*>(
                                          (const LDS_AS uint8_t*)(qlds + (s - QR) * 1024));
-          sacc = mma_32x32x16<kF16>(kf[u], qv, sacc);
+          sacc = mma_32x32x16<kF16>(kcur[u], qv, sacc);
+        }
+        if (kPrefetchK && s0 + 4 < 36) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) kcur[u] = knext[u];
         }
       }
 
@@ -1681,32 +1703,43 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           }
         }
       }
+      // V^T operand of step i = (ks, cb): two transposing reads; the operand of
+      // the next step is read while the MFMAs of this one issue
+      auto read_v = [&](int i) __attribute__((always_inline)) {
+        const uint8_t* vb = stage + (i >> 2) * kGroupBytes + (2 * wave + ((i & 3) >> 1)) * 1024;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS s16x4*)((LDS_AS uint8_t*)(vb + pv_off[0][i & 1])));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS s16x4*)((LDS_AS uint8_t*)(vb + pv_off[1][i & 1])));
+        const bf16x4 a0 = __builtin_bit_cast(bf16x4, v0);
+        const bf16x4 a1 = __builtin_bit_cast(bf16x4, v1);
+        bf16x8 vf;
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        bf16x8 pb[4];
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-          pb[hb] = *reinterpret_cast<const LDS_AS bf16x8*>(
-              (const LDS_AS uint8_t*)(pbuf + ((hb * 2 + ks) * 64 + lane) * 16));
-        const uint8_t* vbase = stage + ks * kGroupBytes + (2 * wave) * 1024;
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          const uint8_t* vb = vbase + (cb >> 1) * 1024;
-          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_AS s16x4*)((LDS_AS uint8_t*)(vb + pv_off[0][cb & 1])));
-          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_AS s16x4*)((LDS_AS uint8_t*)(vb + pv_off[1][cb & 1])));
-          const bf16x4 a0 = __builtin_bit_cast(bf16x4, v0);
-          const bf16x4 a1 = __builtin_bit_cast(bf16x4, v1);
-          bf16x8 vf;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            vf[i] = a0[i];
-            vf[4 + i] = a1[i];
-          }
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) mfma_agpr<kF16>(acc[cb][hb], vf, pb[hb]);
+        for (int j = 0; j < 4; ++j) {
+          vf[j] = a0[j];
+          vf[4 + j] = a1[j];
         }
+        return vf;
+      };
+      bf16x8 pb[4];
+      bf16x8 vcur = read_v(0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ks = i >> 2, cb = i & 3;
+        if (cb == 0) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+            pb[hb] = *reinterpret_cast<const LDS_AS bf16x8*>(
+                (const LDS_AS uint8_t*)(pbuf + ((hb * 2 + ks) * 64 + lane) * 16));
+        }
+        const bf16x8 vnext = read_v(i < 7 ? i + 1 : i);
+#pragma unroll
+        for (int hb = 0; hb < 3; ++hb) mfma_agpr<kF16>(acc[cb][hb], vcur, pb[hb]);
+        if (i < 7)
+          mfma_agpr<kF16>(acc[cb][3], vcur, pb[3]);
+        else
+          mfma_agpr<kF16, true>(acc[cb][3], vcur, pb[3]);
+        vcur = vnext;
       }
     }
     if constexpr (!kC16) vm_wait_n<0>();  // the trailing re-loads have landed

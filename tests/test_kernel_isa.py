@@ -6,10 +6,11 @@ MFMA it did not emit, so it inserts no wait states before a later read of
 those AGPRs; a read it adds on its own (a copy of an accumulator block
 between registers, which happens when the loop runs short of registers)
 would then see the value from before the MFMA.  This test compiles the
-kernels and fails if any v_accvgpr_read / v_accvgpr_mov of an AGPR written by
-such an MFMA comes before 18 wait states have passed (the 32x32 MFMA needs
-fewer; 18 leaves room), counting s_nop N as N + 1 and stopping at control
-flow.
+kernels and fails if any instruction other than an MFMA that names an AGPR
+written by such an MFMA comes before 18 wait states have passed (the 32x32 MFMA needs
+fewer; 18 leaves room), counting s_nop N as N + 1 and following every branch
+(the compiler places such copies and spills on the paths that leave the loop
+as readily as inside it).
 """
 import os
 import re
@@ -44,7 +45,8 @@ def device_asm():
 
 
 def _functions(asm):
-    """(name, instruction list) per kernel; instructions carry an in-asm flag."""
+    """name -> (instructions, labels): instructions carry an in-asm flag, labels
+    map a branch target to the index of the instruction that follows it."""
     funcs = {}
     name = None
     in_asm = False
@@ -52,11 +54,12 @@ def _functions(asm):
         m = re.match(r"^(_Z\S+):", line)
         if m:
             name = m.group(1)
-            funcs[name] = []
+            funcs[name] = ([], {})
             in_asm = False
             continue
         if name is None:
             continue
+        instrs, labels = funcs[name]
         t = line.strip()
         if t.startswith(";;#ASMSTART"):
             in_asm = True
@@ -64,33 +67,63 @@ def _functions(asm):
         if t.startswith(";;#ASMEND"):
             in_asm = False
             continue
+        lb = re.match(r"^(\.LBB\d+_\d+):", t)
+        if lb:
+            labels[lb.group(1)] = len(instrs)
+            continue
         if t == "s_endpgm":
-            funcs[name].append((t, in_asm))
+            instrs.append((t, in_asm))
             name = None
             continue
         if not t or t.startswith(";") or t.startswith(".") or t.endswith(":"):
             continue
-        funcs[name].append((t, in_asm))
+        instrs.append((t, in_asm))
     return funcs
 
 
-def _early_agpr_reads(instrs):
+def _agprs(t):
+    regs = set()
+    for m in re.finditer(r"\ba\[(\d+):(\d+)\]", t):
+        regs |= set(range(int(m.group(1)), int(m.group(2)) + 1))
+    for m in re.finditer(r"\ba(\d+)\b", t):
+        regs.add(int(m.group(1)))
+    return regs
+
+
+def _first_touch(instrs, labels, j, dst, ws, seen):
+    """First non-MFMA instruction on any path from j that names an AGPR of dst
+    before WAIT_STATES have passed (s_nop N counts N + 1), or None."""
+    while j < len(instrs) and ws < WAIT_STATES:
+        if (j, ws) in seen:
+            return None
+        seen.add((j, ws))
+        t = instrs[j][0]
+        if not t.startswith("v_mfma") and _agprs(t) & dst:
+            return (t, ws)
+        n = re.match(r"s_nop (\d+)", t)
+        ws += int(n.group(1)) + 1 if n else 1
+        br = re.match(r"s_(cbranch_\w+|branch) (\.LBB\d+_\d+)", t)
+        if br:
+            hit = _first_touch(instrs, labels, labels[br.group(2)], dst, ws, seen)
+            if hit or br.group(1) == "branch":
+                return hit
+        if re.match(r"s_(setpc|swappc|endpgm)", t):
+            return None
+        j += 1
+    return None
+
+
+def _early_agpr_reads(instrs, labels=None):
+    labels = labels or {}
     bad = []
     for k, (t, asm) in enumerate(instrs):
         m = re.match(r"v_mfma_f32_32x32x16_\w+ a\[(\d+):(\d+)\]", t)
         if not (m and asm):
             continue
-        lo, hi = int(m.group(1)), int(m.group(2))
-        ws = 0
-        for t2, _ in instrs[k + 1:]:
-            if ws >= WAIT_STATES or re.match(r"s_(cbranch|branch|setpc|swappc|endpgm)", t2):
-                break
-            r = re.match(r"v_accvgpr_(?:read_b32|mov_b32) \S+, a(\d+)", t2)
-            if r and lo <= int(r.group(1)) <= hi:
-                bad.append((t, t2, ws))
-                break
-            n = re.match(r"s_nop (\d+)", t2)
-            ws += int(n.group(1)) + 1 if n else 1
+        dst = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        hit = _first_touch(instrs, labels, k + 1, dst, 0, set())
+        if hit:
+            bad.append((t,) + hit)
     return bad
 
 
@@ -103,17 +136,26 @@ def test_compiled_kernels_present(device_asm):
 
 def test_no_accumulator_read_before_asm_mfma_completes(device_asm):
     funcs = _functions(device_asm)
-    bad = {f: _early_agpr_reads(ins) for f, ins in funcs.items() if "mla_" in f}
+    bad = {f: _early_agpr_reads(*fl) for f, fl in funcs.items() if "mla_" in f}
     bad = {f: b for f, b in bad.items() if b}
     assert not bad, bad
 
 
 def test_scanner_flags_a_planted_early_read():
     # the check itself: an AGPR read right after an asm MFMA is found, one after
-    # enough s_nop wait states is not
+    # enough s_nop wait states is not, and a read behind a branch is followed
     early = [("v_mfma_f32_32x32x16_bf16 a[16:31], v[0:3], v[4:7], a[16:31]", True),
              ("s_add_i32 s1, s1, 1", False), ("v_accvgpr_read_b32 v0, a16", False)]
     late = [early[0], ("s_nop 7", True), ("s_nop 7", True), ("s_nop 3", True), early[2]]
     other = [early[0], ("v_accvgpr_read_b32 v0, a32", False)]
     assert _early_agpr_reads(early) and not _early_agpr_reads(late)
     assert not _early_agpr_reads(other)
+    # loop exit: the read sits behind a conditional branch, past an s_endpgm
+    branched = [early[0], ("s_cbranch_scc1 .LBB0_9", False), ("s_endpgm", False),
+                ("scratch_store_dword off, v0, off", False), ("v_accvgpr_read_b32 v0, a22", False)]
+    assert _early_agpr_reads(branched, {".LBB0_9": 4})
+    assert not _early_agpr_reads(branched[:3], {".LBB0_9": 3})
+    # a write of the accumulator (zeroing it for the next segment) counts too
+    zero = [early[0], ("s_branch .LBB0_2", False), ("s_endpgm", False),
+            ("v_accvgpr_write_b32 a31, 0", False)]
+    assert _early_agpr_reads(zero, {".LBB0_2": 3})
