@@ -1274,6 +1274,38 @@ __device__ __forceinline__ void mfma_agpr(f32x16& acc, const bf16x8& a, const bf
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
 
+// S (+)= A B with the accumulator in VGPRs, as assembly.  Were the QK MFMA of
+// the wide kernel a builtin, the compiler would give its accumulator AGPRs
+// (it takes the AGPR form once a kernel uses AGPRs), which O^T fills: every
+// tile would then copy an O^T block out to VGPRs and back around QK.  Being
+// volatile, these statements also keep the LDS reads written before them
+// ahead of them (the scheduler would otherwise sink each operand read down to
+// its MFMA, leaving the LDS latency exposed at every k-step).  INIT: C = 0.
+// SETTLE: the MFMA is followed, in the same statement, by the wait states
+// that must pass before any other instruction reads or writes its result.
+#define MLA_SETTLE_NOPS "\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7"
+#define MLA_MFMA_V(OP, TAIL)                                                   \
+  if constexpr (INIT)                                                          \
+    asm volatile(OP " %0, %1, %2, 0" TAIL : "=&v"(acc) : "v"(a), "v"(b));     \
+  else if constexpr (AFTER_VALU)                                               \
+    asm volatile("s_nop 4\n\t" OP " %0, %1, %2, %0" TAIL : "+v"(acc) : "v"(a), "v"(b)); \
+  else                                                                         \
+    asm volatile(OP " %0, %1, %2, %0" TAIL : "+v"(acc) : "v"(a), "v"(b));
+// AFTER_VALU: C was last written by a VALU instruction (wait states first).
+template <bool F16, bool INIT, bool SETTLE, bool AFTER_VALU = false>
+__device__ __forceinline__ void mfma_vgpr(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  if constexpr (F16 && SETTLE) {
+    MLA_MFMA_V("v_mfma_f32_32x32x16_f16", MLA_SETTLE_NOPS)
+  } else if constexpr (F16) {
+    MLA_MFMA_V("v_mfma_f32_32x32x16_f16", "")
+  } else if constexpr (SETTLE) {
+    MLA_MFMA_V("v_mfma_f32_32x32x16_bf16", MLA_SETTLE_NOPS)
+  } else {
+    MLA_MFMA_V("v_mfma_f32_32x32x16_bf16", "")
+  }
+}
+#undef MLA_MFMA_V
+
 // Wait states between the last MFMA writing AGPRs and VALU reads of them.
 __device__ __forceinline__ void agpr_settle() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
@@ -1596,21 +1628,28 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       };
 
       // ---- QK: S^T[32 tokens][32 heads of this wave] ------------------------
+      // Operands of the 4 k-steps of group g (1 KiB block g of the tile; for
+      // k-steps past the register-resident Q, that Q operand from LDS too):
+      // with a 16-bit cache, group g + 1 is read before the MFMAs of group g
+      // issue.  The chain
+      // accumulates in VGPRs; its last MFMA (and, in the 644-byte variant, the
+      // last ckv step, which the token scale then multiplies) settles.
       f32x16 sacc;
+      auto read_k = [&](int g, bf16x8 (&kf)[4], bf16x8 (&qx)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-      // K operands of the 4 k-steps of group g (1 KiB block g of the tile);
-      // group g + 1 is read while the MFMAs of group g issue (not in the
-      // 644-byte variant, whose loop has no 16 registers to spare)
-      constexpr bool kPrefetchK = !S::kKpe16;
-      auto read_k = [&](int g, bf16x8 (&kf)[4]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
+        for (int u = 0; u < 4; ++u) {
           kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
               (const LDS_AS uint8_t*)(stage + g * 1024 + qk_off[u]));
+          if (4 * g + u >= QR)
+            qx[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+                (const LDS_AS uint8_t*)(qlds + (4 * g + u - QR) * 1024));
+        }
       };
-      bf16x8 kcur[4];
-      if constexpr (kPrefetchK) read_k(0, kcur);
+      // (8-bit caches: a group's operands are read just before its MFMAs; the
+      // registers for a second group are not there)
+      constexpr bool kPrefetchK = S::kCache16;
+      bf16x8 kcur[4], qcur[4];
+      if constexpr (kPrefetchK) read_k(0, kcur, qcur);
 #pragma unroll
       for (int s0 = 0; s0 < 36; s0 += 4) {
         if constexpr (S::kKpe16) {
@@ -1621,20 +1660,28 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             for (int r = 0; r < 16; ++r) sacc[r] *= sig[r];
           }
         }
-        if constexpr (!kPrefetchK) read_k(s0 >> 2, kcur);
-        bf16x8 knext[4];
-        if (kPrefetchK && s0 + 4 < 36) read_k((s0 >> 2) + 1, knext);
+        if constexpr (!kPrefetchK) read_k(s0 >> 2, kcur, qcur);
+        bf16x8 knext[4], qnext[4];
+        if (kPrefetchK && s0 + 4 < 36) read_k((s0 >> 2) + 1, knext, qnext);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int s = s0 + u;
-          const bf16x8 qv = s < QR ? qf[s < QR ? s : 0]
-                                   : *reinterpret_cast<const LDS_AS bf16x8*>(
-                                         (const LDS_AS uint8_t*)(qlds + (s - QR) * 1024));
-          sacc = mma_32x32x16<kF16>(kcur[u], qv, sacc);
+          const bf16x8 qv = s < QR ? qf[s < QR ? s : 0] : qcur[u];
+          if (s == 0)
+            mfma_vgpr<kF16, true, false>(sacc, kcur[u], qv);
+          else if (S::kKpe16 && s == 32)
+            mfma_vgpr<kF16, false, false, true>(sacc, kcur[u], qv);
+          else if (s == 35 || (S::kKpe16 && s == 31))
+            mfma_vgpr<kF16, false, true>(sacc, kcur[u], qv);
+          else
+            mfma_vgpr<kF16, false, false>(sacc, kcur[u], qv);
         }
         if (kPrefetchK && s0 + 4 < 36) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) kcur[u] = knext[u];
+          for (int u = 0; u < 4; ++u) {
+            kcur[u] = knext[u];
+            qcur[u] = qnext[u];
+          }
         }
       }
 

@@ -50,7 +50,9 @@ def counter_avgs(d, counter):
 
 def short(name):
     m = re.search(r"(mla_[a-z0-9_]+_kernel(<[^>]*>)?)", name)
-    return m.group(1) if m else name
+    if m:
+        return m.group(1)
+    return name if len(name) <= 100 else name[:100] + "..."
 
 
 def main():

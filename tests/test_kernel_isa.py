@@ -1,16 +1,16 @@
 """CPU checks of the compiled gfx950 decode kernels (device assembly from hipcc).
 
-The 128-head kernel issues its PV MFMAs as inline assembly with the
-accumulators pinned to AGPRs.  The compiler does not know the latency of an
-MFMA it did not emit, so it inserts no wait states before a later read of
-those AGPRs; a read it adds on its own (a copy of an accumulator block
-between registers, which happens when the loop runs short of registers)
-would then see the value from before the MFMA.  This test compiles the
-kernels and fails if any instruction other than an MFMA that names an AGPR
-written by such an MFMA comes before 18 wait states have passed (the 32x32 MFMA needs
-fewer; 18 leaves room), counting s_nop N as N + 1 and following every branch
-(the compiler places such copies and spills on the paths that leave the loop
-as readily as inside it).
+The 128-head kernel issues its MFMAs as inline assembly: PV with the O^T
+accumulators pinned to AGPRs, QK with the scores in VGPRs.  The compiler does
+not know the latency of an MFMA it did not emit, so it inserts no wait states
+before a later read of those registers; a read it adds on its own (a copy of
+an accumulator block between registers, which happens when the loop runs short
+of registers) would then see the value from before the MFMA.  This test
+compiles the kernels and fails if any instruction other than an MFMA that
+names a register written by such an MFMA comes before 18 wait states have
+passed (the 32x32 MFMA needs fewer; 18 leaves room), counting s_nop N as N + 1
+and following every branch (the compiler places such copies and spills on the
+paths that leave the loop as readily as inside it).
 """
 import os
 import re
@@ -81,30 +81,32 @@ def _functions(asm):
     return funcs
 
 
-def _agprs(t):
+def _regs(t, kind):
+    """Registers of one file ('a' or 'v') that instruction t names."""
     regs = set()
-    for m in re.finditer(r"\ba\[(\d+):(\d+)\]", t):
+    for m in re.finditer(r"\b%s\[(\d+):(\d+)\]" % kind, t):
         regs |= set(range(int(m.group(1)), int(m.group(2)) + 1))
-    for m in re.finditer(r"\ba(\d+)\b", t):
+    for m in re.finditer(r"\b%s(\d+)\b" % kind, t):
         regs.add(int(m.group(1)))
     return regs
 
 
-def _first_touch(instrs, labels, j, dst, ws, seen):
-    """First non-MFMA instruction on any path from j that names an AGPR of dst
-    before WAIT_STATES have passed (s_nop N counts N + 1), or None."""
+def _first_touch(instrs, labels, j, kind, dst, ws, seen):
+    """First non-MFMA instruction on any path from j that names a register of
+    dst (file `kind`) before WAIT_STATES have passed (s_nop N counts N + 1), or
+    None."""
     while j < len(instrs) and ws < WAIT_STATES:
         if (j, ws) in seen:
             return None
         seen.add((j, ws))
         t = instrs[j][0]
-        if not t.startswith("v_mfma") and _agprs(t) & dst:
+        if not t.startswith("v_mfma") and _regs(t, kind) & dst:
             return (t, ws)
         n = re.match(r"s_nop (\d+)", t)
         ws += int(n.group(1)) + 1 if n else 1
         br = re.match(r"s_(cbranch_\w+|branch) (\.LBB\d+_\d+)", t)
         if br:
-            hit = _first_touch(instrs, labels, labels[br.group(2)], dst, ws, seen)
+            hit = _first_touch(instrs, labels, labels[br.group(2)], kind, dst, ws, seen)
             if hit or br.group(1) == "branch":
                 return hit
         if re.match(r"s_(setpc|swappc|endpgm)", t):
@@ -117,11 +119,11 @@ def _early_agpr_reads(instrs, labels=None):
     labels = labels or {}
     bad = []
     for k, (t, asm) in enumerate(instrs):
-        m = re.match(r"v_mfma_f32_32x32x16_\w+ a\[(\d+):(\d+)\]", t)
+        m = re.match(r"v_mfma_f32_32x32x16_\w+ ([av])\[(\d+):(\d+)\]", t)
         if not (m and asm):
             continue
-        dst = set(range(int(m.group(1)), int(m.group(2)) + 1))
-        hit = _first_touch(instrs, labels, k + 1, dst, 0, set())
+        dst = set(range(int(m.group(2)), int(m.group(3)) + 1))
+        hit = _first_touch(instrs, labels, k + 1, m.group(1), dst, 0, set())
         if hit:
             bad.append((t,) + hit)
     return bad
@@ -159,3 +161,9 @@ def test_scanner_flags_a_planted_early_read():
     zero = [early[0], ("s_branch .LBB0_2", False), ("s_endpgm", False),
             ("v_accvgpr_write_b32 a31, 0", False)]
     assert _early_agpr_reads(zero, {".LBB0_2": 3})
+    # an accumulator in VGPRs: a VALU read of the scores too soon is found, one
+    # of another register is not
+    vform = [("v_mfma_f32_32x32x16_bf16 v[32:47], v[0:3], v[4:7], v[32:47]", True),
+             ("v_max_f32_e32 v48, v40, v48", False)]
+    assert _early_agpr_reads(vform)
+    assert not _early_agpr_reads([vform[0], ("v_max_f32_e32 v48, v30, v48", False)])
