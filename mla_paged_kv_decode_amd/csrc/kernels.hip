@@ -1697,14 +1697,28 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         load_sig();
       }
       const int tlim = CAUSAL ? limit_s[32 * wave + l32] : t1;
+      // the whole tile visible to every head of the wave (all tiles but the
+      // last few): no per-token mask (16-bit caches; the 8-bit loop has no
+      // registers for a second copy of this code)
+      const bool full = kC16 && (CAUSAL ? __builtin_amdgcn_ballot_w64(tile_start + T > tlim) == 0
+                                        : tile_start + T <= t1);
       float tmax = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
-        const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
-        const float x = tok < tlim ? raw * a.scale_log2 : -INFINITY;
-        sacc[r] = x;
-        tmax = fmaxf(tmax, x);
+        for (int r = 0; r < 16; ++r) {
+          const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
+          sacc[r] = raw * a.scale_log2;
+          tmax = fmaxf(tmax, sacc[r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
+          const float x = tok < tlim ? raw * a.scale_log2 : -INFINITY;
+          sacc[r] = x;
+          tmax = fmaxf(tmax, x);
+        }
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0) {
@@ -1736,22 +1750,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       lds_barrier();  // P^T and the rescale factors of every wave are in LDS
 
       // ---- PV: O^T[128 w + c][h] += V^T[c][t] P^T[t][h] ---------------------
-      {
-        const u32x4 fl = *reinterpret_cast<const u32x4*>(flags);
-        const unsigned any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
-        if (it > 0 && any != 0) {
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) {
-            if (__builtin_amdgcn_readfirstlane(fl[hb]) != 0) {
-              const float al = alpha_s[32 * hb + l32];
-#pragma unroll
-              for (int cb = 0; cb < 4; ++cb) scale_agpr16(acc[cb][hb], al);
-            }
-          }
-        }
-      }
-      // V^T operand of step i = (ks, cb): two transposing reads; the operand of
-      // the next step is read while the MFMAs of this one issue
+      // V^T operand of step i = (ks, cb): two transposing reads
       auto read_v = [&](int i) __attribute__((always_inline)) {
         const uint8_t* vb = stage + (i >> 2) * kGroupBytes + (2 * wave + ((i & 3) >> 1)) * 1024;
         const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -1768,25 +1767,55 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         }
         return vf;
       };
-      bf16x8 pb[4];
+      // every LDS read the rescale does not decide is issued first: the
+      // flags, the first V^T operands and the P^T operands of the k-steps
+      const u32x4 fl = *reinterpret_cast<const u32x4*>(flags);
+      // V^T read-ahead: two steps (8-bit caches: one; no registers for more)
+      constexpr int kVA = kC16 ? 2 : 1;
+      bf16x8 vq[3];
       bf16x8 vcur = read_v(0);
+      if constexpr (kVA == 2) vq[1] = read_v(1);
+      bf16x8 pb[2][4];
+      auto read_p = [&](int ks) __attribute__((always_inline)) {
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          pb[ks][hb] = *reinterpret_cast<const LDS_AS bf16x8*>(
+              (const LDS_AS uint8_t*)(pbuf + ((hb * 2 + ks) * 64 + lane) * 16));
+      };
+      read_p(0);
+      if constexpr (kC16) read_p(1);  // 8-bit: read at k-step 1 (registers)
+      {
+        const unsigned any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+        if (it > 0 && any != 0) {
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            if (__builtin_amdgcn_readfirstlane(fl[hb]) != 0) {
+              const float al = alpha_s[32 * hb + l32];
+#pragma unroll
+              for (int cb = 0; cb < 4; ++cb) scale_agpr16(acc[cb][hb], al);
+            }
+          }
+        }
+      }
+      // V^T of step i + kVA is read while the MFMAs of step i issue
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ks = i >> 2, cb = i & 3;
-        if (cb == 0) {
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb)
-            pb[hb] = *reinterpret_cast<const LDS_AS bf16x8*>(
-                (const LDS_AS uint8_t*)(pbuf + ((hb * 2 + ks) * 64 + lane) * 16));
+        if (!kC16 && i == 4) read_p(1);
+        bf16x8 vnext;
+        if constexpr (kVA == 2) {
+          if (i > 0) vcur = vq[i % 3];
+          if (i + 2 < 8) vq[(i + 2) % 3] = read_v(i + 2);
+        } else {
+          vnext = read_v(i < 7 ? i + 1 : i);
         }
-        const bf16x8 vnext = read_v(i < 7 ? i + 1 : i);
 #pragma unroll
-        for (int hb = 0; hb < 3; ++hb) mfma_agpr<kF16>(acc[cb][hb], vcur, pb[hb]);
+        for (int hb = 0; hb < 3; ++hb) mfma_agpr<kF16>(acc[cb][hb], vcur, pb[ks][hb]);
         if (i < 7)
-          mfma_agpr<kF16>(acc[cb][3], vcur, pb[3]);
+          mfma_agpr<kF16>(acc[cb][3], vcur, pb[ks][3]);
         else
-          mfma_agpr<kF16, true>(acc[cb][3], vcur, pb[3]);
-        vcur = vnext;
+          mfma_agpr<kF16, true>(acc[cb][3], vcur, pb[ks][3]);
+        if constexpr (kVA == 1) vcur = vnext;
       }
     }
     if constexpr (!kC16) vm_wait_n<0>();  // the trailing re-loads have landed
