@@ -180,6 +180,25 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// The same with the source split into a wave-uniform base (SGPRs) and a
+// 32-bit per-lane byte offset from it.
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t off, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(off), "s"(base), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// A 16-byte global load into registers, as assembly: the compiler neither
+// tracks it nor waits for it, so the caller waits (vm_wait_n, counting it
+// with the direct-to-LDS loads in issue order) before any use of the result
+// and before the result's registers can go out of use.
+__device__ __forceinline__ bf16x8 load16_untracked(const void* p) {
+  bf16x8 v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p));
+  return v;
+}
+
 // The same for lanes 0..7 only (128 bytes at lds_base).  The exec mask is set
 // and restored inside the one asm statement, so the compiler sees no divergent
 // region (a register spilled and reloaded under a partial exec mask would keep
@@ -1446,26 +1465,51 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     //   Past the last tile, the last tile is loaded again (its data lands in
     //   a slot no one reads), which keeps the loads in flight, and so every
     //   vmcnt wait, the same in every iteration.
-    auto issue_tile = [&](int k, int st) {
+    // 16-bit cache: source rows and LDS destination of this wave's 9 loads of
+    // tile k into slot st (load u < 8: ckv block u, load 8: kpe)
+    // (a wave loads 8 rows of one 16-token group, which lies in one page: the
+    // page's addresses are wave-uniform, the offsets inside it per lane)
+    struct TileDma {
+      const uint8_t* cpage;  // ckv / kpe of the group's page
+      const uint8_t* kpage;
+      uint32_t coff, koff;   // this lane's row and swizzled 16-byte piece in it
+      uint32_t dst;
+    };
+    auto plan_tile = [&](int k, int st) __attribute__((always_inline)) {
       const int pg[2] = {pg_next[0], pg_next[1]};
       tile_pages(k + 1);
       const int kc = min(k, ntiles - 1);
+      const int my_group = wave >> 1, my_half = wave & 1;
+      const int gs = min(t0 + kc * T + 16 * my_group, last_group);
+      const int r = my_half * 8 + ld_r_lo;
+      const int tok = min(gs + r, t1 - 1);
+      const size_t page_row = (size_t)pg[my_group] << page_shift;
+      const uint32_t sw = ((lane & 7) ^ swz(r)) * 16;
+      TileDma td;
+      td.cpage = a.ckv + page_row * 1024;
+      td.kpage = a.kpe + page_row * 128;
+      td.coff = (tok & page_mask) * 1024 + sw;
+      td.koff = (tok & page_mask) * 128 + sw;
+      td.dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+          LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
+                           my_half * kHalfGroupBytes));
+      return td;
+    };
+    auto dma_one = [&](const TileDma& td, int u) __attribute__((always_inline)) {
+      if (u < 8)
+        dma16_s(td.cpage, td.coff + u * 128, td.dst + u * 1024);
+      else
+        dma16_s(td.kpage, td.koff, td.dst + 8 * 1024);
+    };
+    auto issue_tile = [&](int k, int st) {
       if constexpr (kC16) {
-        const int my_group = wave >> 1, my_half = wave & 1;
-        const int gs = min(t0 + kc * T + 16 * my_group, last_group);
-        const int r = my_half * 8 + ld_r_lo;
-        const int tok = min(gs + r, t1 - 1);
-        const size_t row = ((size_t)pg[my_group] << page_shift) + (tok & page_mask);
-        const int sw = ((lane & 7) ^ swz(r)) * 16;
-        const uint8_t* cbase = a.ckv + row * 1024 + sw;
-        const uint8_t* kbase = a.kpe + row * 128 + sw;
-        const uint32_t dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
-            LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
-                             my_half * kHalfGroupBytes));
+        const TileDma td = plan_tile(k, st);
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) dma16(cbase + cb * 128, dst + cb * 1024);
-        dma16(kbase, dst + 8 * 1024);
+        for (int u = 0; u < 9; ++u) dma_one(td, u);
       } else {
+        const int pg[2] = {pg_next[0], pg_next[1]};
+        tile_pages(k + 1);
+        const int kc = min(k, ntiles - 1);
         const int tile0 = t0 + kc * T;
         const uint32_t dst0 = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + st * S::kCodeBytes));
@@ -1541,22 +1585,31 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       }
     };
 
-    if (ntiles > 0) tile_pages(0);
-    if constexpr (kC16) {
-      for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
-    } else {
-      if (ntiles > 0)
-        for (int k = 0; k < NS - 1; ++k) issue_tile(k, k);
-    }
-
     // Q^T of heads 32 w .. 32 w + 31: k-step s holds dims 16 s + 8 g .. + 7.
     constexpr int QR = S::kQRegSteps;
     bf16x8 qf[QR];
     uint8_t* const qlds = smem + S::kQOffset + wave * (36 - QR) * 1024 + lane * 16;
-    {
-      const int head = 32 * wave + l32;
-      const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + head) * 512);
-      const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + head) * 64);
+    const int qhead = 32 * wave + l32;
+    const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + qhead) * 512);
+    const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + qhead) * 64);
+    if constexpr (kC16) {
+      // Q first, then the first tiles, and a wait for Q alone (loads complete
+      // in issue order): the first QK starts once Q and tile 0 are in, not
+      // the whole prologue
+#pragma unroll
+      for (int s = 0; s < 36; ++s)
+        qf[s] = load16_untracked(s < 32 ? qn + 2 * s + g : qp + 2 * (s - 32) + g);
+      if (ntiles > 0) tile_pages(0);
+      for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
+      if (ntiles >= NS - 1)
+        vm_wait_n<9 * (NS - 1)>();
+      else
+        vm_wait_n<0>();  // short segment (or none: nothing may stay in flight)
+    } else {
+      if (ntiles > 0) {
+        tile_pages(0);
+        for (int k = 0; k < NS - 1; ++k) issue_tile(k, k);
+      }
 #pragma unroll
       for (int s = 0; s < 36; ++s) {
         const bf16x8 v = s < 32 ? qn[2 * s + g] : qp[2 * (s - 32) + g];
@@ -1565,8 +1618,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         else
           *reinterpret_cast<bf16x8*>(qlds + (s - QR) * 1024) = v;
       }
+      vm_wait_n<0>();
     }
-    vm_wait_n<0>();
     if constexpr (!kC16) {
       if (ntiles > 0) {
         lds_barrier();  // code tile 0 of every wave
@@ -1584,6 +1637,12 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     float m_ref = -INFINITY;  // head 32 w + l32, log2 domain
     float l_run = 0.f;        // this lane's 16 tokens of that head
 
+    // 16-bit cache: the loads of tile it + NS - 1 are issued one per QK
+    // k-step group, behind that group's MFMAs (issued together right after the
+    // barrier, the 36 loads of the workgroup queue at the CU's address unit
+    // for some 600 cycles)
+    bool dma_on = false;
+    TileDma tdma{};
     for (int it = 0; it < ntiles; ++it) {
       const uint8_t* stage;
       if constexpr (kC16) {
@@ -1596,7 +1655,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           vm_wait_n<0>();
         lds_barrier();  // tile `it` landed for every wave; iteration it - 1 done everywhere
         const int nxt = it + NS - 1;
-        if (nxt < ntiles) issue_tile(nxt, nxt % NS);
+        dma_on = nxt < ntiles;
+        if (dma_on) tdma = plan_tile(nxt, nxt % NS);
         stage = smem + (it % NS) * S::kStageBytes;
       } else {
         // code tile it + 1 landed (tiles it + 2 .. it + NS - 2 may be in
@@ -1675,6 +1735,9 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             mfma_vgpr<kF16, false, true>(sacc, kcur[u], qv);
           else
             mfma_vgpr<kF16, false, false>(sacc, kcur[u], qv);
+        }
+        if constexpr (kC16) {
+          if (dma_on) dma_one(tdma, s0 >> 2);
         }
         if (kPrefetchK && s0 + 4 < 36) {
 #pragma unroll

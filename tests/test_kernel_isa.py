@@ -143,6 +143,121 @@ def test_no_accumulator_read_before_asm_mfma_completes(device_asm):
     assert not bad, bad
 
 
+_NO_DEST = re.compile(r"s_(cbranch|branch|waitcnt|nop|barrier|setprio|sleep|endpgm|"
+                      r"setpc|swappc|cmp|bitcmp|dcache|icache|trap|sethalt)")
+
+
+def _step_flags(t, flags):
+    """Known values of 64-bit scalar flag registers (first register -> -1 or
+    0, and 'vcc') after instruction t, for the lane-mask idiom the compiler
+    uses to route uniform branches: s_mov_b64 s[a:b], -1/0, then s_and_b64 /
+    s_andn2_b64 vcc, exec, s[a:b] (exec taken as non-zero)."""
+    m = re.match(r"s_mov_b64 s\[(\d+):\d+\], (-1|0)$", t)
+    if m:
+        return {**flags, int(m.group(1)): int(m.group(2))}
+    m = re.match(r"s_(and|andn2)_b64 vcc, exec, s\[(\d+):\d+\]$", t)
+    if m:
+        f = dict(flags)
+        v = flags.get(int(m.group(2)))
+        f.pop("vcc", None)
+        if v is not None:
+            f["vcc"] = (v != 0) if m.group(1) == "and" else (v == 0)  # True: vcc != 0
+        return f
+    dest = None
+    if t.startswith("s_") and not _NO_DEST.match(t):
+        dest = t.split()[1].rstrip(",") if len(t.split()) > 1 else None
+    elif t.startswith("v_cmp") or t.startswith("v_cmpx"):
+        dest = t.split()[1].rstrip(",")
+    if dest is None:
+        return flags
+    f = dict(flags)
+    if "vcc" in dest:
+        f.pop("vcc", None)
+    for r in list(f):
+        if r != "vcc" and re.search(r"s\[%d:" % r, dest):
+            f.pop(r)
+    return f
+
+
+def _untracked_load_touches(instrs, labels):
+    """Instructions that name a register an assembly global load writes, on
+    some path from the load before any s_waitcnt on vmcnt.  Branches on vcc
+    whose value the flag idiom above fixes follow the one way they can go."""
+    bad = []
+    for k, (t, asm) in enumerate(instrs):
+        m = re.match(r"global_load_dwordx4 v\[(\d+):(\d+)\]", t)
+        if not (m and asm):
+            continue
+        dst = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        stack, seen = [(k + 1, {})], set()
+        while stack:
+            j, flags = stack.pop()
+            while j < len(instrs):
+                key = (j, tuple(sorted(flags.items(), key=str)))
+                if key in seen:
+                    break
+                seen.add(key)
+                t2 = instrs[j][0]
+                if t2.startswith("s_waitcnt") and "vmcnt" in t2:
+                    break
+                if _regs(t2, "v") & dst and not (t2.startswith("global_load_dwordx4")
+                                                   and instrs[j][1]):
+                    bad.append((t, t2))
+                    break
+                br = re.match(r"s_(cbranch_\w+|branch) (\.LBB\d+_\d+)", t2)
+                if br:
+                    kind, target = br.group(1), labels[br.group(2)]
+                    if kind == "branch":
+                        j = target
+                        continue
+                    vcc = flags.get("vcc")
+                    if kind in ("cbranch_vccnz", "cbranch_vccz") and vcc is not None:
+                        if vcc == (kind == "cbranch_vccnz"):
+                            j = target
+                            continue
+                    else:
+                        stack.append((target, flags))
+                if re.match(r"s_(setpc|swappc|endpgm)", t2):
+                    break
+                flags = _step_flags(t2, flags)
+                j += 1
+    return bad
+
+
+def test_untracked_loads_waited_before_use(device_asm):
+    # Q of the 128-head kernel is loaded by assembly (the compiler would wait
+    # for all earlier loads, the KV prologue included, before its first use):
+    # every path from such a load must reach a vmcnt wait before anything else
+    # reads, writes or copies its destination registers
+    funcs = _functions(device_asm)
+    n = sum(1 for f, (ins, _) in funcs.items() if "mla_" in f
+            for t, asm in ins if asm and t.startswith("global_load_dwordx4 v["))
+    assert n > 0
+    bad = {f: _untracked_load_touches(*fl) for f, fl in funcs.items() if "mla_" in f}
+    bad = {f: b for f, b in bad.items() if b}
+    assert not bad, bad
+
+
+def test_scanner_flags_a_planted_untracked_use():
+    load = ("global_load_dwordx4 v[4:7], v[0:1], off", True)
+    use = ("v_mov_b32_e32 v20, v5", False)
+    wait = ("s_waitcnt vmcnt(0)", False)
+    assert _untracked_load_touches([load, use], {})
+    assert not _untracked_load_touches([load, wait, use], {})
+    branched = [load, ("s_cbranch_scc1 .LBB0_1", False), wait, ("s_endpgm", False), use]
+    assert _untracked_load_touches(branched, {".LBB0_1": 4})
+    # the flag idiom: s[4:5] = -1 makes vcc = exec & ~s[4:5] zero, so the
+    # vccnz branch around the wait is never taken ...
+    idiom = [load, ("s_mov_b64 s[4:5], -1", False), ("s_andn2_b64 vcc, exec, s[4:5]", False),
+             ("s_cbranch_vccnz .LBB0_2", False), wait, use]
+    assert not _untracked_load_touches(idiom, {".LBB0_2": 5})
+    # ... but with s[4:5] = 0 it is, and with s[4:5] unknown it may be
+    taken = [idiom[0], ("s_mov_b64 s[4:5], 0", False)] + idiom[2:]
+    assert _untracked_load_touches(taken, {".LBB0_2": 5})
+    unknown = [idiom[0], ("s_cselect_b64 s[4:5], -1, 0", False)] + idiom[2:]
+    assert _untracked_load_touches(unknown, {".LBB0_2": 5})
+
+
 def test_scanner_flags_a_planted_early_read():
     # the check itself: an AGPR read right after an asm MFMA is found, one after
     # enough s_nop wait states is not, and a read behind a branch is followed
