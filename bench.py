@@ -15,6 +15,11 @@ synthetic N(0,1) data resident in HBM; consecutive steps alternate between
 `--copies` separate copies of the inputs, so that a step cannot reuse what the
 previous one left in the 256 MB Infinity Cache.
 
+Each workload also reports `timing`: the mean, median, min and max of the
+per-step decode time (HIP events around the library's kernels) and the step
+time when the same steps replay from hipGraphs (one captured per input copy)
+beside the eager one.
+
 `roofline.achieved` divides the algorithmic bytes (or flops) of one launch by
 the decode kernel's own average duration, measured with HIP events recorded
 around that kernel on its stream by the library over the timed steps.
@@ -129,7 +134,7 @@ def device_inputs(inp, copies: int):
 
 
 def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_split: int = 0,
-            l2_domains: int = 0) -> dict:
+            l2_domains: int = 0, graph: bool = False) -> dict:
     import torch
     import mla_paged_kv_decode_amd as mla
     from mla_paged_kv_decode_amd import synth
@@ -171,14 +176,46 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     wall = time.perf_counter() - w0
     plan.set_events(None, None)
     total_ms = hip.elapsed_ms(start, stop)
-    kern = [hip.elapsed_ms(before[i], after[i]) for i in range(steps)]
+    kern = sorted(hip.elapsed_ms(before[i], after[i]) for i in range(steps))
+    graph_ms = None
+    if graph:
+        # the same steps replayed from hipGraphs (one per input copy, captured
+        # once): what a serving loop that captures its decode step pays
+        side = torch.cuda.Stream()
+        graphs = []
+        for c in range(copies):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                step(c)
+            graphs.append(g)
+        for i in range(warmup):
+            graphs[i % copies].replay()
+        torch.cuda.synchronize()
+        hip.lib.hipEventRecord(start, ctypes.c_void_p(stream))
+        for i in range(steps):
+            graphs[i % copies].replay()
+        hip.lib.hipEventRecord(stop, ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        graph_ms = hip.elapsed_ms(start, stop) / steps
+        del graphs
     for e in before + after + [start, stop]:
         hip.destroy(e)
     info = plan.info()
     return dict(name=name, inp=inp, bytes=inp.algorithmic_bytes(), flops=inp.flops(),
                 ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
-                kernel_ms=sum(kern) / len(kern), kernel_ms_min=min(kern), plan_ms=plan_ms,
-                plan=info)
+                kernel_ms=sum(kern) / len(kern), kernel_ms_min=kern[0],
+                kernel_ms_median=kern[len(kern) // 2], kernel_ms_max=kern[-1],
+                graph_ms_per_step=graph_ms, plan_ms=plan_ms, plan=info)
+
+
+def timing_report(m: dict) -> dict:
+    """Per-launch decode times (HIP events around the library's kernels) and
+    the step time from hipGraph replay beside the eager one."""
+    r = {k: round(m[k], 5) for k in ("kernel_ms", "kernel_ms_median", "kernel_ms_min",
+                                      "kernel_ms_max", "ms_per_step")}
+    g = m.get("graph_ms_per_step")
+    r["graph_ms_per_step"] = round(g, 5) if g is not None else None
+    return r
 
 
 def workload_report(m: dict, peaks: dict) -> dict:
@@ -195,7 +232,8 @@ def workload_report(m: dict, peaks: dict) -> dict:
          "unit": "TFLOP/s" if mfma else "GB/s", "ms_per_step": round(m["ms_per_step"], 5),
          "kernel_ms": round(m["kernel_ms"], 5), "kernel_gbs": round(gbs, 1),
          "kernel_tflops": round(tfs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-         "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "plan": m["plan"]}
+         "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "timing": timing_report(m),
+         "plan": m["plan"]}
     if peaks:
         r["frac_of_measured_read_peak"] = round(gbs / peaks["stream_read_gbs"], 4)
         r["frac_of_measured_mfma_peak"] = round(tfs / peaks["mfma_bf16_tflops"], 4)
@@ -303,6 +341,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-append", action="store_true",
                     help="skip the cache-append measurement")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the hipGraph replay timing of each workload")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured stream-read / MFMA peak kernels")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -339,7 +379,8 @@ def main():
         torch.cuda.empty_cache()
 
     prim = measure(args.workload, args.steps, args.warmup, args.copies, hip,
-                   args.head_split if synth_heads(args.workload) >= 64 else 0, args.l2_domains)
+                   args.head_split if synth_heads(args.workload) >= 64 else 0, args.l2_domains,
+                   graph=not args.no_graph)
     inp = prim["inp"]
     gbs = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
     kern_gbs = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
@@ -369,6 +410,7 @@ def main():
                      "kernel_ms": round(prim["kernel_ms"], 5),
                      "frac_of_measured_read_peak": (round(kern_gbs / peaks["stream_read_gbs"], 4)
                                                     if peaks else None)},
+        "timing": timing_report(prim),
         "plan_ms": round(prim["plan_ms"], 4),
         "measured_peaks": peaks,
         "wall_ms_per_step": round(prim["wall_ms_per_step"], 5),
@@ -377,7 +419,7 @@ def main():
         out["also"] = []
         for name in args.secondary.split(","):
             sec = measure(name, args.steps, args.warmup, args.copies, hip, args.head_split,
-                          args.l2_domains)
+                          args.l2_domains, graph=not args.no_graph)
             out["also"].append(workload_report(sec, peaks))
             del sec
             torch.cuda.empty_cache()

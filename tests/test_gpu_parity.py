@@ -142,18 +142,23 @@ def test_outputs_stay_in_bounds():
     check(*host(o, lse), *ref(inp))
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("heads,kvd", [(16, synth.KV_BF16), (128, synth.KV_BF16),
+                                       (16, synth.KV_FP8_E4M3), (128, synth.KV_INT8)])
+def test_graph_replay_matches_eager(heads, kvd):
+    # 16 heads: one launch that merges split requests itself; 128 heads: the
+    # decode kernel and the combine launch, both in the graph
     import mla_paged_kv_decode_amd as mla
-    inp = synth.make_inputs([1000, 4000, 64], 16, 64, seed=13)
+    inp = synth.make_inputs([1000, 4000, 64], heads, 64, kvd, seed=13)
+    print("case heads=%d kv=%d" % (heads, kvd), flush=True)
     t = dev(inp)
-    B, H = 3, 16
+    B, H = 3, heads
     ws = torch.empty(mla.workspace_bytes(B, H), dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
     with torch.cuda.stream(s):
-        plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 64, workspace=ws, stream=s)
-        args = (t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], None, t["kv_indptr"],
+        plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 64, kvd, workspace=ws, stream=s)
+        args = (t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_scale"], t["kv_indptr"],
                 t["kv_indices"], t["kv_last_page_len"], inp.sm_scale, o, lse)
         plan.run(*args, stream=s)
     torch.cuda.synchronize()
@@ -169,6 +174,7 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), o_eager.view(torch.int16))
         assert torch.equal(lse.view(torch.int32), l_eager.view(torch.int32))
+    check(*host(o, lse), *ref(inp))
 
 
 @pytest.mark.parametrize("name", ["mem_b64_h16_l4096_p64", "compute_b64_h128_l4096_p64",
