@@ -159,6 +159,7 @@ class Plan:
         ip = _host_i32(kv_indptr)
         lp = _host_i32(kv_last_page_len)
         self.batch = int(ip.size - 1)
+        self.num_pages_used = int(ip[-1]) if ip.size else 0  # kv_indices entries the plan reads
         self.num_heads = int(num_heads)
         self.page_size = int(page_size)
         self.kv_dtype = int(kv_dtype)
@@ -228,6 +229,12 @@ class Plan:
                         ("kv_last_page_len", kv_last_page_len)):
             if t.dtype != torch.int32:
                 raise ValueError(name + " must be int32")
+        # the device copies must match the host copies the plan was built from
+        # (the kernels read them without bounds checks)
+        if kv_indptr.numel() != self.batch + 1 or kv_last_page_len.numel() != self.batch:
+            raise ValueError("kv_indptr / kv_last_page_len sizes differ from the plan's")
+        if kv_indices.numel() < self.num_pages_used:
+            raise ValueError("kv_indices holds fewer entries than kv_indptr[-1]")
         if ckv.dim() != 3 or ckv.shape[1] != self.page_size or ckv.shape[2] != D_CKV:
             raise ValueError("ckv must be [pages, page_size, 512]")
         if kpe.dim() != 3 or kpe.shape[1] != self.page_size or kpe.shape[2] != D_KPE:

@@ -310,3 +310,32 @@ def test_cache_append_rejects_bad_arguments(lib):
     assert lib.mla_cache_append(Pp(1), Pp(1), Pp(1), 4, 0, Pp(1), Pp(1), Pp(1), None) == -1
     assert lib.mla_cache_append(None, None, Pp(1), 4, 0, Pp(1), Pp(1), None, None) == -1
     assert lib.mla_cache_append(None, None, None, 0, 1, None, None, None, None) == 0
+
+
+def test_run_rejects_metadata_that_differs_from_the_plan():
+    # the binding checks the device metadata's sizes against the plan's host
+    # copies before anything reaches the library (CPU tensors suffice: the
+    # check comes first)
+    torch = pytest.importorskip("torch")
+    import mla_paged_kv_decode_amd as mla
+    indptr = np.array([0, 2, 5], np.int32)
+    last = np.array([3, 16], np.int32)
+    plan = mla.Plan(indptr, last, 16, 16, num_cus=8)
+    B, H = 2, 16
+    q_nope = torch.zeros((B, H, 512), dtype=torch.bfloat16)
+    q_pe = torch.zeros((B, H, 64), dtype=torch.bfloat16)
+    ckv = torch.zeros((5, 16, 512), dtype=torch.bfloat16)
+    kpe = torch.zeros((5, 16, 64), dtype=torch.bfloat16)
+    o = torch.zeros((B, H, 512), dtype=torch.bfloat16)
+    lse = torch.zeros((B, H), dtype=torch.float32)
+    i32 = lambda a: torch.tensor(a, dtype=torch.int32)
+    good = (i32(indptr), i32(np.arange(5)), i32(last))
+    bad = [(i32(indptr[:2]), good[1], good[2]),          # kv_indptr too short
+           (good[0], good[1], i32(last[:1])),            # kv_last_page_len too short
+           (good[0], i32(np.arange(4)), good[2])]        # fewer kv_indices than pages
+    for ip, ix, lp in bad:
+        with pytest.raises(ValueError):
+            plan.run(q_nope, q_pe, ckv, kpe, None, ip, ix, lp, 0.07, o, lse)
+    # with the right sizes, the next check is the device one
+    with pytest.raises(ValueError, match="device"):
+        plan.run(q_nope, q_pe, ckv, kpe, None, *good, 0.07, o, lse)
