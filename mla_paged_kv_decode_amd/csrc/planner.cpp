@@ -84,6 +84,80 @@ int64_t assign(const std::vector<Piece>& pieces, int32_t workers, std::vector<in
   return worst;
 }
 
+// Improve a longest-first assignment (which leaves the busiest worker some
+// 10% above the mean when each worker gets a few requests of very different
+// lengths): while it helps, the busiest worker moves one of its pieces to, or
+// swaps one with, the partner and pieces that lower the larger of the two
+// loads the most.  Every step lowers the busiest load, or leaves it to a worker
+// with a higher index among equals; the scan orders are fixed, so the result is
+// deterministic.  Returns the largest worker load.
+int64_t refine(const std::vector<Piece>& pieces, int32_t workers, std::vector<int32_t>* owner) {
+  std::vector<int64_t> load((size_t)workers, 0);
+  std::vector<std::vector<int32_t>> items((size_t)workers);
+  for (size_t i = 0; i < pieces.size(); ++i) {
+    load[(*owner)[i]] += pieces[i].cost;
+    items[(*owner)[i]].push_back((int32_t)i);
+  }
+  // workers by (load, index), kept sorted: a step changes two loads
+  auto before = [&](int32_t x, int32_t y) { return load[x] < load[y] || (load[x] == load[y] && x < y); };
+  std::vector<int32_t> by_load((size_t)workers);
+  for (int32_t w = 0; w < workers; ++w) by_load[w] = w;
+  std::sort(by_load.begin(), by_load.end(), before);
+  auto unlink = [&](int32_t w) {
+    by_load.erase(std::lower_bound(by_load.begin(), by_load.end(), w, before));
+  };
+  auto relink = [&](int32_t w) {
+    by_load.insert(std::lower_bound(by_load.begin(), by_load.end(), w, before), w);
+  };
+  const int64_t max_steps = 4 * (int64_t)workers;
+  for (int64_t step = 0; step < max_steps; ++step) {
+    const int32_t hi = by_load[workers - 1];
+    int64_t best = load[hi];
+    int32_t best_a = -1, best_b = -1, best_w = -1;
+    for (int32_t k = 0; k < workers - 1; ++k) {
+      const int32_t lo = by_load[k];
+      const int64_t gap = load[hi] - load[lo];
+      // no exchange with lo (or anyone heavier) can bring the pair below the
+      // mean of their loads
+      if (gap <= 0 || (load[hi] + load[lo] + 1) / 2 >= best) break;
+      for (int32_t a : items[hi]) {
+        const int64_t ca = pieces[a].cost;
+        if (ca < gap) {  // move a
+          const int64_t m = std::max(load[hi] - ca, load[lo] + ca);
+          if (m < best) best = m, best_a = a, best_b = -1, best_w = lo;
+        }
+        for (int32_t b : items[lo]) {  // swap a and b
+          const int64_t d = ca - pieces[b].cost;
+          if (d <= 0 || d >= gap) continue;
+          const int64_t m = std::max(load[hi] - d, load[lo] + d);
+          if (m < best) best = m, best_a = a, best_b = b, best_w = lo;
+        }
+      }
+    }
+    if (best_a < 0) break;
+    unlink(hi);
+    unlink(best_w);
+    auto take = [&](int32_t w, int32_t i) {
+      items[w].erase(std::find(items[w].begin(), items[w].end(), i));
+      load[w] -= pieces[i].cost;
+    };
+    auto put = [&](int32_t w, int32_t i) {
+      items[w].push_back(i);
+      load[w] += pieces[i].cost;
+      (*owner)[i] = w;
+    };
+    take(hi, best_a);
+    put(best_w, best_a);
+    if (best_b >= 0) {
+      take(best_w, best_b);
+      put(hi, best_b);
+    }
+    relink(hi);
+    relink(best_w);
+  }
+  return load[by_load[workers - 1]];
+}
+
 // Reorder workers so that the workers serving the hs rows of one request
 // (the row groups that share its latent cache, with all their chunks) get
 // launch positions congruent modulo the number of L2 domains: workgroups are
@@ -170,17 +244,31 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
       }
     }
     std::sort(cands.begin(), cands.end(), std::greater<int64_t>());  // fewest cuts first
-    for (int64_t c : cands) {
-      cut_requests(len, c, gran, p.num_heads, 0, p.max_splits, &pieces);
+    // longest-first for every candidate; the refinement (the costly part) for
+    // the two best of those
+    std::vector<std::pair<int64_t, int64_t>> ranked;  // (longest-first worst, candidate)
+    for (size_t k = 0; k < cands.size(); ++k) {
+      cut_requests(len, cands[k], gran, p.num_heads, 0, p.max_splits, &pieces);
       if ((int64_t)pieces.size() > seg_cap) continue;
-      const int64_t worst = assign(pieces, p.num_workers, &owner);
+      ranked.push_back({assign(pieces, p.num_workers, &owner), (int64_t)k});
+    }
+    if (ranked.empty()) return -1;  // unreachable: the largest candidate never cuts
+    std::stable_sort(ranked.begin(), ranked.end());
+    const size_t nref = std::min<size_t>(2, ranked.size());
+    std::sort(ranked.begin(), ranked.begin() + nref,
+              [](const std::pair<int64_t, int64_t>& x, const std::pair<int64_t, int64_t>& y) {
+                return x.second < y.second;  // fewest cuts first among them
+              });
+    for (size_t r = 0; r < nref; ++r) {
+      cut_requests(len, cands[ranked[r].second], gran, p.num_heads, 0, p.max_splits, &pieces);
+      assign(pieces, p.num_workers, &owner);
+      const int64_t worst = refine(pieces, p.num_workers, &owner);
       if (best < 0 || worst < best) {
         best = worst;
         best_pieces.swap(pieces);
         best_owner.swap(owner);
       }
     }
-    if (best < 0) return -1;  // unreachable: the largest candidate never cuts
   }
 
   // group by worker, keep assignment order within a worker stable (request order)

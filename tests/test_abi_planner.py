@@ -95,6 +95,27 @@ def test_plan_balances_uniform_batch(lib):
     assert set((seg[:, 2] - seg[:, 1]).tolist()) == {1024}
 
 
+def _worker_loads(seg, wp, heads, lengths):
+    # the planner's cost model: tokens + 64 + H per piece, + 4H per piece of a
+    # request cut into several
+    nsplit = np.bincount(seg[:, 0], minlength=len(lengths))
+    cost = (seg[:, 2] - seg[:, 1]) + 64 + heads + np.where(nsplit[seg[:, 0]] > 1, 4 * heads, 0)
+    return np.array([cost[wp[i]:wp[i + 1]].sum() for i in range(len(wp) - 1)])
+
+
+def test_plan_balances_variable_lengths(lib):
+    # 768 requests of 1..2048 tokens on 256 workers, about three each: the
+    # longest-first assignment alone leaves the busiest worker ~9% above the
+    # mean; the refinement brings it within 1%
+    lengths = [int(x) for x in np.random.default_rng(4).integers(1, 2049, 768)]
+    ip, lp = _table(lengths, 16)
+    plan = mla.Plan(ip, lp, 64, 16, num_cus=256)
+    seg, wp, info = _check_plan(plan, lengths, plan.info()["granularity"])
+    loads = _worker_loads(seg, wp, 64, lengths)
+    assert info["num_workers"] == 256
+    assert loads.max() <= 1.01 * loads.mean(), (loads.max(), loads.mean())
+
+
 def test_plan_is_pure_function_of_lengths(lib):
     lengths = list(np.random.default_rng(9).integers(1, 3000, 300))
     ip, lp = _table(lengths, 16)
