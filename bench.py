@@ -48,7 +48,9 @@ SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
              "fp8ckv_bf16kpe_b64_h128_l8192_p64", "int8ckv_bf16kpe_b64_h16_l8192_p64",
              "int8ckv_bf16kpe_b64_h128_l8192_p64", "mtp_b64_h16_q2_l4096_p64",
              "mtp_b64_h128_q2_l4096_p64", "mem_b64_h16_l4096_p32", "mem_b64_h16_l4096_p16",
-             "fp16_b64_h16_l4096_p64", "fp16_b64_h128_l4096_p64")
+             "fp16_b64_h16_l4096_p64", "fp16_b64_h128_l4096_p64", "longctx_b4_h16_l32768_p64",
+             "longctx_b1_h16_l131072_p64", "longctx_b16_h64_l8192_p64",
+             "longctx_b4_h128_l32768_p64")
 KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8", 3: "fp8_e4m3_ckv_bf16_kpe", 4: "int8_ckv_bf16_kpe",
             5: "fp16"}
 

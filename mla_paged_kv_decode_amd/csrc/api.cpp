@@ -150,6 +150,7 @@ struct mla_plan_s {
   int32_t qo_len = 1, head_split = 1, kernel_heads = 0;
   mla_gpu::DecodeConfig cfg{};
   mla::Plan plan;
+  int32_t max_splits = 0;  // most chunks of one split request
   Layout layout{};
   std::vector<uint8_t> host_meta;  // staged work list (kept alive for the async copy)
   uint8_t* workspace = nullptr;
@@ -248,6 +249,8 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
     return MLA_ERR_INVALID_ARG;
   }
   const mla::Plan& pl = p->plan;
+  for (size_t i = 2; i < pl.combine.size(); i += 4)
+    p->max_splits = std::max(p->max_splits, pl.combine[i]);
   const int64_t ncomb = (int64_t)pl.combine.size() / 4;
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          kernel_heads);
@@ -317,6 +320,10 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o_fp16 = p->kv_dtype == MLA_KV_FP16 ? 1 : 0;
+  // requests cut into many chunks are merged by a launch spread over the GPU
+  // (one workgroup reading a request's n partials alone is latency-bound)
+  const bool merge_in_kernel = p->cfg.fused_merge && p->max_splits <= mla_gpu::kInKernelMergeMax;
+  a.merge_in_kernel = merge_in_kernel ? 1 : 0;
   a.page_shift = p->page_shift;
   a.rows_per_req = p->head_split;
   a.qo_len = p->qo_len;
@@ -329,8 +336,8 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
     hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     const int ncomb = (int)(p->plan.combine.size() / 4);
-    if (!p->cfg.fused_merge && ncomb > 0) {
-      e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, s);
+    if (!merge_in_kernel && ncomb > 0) {
+      e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, p->max_splits, s);
       if (e != hipSuccess) return hip_fail(e, "combine launch");
     }
   }

@@ -27,6 +27,9 @@ struct DecodeArgs {
   const int4* clist;          // 4 ints per split request: row, first slot, chunks, 0
   float scale_log2;           // sm_scale * log2(e)
   int32_t o_fp16;             // 1: o is fp16 (fp16 cache and queries), 0: bf16
+  int32_t merge_in_kernel;    // kernels with fused_merge: 1 = the workgroup finishing the
+                              // last chunk of a split request merges it; 0 = the partials
+                              // are left for launch_combine
   int32_t page_shift;         // log2(page_size)
   int32_t rows_per_req;       // kernel rows per request: row b of q/o/lse (kernel-width
                               // groups of query vectors) reads the latent cache of request
@@ -53,8 +56,13 @@ int decode_config(int heads, int kv_dtype, DecodeConfig* cfg);
 int decode_blocks_per_cu(int heads, int kv_dtype);
 hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
                          hipStream_t stream);
-// Merge of the ncomb split requests listed in a.clist (for kernels with
-// fused_merge = 0): writes o and lse of those rows.
-hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, hipStream_t stream);
+// Merge of the ncomb split requests listed in a.clist, each cut into at most
+// max_splits chunks (after kernels with fused_merge = 0, or launched with
+// merge_in_kernel = 0): writes o and lse of those rows.
+hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, int max_splits,
+                          hipStream_t stream);
+// Split requests with more chunks than this are merged by launch_combine
+// (spread over the GPU) rather than by their last workgroup.
+constexpr int kInKernelMergeMax = 4;
 
 }  // namespace mla_gpu

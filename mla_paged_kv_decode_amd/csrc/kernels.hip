@@ -499,7 +499,7 @@ __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int s
                                                int slot0, int nsplit, int tid, uint8_t* smem,
                                                int* s_last) {
   // ---- last chunk of a split request merges the request's partials --------
-  if (slot >= 0) {
+  if (slot >= 0 && a.merge_in_kernel) {
     vm_wait_n<0>();  // this wave's coherent partial stores have completed
     lds_barrier();
     if (tid == 0) {
@@ -1988,6 +1988,110 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   if (col == 0) a.lse[(size_t)b * H + hd] = lse_v;
 }
 
+// ---------------------------------------------------------------------------
+// Merge of split requests cut into many chunks (more than kInKernelMergeMax;
+// up to 256).  One workgroup per (split request, head, 64-column chunk), so
+// the n partials of a request are read by many workgroups at once rather
+// than by one.  The workgroup reads the head's n partial LSEs (one per
+// thread), reduces them to LSE = M + ln sum_i exp(LSE_i - M), and keeps the
+// weights w_i = exp(LSE_i - LSE) in LDS.  Thread (q, j) (j = tid / 8, q =
+// tid % 8) sums w_i O_i over the 8 columns q of its chunk for partials i = j,
+// j + 32, ...; the 32 sums per 8 columns are added by xor-shuffles within a
+// wave and then wave by wave.  Every reduction has a fixed order, so reruns
+// are bit-identical.
+// ---------------------------------------------------------------------------
+template <int H, bool F16>
+__global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs a) {
+  constexpr int kChunks = 8;   // 64-column chunks of a 512-wide row
+  constexpr int kLanes = 32;   // partial lanes per 8 columns
+  constexpr int kBatch = 4;    // partials in flight per thread
+  __shared__ float s_w[256];
+  __shared__ float s_red[2][4];
+  __shared__ f32x4 s_o[4][8][2];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int req = blockIdx.x / (H * kChunks);
+  const int hd = (blockIdx.x / kChunks) % H;
+  const int ch = blockIdx.x % kChunks;
+  const int* cl = reinterpret_cast<const int*>(a.clist) + req * 4;
+  const int b = ld_const(cl + 0);
+  const int slot0 = ld_const(cl + 1);
+  const int n = ld_const(cl + 2);
+
+  // ---- LSE over the n partials ---------------------------------------------
+  const float* pl = a.part_lse + (size_t)slot0 * H + hd;
+  const float v = tid < n ? pl[(size_t)tid * H] : -INFINITY;
+  float mx = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) s_red[0][wave] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float e = tid < n ? __expf(v - Mu) : 0.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) e += __shfl_xor(e, o);
+  if (lane == 0) s_red[1][wave] = e;
+  __syncthreads();
+  const float sum = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+  const bool empty = !(sum > 0.f);
+  const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
+  if (tid < n) s_w[tid] = empty ? 0.f : __expf(v - lse_v);
+  __syncthreads();
+
+  // ---- O = sum_i w_i O_i over this thread's partials -----------------------
+  const int q = tid & 7, j = tid >> 3;
+  const int col = ch * 64 + q * 8;
+  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
+  float o8[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) o8[c] = 0.f;
+  for (int i0 = j; i0 < n; i0 += kBatch * kLanes) {
+    f32x4 x[kBatch][2];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = min(i0 + u * kLanes, n - 1);
+      x[u][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
+      x[u][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = i0 + u * kLanes;
+      if (i < n) {
+        const float w = s_w[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          o8[c] += w * x[u][0][c];
+          o8[4 + c] += w * x[u][1][c];
+        }
+      }
+    }
+  }
+  // lanes q, q + 8, ..., q + 56 of a wave hold partial lanes j = 8 wave + 0..7
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    o8[c] += __shfl_xor(o8[c], 8);
+    o8[c] += __shfl_xor(o8[c], 16);
+    o8[c] += __shfl_xor(o8[c], 32);
+  }
+  if (lane < 8) {
+    s_o[wave][lane][0] = f32x4{o8[0], o8[1], o8[2], o8[3]};
+    s_o[wave][lane][1] = f32x4{o8[4], o8[5], o8[6], o8[7]};
+  }
+  __syncthreads();
+  if (tid < 8) {
+    bf16x8 out;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const f32x4 r = (s_o[0][tid][h2] + s_o[1][tid][h2]) + (s_o[2][tid][h2] + s_o[3][tid][h2]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) out[4 * h2 + c] = to16<F16>(r[c]);
+    }
+    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + ch * 64 + tid * 8) = out;
+  }
+  if (tid == 0 && ch == 0) a.lse[(size_t)b * H + hd] = lse_v;
+}
+
 // ---------------------------------------------------------------- launchers
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
@@ -2180,18 +2284,30 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
 #undef MLA_RING
 }
 
-hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, hipStream_t stream) {
+template <int H>
+static hipError_t launch_combine_h(const DecodeArgs& a, int ncomb, int max_splits,
+                                   hipStream_t stream) {
+  if (max_splits > kInKernelMergeMax) {
+    const dim3 grid(ncomb * H * 8);
+    if (a.o_fp16)
+      hipLaunchKernelGGL((mla_combine_many_kernel<H, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((mla_combine_many_kernel<H, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(mla_combine_kernel<H>, dim3(ncomb * (H / 4)), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, int max_splits,
+                          hipStream_t stream) {
   if (ncomb <= 0) return hipSuccess;
+  if (max_splits > 256) return hipErrorInvalidValue;
   switch (heads) {
-#define MLA_COMBINE(H)                                                                 \
-  case H:                                                                              \
-    hipLaunchKernelGGL(mla_combine_kernel<H>, dim3(ncomb * (H / 4)), dim3(256), 0, stream, a); \
-    return hipGetLastError();
-    MLA_COMBINE(16)
-    MLA_COMBINE(32)
-    MLA_COMBINE(64)
-    MLA_COMBINE(128)
-#undef MLA_COMBINE
+    case 16: return launch_combine_h<16>(a, ncomb, max_splits, stream);
+    case 32: return launch_combine_h<32>(a, ncomb, max_splits, stream);
+    case 64: return launch_combine_h<64>(a, ncomb, max_splits, stream);
+    case 128: return launch_combine_h<128>(a, ncomb, max_splits, stream);
     default: return hipErrorInvalidValue;
   }
 }

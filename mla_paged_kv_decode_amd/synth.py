@@ -267,6 +267,16 @@ WORKLOADS = {
                                      seed=6, qo_len=2),
     "mtp_b64_h128_q2_l4096_p64": dict(batch=64, heads=128, kv_len=4096, page=64,
                                       kv_dtype=KV_BF16, seed=6, qo_len=2),
+    # long contexts at small batch: every request is cut into many chunks
+    # (64 to 256), whose partials a merge spread over the GPU combines
+    "longctx_b4_h16_l32768_p64": dict(batch=4, heads=16, kv_len=32768, page=64,
+                                      kv_dtype=KV_BF16, seed=7),
+    "longctx_b1_h16_l131072_p64": dict(batch=1, heads=16, kv_len=131072, page=64,
+                                       kv_dtype=KV_BF16, seed=7),
+    "longctx_b16_h64_l8192_p64": dict(batch=16, heads=64, kv_len=8192, page=64,
+                                      kv_dtype=KV_BF16, seed=7),
+    "longctx_b4_h128_l32768_p64": dict(batch=4, heads=128, kv_len=32768, page=64,
+                                       kv_dtype=KV_BF16, seed=7),
 }
 
 

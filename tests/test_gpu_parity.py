@@ -181,14 +181,17 @@ def test_graph_replay_matches_eager(heads, kvd):
                                   "varlen_b768_h64_l1to2048_p16", "fp8_b64_h16_l8192_p64",
                                   "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64",
                                   "int8_b64_h128_l8192_p64", "fp8ckv_bf16kpe_b64_h16_l8192_p64",
-                                  "int8ckv_bf16kpe_b64_h128_l8192_p64"])
+                                  "int8ckv_bf16kpe_b64_h128_l8192_p64",
+                                  "longctx_b4_h16_l32768_p64", "longctx_b1_h16_l131072_p64",
+                                  "longctx_b16_h64_l8192_p64", "longctx_b4_h128_l32768_p64"])
 def test_full_workloads_sampled(name):
     inp = synth.make_workload(name, poison=True)
     print("workload", name, flush=True)
     o, lse = host(*gpu_run(inp))
     B, H = inp.batch, inp.num_heads
     rng = np.random.default_rng(5)
-    rows = np.unique(np.concatenate([rng.choice(B * H, 96, replace=False), [0, B * H - 1]]))
+    rows = np.unique(np.concatenate([rng.choice(B * H, min(96, B * H), replace=False),
+                                     [0, B * H - 1]]))
     o_ref, lse_ref = ref(inp, rows=rows.astype(np.int32))
     check(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
     # properties at every row: finite, |O| within the ckv range, LSE above the max score bound
@@ -343,6 +346,24 @@ def test_fp16_full_workloads_sampled(name):
     o, lse = host(*gpu_run(inp))
     B, H = inp.batch, inp.num_heads
     rng = np.random.default_rng(6)
-    rows = np.unique(np.concatenate([rng.choice(B * H, 96, replace=False), [0, B * H - 1]]))
+    rows = np.unique(np.concatenate([rng.choice(B * H, min(96, B * H), replace=False),
+                                     [0, B * H - 1]]))
     o_ref, lse_ref = ref(inp, rows=rows.astype(np.int32))
     check(o.reshape(-1, 512)[rows], lse.reshape(-1)[rows], o_ref, lse_ref)
+
+
+@pytest.mark.parametrize("heads,lengths", [(16, [131072]), (64, [8192] * 16), (128, [32768] * 2)])
+def test_many_chunk_merge_reruns_bit_identical(heads, lengths):
+    # requests cut into 16 to 256 chunks go through the merge spread over the
+    # GPU; its reductions have a fixed order
+    import mla_paged_kv_decode_amd as mla
+    inp = synth.make_inputs(lengths, heads, 64, seed=31)
+    print("case heads=%d batch=%d L=%d" % (heads, len(lengths), lengths[0]), flush=True)
+    t = dev(inp)
+    o1, l1 = gpu_run(inp, t)
+    o2, l2 = gpu_run(inp, t)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, heads, 64)
+    info = plan.info()
+    assert info["num_partials"] // info["num_split_requests"] > 4
