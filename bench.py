@@ -11,9 +11,10 @@ separately as plan_ms.
 Primary line: the memory-bound h_q = 16 workload (batch 64, kv_len 4096,
 page 64, bf16) in HBM GB/s of algorithmic bytes (every input and output once).
 "secondary" holds the h_q = 128 workload in bf16 TFLOP/s.  Inputs are seeded
-synthetic N(0,1) data resident in HBM; consecutive steps alternate between
-`--copies` separate copies of the inputs, so that a step cannot reuse what the
-previous one left in the 256 MB Infinity Cache.
+synthetic N(0,1) data resident in HBM; consecutive steps cycle through
+separate copies of the inputs (at least `--copies`, and enough that the other
+copies stream 512 MB between two reads of one), so that a step cannot reuse
+what earlier ones left in the 256 MB Infinity Cache.
 
 Each workload also reports `timing`: the mean, median, min and max of the
 per-step decode time (HIP events around the library's kernels) and the step
@@ -142,6 +143,9 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     from mla_paged_kv_decode_amd import synth
 
     inp = synth.make_workload(name)
+    # between two reads of one copy, the other copies stream at least 512 MB
+    # (twice the Infinity Cache), so no step finds its inputs cached
+    copies = max(copies, 1 + -(-512_000_000 // inp.algorithmic_bytes()))
     sets = device_inputs(inp, copies)
     B, H, Q = inp.batch, inp.num_heads, inp.qo_len
     ws = torch.empty(mla.workspace_bytes(B, H, head_split=head_split, qo_len=Q), dtype=torch.uint8,
@@ -207,7 +211,7 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
                 ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
                 kernel_ms=sum(kern) / len(kern), kernel_ms_min=kern[0],
                 kernel_ms_median=kern[len(kern) // 2], kernel_ms_max=kern[-1],
-                graph_ms_per_step=graph_ms, plan_ms=plan_ms, plan=info)
+                graph_ms_per_step=graph_ms, plan_ms=plan_ms, plan=info, copies=copies)
 
 
 def timing_report(m: dict) -> dict:
@@ -235,6 +239,7 @@ def workload_report(m: dict, peaks: dict) -> dict:
          "kernel_ms": round(m["kernel_ms"], 5), "kernel_gbs": round(gbs, 1),
          "kernel_tflops": round(tfs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
          "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "timing": timing_report(m),
+         "input_copies": m["copies"],
          "plan": m["plan"]}
     if peaks:
         r["frac_of_measured_read_peak"] = round(gbs / peaks["stream_read_gbs"], 4)
@@ -404,7 +409,7 @@ def main():
                    "kv_len": int(inp.lengths[0]), "page_size": inp.page_size,
                    "kv_dtype": "bf16", "d_ckv": 512, "d_kpe": 64,
                    "algorithmic_bytes": prim["bytes"], "flops": prim["flops"],
-                   "input_copies": args.copies, "plan": prim["plan"],
+                   "input_copies": prim["copies"], "plan": prim["plan"],
                    "kernel_sha": kernel_sha()},
         "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
