@@ -1990,24 +1990,26 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge of split requests cut into many chunks (more than kInKernelMergeMax;
-// up to 256).  One workgroup per (split request, head, 64-column chunk), so
-// the n partials of a request are read by many workgroups at once rather
-// than by one.  The workgroup reads the head's n partial LSEs (one per
-// thread), reduces them to LSE = M + ln sum_i exp(LSE_i - M), and keeps the
-// weights w_i = exp(LSE_i - LSE) in LDS.  Thread (q, j) (j = tid / 8, q =
-// tid % 8) sums w_i O_i over the 8 columns q of its chunk for partials i = j,
-// j + 32, ...; the 32 sums per 8 columns are added by xor-shuffles within a
-// wave and then wave by wave.  Every reduction has a fixed order, so reruns
-// are bit-identical.
+// up to 256).  One workgroup per (split request, head, column chunk), so the
+// n partials of a request are read by many workgroups at once rather than by
+// one.  L partial lanes per 8 columns (L = 16 for up to 16 chunks, else 32;
+// the workgroup covers 8 * 256 / L columns): thread (q, j) (q = tid % (256 /
+// L), j = tid / (256 / L)) sums w_i O_i over its 8 columns for partials i = j,
+// j + L, ...  Its first partials' loads are issued before the LSE reduction,
+// which they do not depend on: the workgroup reads the head's n partial LSEs
+// (one per thread), reduces them to LSE = M + ln sum_i exp(LSE_i - M) and
+// keeps w_i = exp(LSE_i - LSE) in LDS.  The L sums per 8 columns are added by
+// xor-shuffles within a wave and then wave by wave.  Every reduction has a
+// fixed order, so reruns are bit-identical.
 // ---------------------------------------------------------------------------
-template <int H, bool F16>
+template <int H, bool F16, int L>
 __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs a) {
-  constexpr int kChunks = 8;   // 64-column chunks of a 512-wide row
-  constexpr int kLanes = 32;   // partial lanes per 8 columns
-  constexpr int kBatch = 4;    // partials in flight per thread
+  constexpr int kItems = 256 / L;           // 8-column items per workgroup
+  constexpr int kChunks = 512 / (8 * kItems);
+  constexpr int kBatch = 4;                 // partials in flight per thread
   __shared__ float s_w[256];
   __shared__ float s_red[2][4];
-  __shared__ f32x4 s_o[4][8][2];
+  __shared__ f32x4 s_o[4][kItems][2];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int req = blockIdx.x / (H * kChunks);
@@ -2017,6 +2019,20 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
   const int b = ld_const(cl + 0);
   const int slot0 = ld_const(cl + 1);
   const int n = ld_const(cl + 2);
+
+  const int q = tid % kItems, j = tid / kItems;
+  const int col = ch * (8 * kItems) + q * 8;
+  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
+  auto load_batch = [&](int i0, f32x4 (&x)[kBatch][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = min(i0 + u * L, n - 1);
+      x[u][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
+      x[u][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+    }
+  };
+  f32x4 x[kBatch][2];
+  load_batch(j, x);  // in flight through the LSE reduction
 
   // ---- LSE over the n partials ---------------------------------------------
   const float* pl = a.part_lse + (size_t)slot0 * H + hd;
@@ -2040,23 +2056,14 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
   __syncthreads();
 
   // ---- O = sum_i w_i O_i over this thread's partials -----------------------
-  const int q = tid & 7, j = tid >> 3;
-  const int col = ch * 64 + q * 8;
-  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
   float o8[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) o8[c] = 0.f;
-  for (int i0 = j; i0 < n; i0 += kBatch * kLanes) {
-    f32x4 x[kBatch][2];
+  for (int i0 = j; i0 < n; i0 += kBatch * L) {
+    if (i0 != j) load_batch(i0, x);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int i = min(i0 + u * kLanes, n - 1);
-      x[u][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
-      x[u][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
-    }
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int i = i0 + u * kLanes;
+      const int i = i0 + u * L;
       if (i < n) {
         const float w = s_w[i];
 #pragma unroll
@@ -2067,19 +2074,18 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
       }
     }
   }
-  // lanes q, q + 8, ..., q + 56 of a wave hold partial lanes j = 8 wave + 0..7
+  // a wave holds lanes j = (64 / kItems) wave + 0 .. 64 / kItems - 1 of every
+  // item: lanes that differ in the bits above log2(kItems)
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    o8[c] += __shfl_xor(o8[c], 8);
-    o8[c] += __shfl_xor(o8[c], 16);
-    o8[c] += __shfl_xor(o8[c], 32);
-  }
-  if (lane < 8) {
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int o = kItems; o < 64; o <<= 1) o8[c] += __shfl_xor(o8[c], o);
+  if (lane < kItems) {
     s_o[wave][lane][0] = f32x4{o8[0], o8[1], o8[2], o8[3]};
     s_o[wave][lane][1] = f32x4{o8[4], o8[5], o8[6], o8[7]};
   }
   __syncthreads();
-  if (tid < 8) {
+  if (tid < kItems) {
     bf16x8 out;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
@@ -2087,7 +2093,8 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
 #pragma unroll
       for (int c = 0; c < 4; ++c) out[4 * h2 + c] = to16<F16>(r[c]);
     }
-    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + ch * 64 + tid * 8) = out;
+    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + ch * (8 * kItems) + tid * 8) =
+        out;
   }
   if (tid == 0 && ch == 0) a.lse[(size_t)b * H + hd] = lse_v;
 }
@@ -2288,11 +2295,20 @@ template <int H>
 static hipError_t launch_combine_h(const DecodeArgs& a, int ncomb, int max_splits,
                                    hipStream_t stream) {
   if (max_splits > kInKernelMergeMax) {
-    const dim3 grid(ncomb * H * 8);
-    if (a.o_fp16)
-      hipLaunchKernelGGL((mla_combine_many_kernel<H, true>), grid, dim3(256), 0, stream, a);
-    else
-      hipLaunchKernelGGL((mla_combine_many_kernel<H, false>), grid, dim3(256), 0, stream, a);
+    // 16 partial lanes (4 column chunks of a head) up to 16 chunks, else 32 (8)
+    if (max_splits <= 16) {
+      const dim3 grid(ncomb * H * 4);
+      if (a.o_fp16)
+        hipLaunchKernelGGL((mla_combine_many_kernel<H, true, 16>), grid, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((mla_combine_many_kernel<H, false, 16>), grid, dim3(256), 0, stream, a);
+    } else {
+      const dim3 grid(ncomb * H * 8);
+      if (a.o_fp16)
+        hipLaunchKernelGGL((mla_combine_many_kernel<H, true, 32>), grid, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((mla_combine_many_kernel<H, false, 32>), grid, dim3(256), 0, stream, a);
+    }
   } else {
     hipLaunchKernelGGL(mla_combine_kernel<H>, dim3(ncomb * (H / 4)), dim3(256), 0, stream, a);
   }
