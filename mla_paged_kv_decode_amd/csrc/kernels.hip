@@ -1932,15 +1932,19 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split requests as a launch of its own (after a decode kernel that
-// leaves partials): one thread per (split request, head, 8 columns), so the
-// merge runs on the whole GPU.  LSE = M + ln sum_i exp(LSE_i - M) and
-// O = sum_i exp(LSE_i - LSE) O_i, summed in chunk order i = 0, 1, ...  The 64
-// threads of a wave share one head, so its partial LSEs are one cache line.
+// Merge of split requests as a launch of its own, for requests cut into at
+// most kInKernelMergeMax chunks (launch_combine sends more to the kernel
+// below): one thread per (split request, head, 8 columns), so the merge runs
+// on the whole GPU.  The thread issues the loads of all its partials' LSEs and
+// O slices at once (one memory round trip), then LSE = M + ln sum_i
+// exp(LSE_i - M) and O = sum_i exp(LSE_i - LSE) O_i, summed in chunk order
+// i = 0, 1, ...  The 64 threads of a wave share one head, so its partial LSEs
+// are one cache line.
 // ---------------------------------------------------------------------------
 template <int H>
 __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   constexpr int kBlocksPerReq = H * 64 / 256;
+  constexpr int K = kInKernelMergeMax;
   const int req = blockIdx.x / kBlocksPerReq;
   const int e = (blockIdx.x % kBlocksPerReq) * 256 + threadIdx.x;
   const int hd = e >> 6;
@@ -1948,36 +1952,40 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   const int* cl = reinterpret_cast<const int*>(a.clist) + req * 4;
   const int b = ld_const(cl + 0);
   const int slot0 = ld_const(cl + 1);
-  const int n = ld_const(cl + 2);
+  const int n = min(ld_const(cl + 2), K);
   const float* pl = a.part_lse + (size_t)slot0 * H + hd;
+  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
+  float lv[K];
+  f32x4 x[K][2];
+#pragma unroll
+  for (int v = 0; v < K; ++v) {
+    const int i = min(v, n - 1);
+    lv[v] = pl[(size_t)i * H];
+    x[v][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
+    x[v][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+  }
   float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, pl[i * H]);
+#pragma unroll
+  for (int v = 0; v < K; ++v)
+    if (v < n) M = fmaxf(M, lv[v]);
   const float Mu = M == -INFINITY ? 0.f : M;
   float sum = 0.f;
-  for (int i = 0; i < n; ++i) sum += __expf(pl[i * H] - Mu);
+#pragma unroll
+  for (int v = 0; v < K; ++v)
+    if (v < n) sum += __expf(lv[v] - Mu);
   const bool empty = !(sum > 0.f);
   const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
-  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
   float o8[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) o8[j] = 0.f;
-  for (int i0 = 0; i0 < n; i0 += 4) {
-    f32x4 x[4][2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int i = min(i0 + v, n - 1);
-      x[v][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
-      x[v][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
-    }
+  for (int v = 0; v < K; ++v) {
+    if (v < n) {
+      const float w = empty ? 0.f : __expf(lv[v] - lse_v);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      if (i0 + v < n) {
-        const float w = empty ? 0.f : __expf(pl[(i0 + v) * H] - lse_v);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o8[j] += w * x[v][0][j];
-          o8[4 + j] += w * x[v][1][j];
-        }
+      for (int j = 0; j < 4; ++j) {
+        o8[j] += w * x[v][0][j];
+        o8[4 + j] += w * x[v][1][j];
       }
     }
   }
