@@ -493,7 +493,9 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
 }
 
 // After every head block of a segment is written: the workgroup completing
-// the last chunk of a split request merges the request's partials.
+// the last chunk of a split request merges the request's partials (when the
+// launch merges in the kernel: requests of at most kInKernelMergeMax chunks;
+// otherwise launch_combine does, after this kernel).
 template <int H, int NT, bool F16 = false>
 __device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int slot, int split_req,
                                                int slot0, int nsplit, int tid, uint8_t* smem,
