@@ -142,13 +142,10 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Run the decode for a plan on `stream`: the decode kernel, and the merge of
- * the chunks of requests the plan split.  Requests cut into up to 4 chunks are
- * merged inside the 16/32/64-head kernels by the workgroup that finishes their
- * last chunk; requests cut into more (long contexts at small batch, up to 256
- * chunks), and every split of the 128-head kernel, are merged by a second
- * launch spread over the GPU.  Every merge sums in a fixed order, so the
- * result does not depend on which workgroup finishes first.  Allocates nothing, never
+ * Run the decode for a plan on `stream`: the decode kernel and, when the plan
+ * split requests into chunks (up to 256 per request), a second launch that
+ * merges their partials over the whole GPU.  Every merge sums in a fixed
+ * order, so reruns are bit-identical.  Allocates nothing, never
  * synchronises and never reads device memory from the host, so it may be
  * captured in a HIP graph and replayed while the page-table lengths are
  * unchanged.

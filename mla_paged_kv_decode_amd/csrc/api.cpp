@@ -1,9 +1,9 @@
 // C ABI of the paged MLA decode library (declared in include/mla_decode.h).
 //
 // mla_decode_plan runs the split-KV planner on the host copies of the page
-// table and copies the work list (and zeroed arrival counters) into the
-// caller's workspace; mla_decode_run only launches kernels: the decode kernel
-// and, for kernels that leave split requests as partials, the combine kernel.
+// table and copies the work list into the caller's workspace; mla_decode_run
+// only launches kernels: the decode kernel and, when the plan split requests
+// into chunks, the merge of their partials.
 // It allocates and synchronises nothing, so it is safe to capture in a HIP
 // graph.
 #include <hip/hip_runtime.h>
@@ -43,17 +43,16 @@ int page_shift_of(int32_t p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct Layout {
-  size_t segs, wptr, counters, clist, plse, po, total, meta_bytes;
+  size_t segs, wptr, clist, plse, po, total, meta_bytes;
 };
 
-// workspace: segments (32 B each) | worker_ptr | arrival counters | combine list
-// (16 B per split request) | partial LSE | partial O
+// workspace: segments (32 B each) | worker_ptr | combine list (16 B per split
+// request) | partial LSE | partial O
 Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, int32_t heads) {
   Layout L;
   L.segs = 0;
   L.wptr = align256(L.segs + (size_t)nseg * 32);
-  L.counters = align256(L.wptr + (size_t)(workers + 1) * 4);
-  L.clist = align256(L.counters + (size_t)ncomb * 4);
+  L.clist = align256(L.wptr + (size_t)(workers + 1) * 4);
   L.meta_bytes = L.clist + (size_t)ncomb * 16;
   L.plse = align256(L.meta_bytes);
   L.po = align256(L.plse + (size_t)nparts * heads * 4);
@@ -255,7 +254,7 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          kernel_heads);
 
-  // stage the work list: segments | worker_ptr | zeroed arrival counters | combine list
+  // stage the work list: segments | worker_ptr | combine list
   p->host_meta.assign(p->layout.meta_bytes, 0);
   for (size_t i = 0; i < pl.segments.size(); ++i) {
     const mla::Segment& g = pl.segments[i];
@@ -316,14 +315,9 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.lse = lse;
   a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
   a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
-  a.counters = reinterpret_cast<int32_t*>(ws + p->layout.counters);
   a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o_fp16 = p->kv_dtype == MLA_KV_FP16 ? 1 : 0;
-  // requests cut into many chunks are merged by a launch spread over the GPU
-  // (one workgroup reading a request's n partials alone is latency-bound)
-  const bool merge_in_kernel = p->cfg.fused_merge && p->max_splits <= mla_gpu::kInKernelMergeMax;
-  a.merge_in_kernel = merge_in_kernel ? 1 : 0;
   a.page_shift = p->page_shift;
   a.rows_per_req = p->head_split;
   a.qo_len = p->qo_len;
@@ -336,7 +330,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
     hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     const int ncomb = (int)(p->plan.combine.size() / 4);
-    if (!merge_in_kernel && ncomb > 0) {
+    if (ncomb > 0) {
       e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, p->max_splits, s);
       if (e != hipSuccess) return hip_fail(e, "combine launch");
     }

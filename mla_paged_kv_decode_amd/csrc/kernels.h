@@ -23,13 +23,9 @@ struct DecodeArgs {
   float* lse;                 // [B, H]
   float* part_o;              // [slots, H, 512]
   float* part_lse;            // [slots, H]
-  int32_t* counters;          // arrival counter per split request (0 between launches)
   const int4* clist;          // 4 ints per split request: row, first slot, chunks, 0
   float scale_log2;           // sm_scale * log2(e)
   int32_t o_fp16;             // 1: o is fp16 (fp16 cache and queries), 0: bf16
-  int32_t merge_in_kernel;    // kernels with fused_merge: 1 = the workgroup finishing the
-                              // last chunk of a split request merges it; 0 = the partials
-                              // are left for launch_combine
   int32_t page_shift;         // log2(page_size)
   int32_t rows_per_req;       // kernel rows per request: row b of q/o/lse (kernel-width
                               // groups of query vectors) reads the latent cache of request
@@ -42,9 +38,7 @@ struct DecodeArgs {
 struct DecodeConfig {
   int32_t waves;  // waves per workgroup
   int32_t tile;   // tokens per KV tile = split granularity
-  int32_t lds_bytes;  // LDS per workgroup (also bounds the split merge scratch)
-  int32_t fused_merge;  // 1: the decode kernel merges split requests itself (arrival
-                        // counters); 0: launch_combine does, after the decode kernel
+  int32_t lds_bytes;  // LDS per workgroup
 };
 
 // Kernel for `heads` heads per workgroup and a cache of `kv_dtype` (mla_kv_dtype:
@@ -57,12 +51,12 @@ int decode_blocks_per_cu(int heads, int kv_dtype);
 hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
                          hipStream_t stream);
 // Merge of the ncomb split requests listed in a.clist, each cut into at most
-// max_splits chunks (after kernels with fused_merge = 0, or launched with
-// merge_in_kernel = 0): writes o and lse of those rows.
+// max_splits chunks, after the decode kernel (which leaves their partials):
+// writes o and lse of those rows.
 hipError_t launch_combine(int heads, const DecodeArgs& a, int ncomb, int max_splits,
                           hipStream_t stream);
-// Split requests with more chunks than this are merged by launch_combine
-// (spread over the GPU) rather than by their last workgroup.
-constexpr int kInKernelMergeMax = 4;
+// Up to this many chunks per request, one thread per (head, 8 columns) merges
+// a request; more chunks are spread over several workgroups per head.
+constexpr int kCombineFewMax = 4;
 
 }  // namespace mla_gpu

@@ -45,9 +45,6 @@ namespace mla_gpu {
 
 // 16-head kernel: 1 = the last chunk of a split request merges it, 0 = the
 // separate combine launch does
-#ifndef MLA_STREAM_FUSED_MERGE
-#define MLA_STREAM_FUSED_MERGE 1
-#endif
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -213,30 +210,6 @@ __device__ __forceinline__ void dma16_lanes8(const void* src, uint32_t lds_base)
       : "memory", "m0");
 }
 
-// Device-coherent access to the split partials.  Partials are written and
-// read with the sc1 cache policy (coherent at device scope, as for agent-scope
-// atomic loads and stores), so a workgroup on another XCD sees them without a
-// cache-wide L2 writeback or invalidate, which would also evict the KV data
-// other workgroups are streaming.
-constexpr int kCoherent = 16;  // cache-policy bit SC1
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, 0x00020000);
-}
-__device__ __forceinline__ void store_coherent(const __amdgpu_buffer_rsrc_t r, uint32_t off,
-                                               f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) unsigned, v), r, off, 0, kCoherent);
-}
-__device__ __forceinline__ void store_coherent(const __amdgpu_buffer_rsrc_t r, uint32_t off,
-                                               float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, kCoherent);
-}
-__device__ __forceinline__ f32x4 load_coherent4(const __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCoherent));
-}
-__device__ __forceinline__ float load_coherent1(const __amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, kCoherent));
-}
-
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ (r >> 3); }
 
 __device__ __forceinline__ float wave_max_16(float v) {
@@ -250,123 +223,6 @@ __device__ __forceinline__ float wave_sum_16(float v) {
   v += __shfl_xor(v, 16);
   v += __shfl_xor(v, 32);
   return v;
-}
-
-// Merge of the n partials (slots slot0 .. slot0 + n - 1, in that order) of
-// request b: LSE = M + ln sum_i exp(LSE_i - M), O = sum_i exp(LSE_i - LSE) O_i.
-// Thread items are (head, 8 columns).  Up to kBatch partials, the loads of
-// kPass items of a thread (their heads' partial LSEs and the O slices) are all
-// issued before any is used, so a pass takes one memory round trip and needs
-// no LDS or barrier; more partials take a pass over the LSEs and then the O
-// slices kBatch partials at a time.  The arithmetic per item is the same
-// either way.
-template <int H, int NT, bool F16>
-__device__ __forceinline__ void combine_request(const DecodeArgs& a, int b, int slot0, int n,
-                                                int tid) {
-  constexpr int kItems = H * 64;  // (head, 8 columns)
-  constexpr int K = (kItems + NT - 1) / NT;
-  constexpr int kBatch = 4;
-  constexpr int kPass = K < 2 ? K : 2;  // 72 registers of loads in flight per pass
-  const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + (size_t)slot0 * H);
-  const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + (size_t)slot0 * H * 512);
-  auto finish = [&](int e, float lse_v, const float (&o8)[8]) __attribute__((always_inline)) {
-    const int hd = e >> 6, col = (e & 63) * 8;
-    bf16x8 v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = to16<F16>(o8[j]);
-    *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
-    if ((e & 63) == 0) a.lse[(size_t)b * H + hd] = lse_v;
-  };
-  if (n <= kBatch) {
-#pragma unroll 1
-    for (int k0 = 0; k0 < K; k0 += kPass) {
-    float lv[kPass][kBatch];
-    f32x4 x[kPass][kBatch][2];
-#pragma unroll
-    for (int k = 0; k < kPass; ++k) {
-      const int e = min(tid + (k0 + k) * NT, kItems - 1);
-      const int hd = e >> 6, col = (e & 63) * 8;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = min(u, n - 1);
-        lv[k][u] = load_coherent1(rl, (uint32_t)((i * H + hd) * 4));
-        const uint32_t off = (uint32_t)(((i * H + hd) * 512 + col) * 4);
-        x[k][u][0] = load_coherent4(ro, off);
-        x[k][u][1] = load_coherent4(ro, off + 16);
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kPass; ++k) {
-      const int e = tid + (k0 + k) * NT;
-      if (k0 + k >= K || e >= kItems) break;
-      float M = -INFINITY;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (u < n) M = fmaxf(M, lv[k][u]);
-      const float Mu = M == -INFINITY ? 0.f : M;
-      float sum = 0.f;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u)
-        if (u < n) sum += __expf(lv[k][u] - Mu);
-      const bool empty = !(sum > 0.f);
-      const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
-      float o8[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) o8[j] = 0.f;
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (u < n) {
-          const float w = empty ? 0.f : __expf(lv[k][u] - lse_v);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o8[j] += w * x[k][u][0][j];
-            o8[4 + j] += w * x[k][u][1][j];
-          }
-        }
-      }
-      finish(e, lse_v, o8);
-    }
-    }
-    return;
-  }
-  for (int e = tid; e < kItems; e += NT) {
-    const int hd = e >> 6, col = (e & 63) * 8;
-    float M = -INFINITY;
-    for (int i = 0; i < n; ++i) M = fmaxf(M, load_coherent1(rl, (uint32_t)((i * H + hd) * 4)));
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float sum = 0.f;
-    for (int i = 0; i < n; ++i)
-      sum += __expf(load_coherent1(rl, (uint32_t)((i * H + hd) * 4)) - Mu);
-    const bool empty = !(sum > 0.f);
-    const float lse_v = empty ? -INFINITY : Mu + __logf(sum);
-    float o8[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) o8[j] = 0.f;
-    for (int i0 = 0; i0 < n; i0 += kBatch) {
-      float lv[kBatch];
-      f32x4 x[kBatch][2];
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int i = min(i0 + u, n - 1);
-        lv[u] = load_coherent1(rl, (uint32_t)((i * H + hd) * 4));
-        const uint32_t off = (uint32_t)(((i * H + hd) * 512 + col) * 4);
-        x[u][0] = load_coherent4(ro, off);
-        x[u][1] = load_coherent4(ro, off + 16);
-      }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        if (i0 + u < n) {
-          const float w = empty ? 0.f : __expf(lv[u] - lse_v);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            o8[j] += w * x[u][0][j];
-            o8[4 + j] += w * x[u][1][j];
-          }
-        }
-      }
-    }
-    finish(e, lse_v, o8);
-  }
 }
 
 // End of a segment, one 16-head block: normalise (merging the TS token-split
@@ -409,13 +265,10 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
       }
       if (lane < 16) a.lse[orow] = lse_v;
     } else {
-      const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + ((size_t)slot * H) * 512);
-      const __amdgpu_buffer_rsrc_t rl = coherent_rsrc(a.part_lse + (size_t)slot * H);
+      float* po = a.part_o + ((size_t)slot * H + head) * 512 + 4 * (lane >> 4);
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb)
-        store_coherent(ro, (uint32_t)((head * 512 + cb * 16 + 4 * (lane >> 4)) * 4),
-                       acc[cb] * inv);
-      if (lane < 16) store_coherent(rl, (uint32_t)(head * 4), lse_v);
+      for (int cb = 0; cb < 32; ++cb) *reinterpret_cast<f32x4*>(po + cb * 16) = acc[cb] * inv;
+      if (lane < 16) a.part_lse[(size_t)slot * H + head] = lse_v;
     }
   } else {
     // merge the TS token-split waves of each head group through LDS
@@ -475,48 +328,19 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
         *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
         if (ts == 0 && (e % (kCols / 8)) == 0) a.lse[(size_t)b * H + hd] = lse_v;
       } else {
-        const __amdgpu_buffer_rsrc_t ro = coherent_rsrc(a.part_o + ((size_t)slot * H) * 512);
+        float* po = a.part_o + ((size_t)slot * H + hd) * 512 + col;
         f32x4 y0, y1;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           y0[i] = o8[i] * inv;
           y1[i] = o8[4 + i] * inv;
         }
-        store_coherent(ro, (uint32_t)((hd * 512 + col) * 4), y0);
-        store_coherent(ro, (uint32_t)((hd * 512 + col + 4) * 4), y1);
-        if (ts == 0 && (e % (kCols / 8)) == 0)
-          store_coherent(coherent_rsrc(a.part_lse + (size_t)slot * H), (uint32_t)(hd * 4), lse_v);
+        *reinterpret_cast<f32x4*>(po) = y0;
+        *reinterpret_cast<f32x4*>(po + 4) = y1;
+        if (ts == 0 && (e % (kCols / 8)) == 0) a.part_lse[(size_t)slot * H + hd] = lse_v;
       }
     }
     lds_barrier();  // merge area free before the next segment's loads
-  }
-}
-
-// After every head block of a segment is written: the workgroup completing
-// the last chunk of a split request merges the request's partials (when the
-// launch merges in the kernel: requests of at most kInKernelMergeMax chunks;
-// otherwise launch_combine does, after this kernel).
-template <int H, int NT, bool F16 = false>
-__device__ __forceinline__ void finish_segment(const DecodeArgs& a, int b, int slot, int split_req,
-                                               int slot0, int nsplit, int tid, uint8_t* smem,
-                                               int* s_last) {
-  // ---- last chunk of a split request merges the request's partials --------
-  if (slot >= 0 && a.merge_in_kernel) {
-    vm_wait_n<0>();  // this wave's coherent partial stores have completed
-    lds_barrier();
-    if (tid == 0) {
-      // system scope: the add is performed at memory, coherent for every XCD
-      const int prev = __hip_atomic_fetch_add(a.counters + split_req, 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_SYSTEM);
-      const int last = prev == nsplit - 1;
-      if (last)
-        __hip_atomic_store(a.counters + split_req, 0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_SYSTEM);
-      *s_last = last;
-    }
-    lds_barrier();
-    if (*s_last) combine_request<H, NT, F16>(a, b, slot0, nsplit, tid);
-    lds_barrier();  // merge scratch free before the next segment's loads
   }
 }
 
@@ -565,7 +389,6 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
   constexpr int H = S::kHeads;
   constexpr int T = S::kTile;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (SGPR)
@@ -603,9 +426,6 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
     const int t0 = ld_const(sgp + 1);
     const int send = ld_const(sgp + 2);
     const int slot = ld_const(sgp + 3);
-    const int split_req = ld_const(sgp + 4);
-    const int slot0 = ld_const(sgp + 5);
-    const int nsplit = ld_const(sgp + 6);
     const int kvb = ld_const(sgp + 7);  // request whose latent cache this segment reads
     const int pbeg = ld_const(a.kv_indptr + kvb);
     const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
@@ -852,7 +672,6 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
     for (int hb = 0; hb < HB; ++hb)
       write_head_block<H, HG, TS>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, wh * HB + hb,
                                   wh * HB + hb, ts, lane, smem);
-    finish_segment<H, S::kThreads>(a, b, slot, split_req, slot0, nsplit, tid, smem, &s_last);
   }
 }
 
@@ -932,7 +751,6 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
   constexpr int TS = S::kWaves;
   constexpr int NL = S::kLoads;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
-  __shared__ int s_last;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -982,9 +800,6 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     const int t0 = ld_const(sgp + 1);
     const int send = ld_const(sgp + 2);
     const int slot = ld_const(sgp + 3);
-    const int split_req = ld_const(sgp + 4);
-    const int slot0 = ld_const(sgp + 5);
-    const int nsplit = ld_const(sgp + 6);
     const int kvb = ld_const(sgp + 7);  // request whose latent cache this segment reads
     const int pbeg = ld_const(a.kv_indptr + kvb);
     const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
@@ -1212,9 +1027,6 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     for (int hb = 0; hb < HB; ++hb)
       write_head_block<H, 1, TS, kF16>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave, lane,
                                  smem);
-    if constexpr (MLA_STREAM_FUSED_MERGE)
-      finish_segment<H, S::kThreads, kF16>(a, b, slot, split_req, slot0, nsplit, tid, smem,
-                                           &s_last);
   }
 }
 
@@ -1934,8 +1746,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split requests as a launch of its own, for requests cut into at
-// most kInKernelMergeMax chunks (launch_combine sends more to the kernel
+// Merge of split requests (a launch after the decode kernel), for requests cut
+// into at most kCombineFewMax chunks (launch_combine sends more to the kernel
 // below): one thread per (split request, head, 8 columns), so the merge runs
 // on the whole GPU.  The thread issues the loads of all its partials' LSEs and
 // O slices at once (one memory round trip), then LSE = M + ln sum_i
@@ -1946,7 +1758,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 template <int H>
 __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   constexpr int kBlocksPerReq = H * 64 / 256;
-  constexpr int K = kInKernelMergeMax;
+  constexpr int K = kCombineFewMax;
   const int req = blockIdx.x / kBlocksPerReq;
   const int e = (blockIdx.x % kBlocksPerReq) * 256 + threadIdx.x;
   const int hd = e >> 6;
@@ -1999,8 +1811,8 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge of split requests cut into many chunks (more than kInKernelMergeMax;
-// up to 256).  One workgroup per (split request, head, column chunk), so the
+// Merge of split requests cut into many chunks (more than kCombineFewMax;
+// up to 256), as long contexts at small batch are.  One workgroup per (split request, head, column chunk), so the
 // n partials of a request are read by many workgroups at once rather than by
 // one.  L partial lanes per 8 columns (L = 16 for up to 16 chunks, else 32;
 // the workgroup covers 8 * 256 / L columns): thread (q, j) (q = tid % (256 /
@@ -2131,7 +1943,7 @@ static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream)
 
 template <int KVT>
 static DecodeConfig wide_config() {
-  return DecodeConfig{WideShape<KVT>::kWaves, WideShape<KVT>::kTile, WideShape<KVT>::kLdsBytes, 0};
+  return DecodeConfig{WideShape<KVT>::kWaves, WideShape<KVT>::kTile, WideShape<KVT>::kLdsBytes};
 }
 
 template <int KVT>
@@ -2148,7 +1960,7 @@ static int wide_occupancy() {
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 static DecodeConfig config_of() {
   using S = RingShape<HG, HB, TS, MB, NSTAGE>;
-  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes, 1};
+  return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
 }
 
 template <int HB, int KVT, int NB>
@@ -2162,7 +1974,7 @@ static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t s
 template <int HB, int KVT, int NB>
 static DecodeConfig stream_config_of() {
   using S = StreamShape<HB, KVT, NB>;
-  return DecodeConfig{S::kWaves, 16, S::kLdsBytes, MLA_STREAM_FUSED_MERGE};
+  return DecodeConfig{S::kWaves, 16, S::kLdsBytes};
 }
 
 template <int HB, int KVT, int NB>
@@ -2304,7 +2116,7 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
 template <int H>
 static hipError_t launch_combine_h(const DecodeArgs& a, int ncomb, int max_splits,
                                    hipStream_t stream) {
-  if (max_splits > kInKernelMergeMax) {
+  if (max_splits > kCombineFewMax) {
     // 16 partial lanes (4 column chunks of a head) up to 16 chunks, else 32 (8)
     if (max_splits <= 16) {
       const dim3 grid(ncomb * H * 4);
