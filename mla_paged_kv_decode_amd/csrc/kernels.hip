@@ -814,27 +814,18 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     const int nmine = ngroups > wave ? (ngroups - 1 - wave) / TS + 1 : 0;
 
     // Q^T for the row block into LDS: item (block, chunk c, head h) at
-    // ((block * 72 + c) * 16 + h) * 16
-    uint8_t* qlds = smem + S::kQOffset;
-    lds_barrier();  // previous segment's merge / combine done with this LDS
-    for (int x = tid; x < HB * 72 * 16; x += S::kThreads) {
+    // ((block * 72 + c) * 16 + h) * 16.  Its loads go out first, then the
+    // loads of this wave's first NB groups (into registers), and only then is
+    // Q written to LDS: the group loads are in flight during Q's round trip.
+    constexpr int kQItems = (HB * 72 * 16 + S::kThreads - 1) / S::kThreads;
+    u32x4 qv[kQItems];
+#pragma unroll
+    for (int k = 0; k < kQItems; ++k) {
+      const int x = min(tid + k * S::kThreads, HB * 72 * 16 - 1);
       const int hb = x / (72 * 16);
       const int c = (x >> 4) % 72, h = hb * 16 + (x & 15);
-      const u32x4 v = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
-                             : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
-      *reinterpret_cast<u32x4*>(qlds + x * 16) = v;
-    }
-    lds_barrier();
-    const uint8_t* qbase = qlds + ((lane >> 4) * 16 + qr) * 16;  // + (hb * 72 + s * 4) * 256
-
-    float m_ref[HB], l_run[HB];
-    f32x4 acc[HB][32];
-#pragma unroll
-    for (int hb = 0; hb < HB; ++hb) {
-      m_ref[hb] = -INFINITY;
-      l_run[hb] = 0.f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      qv[k] = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
+                     : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
     }
 
     // Fetch this wave's j-th group into registers: NL 16-byte loads per lane
@@ -893,6 +884,38 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     // Consume group j from registers st: LDS write and refill (always, so the
     // memory queue looks the same on every path), then QK, online softmax and
     // PV if the group exists.
+    u32x4 st[NB][NL];
+    f32x4 sc[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) fetch(u, st[u], sc[u]);
+
+    uint8_t* qlds = smem + S::kQOffset;
+    lds_barrier();  // previous segment's merge / combine done with this LDS
+    {
+      // (computed here, not hoisted out of the segment loop: kept live across
+      // the loop, these addresses would be spilled, and a spill reload waits
+      // for every load in flight, the group fetches above included)
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      uint8_t* qw = qlds + t * 16;  // item t + k kThreads at qw + k kThreads 16
+#pragma unroll
+      for (int k = 0; k < kQItems; ++k)
+        if ((k + 1) * S::kThreads <= HB * 72 * 16 || t + k * S::kThreads < HB * 72 * 16)
+          *reinterpret_cast<u32x4*>(qw + k * S::kThreads * 16) = qv[k];
+    }
+    lds_barrier();
+    const uint8_t* qbase = qlds + ((lane >> 4) * 16 + qr) * 16;  // + (hb * 72 + s * 4) * 256
+
+    float m_ref[HB], l_run[HB];
+    f32x4 acc[HB][32];
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      m_ref[hb] = -INFINITY;
+      l_run[hb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
     auto consume = [&](int j, u32x4 (&st)[NL], f32x4& sc) __attribute__((always_inline)) {
       f32x4 sig = sc;
       if constexpr (kC16) {
@@ -1011,15 +1034,9 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       }
     };
 
-    {
-      u32x4 st[NB][NL];
-      f32x4 sc[NB];
+    for (int j = 0; j < nmine; j += NB) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) fetch(u, st[u], sc[u]);
-      for (int j = 0; j < nmine; j += NB) {
-#pragma unroll
-        for (int u = 0; u < NB; ++u) consume(j + u, st[u], sc[u]);
-      }
+      for (int u = 0; u < NB; ++u) consume(j + u, st[u], sc[u]);
     }
 
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
