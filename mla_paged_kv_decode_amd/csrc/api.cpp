@@ -150,6 +150,7 @@ struct mla_plan_s {
   mla_gpu::DecodeConfig cfg{};
   mla::Plan plan;
   int32_t max_splits = 0;  // most chunks of one split request
+  int32_t one_seg = 0;     // every worker runs exactly the segment of its own index
   Layout layout{};
   std::vector<uint8_t> host_meta;  // staged work list (kept alive for the async copy)
   uint8_t* workspace = nullptr;
@@ -250,6 +251,9 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   const mla::Plan& pl = p->plan;
   for (size_t i = 2; i < pl.combine.size(); i += 4)
     p->max_splits = std::max(p->max_splits, pl.combine[i]);
+  p->one_seg = (int64_t)pl.segments.size() == (int64_t)pl.num_workers ? 1 : 0;
+  for (size_t w = 0; p->one_seg && w < pl.worker_ptr.size(); ++w)
+    if (pl.worker_ptr[w] != (int32_t)w) p->one_seg = 0;
   const int64_t ncomb = (int64_t)pl.combine.size() / 4;
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          kernel_heads);
@@ -322,6 +326,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.rows_per_req = p->head_split;
   a.qo_len = p->qo_len;
   a.head_log2 = log2_exact(p->heads);
+  a.one_seg = p->one_seg;
   if (p->ev_before) {
     hipError_t e = hipEventRecord(p->ev_before, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

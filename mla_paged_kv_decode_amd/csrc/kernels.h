@@ -33,6 +33,8 @@ struct DecodeArgs {
   int32_t qo_len;             // queries per request: query vector j of a request is head
   int32_t head_log2;          // j & (2^head_log2 - 1) of query j >> head_log2, and sees the
                               // first L_b - (qo_len - 1 - (j >> head_log2)) tokens
+  int32_t one_seg;            // 1: worker w runs segment w alone (worker_ptr is the
+                              // identity), so a workgroup skips that load
 };
 
 struct DecodeConfig {

@@ -417,8 +417,8 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
 #pragma unroll
   for (int A = 0; A < 4; ++A) tr_off[A] = tr_base + (((2 * A) | (tr_q >> 1)) ^ swz(tr_r)) * 16;
 
-  const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
-  const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
+  const int seg_begin = a.one_seg ? (int)blockIdx.x : ld_const(a.worker_ptr + blockIdx.x);
+  const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
     const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
@@ -791,8 +791,8 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       st8k[e] = (rk >> 3) * kHalfGroupBytes + 8 * 1024 + ((rk & 7) * 8 + ((2 * (lane & 3) + e) ^ swz(rk))) * 16;
   }
 
-  const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
-  const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
+  const int seg_begin = a.one_seg ? (int)blockIdx.x : ld_const(a.worker_ptr + blockIdx.x);
+  const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
     const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
@@ -1247,8 +1247,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
   float* stat = reinterpret_cast<float*>(smem + S::kStatOffset);
   int* limit_s = reinterpret_cast<int*>(smem + S::kLimitOffset);
 
-  const int seg_begin = ld_const(a.worker_ptr + blockIdx.x);
-  const int seg_end = ld_const(a.worker_ptr + blockIdx.x + 1);
+  const int seg_begin = a.one_seg ? (int)blockIdx.x : ld_const(a.worker_ptr + blockIdx.x);
+  const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
     const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
