@@ -151,6 +151,7 @@ struct mla_plan_s {
   mla::Plan plan;
   int32_t max_splits = 0;  // most chunks of one split request
   int32_t one_seg = 0;     // every worker runs exactly the segment of its own index
+  int32_t req_div = 0;     // with one_seg: segment i reads request i / req_div (0: no such c)
   Layout layout{};
   std::vector<uint8_t> host_meta;  // staged work list (kept alive for the async copy)
   uint8_t* workspace = nullptr;
@@ -254,6 +255,15 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   p->one_seg = (int64_t)pl.segments.size() == (int64_t)pl.num_workers ? 1 : 0;
   for (size_t w = 0; p->one_seg && w < pl.worker_ptr.size(); ++w)
     if (pl.worker_ptr[w] != (int32_t)w) p->one_seg = 0;
+  if (p->one_seg && !pl.segments.empty()) {
+    const int32_t first = pl.segments[0].request / head_split;
+    int32_t c = 0;
+    while (c < (int32_t)pl.segments.size() && pl.segments[c].request / head_split == first) ++c;
+    bool ok = true;
+    for (size_t i = 0; ok && i < pl.segments.size(); ++i)
+      ok = pl.segments[i].request / head_split == (int32_t)i / c;
+    p->req_div = ok ? c : 0;
+  }
   const int64_t ncomb = (int64_t)pl.combine.size() / 4;
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          kernel_heads);
@@ -327,6 +337,7 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
   a.qo_len = p->qo_len;
   a.head_log2 = log2_exact(p->heads);
   a.one_seg = p->one_seg;
+  a.req_div = p->req_div;
   if (p->ev_before) {
     hipError_t e = hipEventRecord(p->ev_before, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");

@@ -35,6 +35,9 @@ struct DecodeArgs {
                               // first L_b - (qo_len - 1 - (j >> head_log2)) tokens
   int32_t one_seg;            // 1: worker w runs segment w alone (worker_ptr is the
                               // identity), so a workgroup skips that load
+  int32_t req_div;            // > 0 (only with one_seg): segment i reads the latent cache of
+                              // request i / req_div, so its page-table loads need not wait
+                              // for the segment record
 };
 
 struct DecodeConfig {

@@ -382,6 +382,55 @@ struct RingShape {
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
+// Metadata of segment si: its record (request row, token range, partial slot)
+// and the device page-table entries of the request whose latent cache it reads.
+// When the plan fixes that request as si / req_div, the page-table loads do not
+// wait for the record, so all of them arrive in one memory round trip; the
+// last-page length is loaded unconditionally (in bounds for every request).
+struct SegMeta {
+  int b, t0, send, slot, kvb, pbeg, npg, last_len;
+};
+__device__ __forceinline__ SegMeta load_seg(const DecodeArgs& a, int si) {
+  const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
+  SegMeta m;
+  if (a.req_div > 0) {
+    // One asm statement issues the three scalar loads and waits for them, so
+    // the compiler can neither sink the record load below the others nor read
+    // a destination before the wait.
+    m.kvb = si / a.req_div;
+    typedef int i32x4s __attribute__((ext_vector_type(4)));
+    typedef int i32x2s __attribute__((ext_vector_type(2)));
+    i32x4s rec;
+    i32x2s ip;
+    int last;
+    asm volatile(
+        "s_load_dwordx4 %0, %3, 0x0\n\t"
+        "s_load_dwordx2 %1, %4, 0x0\n\t"
+        "s_load_dword %2, %5, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(rec), "=&s"(ip), "=&s"(last)
+        : "s"(sgp), "s"(a.kv_indptr + m.kvb), "s"(a.kv_last_page_len + m.kvb)
+        : "memory");
+    m.b = rec.x;
+    m.t0 = rec.y;
+    m.send = rec.z;
+    m.slot = rec.w;
+    m.pbeg = ip.x;
+    m.npg = ip.y - ip.x;
+    m.last_len = last;
+  } else {
+    m.b = ld_const(sgp + 0);
+    m.t0 = ld_const(sgp + 1);
+    m.send = ld_const(sgp + 2);
+    m.slot = ld_const(sgp + 3);
+    m.kvb = ld_const(sgp + 7);
+    m.pbeg = ld_const(a.kv_indptr + m.kvb);
+    m.npg = ld_const(a.kv_indptr + m.kvb + 1) - m.pbeg;
+    m.last_len = ld_const(a.kv_last_page_len + m.kvb);
+  }
+  return m;
+}
+
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 __global__ void __launch_bounds__(64 * (HG / HB) * TS)
     mla_decode_ring_kernel(const DecodeArgs a) {
@@ -421,15 +470,10 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
   const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
-    const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
-    const int b = ld_const(sgp + 0);
-    const int t0 = ld_const(sgp + 1);
-    const int send = ld_const(sgp + 2);
-    const int slot = ld_const(sgp + 3);
-    const int kvb = ld_const(sgp + 7);  // request whose latent cache this segment reads
-    const int pbeg = ld_const(a.kv_indptr + kvb);
-    const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
-    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
+    const SegMeta sm = load_seg(a, si);
+    const int b = sm.b, t0 = sm.t0, send = sm.send, slot = sm.slot;
+    const int kvb = sm.kvb, pbeg = sm.pbeg;
+    const int ldev = sm.npg > 0 ? ((sm.npg - 1) << page_shift) + sm.last_len : 0;
     const int t1 = min(send, ldev);
     // score rows at or past tlim[hb] are masked (end of chunk, or causal limit)
     int tlim[HB];
@@ -795,15 +839,10 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
   const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
-    const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
-    const int b = ld_const(sgp + 0);
-    const int t0 = ld_const(sgp + 1);
-    const int send = ld_const(sgp + 2);
-    const int slot = ld_const(sgp + 3);
-    const int kvb = ld_const(sgp + 7);  // request whose latent cache this segment reads
-    const int pbeg = ld_const(a.kv_indptr + kvb);
-    const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
-    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
+    const SegMeta sm = load_seg(a, si);
+    const int b = sm.b, t0 = sm.t0, send = sm.send, slot = sm.slot;
+    const int kvb = sm.kvb, pbeg = sm.pbeg;
+    const int ldev = sm.npg > 0 ? ((sm.npg - 1) << page_shift) + sm.last_len : 0;
     const int t1 = min(send, ldev);
     // score rows at or past tlim[hb] are masked (end of chunk, or causal limit)
     int tlim[HB];
@@ -1251,15 +1290,10 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
   const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
-    const int* sgp = reinterpret_cast<const int*>(a.segs) + si * 8;
-    const int b = ld_const(sgp + 0);
-    const int t0 = ld_const(sgp + 1);
-    const int send = ld_const(sgp + 2);
-    const int slot = ld_const(sgp + 3);
-    const int kvb = ld_const(sgp + 7);
-    const int pbeg = ld_const(a.kv_indptr + kvb);
-    const int npg = ld_const(a.kv_indptr + kvb + 1) - pbeg;
-    const int ldev = npg > 0 ? ((npg - 1) << page_shift) + ld_const(a.kv_last_page_len + kvb) : 0;
+    const SegMeta sm = load_seg(a, si);
+    const int b = sm.b, t0 = sm.t0, send = sm.send, slot = sm.slot;
+    const int kvb = sm.kvb, pbeg = sm.pbeg;
+    const int ldev = sm.npg > 0 ? ((sm.npg - 1) << page_shift) + sm.last_len : 0;
     const int t1 = min(send, ldev);
     // CAUSAL (several queries per request): score rows of this lane's QK
     // head at or past its causal limit are masked too.  The limit is kept in
