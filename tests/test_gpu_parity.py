@@ -367,3 +367,34 @@ def test_many_chunk_merge_reruns_bit_identical(heads, lengths):
     plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, heads, 64)
     info = plan.info()
     assert info["num_partials"] // info["num_split_requests"] > 4
+
+
+@pytest.mark.gpu
+def test_one_segment_fast_path_matches_general_path():
+    # The same chunks, run one per workgroup (the workgroup's segment is its own
+    # index and its request is computed from it, so the segment record and the
+    # page-table loads go out together) and two per workgroup (segment range
+    # from worker_ptr, request from the record): the partials and their merge are
+    # the same, so the results are bit-identical.
+    import mla_paged_kv_decode_amd as mla
+    B, H = 64, 16
+    inp = synth.make_inputs([1024] * B, H, 64, seed=37)
+    t = dev(inp)
+    res = []
+    for mw in (0, 128):
+        ws = torch.empty(mla.workspace_bytes(B, H), dtype=torch.uint8, device="cuda")
+        plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 64, inp.kv_dtype, ws,
+                        force_splits=4, max_workers=mw)
+        info = plan.info()
+        print("case max_workers=%d workers=%d segments=%d" %
+              (mw, info["num_workers"], info["num_segments"]), flush=True)
+        o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        plan.run(t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_scale"], t["kv_indptr"],
+                 t["kv_indices"], t["kv_last_page_len"], inp.sm_scale, o, lse)
+        torch.cuda.synchronize()
+        res.append((o, lse, info))
+    assert res[0][2]["num_workers"] == res[0][2]["num_segments"] == 4 * B
+    assert res[1][2]["num_workers"] < res[1][2]["num_segments"] == 4 * B
+    assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
+    assert torch.equal(res[0][1], res[1][1])
