@@ -171,6 +171,35 @@ mla_status mla_decode_run(mla_plan_t plan, const void* q_nope, const void* q_pe,
                           float sm_scale, void* o, float* lse, void* stream);
 
 /*
+ * mla_decode_run without a caller workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The plan's work list and the split partials go to a
+ * device array that the library holds on each GPU it runs on (one per GPU,
+ * for the life of the process) of MLA_NOALLOC_SCRATCH_BYTES; each call first
+ * copies the plan's work list there (hipMemcpyAsync on `stream`, from the
+ * plan's host memory, which must stay alive while the call may execute),
+ * then launches what mla_decode_run launches.  Nothing is allocated on the
+ * device or the host.
+ *   p: any plan, also one made without a workspace (workspace == NULL in
+ *   mla_decode_plan); its own workspace, if any, is not used.  The other
+ *   arguments, results and determinism are those of mla_decode_run.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that may overlap on one GPU (other streams, other threads,
+ * other plans in flight) race and give wrong results.  Calls in order on one
+ * stream are safe.
+ * Errors: those of mla_decode_run (MLA_ERR_NOT_UPLOADED aside), and
+ * MLA_ERR_WORKSPACE_TOO_SMALL (nothing launched; mla_last_error() gives the
+ * sizes) when the plan needs more than MLA_NOALLOC_SCRATCH_BYTES, e.g. more
+ * than 256 partial chunks at 128 heads.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+mla_status mla_decode_run_noalloc(mla_plan_t plan, const void* q_nope, const void* q_pe,
+                                  const void* ckv, const void* kpe, const float* kv_scale,
+                                  const int32_t* kv_indptr, const int32_t* kv_indices,
+                                  const int32_t* kv_last_page_len, float sm_scale, void* o,
+                                  float* lse, void* stream);
+
+/*
  * Optional instrumentation for measuring the decode kernel on its own: when
  * set, mla_decode_run records `before` on its stream right before the decode
  * kernel and `after` right after it (hipEvent_t values passed as void*; the

@@ -29,11 +29,14 @@ _KPE_BF16 = (KV_FP8_E4M3_KPE_BF16, KV_INT8_KPE_BF16)
 # fp16 inputs: fp16 cache, queries and output
 KV_FP16 = 5
 D_CKV, D_KPE = 512, 64
+# MLA_NOALLOC_SCRATCH_BYTES: the per-GPU array that mla_decode_run_noalloc uses
+NOALLOC_SCRATCH_BYTES = 72 << 20
 
 EXPORTED_SYMBOLS = (
     "mla_decode_workspace_bytes",
     "mla_decode_plan",
     "mla_decode_run",
+    "mla_decode_run_noalloc",
     "mla_decode_plan_destroy",
     "mla_status_string",
     "mla_last_error",
@@ -81,6 +84,8 @@ def load_library(path: str = LIB_PATH):
     lib.mla_decode_plan.restype = ctypes.c_int
     lib.mla_decode_run.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P]
     lib.mla_decode_run.restype = ctypes.c_int
+    lib.mla_decode_run_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, ctypes.c_float, P, P, P]
+    lib.mla_decode_run_noalloc.restype = ctypes.c_int
     lib.mla_decode_plan_destroy.argtypes = [P]
     lib.mla_decode_plan_destroy.restype = None
     lib.mla_status_string.argtypes = [ctypes.c_int]
@@ -214,6 +219,20 @@ class Plan:
     def run(self, q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len,
             sm_scale: float, o, lse, stream=None) -> None:
         """``mla_decode_run`` on device tensors (o and lse are written)."""
+        self._run(self._lib.mla_decode_run, "mla_decode_run", q_nope, q_pe, ckv, kpe, kv_scale,
+                  kv_indptr, kv_indices, kv_last_page_len, sm_scale, o, lse, stream)
+
+    def run_noalloc(self, q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices,
+                    kv_last_page_len, sm_scale: float, o, lse, stream=None) -> None:
+        """``mla_decode_run_noalloc``: as ``run``, with the work list and partials in
+        the library's per-GPU scratch instead of the plan's workspace (which may be
+        None).  Calls that overlap on one GPU race."""
+        self._run(self._lib.mla_decode_run_noalloc, "mla_decode_run_noalloc", q_nope, q_pe, ckv,
+                  kpe, kv_scale, kv_indptr, kv_indices, kv_last_page_len, sm_scale, o, lse,
+                  stream)
+
+    def _run(self, fn, name, q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr, kv_indices,
+             kv_last_page_len, sm_scale, o, lse, stream) -> None:
         import torch
         B, H = self.batch * self.qo_len, self.num_heads
         t16 = torch.float16 if self.kv_dtype == KV_FP16 else torch.bfloat16
@@ -260,12 +279,11 @@ class Plan:
                         ("kv_scale", kv_scale), ("o", o), ("lse", lse)):
             if t is not None and not t.is_contiguous():
                 raise ValueError(name + " must be contiguous")
-        st = self._lib.mla_decode_run(
-            self._h, _dptr(q_nope), _dptr(q_pe), _dptr(ckv), _dptr(kpe), _dptr(kv_scale),
-            _dptr(kv_indptr), _dptr(kv_indices), _dptr(kv_last_page_len), float(sm_scale),
-            _dptr(o), _dptr(lse), _stream_ptr(stream))
+        st = fn(self._h, _dptr(q_nope), _dptr(q_pe), _dptr(ckv), _dptr(kpe), _dptr(kv_scale),
+                _dptr(kv_indptr), _dptr(kv_indices), _dptr(kv_last_page_len), float(sm_scale),
+                _dptr(o), _dptr(lse), _stream_ptr(stream))
         if st != MLA_OK:
-            raise MlaError(st, "mla_decode_run")
+            raise MlaError(st, name)
 
 
 def cache_append(ckv_new, kpe_new, slots, ckv, kpe, kv_dtype: int = KV_BF16, kv_scale=None,

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla_decode.so")
-SOURCES = ["api.cpp", "planner.cpp", "kernels.hip", "append.hip", "peaks.hip"]
+SOURCES = ["api.cpp", "planner.cpp", "kernels.hip", "append.hip", "peaks.hip",
+           "noalloc.hip"]
 
 
 def hipcc() -> str:

@@ -18,16 +18,30 @@
 #include "../../include/mla_decode.h"
 #include "append.h"
 #include "kernels.h"
+#include "plan_internal.h"
 #include "planner.h"
 
 namespace {
 
 thread_local std::string g_last_error;
 
+}  // namespace
+
+namespace mla_abi {
+
+void set_last_error(const std::string& what) { g_last_error = what; }
+
 mla_status hip_fail(hipError_t e, const char* what) {
   g_last_error = std::string(what) + ": " + hipGetErrorString(e);
   return MLA_ERR_HIP;
 }
+
+}  // namespace mla_abi
+
+namespace {
+
+using mla_abi::hip_fail;
+using mla_abi::Layout;
 
 bool supported_heads(int32_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
 
@@ -41,10 +55,6 @@ int page_shift_of(int32_t p) {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-struct Layout {
-  size_t segs, wptr, clist, plse, po, total, meta_bytes;
-};
 
 // workspace: segments (32 B each) | worker_ptr | combine list (16 B per split
 // request) | partial LSE | partial O
@@ -144,19 +154,67 @@ mla::PlanParams plan_params(int32_t num_queries, int32_t head_split, int32_t wor
 
 }  // namespace
 
-struct mla_plan_s {
-  int32_t batch = 0, heads = 0, page_size = 0, page_shift = 0, kv_dtype = 0;
-  int32_t qo_len = 1, head_split = 1, kernel_heads = 0;
-  mla_gpu::DecodeConfig cfg{};
-  mla::Plan plan;
-  int32_t max_splits = 0;  // most chunks of one split request
-  int32_t one_seg = 0;     // every worker runs exactly the segment of its own index
-  int32_t req_div = 0;     // with one_seg: segment i reads request i / req_div (0: no such c)
-  Layout layout{};
-  std::vector<uint8_t> host_meta;  // staged work list (kept alive for the async copy)
-  uint8_t* workspace = nullptr;
-  hipEvent_t ev_before = nullptr, ev_after = nullptr;
-};
+namespace mla_abi {
+
+mla_status run_on_workspace(mla_plan_s* p, uint8_t* ws, const void* q_nope, const void* q_pe,
+                            const void* ckv, const void* kpe, const float* kv_scale,
+                            const int32_t* kv_indptr, const int32_t* kv_indices,
+                            const int32_t* kv_last_page_len, float sm_scale, void* o, float* lse,
+                            void* stream) {
+  if (p->batch == 0) return MLA_OK;
+  if (!q_nope || !q_pe || !ckv || !kpe || !kv_indptr || !kv_indices || !kv_last_page_len || !o ||
+      !lse)
+    return MLA_ERR_INVALID_ARG;
+  const bool scaled = p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP16;
+  if (scaled != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return MLA_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+
+  mla_gpu::DecodeArgs a;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_pe = static_cast<const uint16_t*>(q_pe);
+  a.ckv = static_cast<const uint8_t*>(ckv);
+  a.kpe = static_cast<const uint8_t*>(kpe);
+  a.kv_scale = kv_scale;
+  a.kv_indptr = kv_indptr;
+  a.kv_indices = kv_indices;
+  a.kv_last_page_len = kv_last_page_len;
+  a.segs = reinterpret_cast<const int4*>(ws + p->layout.segs);
+  a.worker_ptr = reinterpret_cast<const int32_t*>(ws + p->layout.wptr);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
+  a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
+  a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.o_fp16 = p->kv_dtype == MLA_KV_FP16 ? 1 : 0;
+  a.page_shift = p->page_shift;
+  a.rows_per_req = p->head_split;
+  a.qo_len = p->qo_len;
+  a.head_log2 = log2_exact(p->heads);
+  a.one_seg = p->one_seg;
+  a.req_div = p->req_div;
+  if (p->ev_before) {
+    hipError_t e = hipEventRecord(p->ev_before, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  if (p->plan.num_workers > 0) {
+    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    const int ncomb = (int)(p->plan.combine.size() / 4);
+    if (ncomb > 0) {
+      e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, p->max_splits, s);
+      if (e != hipSuccess) return hip_fail(e, "combine launch");
+    }
+  }
+  if (p->ev_after) {
+    hipError_t e = hipEventRecord(p->ev_after, s);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  return MLA_OK;
+}
+
+}  // namespace mla_abi
 
 extern "C" {
 
@@ -304,58 +362,8 @@ mla_status mla_decode_run(mla_plan_t p, const void* q_nope, const void* q_pe, co
                           float sm_scale, void* o, float* lse, void* stream) {
   if (!p) return MLA_ERR_INVALID_ARG;
   if (!p->workspace) return MLA_ERR_NOT_UPLOADED;
-  if (p->batch == 0) return MLA_OK;
-  if (!q_nope || !q_pe || !ckv || !kpe || !kv_indptr || !kv_indices || !kv_last_page_len || !o ||
-      !lse)
-    return MLA_ERR_INVALID_ARG;
-  const bool scaled = p->kv_dtype != MLA_KV_BF16 && p->kv_dtype != MLA_KV_FP16;
-  if (scaled != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
-  if (!(sm_scale == sm_scale)) return MLA_ERR_INVALID_ARG;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = p->workspace;
-
-  mla_gpu::DecodeArgs a;
-  a.q_nope = static_cast<const uint16_t*>(q_nope);
-  a.q_pe = static_cast<const uint16_t*>(q_pe);
-  a.ckv = static_cast<const uint8_t*>(ckv);
-  a.kpe = static_cast<const uint8_t*>(kpe);
-  a.kv_scale = kv_scale;
-  a.kv_indptr = kv_indptr;
-  a.kv_indices = kv_indices;
-  a.kv_last_page_len = kv_last_page_len;
-  a.segs = reinterpret_cast<const int4*>(ws + p->layout.segs);
-  a.worker_ptr = reinterpret_cast<const int32_t*>(ws + p->layout.wptr);
-  a.o = static_cast<uint16_t*>(o);
-  a.lse = lse;
-  a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
-  a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
-  a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
-  a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.o_fp16 = p->kv_dtype == MLA_KV_FP16 ? 1 : 0;
-  a.page_shift = p->page_shift;
-  a.rows_per_req = p->head_split;
-  a.qo_len = p->qo_len;
-  a.head_log2 = log2_exact(p->heads);
-  a.one_seg = p->one_seg;
-  a.req_div = p->req_div;
-  if (p->ev_before) {
-    hipError_t e = hipEventRecord(p->ev_before, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  if (p->plan.num_workers > 0) {
-    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
-    if (e != hipSuccess) return hip_fail(e, "decode launch");
-    const int ncomb = (int)(p->plan.combine.size() / 4);
-    if (ncomb > 0) {
-      e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, p->max_splits, s);
-      if (e != hipSuccess) return hip_fail(e, "combine launch");
-    }
-  }
-  if (p->ev_after) {
-    hipError_t e = hipEventRecord(p->ev_after, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
-  return MLA_OK;
+  return mla_abi::run_on_workspace(p, p->workspace, q_nope, q_pe, ckv, kpe, kv_scale, kv_indptr,
+                                   kv_indices, kv_last_page_len, sm_scale, o, lse, stream);
 }
 
 void mla_decode_plan_destroy(mla_plan_t p) { delete p; }
