@@ -39,6 +39,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace mla_gpu {
@@ -1360,6 +1362,35 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
                            my_half * kHalfGroupBytes));
       return td;
     };
+    // The same in two steps: the page numbers of tile k (scalar loads), and
+    // the plan from them (no memory access), so that the loads can be put
+    // where a wait covers their latency anyway.
+    auto pages_of = [&](int k, int (&pg)[2]) __attribute__((always_inline)) {
+      const int kc = min(k, ntiles - 1);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int gs = min(t0 + kc * T + 16 * gi, last_group);
+        pg[gi] = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
+      }
+    };
+    auto plan_from = [&](int k, int st, const int (&pg)[2]) __attribute__((always_inline)) {
+      const int kc = min(k, ntiles - 1);
+      const int my_group = wave >> 1, my_half = wave & 1;
+      const int gs = min(t0 + kc * T + 16 * my_group, last_group);
+      const int r = my_half * 8 + ld_r_lo;
+      const int tok = min(gs + r, t1 - 1);
+      const size_t page_row = (size_t)pg[my_group] << page_shift;
+      const uint32_t sw = ((lane & 7) ^ swz(r)) * 16;
+      TileDma td;
+      td.cpage = a.ckv + page_row * 1024;
+      td.kpage = a.kpe + page_row * 128;
+      td.coff = (tok & page_mask) * 1024 + sw;
+      td.koff = (tok & page_mask) * 128 + sw;
+      td.dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+          LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
+                           my_half * kHalfGroupBytes));
+      return td;
+    };
     auto dma_one = [&](const TileDma& td, int u) __attribute__((always_inline)) {
       if (u < 8)
         dma16_s(td.cpage, td.coff + u * 128, td.dst + u * 1024);
@@ -1464,12 +1495,16 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 #pragma unroll
       for (int s = 0; s < 36; ++s)
         qf[s] = load16_untracked(s < 32 ? qn + 2 * s + g : qp + 2 * (s - 32) + g);
-      if (ntiles > 0) tile_pages(0);
-      for (int k = 0; k < NS - 1 && k < ntiles; ++k) issue_tile(k, k);
-      if (ntiles >= NS - 1)
+      // (tiles past the last one load the last tile again, into a ring slot
+      // that is not read: every wait below is then the same constant)
+      if (ntiles > 0) {
+        tile_pages(0);
+#pragma unroll
+        for (int k = 0; k < NS - 1; ++k) issue_tile(k, k);
         vm_wait_n<9 * (NS - 1)>();
-      else
-        vm_wait_n<0>();  // short segment (or none: nothing may stay in flight)
+      } else {
+        vm_wait_n<0>();  // no tile: nothing may stay in flight
+      }
     } else {
       if (ntiles > 0) {
         tile_pages(0);
@@ -1502,12 +1537,268 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     float m_ref = -INFINITY;  // head 32 w + l32, log2 domain
     float l_run = 0.f;        // this lane's 16 tokens of that head
 
-    // 16-bit cache: the loads of tile it + NS - 1 are issued one per QK
-    // k-step group, behind that group's MFMAs (issued together right after the
-    // barrier, the 36 loads of the workgroup queue at the CU's address unit
-    // for some 600 cycles)
+    if constexpr (kC16) {
+      // ---- 16-bit cache: software-pipelined tile loop ------------------------
+      // Iteration it: [tile it + 1 landed; barrier] P^T and the rescale of
+      // tile it, kept in registers since its softmax, go to LDS; QK of tile
+      // it + 1, with the loads of tile it + 3 issued one per k-step group;
+      // [barrier] PV of tile it, with the softmax of tile it + 1 placed
+      // between its MFMAs: the VALU work of the softmax issues while the
+      // matrix core works instead of between the two contractions.  Tiles it ..
+      // it + 3 fill the 4 ring slots (tile it + 3 goes to the slot of tile
+      // it - 1, whose PV every wave finished before the first barrier).  The
+      // arithmetic of every tile is the one of a loop without the overlap.
+      static_assert(NS == 4 && QR == 36, "16-bit pipeline: 4 ring slots, Q^T in registers");
+      f32x16 sacc;                  // scores of the tile whose softmax comes next
+      bf16x8 pq0 = {}, pq1 = {};    // P^T of the last softmaxed tile (PV B operand)
+      float alpha_q = 1.f;          // its rescale factor (1: none)
+      unsigned resc_q = 0;          // wave-uniform: its softmax moved the reference max
+      float tmax = -INFINITY, psum = 0.f, m_use = 0.f;
+      const int tlim = CAUSAL ? limit_s[32 * wave + l32] : t1;
+      // LDS addresses of the P^T, rescale-factor and flag areas: one opaque
+      // base, so that the accesses take immediate offsets from two per-lane
+      // registers instead of a register per address
+      uint32_t small_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + S::kPOffset);
+      asm volatile("" : "+s"(small_base));
+      const uint32_t p_lane = small_base + lane * 16;  // P^T [wave][ks][lane]
+      const uint32_t a_lane = small_base + l32 * 4;    // alpha [head]
+      constexpr uint32_t kAl = S::kAlphaOffset - S::kPOffset, kFl = S::kFlagOffset - S::kPOffset;
+      auto lds_at = [](uint32_t addr) __attribute__((always_inline)) {
+        return (LDS_AS uint8_t*)(uintptr_t)addr;
+      };
+
+      // QK: S^T[32 tokens][32 heads of this wave] of the tile at `stage`.  The
+      // K operands of k-step group g are read two groups ahead (every wave
+      // reads the whole tile here, so LDS latency is several MFMA durations);
+      // the loads of a later tile go out one per group.  The scheduling
+      // barriers keep each group's reads, MFMAs and load where they are put.
+      auto qk_tile = [&](const uint8_t* stage, bool dma_on, const TileDma& tdma)
+          __attribute__((always_inline)) {
+        // qk_off[u] = qk_off[0] ^ 32 u (the swizzle flips bits 5-6 only, and the
+        // tile base is a multiple of 1 KiB), so one register per tile serves all 4
+        // (computed here, per tile: kept live across the loop, such addresses
+        // are spilled, and a spill reload waits for every load in flight)
+        uint32_t kbase = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)stage + qk_off[0];
+        asm volatile("" : "+v"(kbase));
+        auto read_k = [&](int gi, bf16x8 (&kf)[4]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            kf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+                lds_at((kbase ^ (32u * u)) + gi * 1024));
+        };
+        bf16x8 kq[3][4];
+        read_k(0, kq[0]);
+        read_k(1, kq[1]);
+#pragma unroll
+        for (int gi = 0; gi < 9; ++gi) {
+          if (gi + 2 < 9) read_k(gi + 2, kq[(gi + 2) % 3]);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int s = 4 * gi + u;
+            if (s == 0)
+              mfma_vgpr<kF16, true, false>(sacc, kq[gi % 3][u], qf[s]);
+            else if (s == 35)
+              mfma_vgpr<kF16, false, true>(sacc, kq[gi % 3][u], qf[s]);
+            else
+              mfma_vgpr<kF16, false, false>(sacc, kq[gi % 3][u], qf[s]);
+          }
+          if (dma_on) dma_one(tdma, gi);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+
+      // Online softmax of the scores in sacc (log2 domain, lazy rescale), cut
+      // into 32 slots so that PV can issue one slot behind each of its 32
+      // MFMAs, while the matrix core is busy with it (a wave's VALU work
+      // overlaps its own MFMAs as long as a slot stays within about 4 simple
+      // instructions).  sacc holds raw scores here, -inf where masked
+      // (mask_tile); the scale s = sm_scale log2 e > 0 commutes with the max,
+      // so the row max is taken over raw scores and scaled once, and each
+      // probability is exp2(fma(raw, s, -m)).  Slots 0-3: row max over this
+      // lane's 16 scores; 4: with the other lane half of the head; 5-7: the
+      // rescale decision (alpha = 1 unless the wave moves its reference max; a
+      // head with no visible token so far keeps alpha = 1) and the new
+      // reference; 8-23: the probabilities, summed in pairs (r, r + 8) in
+      // order r = 0..7; 24: the row sum.
+      float m_next = 0.f;
+      auto sm_slot = [&](int j) __attribute__((always_inline)) {
+        if (j < 4) {
+          tmax = fmaxf(fmaxf(tmax, sacc[4 * j]), sacc[4 * j + 1]);
+          tmax = fmaxf(fmaxf(tmax, sacc[4 * j + 2]), sacc[4 * j + 3]);
+        } else if (j == 4) {
+          // max with lane l ^ 32 (the same head's other 16 tokens)
+          float lo = tmax, hi = tmax;
+          asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1"
+                       : "+v"(lo), "+v"(hi));
+          tmax = fmaxf(lo, hi) * a.scale_log2;
+        } else if (j == 5) {
+          resc_q = __builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0 ? 1u : 0u;
+          m_next = resc_q ? fmaxf(m_ref, tmax) : m_ref;
+        } else if (j == 6) {
+          alpha_q = (resc_q && m_next != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_next) : 1.f;
+          m_ref = m_next;
+          m_use = m_ref == -INFINITY ? 0.f : -m_ref;  // the negated reference
+        } else if (j == 7) {
+          l_run *= alpha_q;
+          tmax = -INFINITY;
+          psum = 0.f;
+        } else if (j < 24) {
+          const int r = (j - 8) >> 1;
+          if (((j - 8) & 1) == 0) {
+            sacc[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[r], a.scale_log2, m_use));
+          } else {
+            const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[8 + r], a.scale_log2, m_use));
+            psum += sacc[r] + e1;
+            pq0[r] = to16<kF16>(sacc[r]);
+            pq1[r] = to16<kF16>(e1);
+          }
+        } else if (j == 24) {
+          l_run += psum;
+        }
+      };
+      // Scores of tokens past this lane's limit become -inf, in one pass when
+      // the tile is not visible to every head of the wave (the last tiles of a
+      // segment, or the causal tail), so that the slots need no per-element mask
+      auto mask_tile = [&](int tile_start) __attribute__((always_inline)) {
+        if (__builtin_amdgcn_ballot_w64(tile_start + T > tlim) != 0) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
+            sacc[r] = tok < tlim ? sacc[r] : -INFINITY;
+          }
+        }
+      };
+
+      // PV of the tile at `stage` (P^T of every wave and the rescale flags are
+      // in LDS); WITH_SM: the softmax slots of the next tile behind its MFMAs.
+      auto pv_tile = [&](auto with_sm, const uint8_t* stage)
+          __attribute__((always_inline)) {
+        constexpr bool kSm = decltype(with_sm)::value;
+        // pv_off[h][c1] = (pv_off[0][0] ^ (16 h + 64 c1)) + 9216 h (the swizzle
+        // flips bits 4 and 6 only; tile and block bases are multiples of 1 KiB),
+        // so the 4 addresses of a tile come from one register, the rest are
+        // immediates
+        uint32_t vt = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)stage + 2048 * wave + pv_off[0][0];
+        asm volatile("" : "+v"(vt));
+        uint32_t vx[2][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int c1 = 0; c1 < 2; ++c1) vx[h][c1] = vt ^ (16u * h + 64u * c1);
+        auto read_v = [&](int i) __attribute__((always_inline)) {
+          const uint32_t off = (i >> 2) * kGroupBytes + ((i & 3) >> 1) * 1024;
+          const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_AS s16x4*)lds_at(vx[0][i & 1] + off));
+          const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (LDS_AS s16x4*)lds_at(vx[1][i & 1] + off + kHalfGroupBytes));
+          const bf16x4 a0 = __builtin_bit_cast(bf16x4, v0);
+          const bf16x4 a1 = __builtin_bit_cast(bf16x4, v1);
+          bf16x8 vf;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            vf[jj] = a0[jj];
+            vf[4 + jj] = a1[jj];
+          }
+          return vf;
+        };
+        const u32x4 fl = *reinterpret_cast<const LDS_AS u32x4*>(lds_at(small_base + kFl));
+        bf16x8 vcur = read_v(0);  // V^T of step i; step i + 1 is read at the start of step i
+        // P^T operands of k-step 0; those of k-step 1 into the same registers,
+        // each right after the last MFMA that reads its k-step-0 operand
+        bf16x8 pb[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb)
+          pb[hb] = *reinterpret_cast<const LDS_AS bf16x8*>(lds_at(p_lane + (hb * 2) * 1024));
+        {
+          const unsigned any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+          if (any != 0) {
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) {
+              if (__builtin_amdgcn_readfirstlane(fl[hb]) != 0) {
+                const float al = *reinterpret_cast<const LDS_AS float*>(
+                    lds_at(a_lane + kAl + 128 * hb));
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) scale_agpr16(acc[cb][hb], al);
+              }
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int cb = i & 3;
+          const bf16x8 vnext = read_v(i < 7 ? i + 1 : i);
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) {
+            if (i == 7 && hb == 3)
+              mfma_agpr<kF16, true>(acc[cb][hb], vcur, pb[hb]);
+            else
+              mfma_agpr<kF16>(acc[cb][hb], vcur, pb[hb]);
+            if (i == 3)
+              pb[hb] = *reinterpret_cast<const LDS_AS bf16x8*>(lds_at(p_lane + (hb * 2 + 1) * 1024));
+            if constexpr (kSm) {
+              __builtin_amdgcn_sched_barrier(0);
+              sm_slot(4 * i + hb);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
+          vcur = vnext;
+        }
+      };
+
+      // The page numbers of tile it + 3 are loaded at the top of iteration
+      // it: scalar loads share the lgkm counter with LDS reads and complete
+      // out of order, so a wait for any K read issued after them would be a
+      // wait for all; issued before the tile wait and the barrier, whose own
+      // lgkm wait covers them, their latency is hidden.
+      if (ntiles > 0) {
+        // tile 0 landed (tiles 1 and 2 may be in flight), QK and softmax of it
+        vm_wait_n<18>();
+        lds_barrier();
+        qk_tile(smem, false, TileDma{});
+        mask_tile(t0);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) sm_slot(j);
+      }
+      auto iteration = [&](auto with_sm, int it) __attribute__((always_inline)) {
+        constexpr bool nxt = decltype(with_sm)::value;  // a tile it + 1 exists
+        // tile it + 1 landed: tiles 0 .. it + 2 have been issued (the last
+        // ones possibly as reloads of the last tile), so tile it + 2 may still
+        // be in flight
+        int pg3[2] = {0, 0};
+        if constexpr (nxt) {
+          pages_of(it + 3, pg3);
+          vm_wait_n<9>();
+        }
+        lds_barrier();  // PV of tile it - 1 done everywhere; tile it + 1 in LDS
+        *reinterpret_cast<LDS_AS bf16x8*>(lds_at(p_lane + wave * 2048)) = pq0;
+        *reinterpret_cast<LDS_AS bf16x8*>(lds_at(p_lane + wave * 2048 + 1024)) = pq1;
+        if (resc_q && lane < 32)
+          *reinterpret_cast<LDS_AS float*>(lds_at(a_lane + kAl + 128 * wave)) = alpha_q;
+        // (tile 0: the accumulators are still zero, nothing to rescale; a flag
+        // rather than a branch on it, so that the loop is not peeled for it)
+        if (lane == 0)
+          *reinterpret_cast<LDS_AS unsigned*>(lds_at(small_base + kFl + 4 * wave)) =
+              it > 0 ? resc_q : 0u;
+        if constexpr (nxt) {
+          // tile it + 3 into the slot of tile it - 1 (past the end: the last
+          // tile again)
+          const TileDma tdma = plan_from(it + 3, (it + 3) % NS, pg3);
+          qk_tile(smem + ((it + 1) % NS) * S::kStageBytes, true, tdma);
+          mask_tile(t0 + (it + 1) * T);
+        }
+        lds_barrier();  // P^T and the rescale of tile it from every wave
+        pv_tile(with_sm, smem + (it % NS) * S::kStageBytes);
+      };
+      for (int it = 0; it + 1 < ntiles; ++it) iteration(std::true_type{}, it);
+      if (ntiles > 0) iteration(std::false_type{}, ntiles - 1);
+      vm_wait_n<0>();  // the trailing reloads have landed (their slots are reused)
+    }
+
+    // 8-bit cache: one tile per iteration (QK, softmax, PV in turn); the codes
+    // of the next tile are converted to bf16 while the current one is computed
     bool dma_on = false;
     TileDma tdma{};
+    if constexpr (!kC16)
     for (int it = 0; it < ntiles; ++it) {
       const uint8_t* stage;
       if constexpr (kC16) {
@@ -1651,7 +1942,9 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0) {
         const float m_new = fmaxf(m_ref, tmax);
-        const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 when m_ref = -inf
+        // 0 when m_ref = -inf; 1 for a head with no visible token yet (its
+        // wave may hold another query's heads that moved the max)
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);
         l_run *= alpha;
         m_ref = m_new;
         if (lane < 32) alpha_s[32 * wave + lane] = alpha;
