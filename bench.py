@@ -22,8 +22,11 @@ time when the same steps replay from hipGraphs (one captured per input copy)
 beside the eager one.
 
 `roofline.achieved` divides the algorithmic bytes (or flops) of one launch by
-the decode kernel's own average duration, measured with HIP events recorded
-around that kernel on its stream by the library over the timed steps.
+the decode kernel's own average duration, measured with HIP events that the
+library records right before and right after that kernel on its stream over
+the timed steps; `decode_plus_merge` gives the same figures for the whole
+mla_decode_run (decode kernel and, for split requests, the merge launch),
+from events the bench records around each call on the same stream.
 """
 from __future__ import annotations
 
@@ -54,6 +57,21 @@ SECONDARY = ("compute_b64_h128_l4096_p64", "varlen_b768_h64_l1to2048_p16",
              "longctx_b4_h128_l32768_p64")
 KV_NAMES = {0: "bf16", 1: "fp8_e4m3", 2: "int8", 3: "fp8_e4m3_ckv_bf16_kpe", 4: "int8_ckv_bf16_kpe",
             5: "fp16"}
+# the arithmetic type of the contractions: bf16 MFMAs (8-bit codes are
+# converted to bf16 exactly), fp16 MFMAs for fp16 inputs
+DTYPE_NAMES = {0: "bf16", 1: "bf16", 2: "bf16", 3: "bf16", 4: "bf16", 5: "f16"}
+
+
+def kernel_name(info: dict) -> str:
+    """The decode kernel a plan launches (as rocprofv3 names it)."""
+    w, k, q = info["kernel_heads"], info["kv_dtype"], info["qo_len"]
+    if w == 16:
+        return "mla_decode_stream_kernel<1, %d, 2>" % k
+    if w == 32:
+        return "mla_decode_ring_kernel<2, 1, 2, 1, 4>"
+    if w == 64:
+        return "mla_decode_ring_kernel<4, 1, 1, 2, 4>"
+    return "mla_decode_wide_kernel<%d, %s>" % (k, "true" if q > 1 else "false")
 
 
 class Hip:
@@ -84,7 +102,7 @@ class Hip:
 
 
 def synth_heads(name: str) -> int:
-    from mla_paged_kv_decode_amd import synth
+    import synth
     return synth.WORKLOADS[name]["heads"]
 
 
@@ -140,7 +158,7 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
             l2_domains: int = 0, graph: bool = False) -> dict:
     import torch
     import mla_paged_kv_decode_amd as mla
-    from mla_paged_kv_decode_amd import synth
+    import synth
 
     inp = synth.make_workload(name)
     # between two reads of one copy, the other copies stream at least 512 MB
@@ -167,8 +185,9 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    before = [hip.event() for _ in range(steps)]
+    before = [hip.event() for _ in range(steps)]  # decode kernel (library events)
     after = [hip.event() for _ in range(steps)]
+    call_end = [hip.event() for _ in range(steps)]  # end of the whole call
     start, stop = hip.event(), hip.event()
     stream = torch.cuda.current_stream().cuda_stream
     torch.cuda.synchronize()
@@ -177,12 +196,14 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     for i in range(steps):
         plan.set_events(before[i], after[i])
         step(i)
+        hip.lib.hipEventRecord(call_end[i], ctypes.c_void_p(stream))
     hip.lib.hipEventRecord(stop, ctypes.c_void_p(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     plan.set_events(None, None)
     total_ms = hip.elapsed_ms(start, stop)
     kern = sorted(hip.elapsed_ms(before[i], after[i]) for i in range(steps))
+    call = sorted(hip.elapsed_ms(before[i], call_end[i]) for i in range(steps))
     graph_ms = None
     if graph:
         # the same steps replayed from hipGraphs (one per input copy, captured
@@ -204,51 +225,82 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
         torch.cuda.synchronize()
         graph_ms = hip.elapsed_ms(start, stop) / steps
         del graphs
-    for e in before + after + [start, stop]:
+    for e in before + after + call_end + [start, stop]:
         hip.destroy(e)
     info = plan.info()
     return dict(name=name, inp=inp, bytes=inp.algorithmic_bytes(), flops=inp.flops(),
                 ms_per_step=total_ms / steps, wall_ms_per_step=wall * 1e3 / steps,
                 kernel_ms=sum(kern) / len(kern), kernel_ms_min=kern[0],
                 kernel_ms_median=kern[len(kern) // 2], kernel_ms_max=kern[-1],
+                call_ms=sum(call) / len(call), call_ms_median=call[len(call) // 2],
                 graph_ms_per_step=graph_ms, plan_ms=plan_ms, plan=info, copies=copies)
 
 
 def timing_report(m: dict) -> dict:
-    """Per-launch decode times (HIP events around the library's kernels) and
-    the step time from hipGraph replay beside the eager one."""
+    """Per-launch decode-kernel times (library events around that kernel),
+    whole-call times (decode + merge), and the step time from hipGraph replay
+    beside the eager one."""
     r = {k: round(m[k], 5) for k in ("kernel_ms", "kernel_ms_median", "kernel_ms_min",
-                                      "kernel_ms_max", "ms_per_step")}
+                                      "kernel_ms_max", "call_ms", "call_ms_median",
+                                      "ms_per_step")}
     g = m.get("graph_ms_per_step")
     r["graph_ms_per_step"] = round(g, 5) if g is not None else None
     return r
 
 
+def roofline_report(m: dict, peaks: dict):
+    """(roofline, decode_plus_merge) of one measured workload.  The roofline is
+    the decode kernel's (the dominant kernel, timed alone): HBM bytes for the
+    memory-bound shapes (at most 64 query vectors per request), bf16 MFMA flops
+    from 128 query vectors per request.  decode_plus_merge: the same figures for
+    the whole call."""
+    inp, info = m["inp"], m["plan"]
+    mfma = inp.num_heads * inp.qo_len >= 128
+
+    def rate(ms):
+        s_ = ms * 1e-3
+        return m["bytes"] / s_ / 1e9, m["flops"] / s_ / 1e12
+
+    gbs, tfs = rate(m["kernel_ms"])
+    if mfma:
+        roof = {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    roof["traffic"] = measured_traffic(m["name"])
+    roof["kernel"] = kernel_name(info)
+    roof["kernel_ms"] = round(m["kernel_ms"], 5)
+    roof["kernel_dtype"] = DTYPE_NAMES[inp.kv_dtype]
+    cgbs, ctfs = rate(m["call_ms"])
+    dpm = {"ms": round(m["call_ms"], 5), "gbs": round(cgbs, 1), "tflops": round(ctfs, 1),
+           "frac": round((ctfs / MFMA_BF16_PEAK_TFS) if mfma else (cgbs / HBM_PEAK_GBS), 4)}
+    if peaks:
+        meas = peaks["mfma_bf16_tflops"] if mfma else peaks["stream_read_gbs"]
+        roof["frac_of_measured_peak"] = round((tfs if mfma else gbs) / meas, 4)
+        dpm["frac_of_measured_peak"] = round((ctfs if mfma else cgbs) / meas, 4)
+    return roof, dpm
+
+
 def workload_report(m: dict, peaks: dict) -> dict:
-    """Throughput of one measured workload against both roofs: HBM bytes for
-    the memory-bound shapes (at most 64 query vectors per request), bf16 MFMA
-    flops from 128 (h_q = 128, or h_q x qo_len >= 128)."""
+    """Throughput of one measured workload (value per eager step) with its
+    roofline entry."""
     inp = m["inp"]
+    mfma = inp.num_heads * inp.qo_len >= 128
     k_s = m["kernel_ms"] * 1e-3
     gbs, tfs = m["bytes"] / k_s / 1e9, m["flops"] / k_s / 1e12
-    mfma = inp.num_heads * inp.qo_len >= 128
+    roof, dpm = roofline_report(m, peaks)
     r = {"workload": m["name"], "kv_dtype": KV_NAMES[inp.kv_dtype], "qo_len": inp.qo_len,
          "value": round((m["flops"] / 1e12 if mfma else m["bytes"] / 1e9)
                         / (m["ms_per_step"] * 1e-3), 2),
          "unit": "TFLOP/s" if mfma else "GB/s", "ms_per_step": round(m["ms_per_step"], 5),
          "kernel_ms": round(m["kernel_ms"], 5), "kernel_gbs": round(gbs, 1),
-         "kernel_tflops": round(tfs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
-         "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4), "timing": timing_report(m),
-         "input_copies": m["copies"],
-         "plan": m["plan"]}
+         "kernel_tflops": round(tfs, 1), "timing": timing_report(m),
+         "input_copies": m["copies"], "plan": m["plan"], "roofline": roof,
+         "decode_plus_merge": dpm}
     if peaks:
         r["frac_of_measured_read_peak"] = round(gbs / peaks["stream_read_gbs"], 4)
         r["frac_of_measured_mfma_peak"] = round(tfs / peaks["mfma_bf16_tflops"], 4)
-    r["roofline"] = ({"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                      "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)} if mfma else
-                     {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)})
-    r["roofline"]["traffic"] = measured_traffic(m["name"])
     return r
 
 
@@ -299,34 +351,59 @@ def measure_append(kv_dtype: int, n: int, steps: int, warmup: int, hip: Hip) -> 
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}}
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inp, target_s: float) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload:
     the first n (request, head) rows, doubling n until the run takes at least
     target_s seconds or covers the workload; scaled to GB/s of algorithmic bytes
-    of the rows done."""
+    of the rows done.  Also: the whole tiny workload (batch 4, 16 heads, 256
+    tokens) on one thread, median of 5 runs."""
     import numpy as np
     import oracle
-    threads = os.cpu_count() or 1
+    import synth
+    nproc = os.cpu_count() or 1
+    threads = nproc
     env = os.environ.get("OMP_NUM_THREADS")
     if env and env.isdigit():
         threads = min(threads, int(env))
-    total_rows = inp.batch * inp.num_heads
+    total_rows = inp.batch * inp.num_heads * inp.qo_len
     n = min(total_rows, max(threads, 16))
     while True:
         rows = np.arange(n, dtype=np.int32)
         t0 = time.perf_counter()
         oracle.decode(inp.q_nope, inp.q_pe, inp.ckv, inp.kpe, inp.kv_indptr, inp.kv_indices,
                       inp.kv_last_page_len, inp.sm_scale, inp.page_size, inp.kv_dtype,
-                      inp.kv_scale, rows=rows, threads=threads)
+                      inp.kv_scale, rows=rows, threads=threads, qo_len=inp.qo_len)
         dt = time.perf_counter() - t0
         if dt >= target_s or n >= total_rows:
             break
         n = min(total_rows, max(n * 2, int(n * target_s / max(dt, 1e-3) * 1.1)))
     frac = n / total_rows
+    tiny = synth.make_workload("tiny_b4_h16_l256_p16")
+    single = []
+    for _ in range(5):
+        t0 = time.perf_counter()
+        oracle.decode(tiny.q_nope, tiny.q_pe, tiny.ckv, tiny.kpe, tiny.kv_indptr,
+                      tiny.kv_indices, tiny.kv_last_page_len, tiny.sm_scale, tiny.page_size,
+                      tiny.kv_dtype, tiny.kv_scale, threads=1)
+        single.append(time.perf_counter() - t0)
+    single.sort()
     return {"value": round(inp.algorithmic_bytes() * frac / dt / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "sample": "first %d of %d (request, head) rows of the same workload, fp64 C oracle, "
-                      "%.2f s" % (n, total_rows, dt)}
+                      "%d threads, %.2f s" % (n, total_rows, threads, dt),
+            "cpu_model": cpu_model(), "nproc": nproc,
+            "single_thread_tiny_b4_h16_l256_p16_s": round(single[2], 5)}
 
 
 def main():
@@ -389,13 +466,13 @@ def main():
                    args.head_split if synth_heads(args.workload) >= 64 else 0, args.l2_domains,
                    graph=not args.no_graph)
     inp = prim["inp"]
-    gbs = prim["bytes"] / (prim["ms_per_step"] * 1e-3) / 1e9
-    kern_gbs = prim["bytes"] / (prim["kernel_ms"] * 1e-3) / 1e9
-    traffic = measured_traffic(args.workload)
+    mfma = inp.num_heads * inp.qo_len >= 128
+    per_step_s = prim["ms_per_step"] * 1e-3
+    roof, dpm = roofline_report(prim, peaks)
     out = {
         "metric": METRIC,
-        "value": round(gbs, 2),
-        "unit": "GB/s",
+        "value": round((prim["flops"] / 1e12 if mfma else prim["bytes"] / 1e9) / per_step_s, 2),
+        "unit": "TFLOP/s" if mfma else "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -403,20 +480,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": DTYPE_NAMES[inp.kv_dtype],
         "data": "synthetic",
         "config": {"workload": args.workload, "batch": inp.batch, "h_q": inp.num_heads,
-                   "kv_len": int(inp.lengths[0]), "page_size": inp.page_size,
-                   "kv_dtype": "bf16", "d_ckv": 512, "d_kpe": 64,
-                   "algorithmic_bytes": prim["bytes"], "flops": prim["flops"],
-                   "input_copies": prim["copies"], "plan": prim["plan"],
+                   "qo_len": inp.qo_len, "kv_len": int(inp.lengths[0]),
+                   "page_size": inp.page_size, "kv_dtype": KV_NAMES[inp.kv_dtype],
+                   "d_ckv": 512, "d_kpe": 64, "algorithmic_bytes": prim["bytes"],
+                   "flops": prim["flops"], "input_copies": prim["copies"], "plan": prim["plan"],
                    "kernel_sha": kernel_sha()},
-        "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "mla_decode_stream_kernel<1, 0, 2>",
-                     "kernel_ms": round(prim["kernel_ms"], 5),
-                     "frac_of_measured_read_peak": (round(kern_gbs / peaks["stream_read_gbs"], 4)
-                                                    if peaks else None)},
+        "roofline": roof,
+        "decode_plus_merge": dpm,
         "timing": timing_report(prim),
         "plan_ms": round(prim["plan_ms"], 4),
         "measured_peaks": peaks,

@@ -32,6 +32,9 @@
  *     is reported as MLA_ERR_HIP and the text of the last error is available
  *     from mla_last_error().
  *   - stream is a hipStream_t passed as void* (NULL = the null stream).
+ *   - kv_dtype and status arguments are int32_t holding a value of
+ *     mla_kv_dtype / mla_status, so that any integer a caller passes is
+ *     checked rather than read as an out-of-range enum.
  *   - qo_len (mla_plan_opts.qo_len, default 1) queries per request: q_nope is
  *     [batch * qo_len, H, 512], q_pe [batch * qo_len, H, 64], o
  *     [batch * qo_len, H, 512], lse [batch * qo_len, H]; row b * qo_len + i is
@@ -138,7 +141,7 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
  */
 mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
                            const int32_t* kv_last_page_len_host, int32_t batch, int32_t num_heads,
-                           int32_t page_size, mla_kv_dtype kv_dtype, const mla_plan_opts* opts,
+                           int32_t page_size, int32_t kv_dtype, const mla_plan_opts* opts,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -147,17 +150,24 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
  * merges their partials over the whole GPU.  Every merge sums in a fixed
  * order, so reruns are bit-identical.  Allocates nothing, never
  * synchronises and never reads device memory from the host, so it may be
- * captured in a HIP graph and replayed while the page-table lengths are
- * unchanged.
+ * captured in a HIP graph and replayed.  A plan stays valid while requests
+ * grow: the chunk boundaries are fixed at plan time, but the last chunk of
+ * every request (and the one chunk of a request that was empty) runs to the
+ * request's length as the device page table gives it at run time, so tokens
+ * appended after planning (new slots, new pages, later pages renumbered in
+ * kv_indptr) are decoded by the same plan and graph; only the balance of the
+ * work across CUs reflects the plan-time lengths.  A request must not become
+ * shorter than it was at plan time.
  *   q_nope  device bf16 [batch * qo_len, H, 512]   q_pe device bf16 [batch * qo_len, H, 64]
  *           (fp16 for MLA_KV_FP16, as are ckv, kpe and o)
  *   ckv     device [pages, P, 512]           kpe  device [pages, P, 64]
  *           (bf16, or 8-bit codes per the plan's kv_dtype)
  *   kv_scale device fp32 [pages, P] for 8-bit caches, NULL for bf16
  *   kv_indptr [batch+1], kv_indices [n], kv_last_page_len [batch]: device int32
- *           copies of the page table the plan was made from.  The kernel never
- *           reads past a request's device-side length; kv_indices entries must
- *           be valid page numbers (not checked on the device).
+ *           page table of the plan's batch as it stands at run time (the one the
+ *           plan was made from, or the same requests grown since).  The kernel
+ *           never reads past a request's device-side length; kv_indices entries
+ *           must be valid page numbers (not checked on the device).
  *   sm_scale softmax scale applied to the whole 576-wide score
  *   o       device bf16 [batch * qo_len, H, 512] (written)
  *   lse     device fp32 [batch * qo_len, H] (written)
@@ -201,8 +211,9 @@ mla_status mla_decode_run_noalloc(mla_plan_t plan, const void* q_nope, const voi
 
 /*
  * Optional instrumentation for measuring the decode kernel on its own: when
- * set, mla_decode_run records `before` on its stream right before the decode
- * kernel and `after` right after it (hipEvent_t values passed as void*; the
+ * set, mla_decode_run (and mla_decode_run_noalloc) records `before` on its
+ * stream right before the decode kernel and `after` right after it, before
+ * the merge launch of split requests (hipEvent_t values passed as void*; the
  * caller owns them).  Passing NULL for both turns it off.  Host-only call.
  */
 mla_status mla_decode_plan_set_events(mla_plan_t plan, void* before, void* after);
@@ -211,7 +222,7 @@ mla_status mla_decode_plan_set_events(mla_plan_t plan, void* before, void* after
 void mla_decode_plan_destroy(mla_plan_t plan);
 
 /* Static description of a status code. */
-const char* mla_status_string(mla_status status);
+const char* mla_status_string(int32_t status);
 
 /* Text of the last HIP error seen by this library on the calling thread ("" if none). */
 const char* mla_last_error(void);
@@ -222,16 +233,21 @@ const char* mla_last_error(void);
  *   (grid size), [5] num_segments, [6] num_partials (split partial slots),
  *   [7] num_split_requests, [8] split granularity in tokens, [9] waves per
  *   workgroup, [10] head split, [11] query vectors per workgroup, [12]
- *   qo_len.  With a head split n > 1, segment requests count groups: row r
+ *   qo_len, [13] 1 when every workgroup runs exactly the segment of its own
+ *   index (the kernels then skip the worker_ptr load), [14] c > 0 when, in
+ *   addition, segment i reads the latent cache of request i / c (the kernels
+ *   then load the segment record and the request's page-table entries in one
+ *   round trip), else 0.  With a head split n > 1, segment requests count groups: row r
  *   covers query vectors (r % n) * W .. (r % n) * W + W - 1 (W = info[11]) of
  *   request r / n, where query vector j is head j % num_heads of query
  *   j / num_heads.
  * mla_decode_plan_segments copies the work list: seg[4*i..4*i+3] =
  * {request, token_begin, token_end, partial_slot (-1 = writes o/lse directly)}
- * for i < num_segments, and worker_ptr[w], worker_ptr[w+1] delimit the
+ * for i < num_segments (token_end as planned; a run takes the last chunk of
+ * each request to the request's run-time length), and worker_ptr[w], worker_ptr[w+1] delimit the
  * segments of workgroup w (worker_ptr has num_workers + 1 entries).
  */
-mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[13]);
+mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[15]);
 mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* worker_ptr);
 
 /*
@@ -258,7 +274,7 @@ mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* work
  * launch on stream; nothing is allocated or synchronised.
  */
 mla_status mla_cache_append(const void* ckv_new, const void* kpe_new, const int64_t* slots,
-                            int32_t n, mla_kv_dtype kv_dtype, void* ckv, void* kpe,
+                            int32_t n, int32_t kv_dtype, void* ckv, void* kpe,
                             float* kv_scale, void* stream);
 
 #ifdef __cplusplus

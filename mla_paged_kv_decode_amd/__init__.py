@@ -191,13 +191,13 @@ class Plan:
             self._h = None
 
     def info(self) -> dict:
-        buf = np.zeros(13, np.int32)
+        buf = np.zeros(15, np.int32)
         st = self._lib.mla_decode_plan_info(self._h, buf.ctypes.data_as(ctypes.c_void_p))
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_plan_info")
         keys = ("batch", "num_heads", "page_size", "kv_dtype", "num_workers", "num_segments",
                 "num_partials", "num_split_requests", "granularity", "waves", "head_split",
-                "kernel_heads", "qo_len")
+                "kernel_heads", "qo_len", "one_seg", "req_div")
         return {k: int(v) for k, v in zip(keys, buf)}
 
     def segments(self):
@@ -211,7 +211,8 @@ class Plan:
         return seg[:inf["num_segments"]], wp
 
     def set_events(self, before, after) -> None:
-        """Record raw hipEvent_t handles (ints) around the decode kernel in run()."""
+        """Record raw hipEvent_t handles (ints) around the decode kernel alone in
+        run() (the merge launch of split requests comes after ``after``)."""
         st = self._lib.mla_decode_plan_set_events(self._h, before, after)
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_plan_set_events")
@@ -248,12 +249,12 @@ class Plan:
                         ("kv_last_page_len", kv_last_page_len)):
             if t.dtype != torch.int32:
                 raise ValueError(name + " must be int32")
-        # the device copies must match the host copies the plan was built from
-        # (the kernels read them without bounds checks)
+        # the device page table is the plan's batch, as planned or grown since
+        # (the kernels read it without bounds checks)
         if kv_indptr.numel() != self.batch + 1 or kv_last_page_len.numel() != self.batch:
             raise ValueError("kv_indptr / kv_last_page_len sizes differ from the plan's")
         if kv_indices.numel() < self.num_pages_used:
-            raise ValueError("kv_indices holds fewer entries than kv_indptr[-1]")
+            raise ValueError("kv_indices holds fewer entries than the plan-time kv_indptr[-1]")
         if ckv.dim() != 3 or ckv.shape[1] != self.page_size or ckv.shape[2] != D_CKV:
             raise ValueError("ckv must be [pages, page_size, 512]")
         if kpe.dim() != 3 or kpe.shape[1] != self.page_size or kpe.shape[2] != D_KPE:

@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <cstring>
 #include <new>
@@ -147,8 +148,8 @@ mla::PlanParams plan_params(int32_t num_queries, int32_t head_split, int32_t wor
   pp.force_splits = opts ? opts->force_splits : 0;
   pp.head_split = head_split;
   if (opts && opts->l2_domains > 0) pp.xcd_count = opts->l2_domains;
-  // the merge of a split request keeps one float per (chunk, head) in LDS
-  pp.max_splits = std::min<int32_t>(256, cfg.lds_bytes / (4 * pp.num_heads));
+  // the merge launch weighs up to 256 chunks of one request (one LDS weight each)
+  pp.max_splits = 256;
   return pp;
 }
 
@@ -201,15 +202,15 @@ mla_status run_on_workspace(mla_plan_s* p, uint8_t* ws, const void* q_nope, cons
   if (p->plan.num_workers > 0) {
     hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-    const int ncomb = (int)(p->plan.combine.size() / 4);
-    if (ncomb > 0) {
-      e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, p->max_splits, s);
-      if (e != hipSuccess) return hip_fail(e, "combine launch");
-    }
   }
-  if (p->ev_after) {
+  if (p->ev_after) {  // the decode kernel alone, without the merge below
     hipError_t e = hipEventRecord(p->ev_after, s);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  }
+  const int ncomb = (int)(p->plan.combine.size() / 4);
+  if (p->plan.num_workers > 0 && ncomb > 0) {
+    hipError_t e = mla_gpu::launch_combine(p->kernel_heads, a, ncomb, p->max_splits, s);
+    if (e != hipSuccess) return hip_fail(e, "combine launch");
   }
   return MLA_OK;
 }
@@ -218,7 +219,7 @@ mla_status run_on_workspace(mla_plan_s* p, uint8_t* ws, const void* q_nope, cons
 
 extern "C" {
 
-const char* mla_status_string(mla_status s) {
+const char* mla_status_string(int32_t s) {
   switch (s) {
     case MLA_OK: return "ok";
     case MLA_ERR_INVALID_ARG: return "invalid argument";
@@ -259,7 +260,7 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
 
 mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
                            const int32_t* kv_last_page_len_host, int32_t batch, int32_t num_heads,
-                           int32_t page_size, mla_kv_dtype kv_dtype, const mla_plan_opts* opts,
+                           int32_t page_size, int32_t kv_dtype, const mla_plan_opts* opts,
                            void* workspace, size_t workspace_bytes, void* stream) {
   if (!out) return MLA_ERR_INVALID_ARG;
   *out = nullptr;
@@ -326,11 +327,16 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
                          kernel_heads);
 
-  // stage the work list: segments | worker_ptr | combine list
+  // stage the work list: segments | worker_ptr | combine list.  The last chunk
+  // of every request ends at INT32_MAX, i.e. at the request's length as the
+  // device page table gives it when a run reads it (the kernels clamp every
+  // chunk to that length): tokens appended after planning are decoded by the
+  // same plan, and only the balance of the work depends on the plan-time lengths.
   p->host_meta.assign(p->layout.meta_bytes, 0);
   for (size_t i = 0; i < pl.segments.size(); ++i) {
     const mla::Segment& g = pl.segments[i];
-    const int32_t v[8] = {g.request, g.begin, g.end, g.slot, g.split_request, g.first_slot,
+    const int32_t end = g.last ? INT32_MAX : g.end;
+    const int32_t v[8] = {g.request, g.begin, end, g.slot, g.split_request, g.first_slot,
                           g.num_splits, g.request / head_split};
     std::memcpy(p->host_meta.data() + p->layout.segs + i * 32, v, 32);
   }
@@ -375,7 +381,7 @@ mla_status mla_decode_plan_set_events(mla_plan_t p, void* before, void* after) {
   return MLA_OK;
 }
 
-mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[13]) {
+mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[15]) {
   if (!p || !info) return MLA_ERR_INVALID_ARG;
   info[0] = p->batch;
   info[1] = p->heads;
@@ -390,6 +396,8 @@ mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[13]) {
   info[10] = p->head_split;
   info[11] = p->kernel_heads;
   info[12] = p->qo_len;
+  info[13] = p->one_seg;
+  info[14] = p->req_div;
   return MLA_OK;
 }
 
@@ -406,7 +414,7 @@ mla_status mla_decode_plan_segments(mla_plan_t p, int32_t* seg, int32_t* worker_
 }
 
 mla_status mla_cache_append(const void* ckv_new, const void* kpe_new, const int64_t* slots,
-                            int32_t n, mla_kv_dtype kv_dtype, void* ckv, void* kpe,
+                            int32_t n, int32_t kv_dtype, void* ckv, void* kpe,
                             float* kv_scale, void* stream) {
   if (n < 0) return MLA_ERR_INVALID_ARG;
   if (kv_dtype < MLA_KV_BF16 || kv_dtype > MLA_KV_FP16) return MLA_ERR_UNSUPPORTED;

@@ -30,12 +30,10 @@
 //
 // Output: each segment is either a whole request (o bf16 and lse fp32 written
 // directly) or a chunk of one (normalised fp32 partial O and its LSE written to
-// a partial slot).  The workgroup that finishes the last chunk of a split
-// request (an arrival counter per request, behind agent-scope release/acquire
-// fences so that partials written on other XCDs are visible) merges the
-// chunks in chunk order, weighting each by exp(LSE_i - LSE); which workgroup
-// does it never changes the arithmetic, so results are deterministic.  The
-// counter is reset by that workgroup, ready for the next launch.
+// a partial slot with plain stores).  A second launch after the decode kernel
+// (mla_combine_kernel / mla_combine_many_kernel) merges the chunks of every
+// split request in chunk order, weighting each by exp(LSE_i - LSE), so results
+// are deterministic and no state survives from one launch to the next.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -44,9 +42,6 @@
 #include "kernels.h"
 
 namespace mla_gpu {
-
-// 16-head kernel: 1 = the last chunk of a split request merges it, 0 = the
-// separate combine launch does
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -1796,34 +1791,16 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 
     // 8-bit cache: one tile per iteration (QK, softmax, PV in turn); the codes
     // of the next tile are converted to bf16 while the current one is computed
-    bool dma_on = false;
-    TileDma tdma{};
     if constexpr (!kC16)
     for (int it = 0; it < ntiles; ++it) {
-      const uint8_t* stage;
-      if constexpr (kC16) {
-        const int later = min(NS - 2, ntiles - 1 - it);
-        if (later >= 2)
-          vm_wait_n<18>();
-        else if (later == 1)
-          vm_wait_n<9>();
-        else
-          vm_wait_n<0>();
-        lds_barrier();  // tile `it` landed for every wave; iteration it - 1 done everywhere
-        const int nxt = it + NS - 1;
-        dma_on = nxt < ntiles;
-        if (dma_on) tdma = plan_tile(nxt, nxt % NS);
-        stage = smem + (it % NS) * S::kStageBytes;
-      } else {
-        // code tile it + 1 landed (tiles it + 2 .. it + NS - 2 may be in
-        // flight); bf16 tile `it` converted; iteration it - 1 done everywhere
-        vm_wait_n<S::kDmaPerWave * (NS - 3)>();
-        lds_barrier();
-        issue_tile(it + NS - 1, (it + NS - 1) % NS);
-        if (it + 1 < ntiles)
-          convert_tile((it + 1) % NS, smem + S::kBf16Offset + ((it + 1) & 1) * S::kStageBytes);
-        stage = smem + S::kBf16Offset + (it & 1) * S::kStageBytes;
-      }
+      // code tile it + 1 landed (tiles it + 2 .. it + NS - 2 may be in
+      // flight); bf16 tile `it` converted; iteration it - 1 done everywhere
+      vm_wait_n<S::kDmaPerWave * (NS - 3)>();
+      lds_barrier();
+      issue_tile(it + NS - 1, (it + NS - 1) % NS);
+      if (it + 1 < ntiles)
+        convert_tile((it + 1) % NS, smem + S::kBf16Offset + ((it + 1) & 1) * S::kStageBytes);
+      const uint8_t* stage = smem + S::kBf16Offset + (it & 1) * S::kStageBytes;
       const int tile_start = t0 + it * T;
 
       // 8-bit: the token scales of this lane's score rows (rows past the end may
@@ -1845,11 +1822,11 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 
       // ---- QK: S^T[32 tokens][32 heads of this wave] ------------------------
       // Operands of the 4 k-steps of group g (1 KiB block g of the tile; for
-      // k-steps past the register-resident Q, that Q operand from LDS too):
-      // with a 16-bit cache, group g + 1 is read before the MFMAs of group g
-      // issue.  The chain
-      // accumulates in VGPRs; its last MFMA (and, in the 644-byte variant, the
-      // last ckv step, which the token scale then multiplies) settles.
+      // the kpe k-steps, whose Q^T lives in LDS, that Q operand too), read
+      // just before the group's MFMAs (the registers for a second group are
+      // not there).  The chain accumulates in VGPRs; its last MFMA (and, in
+      // the 644-byte variant, the last ckv step, which the token scale then
+      // multiplies) settles.
       f32x16 sacc;
       auto read_k = [&](int g, bf16x8 (&kf)[4], bf16x8 (&qx)[4]) __attribute__((always_inline)) {
 #pragma unroll
@@ -1861,11 +1838,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
                 (const LDS_AS uint8_t*)(qlds + (4 * g + u - QR) * 1024));
         }
       };
-      // (8-bit caches: a group's operands are read just before its MFMAs; the
-      // registers for a second group are not there)
-      constexpr bool kPrefetchK = S::kCache16;
       bf16x8 kcur[4], qcur[4];
-      if constexpr (kPrefetchK) read_k(0, kcur, qcur);
 #pragma unroll
       for (int s0 = 0; s0 < 36; s0 += 4) {
         if constexpr (S::kKpe16) {
@@ -1876,9 +1849,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             for (int r = 0; r < 16; ++r) sacc[r] *= sig[r];
           }
         }
-        if constexpr (!kPrefetchK) read_k(s0 >> 2, kcur, qcur);
-        bf16x8 knext[4], qnext[4];
-        if (kPrefetchK && s0 + 4 < 36) read_k((s0 >> 2) + 1, knext, qnext);
+        read_k(s0 >> 2, kcur, qcur);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int s = s0 + u;
@@ -1891,16 +1862,6 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             mfma_vgpr<kF16, false, true>(sacc, kcur[u], qv);
           else
             mfma_vgpr<kF16, false, false>(sacc, kcur[u], qv);
-        }
-        if constexpr (kC16) {
-          if (dma_on) dma_one(tdma, s0 >> 2);
-        }
-        if (kPrefetchK && s0 + 4 < 36) {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            kcur[u] = knext[u];
-            qcur[u] = qnext[u];
-          }
         }
       }
 
@@ -1916,28 +1877,14 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         load_sig();
       }
       const int tlim = CAUSAL ? limit_s[32 * wave + l32] : t1;
-      // the whole tile visible to every head of the wave (all tiles but the
-      // last few): no per-token mask (16-bit caches; the 8-bit loop has no
-      // registers for a second copy of this code)
-      const bool full = kC16 && (CAUSAL ? __builtin_amdgcn_ballot_w64(tile_start + T > tlim) == 0
-                                        : tile_start + T <= t1);
       float tmax = -INFINITY;
-      if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
-          sacc[r] = raw * a.scale_log2;
-          tmax = fmaxf(tmax, sacc[r]);
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
-          const float x = tok < tlim ? raw * a.scale_log2 : -INFINITY;
-          sacc[r] = x;
-          tmax = fmaxf(tmax, x);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int tok = tile_start + 8 * (r >> 2) + 4 * g + (r & 3);
+        const float raw = (KVT == 1 || KVT == 2) ? sacc[r] * sig[r] : sacc[r];
+        const float x = tok < tlim ? raw * a.scale_log2 : -INFINITY;
+        sacc[r] = x;
+        tmax = fmaxf(tmax, x);
       }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0) {
@@ -1961,8 +1908,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           const float e0 = __builtin_amdgcn_exp2f(sacc[r] - m_use);
           const float e1 = __builtin_amdgcn_exp2f(sacc[8 + r] - m_use);
           psum += e0 + e1;
-          p0[r] = to16<kF16>(kC16 ? e0 : e0 * sig[r]);
-          p1[r] = to16<kF16>(kC16 ? e1 : e1 * sig[8 + r]);
+          p0[r] = to16<kF16>(e0 * sig[r]);  // V = scale x codes
+          p1[r] = to16<kF16>(e1 * sig[8 + r]);
         }
         l_run += psum;
         *reinterpret_cast<bf16x8*>(pbuf + ((wave * 2 + 0) * 64 + lane) * 16) = p0;
@@ -1989,13 +1936,9 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         return vf;
       };
       // every LDS read the rescale does not decide is issued first: the
-      // flags, the first V^T operands and the P^T operands of the k-steps
+      // flags, the first V^T operand and the P^T operands of k-step 0
       const u32x4 fl = *reinterpret_cast<const u32x4*>(flags);
-      // V^T read-ahead: two steps (8-bit caches: one; no registers for more)
-      constexpr int kVA = kC16 ? 2 : 1;
-      bf16x8 vq[3];
       bf16x8 vcur = read_v(0);
-      if constexpr (kVA == 2) vq[1] = read_v(1);
       bf16x8 pb[2][4];
       auto read_p = [&](int ks) __attribute__((always_inline)) {
 #pragma unroll
@@ -2004,7 +1947,6 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
               (const LDS_AS uint8_t*)(pbuf + ((hb * 2 + ks) * 64 + lane) * 16));
       };
       read_p(0);
-      if constexpr (kC16) read_p(1);  // 8-bit: read at k-step 1 (registers)
       {
         const unsigned any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
         if (it > 0 && any != 0) {
@@ -2018,25 +1960,20 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           }
         }
       }
-      // V^T of step i + kVA is read while the MFMAs of step i issue
+      // V^T of step i + 1 is read while the MFMAs of step i issue; the P^T
+      // operands of k-step 1 at step 4 (no registers to hold both k-steps)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ks = i >> 2, cb = i & 3;
-        if (!kC16 && i == 4) read_p(1);
-        bf16x8 vnext;
-        if constexpr (kVA == 2) {
-          if (i > 0) vcur = vq[i % 3];
-          if (i + 2 < 8) vq[(i + 2) % 3] = read_v(i + 2);
-        } else {
-          vnext = read_v(i < 7 ? i + 1 : i);
-        }
+        if (i == 4) read_p(1);
+        const bf16x8 vnext = read_v(i < 7 ? i + 1 : i);
 #pragma unroll
         for (int hb = 0; hb < 3; ++hb) mfma_agpr<kF16>(acc[cb][hb], vcur, pb[ks][hb]);
         if (i < 7)
           mfma_agpr<kF16>(acc[cb][3], vcur, pb[ks][3]);
         else
           mfma_agpr<kF16, true>(acc[cb][3], vcur, pb[ks][3]);
-        if constexpr (kVA == 1) vcur = vnext;
+        vcur = vnext;
       }
     }
     if constexpr (!kC16) vm_wait_n<0>();  // the trailing re-loads have landed
@@ -2333,35 +2270,6 @@ static int stream_occupancy_of() {
   return n < 1 ? 1 : n;
 }
 
-// Ring-kernel shape per head count: <16-head blocks, blocks per wave,
-// token-split waves, row groups per wave per tile, ring stages>.
-#ifndef MLA_CFG_H64
-#define MLA_CFG_H64 4, 1, 1, 2, 4
-#endif
-#ifndef MLA_CFG_H128
-#define MLA_CFG_H128 8, 1, 1, 2, 4
-#endif
-// 32-head bf16 rows: 0 = LDS ring <2, 1, 2, 1, 4>, 1 = register-staged
-// stream kernel with two head blocks per wave (needs more than the 512
-// registers of a lane, so it spills; kept for comparison).
-#ifndef MLA_H32_STREAM
-#define MLA_H32_STREAM 0
-#endif
-// 128-head bf16 rows: 1 = wide kernel (QK split by heads, PV by channels),
-// 0 = LDS ring with 8 waves of 16 heads.
-#ifndef MLA_H128_WIDE
-#define MLA_H128_WIDE 1
-#endif
-// groups staged in registers per wave for 16-head 8-bit rows (a group is
-// half the bytes of a bf16 one)
-#ifndef MLA_H16_NB8
-#define MLA_H16_NB8 2
-#endif
-// groups staged in registers per wave for 32-head rows
-#ifndef MLA_H32_NB
-#define MLA_H32_NB 1
-#endif
-
 template <int HG, int HB, int TS, int MB, int NSTAGE>
 static int occupancy_of() {
   using S = RingShape<HG, HB, TS, MB, NSTAGE>;
@@ -2399,47 +2307,42 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
     if (op == 2) *err = launch_decode_cfg<__VA_ARGS__>(*a, grid, stream);   \
     return 1;                                                               \
   } while (0)
+  // ring-kernel shapes: <16-head blocks, blocks per wave, token-split waves,
+  // row groups per wave per tile, ring stages>; stream-kernel shapes: <head
+  // blocks, cache layout, groups staged in registers per wave>
   if (kv_dtype == 0) {
     switch (heads) {
       case 16: MLA_STREAM(1, 0, 2);
-#if MLA_H32_STREAM
-      case 32: MLA_STREAM(2, 0, MLA_H32_NB);
-#else
       case 32: MLA_RING(2, 1, 2, 1, 4);
-#endif
-      case 64: MLA_RING(MLA_CFG_H64);
-#if MLA_H128_WIDE
+      case 64: MLA_RING(4, 1, 1, 2, 4);
       case 128: MLA_WIDE(0);
-#else
-      case 128: MLA_RING(MLA_CFG_H128);
-#endif
       default: return 0;
     }
   }
   if (kv_dtype == 1) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 1, MLA_H16_NB8);
+      case 16: MLA_STREAM(1, 1, 2);
       case 128: MLA_WIDE(1);
       default: return 0;
     }
   }
   if (kv_dtype == 2) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 2, MLA_H16_NB8);
+      case 16: MLA_STREAM(1, 2, 2);
       case 128: MLA_WIDE(2);
       default: return 0;
     }
   }
   if (kv_dtype == 3) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 3, MLA_H16_NB8);
+      case 16: MLA_STREAM(1, 3, 2);
       case 128: MLA_WIDE(3);
       default: return 0;
     }
   }
   if (kv_dtype == 4) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 4, MLA_H16_NB8);
+      case 16: MLA_STREAM(1, 4, 2);
       case 128: MLA_WIDE(4);
       default: return 0;
     }

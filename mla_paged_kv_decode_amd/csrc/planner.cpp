@@ -31,32 +31,62 @@ struct Piece {
   int64_t cost;
 };
 
+// Chunks of a request of L tokens for chunk size `chunk` (or `force` chunks):
+// near-equal, with boundaries on multiples of gran; returns the count and the
+// step between boundaries.
+std::pair<int64_t, int64_t> cut_of(int64_t L, int64_t chunk, int32_t gran, int32_t force,
+                                   int32_t max_splits) {
+  int64_t n = 1;
+  if (L > 0) {
+    if (force > 0)
+      n = std::min<int64_t>(force, (L + gran - 1) / gran);
+    else
+      n = (L + chunk - 1) / chunk;
+    if (n < 1) n = 1;
+    if (n > max_splits) n = max_splits;
+  }
+  int64_t step = (L + n - 1) / n;
+  step = ((step + gran - 1) / gran) * gran;
+  if (step <= 0) step = gran;
+  n = L > 0 ? (L + step - 1) / step : 1;
+  return {n, step};
+}
+
+int64_t piece_cost(int64_t tokens, int64_t n, int32_t heads) {
+  return tokens + kFixed + heads + (n > 1 ? 4 * (int64_t)heads : 0);
+}
+
+// Pieces, total cost and largest piece of a cut, without building it: the
+// candidate search skips cuts whose bound cannot beat what it has.
+struct CutSummary {
+  int64_t pieces = 0, total = 0, largest = 0;
+};
+CutSummary summarize(const std::vector<int64_t>& len, int64_t chunk, int32_t gran, int32_t heads,
+                     int32_t max_splits) {
+  CutSummary c;
+  for (int64_t L : len) {
+    const std::pair<int64_t, int64_t> ns = cut_of(L, chunk, gran, 0, max_splits);
+    c.pieces += ns.first;
+    c.total += L + ns.first * piece_cost(0, ns.first, heads);
+    c.largest = std::max(c.largest, piece_cost(std::min(L, ns.second), ns.first, heads));
+  }
+  return c;
+}
+
 void cut_requests(const std::vector<int64_t>& len, int64_t chunk, int32_t gran, int32_t heads,
                   int32_t force, int32_t max_splits, std::vector<Piece>* pieces) {
   pieces->clear();
   for (size_t b = 0; b < len.size(); ++b) {
     const int64_t L = len[b];
-    int64_t n = 1;
-    if (L > 0) {
-      if (force > 0)
-        n = std::min<int64_t>(force, (L + gran - 1) / gran);
-      else
-        n = (L + chunk - 1) / chunk;
-      if (n < 1) n = 1;
-      if (n > max_splits) n = max_splits;
-    }
-    // near-equal chunks with boundaries on multiples of gran
-    int64_t step = (L + n - 1) / n;
-    step = ((step + gran - 1) / gran) * gran;
-    if (step <= 0) step = gran;
-    n = L > 0 ? (L + step - 1) / step : 1;
+    const std::pair<int64_t, int64_t> ns = cut_of(L, chunk, gran, force, max_splits);
+    const int64_t n = ns.first, step = ns.second;
     for (int64_t k = 0; k < n; ++k) {
       Piece p;
       p.request = (int32_t)b;
       p.begin = (int32_t)std::min<int64_t>(L, k * step);
       p.end = (int32_t)std::min<int64_t>(L, (k + 1) * step);
       p.nsplit = (int32_t)n;
-      p.cost = (p.end - p.begin) + kFixed + heads + (n > 1 ? 4 * (int64_t)heads : 0);
+      p.cost = piece_cost(p.end - p.begin, n, heads);
       pieces->push_back(p);
     }
   }
@@ -91,7 +121,8 @@ int64_t assign(const std::vector<Piece>& pieces, int32_t workers, std::vector<in
 // loads the most.  Every step lowers the busiest load, or leaves it to a worker
 // with a higher index among equals; the scan orders are fixed, so the result is
 // deterministic.  Returns the largest worker load.
-int64_t refine(const std::vector<Piece>& pieces, int32_t workers, std::vector<int32_t>* owner) {
+int64_t refine(const std::vector<Piece>& pieces, int32_t workers, int64_t bound,
+               std::vector<int32_t>* owner) {
   std::vector<int64_t> load((size_t)workers, 0);
   std::vector<std::vector<int32_t>> items((size_t)workers);
   for (size_t i = 0; i < pieces.size(); ++i) {
@@ -112,6 +143,7 @@ int64_t refine(const std::vector<Piece>& pieces, int32_t workers, std::vector<in
   const int64_t max_steps = 4 * (int64_t)workers;
   for (int64_t step = 0; step < max_steps; ++step) {
     const int32_t hi = by_load[workers - 1];
+    if (load[hi] <= bound) break;  // no assignment does better
     int64_t best = load[hi];
     int32_t best_a = -1, best_b = -1, best_w = -1;
     for (int32_t k = 0; k < workers - 1; ++k) {
@@ -245,28 +277,42 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
     }
     std::sort(cands.begin(), cands.end(), std::greater<int64_t>());  // fewest cuts first
     // longest-first for every candidate; the refinement (the costly part) for
-    // the two best of those
-    std::vector<std::pair<int64_t, int64_t>> ranked;  // (longest-first worst, candidate)
+    // the two best of those.  A candidate's longest-first load is at least its
+    // bound (the mean load, or its largest piece), so one whose bound exceeds
+    // the second best load found so far cannot be among the two and is not
+    // assigned; candidates with more pieces than the workspace holds are
+    // skipped before they are cut.
+    struct Ranked {
+      int64_t worst, k, bound;
+      std::vector<Piece> pieces;
+      std::vector<int32_t> owner;
+    };
+    std::vector<Ranked> top;  // the two best so far, by (worst, candidate order)
     for (size_t k = 0; k < cands.size(); ++k) {
+      const CutSummary cs = summarize(len, cands[k], gran, p.num_heads, p.max_splits);
+      if (cs.pieces > seg_cap) continue;
+      const int64_t bound = std::max((cs.total + p.num_workers - 1) / p.num_workers, cs.largest);
+      if (top.size() == 2 && bound > top[1].worst) continue;
       cut_requests(len, cands[k], gran, p.num_heads, 0, p.max_splits, &pieces);
-      if ((int64_t)pieces.size() > seg_cap) continue;
-      ranked.push_back({assign(pieces, p.num_workers, &owner), (int64_t)k});
+      const int64_t worst = assign(pieces, p.num_workers, &owner);
+      Ranked r{worst, (int64_t)k, bound, pieces, owner};
+      auto pos = std::upper_bound(top.begin(), top.end(), r, [](const Ranked& x, const Ranked& y) {
+        return x.worst < y.worst;
+      });
+      top.insert(pos, std::move(r));
+      if (top.size() > 2) top.pop_back();
     }
-    if (ranked.empty()) return -1;  // unreachable: the largest candidate never cuts
-    std::stable_sort(ranked.begin(), ranked.end());
-    const size_t nref = std::min<size_t>(2, ranked.size());
-    std::sort(ranked.begin(), ranked.begin() + nref,
-              [](const std::pair<int64_t, int64_t>& x, const std::pair<int64_t, int64_t>& y) {
-                return x.second < y.second;  // fewest cuts first among them
-              });
-    for (size_t r = 0; r < nref; ++r) {
-      cut_requests(len, cands[ranked[r].second], gran, p.num_heads, 0, p.max_splits, &pieces);
-      assign(pieces, p.num_workers, &owner);
-      const int64_t worst = refine(pieces, p.num_workers, &owner);
+    if (top.empty()) return -1;  // unreachable: the largest candidate never cuts
+    std::sort(top.begin(), top.end(),
+              [](const Ranked& x, const Ranked& y) { return x.k < y.k; });  // fewest cuts first
+    for (Ranked& r : top) {
+      // refining cannot go below the bound: skip a candidate that cannot win
+      if (best >= 0 && r.bound >= best) continue;
+      const int64_t worst = refine(r.pieces, p.num_workers, r.bound, &r.owner);
       if (best < 0 || worst < best) {
         best = worst;
-        best_pieces.swap(pieces);
-        best_owner.swap(owner);
+        best_pieces.swap(r.pieces);
+        best_owner.swap(r.owner);
       }
     }
   }
@@ -318,6 +364,7 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
     s.split_request = split_index[pc.request];
     s.first_slot = first_slot[pc.request];
     s.num_splits = pc.nsplit;
+    s.last = (i + 1 == best_pieces.size() || best_pieces[i + 1].request != pc.request) ? 1 : 0;
     const int32_t w = remap[best_owner[i]];
     out->segments[fill[w]++] = s;
   }

@@ -19,7 +19,7 @@ struct PlanParams {
   int32_t num_workers = 0;   // grid size to balance over
   int32_t granularity = 64;  // chunk boundaries are multiples of this many tokens
   int32_t force_splits = 0;  // > 0: every request cut into this many chunks (at most)
-  int32_t max_splits = 256;  // chunks per request at most (the merge keeps n * H floats in LDS)
+  int32_t max_splits = 256;  // chunks per request at most (what the merge launch weighs)
   int32_t head_split = 1;    // > 1: each request's heads run as this many sub-requests
                              // (rows b * head_split + g of q/o viewed with H / head_split heads)
   int32_t xcd_count = 8;     // workgroups are dealt round-robin to this many L2 domains
@@ -33,6 +33,7 @@ struct Segment {
   int32_t split_request;  // index of the request among the split ones, or -1
   int32_t first_slot;     // first partial slot of the request (split requests)
   int32_t num_splits;     // chunks of the request (1 when not split)
+  int32_t last;           // 1 for the last chunk of its request (end = the request's length)
 };
 
 struct Plan {

@@ -155,7 +155,12 @@ def decode(q_nope, q_pe, ckv, kpe, kv_indptr, kv_indices, kv_last_page_len, sm_s
     ix = _c(kv_indices, np.int32)
     lp = _c(kv_last_page_len, np.int32)
     if threads <= 0:
+        # the host's cores, capped by OMP_NUM_THREADS when set (the share of a
+        # machine this process may use)
         threads = os.cpu_count() or 1
+        env = os.environ.get("OMP_NUM_THREADS", "")
+        if env.isdigit() and int(env) > 0:
+            threads = min(threads, int(env))
     if rows is None:
         o = np.zeros((NQ, H, D_CKV), np.float64)
         lse = np.zeros((NQ, H), np.float64)

@@ -14,7 +14,7 @@ summarised.  Writes ``profiles/<kernel>_<workload>.md`` and
 ``profiles/traffic_<workload>.json`` (HBM bytes per launch, keyed by the
 kernel-source hash printed by bench.py so that stale counters are not used).
 
-usage: python -m mla_paged_kv_decode_amd.profile_summary --stats DIR --fetch DIR
+usage: python profile_summary.py --stats DIR --fetch DIR
        --write DIR --bench-log FILE --calib-mib N --out profiles --command-stats "..."
        --command-fetch "..." --command-write "..."
 """

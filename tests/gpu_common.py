@@ -7,7 +7,7 @@ import numpy as np
 import torch
 
 import oracle
-from mla_paged_kv_decode_amd import synth
+import synth
 
 COS_TOL, ABS_TOL, LSE_TOL = 1e-4, 2e-2, 1e-3
 

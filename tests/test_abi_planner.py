@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import mla_paged_kv_decode_amd as mla
-from mla_paged_kv_decode_amd import synth
+import synth
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from mla_paged_kv_decode_amd import synth
+import synth
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu

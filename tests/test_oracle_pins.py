@@ -32,7 +32,7 @@ import scipy.special
 import torch
 
 import oracle
-from mla_paged_kv_decode_amd import synth
+import synth
 
 SM = synth.SM_SCALE_192
 

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import mla_paged_kv_decode_amd as mla
-from mla_paged_kv_decode_amd import synth
+import synth
 import gpu_common as gc
 
 def _both(inp, force_splits=0, host_only_plan=False):
