@@ -69,9 +69,10 @@ def kernel_name(info: dict) -> str:
         return "mla_decode_stream_kernel<1, %d, 2>" % k
     if w == 32:
         return "mla_decode_ring_kernel<2, 1, 2, 1, 4>"
+    causal = "true" if q > 1 else "false"
     if w == 64:
-        return "mla_decode_ring_kernel<4, 1, 1, 2, 4>"
-    return "mla_decode_wide_kernel<%d, %s>" % (k, "true" if q > 1 else "false")
+        return "mla_decode_pair_kernel<%d, %s>" % (k, causal)
+    return "mla_decode_wide_kernel<%d, %s>" % (k, causal)
 
 
 class Hip:

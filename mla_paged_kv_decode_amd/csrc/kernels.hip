@@ -2027,6 +2027,494 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
 }
 
 // ---------------------------------------------------------------------------
+// 64-head kernel (16-bit cache).  Split as in the 128-head kernel, only two
+// waves would have QK work and PV would fill half of the accumulators.  Here
+// the 4 waves (one per SIMD) share each 32-token tile of the same 4-slot LDS
+// ring this way:
+//   * QK: wave w (head block hw = w & 1, key half kw = w >> 1) runs the
+//     k-steps s = 4 gi + 2 kw + v (gi = 0..8, v = 0, 1) of heads
+//     32 hw .. 32 hw + 31: 18 of the 36 32x32x16 MFMAs of those heads, with
+//     Q^T for its k-steps in 72 VGPRs.  A wave of key half 1 feeds the token
+//     rows to the MFMA in the order t ^ 16, so that in both waves of a head
+//     block the score registers r = 0..7 of the S^T layout below hold the
+//     wave's own token half (tokens 16 kw .. 16 kw + 15) and r = 8..15 the
+//     other half;
+//   * the two waves of a head block exchange those other halves through LDS
+//     and add them: the score of a token is its two key-half partials summed;
+//   * a (head, token half) pair is then a "virtual head" with its own online
+//     softmax: wave w owns virtual heads 32 w .. 32 w + 31 (heads 32 hw + l,
+//     tokens of half kw) and writes their P^T (one 16-token PV k-step) and
+//     rescale factors to LDS;
+//   * PV by value channels: wave w accumulates O^T for channels 128 w .. + 127
+//     of all 128 virtual heads (256 AGPRs; virtual head block vb takes the
+//     k-step vb >> 1 only): 16 MFMAs per tile;
+//   * the epilogue merges the two virtual heads of every head (the merge of
+//     two disjoint token sets, lane by lane, exact up to rounding) into O and
+//     LSE, or into the partial of a chunk.
+// A tile costs every wave 34 MFMAs.  The loop is the software pipeline of the
+// 128-head kernel: QK of tile k + 1 before PV of tile k, the loads of tile
+// k + 3 issued one per QK group, and the softmax of tile k + 1 issued
+// between PV's MFMAs.
+// ---------------------------------------------------------------------------
+struct PairShape {
+  static constexpr int kWaves = 4;
+  static constexpr int kThreads = 256;
+  static constexpr int kHeads = 64;
+  static constexpr int kTile = 32;
+  static constexpr int kStages = 4;
+  static constexpr int kStageBytes = kTile * kRowBytes;       // 36 KiB bf16 tile
+  static constexpr int kPOffset = kStages * kStageBytes;      // P^T [wave][lane] x 16 B
+  static constexpr int kXOffset = kPOffset + 4 * 64 * 16;     // score halves [wave][lane] x 32 B
+  static constexpr int kAlphaOffset = kXOffset + 4 * 64 * 32;  // [128] rescale factors
+  static constexpr int kFlagOffset = kAlphaOffset + 128 * 4;   // [4] rescale flags
+  static constexpr int kLdsBytes = kFlagOffset + 16;
+  static constexpr int kStatOffset = kXOffset;  // epilogue: (m, l) of the 128 virtual heads
+  static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+template <int KVT, bool CAUSAL>
+__global__ void __launch_bounds__(256) mla_decode_pair_kernel(const DecodeArgs a) {
+  static_assert(KVT == 0 || KVT == 5, "16-bit caches");
+  using S = PairShape;
+  constexpr int H = S::kHeads;
+  constexpr bool kF16 = KVT == 5;  // fp16 q, cache, P and O
+  constexpr int T = S::kTile;
+  constexpr int NS = S::kStages;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::kLdsBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int hw = wave & 1;   // head block: heads 32 hw .. 32 hw + 31
+  const int kw = wave >> 1;  // key half of QK, token half after the exchange
+  const int page_shift = a.page_shift;
+  const int page_mask = (1 << page_shift) - 1;
+  const int ld_r_lo = lane >> 3;
+
+  // QK A operand (ds_read_b128): token l32 ^ 16 kw of the tile, k-step
+  // s = 4 gi + 2 kw + v, i.e. chunk 2 s + g of the group gi block:
+  // qk_w ^ 32 v + 1024 gi from the tile base (the swizzle flips bits 4-6 only)
+  uint32_t qk_w;
+  {
+    const int tr = l32 ^ (16 * kw);
+    const int r = tr & 15, half = r >> 3, rr = r & 7;
+    const int base = (tr >> 4) * kGroupBytes + half * kHalfGroupBytes + rr * 128;
+    qk_w = (uint32_t)(base + (((4 * kw + g) ^ rr ^ half) * 16));
+  }
+  // PV A operand (ds_read_b64_tr_b16), as in the 128-head kernel
+  int pv_off0;
+  {
+    const int G = lane >> 4, sl = lane & 15;
+    const int rr = 4 * (G >> 1) + (sl >> 2);
+    const int e = 2 * (G & 1) + ((sl >> 1) & 1);
+    pv_off0 = rr * 128 + ((e ^ rr) * 16) + (sl & 1) * 8;
+  }
+
+  const int seg_begin = a.one_seg ? (int)blockIdx.x : ld_const(a.worker_ptr + blockIdx.x);
+  const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
+
+  for (int si = seg_begin; si < seg_end; ++si) {
+    const SegMeta sm = load_seg(a, si);
+    const int b = sm.b, t0 = sm.t0, send = sm.send, slot = sm.slot;
+    const int kvb = sm.kvb, pbeg = sm.pbeg;
+    const int ldev = sm.npg > 0 ? ((sm.npg - 1) << page_shift) + sm.last_len : 0;
+    const int t1 = min(send, ldev);
+    // scores of this lane's head at or past tlim are masked (end of the
+    // chunk; several queries per request: the causal limit of its query)
+    const int tlim = CAUSAL ? min(t1, causal_limit<H>(a, b, kvb, 32 * hw + l32, ldev)) : t1;
+    const int ntiles = t1 > t0 ? (t1 - t0 + T - 1) / T : 0;
+
+    // Page numbers and direct-to-LDS loads of a tile: wave w loads half group w
+    // (group w / 2, rows 8 (w % 2) .. + 7), 9 blocks of 1 KiB; past the last
+    // tile the last tile is loaded again, into a slot no one reads, so every
+    // vmcnt wait is the same constant.
+    const int last_group = t1 > 0 ? ((t1 - 1) >> 4) << 4 : 0;
+    struct TileDma {
+      const uint8_t* cpage;
+      const uint8_t* kpage;
+      uint32_t coff, koff;
+      uint32_t dst;
+    };
+    auto pages_of = [&](int k, int (&pg)[2]) __attribute__((always_inline)) {
+      const int kc = min(k, ntiles - 1);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const int gs = min(t0 + kc * T + 16 * gi, last_group);
+        pg[gi] = ld_const(a.kv_indices + pbeg + (gs >> page_shift));
+      }
+    };
+    auto plan_from = [&](int k, int st, const int (&pg)[2]) __attribute__((always_inline)) {
+      const int kc = min(k, ntiles - 1);
+      const int my_group = wave >> 1, my_half = wave & 1;
+      const int gs = min(t0 + kc * T + 16 * my_group, last_group);
+      const int r = my_half * 8 + ld_r_lo;
+      const int tok = min(gs + r, t1 - 1);
+      const size_t page_row = (size_t)pg[my_group] << page_shift;
+      const uint32_t sw = ((lane & 7) ^ swz(r)) * 16;
+      TileDma td;
+      td.cpage = a.ckv + page_row * 1024;
+      td.kpage = a.kpe + page_row * 128;
+      td.coff = (tok & page_mask) * 1024 + sw;
+      td.koff = (tok & page_mask) * 128 + sw;
+      td.dst = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(
+          LDS_AS uint8_t*)(smem + st * S::kStageBytes + my_group * kGroupBytes +
+                           my_half * kHalfGroupBytes));
+      return td;
+    };
+    auto dma_one = [&](const TileDma& td, int u) __attribute__((always_inline)) {
+      if (u < 8)
+        dma16_s(td.cpage, td.coff + u * 128, td.dst + u * 1024);
+      else
+        dma16_s(td.kpage, td.koff, td.dst + 8 * 1024);
+    };
+
+    // Q^T of heads 32 hw .. 32 hw + 31 for this wave's k-steps: qf[2 gi + v]
+    // holds dims 16 s + 8 g .. + 7 of k-step s = 4 gi + 2 kw + v (gi < 8:
+    // q_nope, gi = 8: q_pe).  Loaded by assembly before the prologue tiles and
+    // waited for alone (loads complete in issue order).
+    bf16x8 qf[18];
+    {
+      const int qhead = 32 * hw + l32;
+      const bf16x8* qn =
+          reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + qhead) * 512) + 4 * kw + g;
+      const bf16x8* qp =
+          reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + qhead) * 64) + 4 * kw + g;
+#pragma unroll
+      for (int j = 0; j < 18; ++j)
+        qf[j] = load16_untracked(j < 16 ? qn + 8 * (j >> 1) + 2 * (j & 1) : qp + 2 * (j & 1));
+    }
+    if (ntiles > 0) {
+      int pg[2];
+      pages_of(0, pg);
+#pragma unroll
+      for (int k = 0; k < NS - 1; ++k) {
+        int pn[2];
+        pages_of(k + 1, pn);
+        const TileDma td = plan_from(k, k, pg);
+#pragma unroll
+        for (int u = 0; u < 9; ++u) dma_one(td, u);
+        pg[0] = pn[0];
+        pg[1] = pn[1];
+      }
+      vm_wait_n<9 * (NS - 1)>();
+    } else {
+      vm_wait_n<0>();  // no tile: nothing may stay in flight
+    }
+
+    f32x16 acc[4][4];  // O^T [channel block cb][virtual head block vb]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[cb][vb][i] = 0.f;
+    float m_ref = -INFINITY;  // virtual head 32 w + l32, log2 domain
+    float l_run = 0.f;        // this lane's 8 tokens of it
+
+    f32x16 sacc;           // partial, then (r < 8) full scores of the tile softmaxed next
+    bf16x8 pq = {};        // P^T of the last softmaxed tile (PV B operand)
+    float alpha_q = 1.f;   // its rescale factor (1: none)
+    unsigned resc_q = 0;   // wave-uniform: its softmax moved the reference max
+    float tmax = -INFINITY, psum = 0.f, m_use = 0.f, m_next = 0.f;
+    f32x4 xin0 = {}, xin1 = {};  // the other key half's partial of this wave's tokens
+    int ts_next = t0;            // first token of the tile softmaxed next
+    uint32_t small_base = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)(smem + S::kPOffset);
+    asm volatile("" : "+s"(small_base));
+    constexpr uint32_t kX = S::kXOffset - S::kPOffset, kAl = S::kAlphaOffset - S::kPOffset,
+                       kFl = S::kFlagOffset - S::kPOffset;
+    const uint32_t p_lane = small_base + lane * 16;       // P^T [wave][lane]
+    const uint32_t x_lane = small_base + kX + lane * 32;  // score halves [wave][lane]
+    const uint32_t a_lane = small_base + kAl + l32 * 4;   // alpha [virtual head]
+    auto lds_at = [](uint32_t addr) __attribute__((always_inline)) {
+      return (LDS_AS uint8_t*)(uintptr_t)addr;
+    };
+
+    // QK of the tile at `stage`: 9 groups of 2 k-steps, operands read three
+    // groups ahead, the loads of a later tile one per group.
+    auto qk_tile = [&](const uint8_t* stage, bool dma_on, const TileDma& tdma)
+        __attribute__((always_inline)) {
+      uint32_t kbase = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)stage + qk_w;
+      asm volatile("" : "+v"(kbase));
+      auto read_k = [&](int gi, bf16x8 (&kf)[2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v)
+          kf[v] = *reinterpret_cast<const LDS_AS bf16x8*>(lds_at((kbase ^ (32u * v)) + gi * 1024));
+      };
+      bf16x8 kq[4][2];
+      read_k(0, kq[0]);
+      read_k(1, kq[1]);
+      read_k(2, kq[2]);
+#pragma unroll
+      for (int gi = 0; gi < 9; ++gi) {
+        if (gi + 3 < 9) read_k(gi + 3, kq[(gi + 3) % 4]);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int j = 2 * gi + v;
+          if (j == 0)
+            mfma_vgpr<kF16, true, false>(sacc, kq[gi % 4][v], qf[j]);
+          else if (j == 17)
+            mfma_vgpr<kF16, false, true>(sacc, kq[gi % 4][v], qf[j]);
+          else
+            mfma_vgpr<kF16, false, false>(sacc, kq[gi % 4][v], qf[j]);
+        }
+        if (dma_on) dma_one(tdma, gi);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    // the other token half of the partial scores, for the other wave of the head block
+    auto send_half = [&]() __attribute__((always_inline)) {
+      const uint32_t xo = x_lane + 2048u * wave;
+      *reinterpret_cast<LDS_AS f32x4*>(lds_at(xo)) = f32x4{sacc[8], sacc[9], sacc[10], sacc[11]};
+      *reinterpret_cast<LDS_AS f32x4*>(lds_at(xo + 16)) =
+          f32x4{sacc[12], sacc[13], sacc[14], sacc[15]};
+    };
+    auto recv_half = [&]() __attribute__((always_inline)) {
+      const uint32_t xi = x_lane + 2048u * (wave ^ 2);
+      xin0 = *reinterpret_cast<const LDS_AS f32x4*>(lds_at(xi));
+      xin1 = *reinterpret_cast<const LDS_AS f32x4*>(lds_at(xi + 16));
+    };
+
+    // Online softmax of the virtual head's 16 scores (this lane's 8 in sacc[0..7]
+    // once the other key half is added; the lane l ^ 32 holds the other 8),
+    // in slots issued one behind each of PV's 16 MFMAs.  0: the other key
+    // half added; 1: scores past the limit set to -inf; 2-3: the lane's max;
+    // 4: with lane l ^ 32, scaled (s = sm_scale log2 e > 0 commutes with the
+    // max); 5-7: the rescale decision (alpha = 1 unless the wave moves its
+    // reference max; a head with no visible token keeps alpha = 1) and the
+    // new reference; 8-11: the probabilities exp2(fma(raw, s, -m)), summed in
+    // pairs in order; 12: the row sum.
+    auto sm_slot = [&](int j) __attribute__((always_inline)) {
+      if (j == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sacc[i] += xin0[i];
+          sacc[4 + i] += xin1[i];
+        }
+      } else if (j == 1) {
+        if (__builtin_amdgcn_ballot_w64(ts_next + T > tlim) != 0) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int tok = ts_next + 16 * kw + 8 * (i >> 2) + 4 * g + (i & 3);
+            sacc[i] = tok < tlim ? sacc[i] : -INFINITY;
+          }
+        }
+      } else if (j == 2) {
+        tmax = fmaxf(fmaxf(sacc[0], sacc[1]), fmaxf(sacc[2], sacc[3]));
+      } else if (j == 3) {
+        tmax = fmaxf(tmax, fmaxf(fmaxf(sacc[4], sacc[5]), fmaxf(sacc[6], sacc[7])));
+      } else if (j == 4) {
+        float lo = tmax, hi = tmax;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1"
+                     : "+v"(lo), "+v"(hi));
+        tmax = fmaxf(lo, hi) * a.scale_log2;
+      } else if (j == 5) {
+        resc_q = __builtin_amdgcn_ballot_w64(tmax > m_ref + kRescaleSlack) != 0 ? 1u : 0u;
+        m_next = resc_q ? fmaxf(m_ref, tmax) : m_ref;
+      } else if (j == 6) {
+        alpha_q = (resc_q && m_next != -INFINITY) ? __builtin_amdgcn_exp2f(m_ref - m_next) : 1.f;
+        m_ref = m_next;
+        m_use = m_ref == -INFINITY ? 0.f : -m_ref;
+      } else if (j == 7) {
+        l_run *= alpha_q;
+        psum = 0.f;
+      } else if (j < 12) {
+        const int k = 2 * (j - 8);
+        const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k], a.scale_log2, m_use));
+        const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sacc[k + 1], a.scale_log2, m_use));
+        psum += e0 + e1;
+        pq[k] = to16<kF16>(e0);
+        pq[k + 1] = to16<kF16>(e1);
+      } else if (j == 12) {
+        l_run += psum;
+      }
+    };
+
+    // PV of the tile at `stage` (P^T of every wave and the rescale flags are
+    // in LDS); WITH_SM: the softmax slots of the next tile behind its MFMAs.
+    auto pv_tile = [&](auto with_sm, const uint8_t* stage) __attribute__((always_inline)) {
+      constexpr bool kSm = decltype(with_sm)::value;
+      uint32_t vt = (uint32_t)(uintptr_t)(LDS_AS uint8_t*)stage + 2048 * wave + pv_off0;
+      asm volatile("" : "+v"(vt));
+      uint32_t vx[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int c1 = 0; c1 < 2; ++c1) vx[h][c1] = vt ^ (16u * h + 64u * c1);
+      // V^T operand of step i = 4 ks + cb: channels 32 cb .. + 31 of this wave's
+      // 128, tokens 16 ks .. 16 ks + 15
+      auto read_v = [&](int i) __attribute__((always_inline)) {
+        const uint32_t off = (i >> 2) * kGroupBytes + ((i & 3) >> 1) * 1024;
+        const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS s16x4*)lds_at(vx[0][i & 1] + off));
+        const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_AS s16x4*)lds_at(vx[1][i & 1] + off + kHalfGroupBytes));
+        const bf16x4 a0 = __builtin_bit_cast(bf16x4, v0);
+        const bf16x4 a1 = __builtin_bit_cast(bf16x4, v1);
+        bf16x8 vf;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          vf[jj] = a0[jj];
+          vf[4 + jj] = a1[jj];
+        }
+        return vf;
+      };
+      const u32x4 fl = *reinterpret_cast<const LDS_AS u32x4*>(lds_at(small_base + kFl));
+      bf16x8 vcur = read_v(0);
+      bf16x8 pb[4];
+#pragma unroll
+      for (int vb = 0; vb < 4; ++vb)
+        pb[vb] = *reinterpret_cast<const LDS_AS bf16x8*>(lds_at(p_lane + vb * 1024));
+      if constexpr (kSm) recv_half();
+      {
+        const unsigned any = __builtin_amdgcn_readfirstlane(fl[0] | fl[1] | fl[2] | fl[3]);
+        if (any != 0) {
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb) {
+            if (__builtin_amdgcn_readfirstlane(fl[vb]) != 0) {
+              const float al =
+                  *reinterpret_cast<const LDS_AS float*>(lds_at(a_lane + 128 * vb));
+#pragma unroll
+              for (int cb = 0; cb < 4; ++cb) scale_agpr16(acc[cb][vb], al);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int ks = i >> 2, cb = i & 3;
+        const bf16x8 vnext = read_v(i < 7 ? i + 1 : i);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          const int vb = 2 * ks + v;
+          if (i == 7 && v == 1)
+            mfma_agpr<kF16, true>(acc[cb][vb], vcur, pb[vb]);
+          else
+            mfma_agpr<kF16>(acc[cb][vb], vcur, pb[vb]);
+          if constexpr (kSm) {
+            __builtin_amdgcn_sched_barrier(0);
+            sm_slot(2 * i + v);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        vcur = vnext;
+      }
+    };
+
+    if (ntiles > 0) {
+      // tile 0 landed (tiles 1 and 2 may be in flight): its QK, the exchange,
+      // its softmax
+      vm_wait_n<18>();
+      lds_barrier();
+      qk_tile(smem, false, TileDma{});
+      send_half();
+      lds_barrier();
+      recv_half();
+#pragma unroll
+      for (int j = 0; j < 16; ++j) sm_slot(j);
+    }
+    auto iteration = [&](auto with_sm, int it) __attribute__((always_inline)) {
+      constexpr bool nxt = decltype(with_sm)::value;  // a tile it + 1 exists
+      // tile it + 1 landed (tile it + 2 may be in flight); the page numbers of
+      // tile it + 3 are loaded before the waits that cover their latency
+      int pg3[2] = {0, 0};
+      if constexpr (nxt) {
+        pages_of(it + 3, pg3);
+        vm_wait_n<9>();
+      }
+      lds_barrier();  // PV of tile it - 1 and the reads of the exchange done everywhere
+      *reinterpret_cast<LDS_AS bf16x8*>(lds_at(p_lane + wave * 1024)) = pq;
+      if (resc_q && lane < 32)
+        *reinterpret_cast<LDS_AS float*>(lds_at(a_lane + 128 * wave)) = alpha_q;
+      // (tile 0: the accumulators are still zero, nothing to rescale)
+      if (lane == 0)
+        *reinterpret_cast<LDS_AS unsigned*>(lds_at(small_base + kFl + 4 * wave)) =
+            it > 0 ? resc_q : 0u;
+      if constexpr (nxt) {
+        const TileDma tdma = plan_from(it + 3, (it + 3) % NS, pg3);
+        qk_tile(smem + ((it + 1) % NS) * S::kStageBytes, true, tdma);
+        send_half();
+        ts_next = t0 + (it + 1) * T;
+      }
+      lds_barrier();  // P^T, rescale and score halves of every wave
+      pv_tile(with_sm, smem + (it % NS) * S::kStageBytes);
+    };
+    for (int it = 0; it + 1 < ntiles; ++it) iteration(std::true_type{}, it);
+    if (ntiles > 0) iteration(std::false_type{}, ntiles - 1);
+    vm_wait_n<0>();  // the trailing reloads have landed (their slots are reused)
+    lds_barrier();   // ring, P^T, flags and score halves free
+    agpr_settle();
+
+    // ---- epilogue: merge the two token halves of every head ------------------
+    // stat[0][v] = m, stat[1][v] = l of virtual head v (log2 domain)
+    float* stat = reinterpret_cast<float*>(smem + S::kStatOffset);
+    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    if (lane < 32) {
+      stat[32 * wave + l32] = m_ref;
+      stat[128 + 32 * wave + l32] = l_tot;
+    }
+    lds_barrier();
+    // head 32 hb + l32 = virtual heads hb (tokens of half 0) and hb + 2 (half 1),
+    // whose accumulators A0, A1 are unnormalised (sums of 2^(x - m) v):
+    // O = (2^(m0 - M) A0 + 2^(m1 - M) A1) / L, L = l0 2^(m0 - M) + l1 2^(m1 - M)
+    float c0[2], c1[2], lse_h[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float m0 = stat[32 * hb + l32], m1 = stat[32 * (hb + 2) + l32];
+      const float l0 = stat[128 + 32 * hb + l32], l1 = stat[128 + 32 * (hb + 2) + l32];
+      const float M = fmaxf(m0, m1);
+      // a half with no visible token has l = 0 (and m = -inf): weight 0
+      const float e0 = l0 > 0.f ? __builtin_amdgcn_exp2f(m0 - M) : 0.f;
+      const float e1 = l1 > 0.f ? __builtin_amdgcn_exp2f(m1 - M) : 0.f;
+      const float L = l0 * e0 + l1 * e1;
+      const bool empty = !(L > 0.f);
+      const float inv = empty ? 0.f : 1.f / L;
+      c0[hb] = e0 * inv;
+      c1[hb] = e1 * inv;
+      lse_h[hb] = empty ? -INFINITY : (M + __log2f(L)) * kLn2;
+    }
+    const float lse_v = wave == 0 ? lse_h[0] : lse_h[1];  // waves 0 and 1 write heads 32 w + l32
+    if (slot < 0) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        uint16_t* op = a.o + ((size_t)b * H + 32 * hb + l32) * 512 + 128 * wave + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            bf16x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v[i] = to16<kF16>(acc[cb][hb][4 * q + i] * c0[hb] + acc[cb][hb + 2][4 * q + i] * c1[hb]);
+            *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * q) = v;
+          }
+      }
+      if (wave < 2 && lane < 32) a.lse[(size_t)b * H + 32 * wave + l32] = lse_v;
+    } else {
+      // partial of a chunk: merged by the combine kernel after this launch
+      float* po = a.part_o + (size_t)slot * H * 512;
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        float* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              v[i] = acc[cb][hb][4 * q + i] * c0[hb] + acc[cb][hb + 2][4 * q + i] * c1[hb];
+            *reinterpret_cast<f32x4*>(prow + 32 * cb + 8 * q) = v;
+          }
+      }
+      if (wave < 2 && lane < 32) a.part_lse[(size_t)slot * H + 32 * wave + l32] = lse_v;
+    }
+    lds_barrier();  // stat read by every wave before the next segment reuses the area
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Merge of split requests (a launch after the decode kernel), for requests cut
 // into at most kCombineFewMax chunks (launch_combine sends more to the kernel
 // below): one thread per (split request, head, 8 columns), so the merge runs
@@ -2223,6 +2711,32 @@ static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream)
 }
 
 template <int KVT>
+static hipError_t launch_pair(const DecodeArgs& a, int grid, hipStream_t stream) {
+  if (a.qo_len > 1)
+    hipLaunchKernelGGL((mla_decode_pair_kernel<KVT, true>), dim3(grid), dim3(PairShape::kThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((mla_decode_pair_kernel<KVT, false>), dim3(grid), dim3(PairShape::kThreads),
+                       0, stream, a);
+  return hipGetLastError();
+}
+
+static DecodeConfig pair_config() {
+  return DecodeConfig{PairShape::kWaves, PairShape::kTile, PairShape::kLdsBytes};
+}
+
+template <int KVT>
+static int pair_occupancy() {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, reinterpret_cast<const void*>(&mla_decode_pair_kernel<KVT, false>),
+          PairShape::kThreads, 0) != hipSuccess ||
+      n < 1)
+    n = 1;
+  return n;
+}
+
+template <int KVT>
 static DecodeConfig wide_config() {
   return DecodeConfig{WideShape<KVT>::kWaves, WideShape<KVT>::kTile, WideShape<KVT>::kLdsBytes};
 }
@@ -2300,6 +2814,13 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
     if (op == 2) *err = launch_wide<K>(*a, grid, stream);                   \
     return 1;                                                               \
   } while (0)
+#define MLA_PAIR(K)                                                         \
+  do {                                                                      \
+    if (op == 0) *cfg = pair_config();                                      \
+    if (op == 1) return pair_occupancy<K>();                                \
+    if (op == 2) *err = launch_pair<K>(*a, grid, stream);                   \
+    return 1;                                                               \
+  } while (0)
 #define MLA_RING(...)                                                       \
   do {                                                                      \
     if (op == 0) *cfg = config_of<__VA_ARGS__>();                           \
@@ -2314,7 +2835,7 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
     switch (heads) {
       case 16: MLA_STREAM(1, 0, 2);
       case 32: MLA_RING(2, 1, 2, 1, 4);
-      case 64: MLA_RING(4, 1, 1, 2, 4);
+      case 64: MLA_PAIR(0);
       case 128: MLA_WIDE(0);
       default: return 0;
     }
@@ -2350,6 +2871,7 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   if (kv_dtype == 5) {  // fp16: 32- and 64-wide requests run as 16-wide rows
     switch (heads) {
       case 16: MLA_STREAM(1, 5, 2);
+      case 64: MLA_PAIR(5);
       case 128: MLA_WIDE(5);
       default: return 0;
     }
@@ -2357,6 +2879,7 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   return 0;
 #undef MLA_STREAM
 #undef MLA_WIDE
+#undef MLA_PAIR
 #undef MLA_RING
 }
 
