@@ -58,7 +58,8 @@ int page_shift_of(int32_t p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace: segments (32 B each) | worker_ptr | combine list (16 B per split
-// request) | partial LSE | partial O
+// request) | partial LSE | partial O (fp32 [parts, heads, 512]; 128-head rows
+// keep it in fp16, followed by one fp32 scale per 128-column block)
 Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, int32_t heads) {
   Layout L;
   L.segs = 0;
@@ -67,6 +68,7 @@ Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, 
   L.meta_bytes = L.clist + (size_t)ncomb * 16;
   L.plse = align256(L.meta_bytes);
   L.po = align256(L.plse + (size_t)nparts * heads * 4);
+  L.pscale = L.po + (size_t)nparts * heads * 512 * 2;
   L.total = align256(L.po + (size_t)nparts * heads * 512 * 4);
   return L;
 }
@@ -186,6 +188,7 @@ mla_status run_on_workspace(mla_plan_s* p, uint8_t* ws, const void* q_nope, cons
   a.lse = lse;
   a.part_o = reinterpret_cast<float*>(ws + p->layout.po);
   a.part_lse = reinterpret_cast<float*>(ws + p->layout.plse);
+  a.part_scale = reinterpret_cast<float*>(ws + p->layout.pscale);
   a.clist = reinterpret_cast<const int4*>(ws + p->layout.clist);
   a.scale_log2 = sm_scale * 1.4426950408889634f;
   a.o_fp16 = p->kv_dtype == MLA_KV_FP16 ? 1 : 0;

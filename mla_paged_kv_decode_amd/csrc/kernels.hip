@@ -2005,20 +2005,40 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       }
       if (lane < 32) a.lse[(size_t)b * H + 32 * wave + lane] = lse_v;
     } else {
-      // partial of a chunk: merged by the combine kernel after this launch
-      float* po = a.part_o + (size_t)slot * H * 512;
+      // Partial of a chunk, merged by the combine kernel after this launch:
+      // fp16 with one power-of-two scale per (head, 128-column block) that
+      // puts the block's largest |value| in [2^14, 2^15), so each value is
+      // kept to 2^-11 of that largest one, relative (half the bytes of fp32;
+      // a 64 MB round trip at batch 64 x 4096 tokens becomes 32 MB).  This
+      // wave's block of head 32 hb + l32 is spread over lanes l32 and
+      // l32 + 32.
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (size_t)slot * H * 512;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
-        float* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
+        float mx = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(acc[cb][hb][i]));
+        float lo = mx, hi = mx;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+        mx = fmaxf(lo, hi) * inv[hb];
+        // mx < 2^e (frexp); the scale 2^(e - 15) maps mx into [2^14, 2^15)
+        const int ex = min(max(__builtin_amdgcn_frexp_expf(mx) - 15, -126), 127);
+        const float mult = __builtin_amdgcn_ldexpf(inv[hb], -ex);
+        uint16_t* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            f32x4 v;
+            f16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = acc[cb][hb][4 * q + i] * inv[hb];
-            *reinterpret_cast<f32x4*>(prow + 32 * cb + 8 * q) = v;
+            for (int i = 0; i < 4; ++i) v[i] = (_Float16)(acc[cb][hb][4 * q + i] * mult);
+            *reinterpret_cast<f16x4*>(prow + 32 * cb + 8 * q) = v;
           }
+        if (g == 0)
+          a.part_scale[((size_t)slot * H + 32 * hb + l32) * 4 + wave] =
+              __builtin_amdgcn_ldexpf(1.f, ex);
       }
       if (lane < 32) a.part_lse[(size_t)slot * H + 32 * wave + lane] = lse_v;
     }
@@ -2538,14 +2558,23 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   const int n = min(ld_const(cl + 2), K);
   const float* pl = a.part_lse + (size_t)slot0 * H + hd;
   const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
-  float lv[K];
+  // 128 heads: fp16 partials and the scale of their 128-column block
+  const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.part_o) + ((size_t)slot0 * H + hd) * 512 + col;
+  const float* ps = a.part_scale + ((size_t)slot0 * H + hd) * 4 + (col >> 7);
+  float lv[K], sv[K];
   f32x4 x[K][2];
+  f16x8 xh[K];
 #pragma unroll
   for (int v = 0; v < K; ++v) {
     const int i = min(v, n - 1);
     lv[v] = pl[(size_t)i * H];
-    x[v][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
-    x[v][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+    if constexpr (H == 128) {
+      xh[v] = *reinterpret_cast<const f16x8*>(ph + (size_t)i * H * 512);
+      sv[v] = ps[(size_t)i * H * 4];
+    } else {
+      x[v][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
+      x[v][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+    }
   }
   float M = -INFINITY;
 #pragma unroll
@@ -2565,10 +2594,16 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   for (int v = 0; v < K; ++v) {
     if (v < n) {
       const float w = empty ? 0.f : __expf(lv[v] - lse_v);
+      if constexpr (H == 128) {
+        const float ws = w * sv[v];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o8[j] += w * x[v][0][j];
-        o8[4 + j] += w * x[v][1][j];
+        for (int j = 0; j < 8; ++j) o8[j] += ws * (float)xh[v][j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          o8[j] += w * x[v][0][j];
+          o8[4 + j] += w * x[v][1][j];
+        }
       }
     }
   }
@@ -2614,16 +2649,26 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
   const int q = tid % kItems, j = tid / kItems;
   const int col = ch * (8 * kItems) + q * 8;
   const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
-  auto load_batch = [&](int i0, f32x4 (&x)[kBatch][2]) __attribute__((always_inline)) {
+  // 128 heads: fp16 partials and the scale of their 128-column block
+  const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.part_o) + ((size_t)slot0 * H + hd) * 512 + col;
+  const float* ps = a.part_scale + ((size_t)slot0 * H + hd) * 4 + (col >> 7);
+  f32x4 x[kBatch][2];
+  f16x8 xh[kBatch];
+  float sv[kBatch];
+  auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = min(i0 + u * L, n - 1);
-      x[u][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
-      x[u][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+      if constexpr (H == 128) {
+        xh[u] = *reinterpret_cast<const f16x8*>(ph + (size_t)i * H * 512);
+        sv[u] = ps[(size_t)i * H * 4];
+      } else {
+        x[u][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
+        x[u][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
+      }
     }
   };
-  f32x4 x[kBatch][2];
-  load_batch(j, x);  // in flight through the LSE reduction
+  load_batch(j);  // in flight through the LSE reduction
 
   // ---- LSE over the n partials ---------------------------------------------
   const float* pl = a.part_lse + (size_t)slot0 * H + hd;
@@ -2651,16 +2696,22 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
 #pragma unroll
   for (int c = 0; c < 8; ++c) o8[c] = 0.f;
   for (int i0 = j; i0 < n; i0 += kBatch * L) {
-    if (i0 != j) load_batch(i0, x);
+    if (i0 != j) load_batch(i0);
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = i0 + u * L;
       if (i < n) {
         const float w = s_w[i];
+        if constexpr (H == 128) {
+          const float ws = w * sv[u];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          o8[c] += w * x[u][0][c];
-          o8[4 + c] += w * x[u][1][c];
+          for (int c = 0; c < 8; ++c) o8[c] += ws * (float)xh[u][c];
+        } else {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            o8[c] += w * x[u][0][c];
+            o8[4 + c] += w * x[u][1][c];
+          }
         }
       }
     }

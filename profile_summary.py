@@ -14,9 +14,16 @@ summarised.  Writes ``profiles/<kernel>_<workload>.md`` and
 ``profiles/traffic_<workload>.json`` (HBM bytes per launch, keyed by the
 kernel-source hash printed by bench.py so that stale counters are not used).
 
+With ``--sq DIR ...`` (runs with SQ / GRBM counters, ``--command-sq`` giving
+their commands in the same order) it adds, for the same kernel, the MFMA
+pipes' busy fraction (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs times the
+kernel's cycles, GRBM_GUI_ACTIVE / 8 XCDs), the MFMA flops counted by
+SQ_INSTS_VALU_MFMA_MOPS_* (units of 512), the share of LDS cycles lost to bank
+conflicts, and where the waves spent their cycles.
+
 usage: python profile_summary.py --stats DIR --fetch DIR
        --write DIR --bench-log FILE --calib-mib N --out profiles --command-stats "..."
-       --command-fetch "..." --command-write "..."
+       --command-fetch "..." --command-write "..." [--sq DIR ... --command-sq "..." ...]
 """
 from __future__ import annotations
 
@@ -48,6 +55,65 @@ def counter_avgs(d, counter):
     return {r[0]: dict(n=r[1], avg=r[2], max=r[3]) for r in rows}
 
 
+def all_counters(d):
+    cur = _db(d).cursor()
+    rows = cur.execute("select kernel_name, counter_name, avg(value) from counters_collection "
+                       "group by kernel_name, counter_name").fetchall()
+    out = {}
+    for k, c, v in rows:
+        out.setdefault(k, {})[c] = v
+    return out
+
+
+N_XCD, N_SIMD = 8, 1024  # MI355X: 8 XCDs, 256 CUs x 4 SIMDs
+
+
+def sq_section(kname, sq_dirs, commands, flops, avg_us):
+    """Markdown lines of the SQ / GRBM counters of kernel kname (per dispatch,
+    averaged over the dispatches of each run)."""
+    c = {}
+    for d in sq_dirs:
+        for k, vals in all_counters(d).items():
+            if kname in k:
+                c.update(vals)
+    if not c:
+        return []
+    lines = ["", "## Matrix cores, LDS and wave states of `%s` (per launch)" % kname, "",
+             "Counter commands (one pass each):", ""] + ["    " + x for x in commands] + [
+             "", "| quantity | value |", "|---|---|"]
+    for name in sorted(c):
+        lines.append("| %s | %.4g |" % (name, c[name]))
+    cyc = c.get("GRBM_GUI_ACTIVE", 0.0) / N_XCD
+    busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+    derived = []
+    if cyc > 0 and busy is not None:
+        derived.append(("kernel cycles (GRBM_GUI_ACTIVE / %d XCDs)" % N_XCD, "%.0f" % cyc))
+        derived.append(("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x cycles)" % N_SIMD,
+                        "%.1f %%" % (100.0 * busy / (N_SIMD * cyc))))
+        if c.get("SQ_INSTS_MFMA"):
+            derived.append(("busy cycles per MFMA instruction", "%.1f" % (busy / c["SQ_INSTS_MFMA"])))
+    mops = sum(v for k, v in c.items() if k.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    if mops:
+        derived.append(("MFMA flops counted (MOPS x 512)", "%.4g" % (mops * 512)))
+        if flops:
+            derived.append(("algorithmic flops of the launch", "%.4g" % flops))
+        if avg_us:
+            derived.append(("MFMA TFLOP/s at the traced duration", "%.1f" % (mops * 512 / avg_us / 1e6)))
+    if c.get("SQ_LDS_IDX_ACTIVE"):
+        derived.append(("LDS bank-conflict cycles / LDS active cycles", "%.1f %%" % (
+            100.0 * c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_LDS_IDX_ACTIVE"])))
+    wc = c.get("SQ_WAVE_CYCLES")
+    if wc:
+        for k in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS", "SQ_WAIT_ANY",
+                  "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
+            if k in c:
+                derived.append(("%s / SQ_WAVE_CYCLES" % k, "%.1f %%" % (100.0 * c[k] / wc)))
+    if derived:
+        lines += ["", "| derived | value |", "|---|---|"]
+        lines += ["| %s | %s |" % d for d in derived]
+    return lines
+
+
 def short(name):
     m = re.search(r"(mla_[a-z0-9_]+_kernel(<[^>]*>)?)", name)
     if m:
@@ -66,6 +132,8 @@ def main():
     ap.add_argument("--command-stats", required=True)
     ap.add_argument("--command-fetch", required=True)
     ap.add_argument("--command-write", required=True)
+    ap.add_argument("--sq", nargs="*", default=[])
+    ap.add_argument("--command-sq", nargs="*", default=[])
     args = ap.parse_args()
 
     bench = None
@@ -125,6 +193,8 @@ def main():
         ]
         lines.append("| algorithmic bytes (inputs + outputs once) | %d |" % alg)
         lines.append("| traffic / algorithmic | %.3f |" % ((fetch_b + write_b) / alg))
+        lines += sq_section(kname, args.sq, args.command_sq, bench["config"].get("flops"),
+                            avg_us[0] if avg_us else None)
         lines.append("")
         lines.append("kernel source hash (bench.py `kernel_sha`): `%s`" % sha)
         with open(os.path.join(args.out, "%s_%s.md" % (re.sub(r"[^a-z0-9_]", "", kname.split("<")[0]),

@@ -51,6 +51,45 @@ def test_head_split_matches_oracle(heads, hs):
     check(o2, lse2, *ref(inp))
 
 
+@pytest.mark.parametrize("heads,kvd", [(16, synth.KV_BF16), (32, synth.KV_BF16),
+                                       (64, synth.KV_BF16), (64, synth.KV_FP16),
+                                       (128, synth.KV_BF16), (16, synth.KV_FP8_E4M3),
+                                       (128, synth.KV_INT8)])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_many_segments_per_workgroup(heads, kvd, splits):
+    # few workgroups, so each runs a long list of segments: empty requests,
+    # one- and two-tile ones, tile-aligned ends, chunks of split requests
+    # (partials) and whole requests in one list (the 64-head kernel fetches
+    # the next segment's first tiles while it finishes the current one)
+    import mla_paged_kv_decode_amd as mla
+    rng = np.random.default_rng(900 + heads + splits)
+    lengths = [0, 1, 31, 32, 33, 64, 65, 96, 0, 17, 700, 1500, 2, 128, 129, 0, 250, 1000]
+    lengths += [int(x) for x in rng.integers(1, 400, 22)]
+    inp = synth.make_inputs(lengths, heads, 16, kvd, seed=77 + heads, poison=True, extra_pages=4)
+    t = dev(inp)
+    B, H = inp.batch, heads
+    print("case heads=%d kv=%d splits=%d" % (heads, kvd, splits), flush=True)
+    ws = torch.empty(mla.workspace_bytes(B, H, force_splits=splits, max_workers=7),
+                     dtype=torch.uint8, device="cuda")
+    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 16, kvd, ws, force_splits=splits,
+                    max_workers=7)
+    info = plan.info()
+    _, wp = plan.segments()
+    assert info["num_workers"] == 7 and int(np.diff(wp).max()) >= 6
+    t16 = torch.float16 if kvd == synth.KV_FP16 else torch.bfloat16
+    outs = []
+    for _ in range(2):
+        o = torch.empty((B, H, 512), dtype=t16, device="cuda")
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        plan.run(t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_scale"], t["kv_indptr"],
+                 t["kv_indices"], t["kv_last_page_len"], inp.sm_scale, o, lse)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    assert torch.equal(outs[0][1], outs[1][1])
+    check(*host(*outs[0]), *ref(inp))
+
+
 def test_tiny_workload():
     inp = synth.make_workload("tiny_b4_h16_l256_p16")
     o, lse = host(*gpu_run(inp))
