@@ -92,7 +92,7 @@ typedef struct {
                            vectors as n groups of qo_len * num_heads / n sharing the
                            request's latent cache (n = 1: all in one workgroup).  The group
                            width must be one the kernels serve: 16, 32, 64 or 128 (bf16),
-                           16 or 128 (8-bit caches). */
+                           16, 64 or 128 (fp16), 16 or 128 (8-bit caches). */
   int32_t qo_len;       /* queries per request, 1..64; 0 means 1 */
   int32_t l2_domains;   /* L2 domains (XCDs) that workgroups are dealt to round-robin in
                            launch order; the rows of one request are placed in one of them
@@ -103,7 +103,8 @@ typedef struct {
 typedef struct mla_plan_s* mla_plan_t;
 
 /* Supported shapes: num_heads in {16, 32, 64, 128}; page_size in {16, 32, 64};
-   every kv_dtype (8-bit caches run 16- and 128-wide rows);
+   every kv_dtype (8-bit caches run 16- and 128-wide rows, fp16 16-, 64- and
+   128-wide rows);
    qo_len in 1..64.  The automatic group width is the largest served width that
    divides qo_len * num_heads. */
 
@@ -117,7 +118,12 @@ size_t mla_decode_workspace_bytes(int32_t batch, int32_t num_heads, const mla_pl
 
 /*
  * Build the split-KV schedule for one batch (the balanced scheduler; runs on
- * the host, launches no kernel).  A request whose qo_len * num_heads query
+ * the host, launches no kernel).  FlashMLA PR 233, "What is added": a
+ * scheduler that balances requests of different lengths over the GPU's
+ * compute units, with its metadata computed before the decode launch so that
+ * the launch can be captured in a graph.  The run of a batch-decode wrapper
+ * is what "Benchmarking MLA" times; this split keeps all host work out of
+ * that run.  A request whose qo_len * num_heads query
  * vectors are wider than one workgroup serves (see head_split) runs as
  * several rows of the served width; the workgroups of those rows are placed
  * on one XCD so that the request's latent cache is fetched from HBM about
@@ -147,7 +153,11 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
 /*
  * Run the decode for a plan on `stream`: the decode kernel and, when the plan
  * split requests into chunks (up to 256 per request), a second launch that
- * merges their partials over the whole GPU.  Every merge sums in a fixed
+ * merges their partials over the whole GPU.  The operands are those of the
+ * decode call in "Benchmarking MLA" (nvbench snippet: q_nope, q_pe, ckv, kpe,
+ * kv_indptr, kv_indices, kv_last_page_len, o) with the shapes of flashinfer
+ * PR 844; the merge is the deterministic LSE-weighted combine of FlashMLA PR
+ * 233, "What is added".  Every merge sums in a fixed
  * order, so reruns are bit-identical.  Allocates nothing, never
  * synchronises and never reads device memory from the host, so it may be
  * captured in a HIP graph and replayed.  A plan stays valid while requests
