@@ -58,8 +58,8 @@ int page_shift_of(int32_t p) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace: segments (32 B each) | worker_ptr | combine list (16 B per split
-// request) | partial LSE | partial O (fp32 [parts, heads, 512]; 128-head rows
-// keep it in fp16, followed by one fp32 scale per 128-column block)
+// request) | partial LSE | partial O (sized as fp32 [parts, heads, 512]; held
+// as fp16, followed by one fp32 scale per 128-column block)
 Layout layout_for(int64_t nseg, int64_t workers, int64_t ncomb, int64_t nparts, int32_t heads) {
   Layout L;
   L.segs = 0;

@@ -21,11 +21,11 @@ struct DecodeArgs {
   const int32_t* worker_ptr;  // grid + 1
   uint16_t* o;                // bf16 [B, H, 512]
   float* lse;                 // [B, H]
-  float* part_o;              // [slots, H, 512] (fp16 for H = 128, as below)
+  float* part_o;              // partial O: fp16 [slots, H, 512] (typed float* for the
+                              // workspace's fp32 sizing; the scales follow the fp16 data)
   float* part_lse;            // [slots, H]
-  float* part_scale;          // H = 128: part_o holds fp16 [slots, H, 512] and this the
-                              // power-of-two scale of each 128-column block [slots, H, 4]:
-                              // the partial is fp16 value x scale
+  float* part_scale;          // power-of-two scale of each 128-column block of part_o
+                              // [slots, H, 4]: the partial is fp16 value x scale
   const int4* clist;          // 4 ints per split request: row, first slot, chunks, 0
   float scale_log2;           // sm_scale * log2(e)
   int32_t o_fp16;             // 1: o is fp16 (fp16 cache and queries), 0: bf16

@@ -234,6 +234,14 @@ constexpr int merge_bytes() {
   return TS > 1 ? HG * TS * 16 * kMergeStride * 4 + HG * TS * 16 * 8 : 0;
 }
 
+// Partials of split chunks are stored in fp16 with one power-of-two scale per
+// (head, 128-column block): scale_exp(m) for the block's largest |value| m is
+// the e with m * 2^-e in [2^14, 2^15), so every value keeps 2^-11 of m,
+// relative, and cannot overflow; the stored scale is 2^e (value = fp16 x 2^e).
+__device__ __forceinline__ int scale_exp(float m) {
+  return min(max(__builtin_amdgcn_frexp_expf(m) - 15, -126), 127);
+}
+
 // HG here is the number of merge-slot columns: a call merges slot (ts, hg) ->
 // ts * HG + hg; `hblock` is the 16-head block of the output rows it writes.
 template <int H, int HG, int TS, bool F16 = false>
@@ -262,9 +270,29 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
       }
       if (lane < 16) a.lse[orow] = lse_v;
     } else {
-      float* po = a.part_o + ((size_t)slot * H + head) * 512 + 4 * (lane >> 4);
+      // fp16 with a scale per 128-column block k = columns 16 cb + ..., cb in
+      // [8k, 8k + 8), held by the 4 lanes of this head
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + ((size_t)slot * H + head) * 512 +
+                     4 * (lane >> 4);
 #pragma unroll
-      for (int cb = 0; cb < 32; ++cb) *reinterpret_cast<f32x4*>(po + cb * 16) = acc[cb] * inv;
+      for (int k = 0; k < 4; ++k) {
+        float mx = 0.f;
+#pragma unroll
+        for (int cb = 8 * k; cb < 8 * k + 8; ++cb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, fabsf(acc[cb][i]));
+        const int ex = scale_exp(wave_max_16(mx) * inv);
+        const float mult = __builtin_amdgcn_ldexpf(inv, -ex);
+#pragma unroll
+        for (int cb = 8 * k; cb < 8 * k + 8; ++cb) {
+          f16x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = (_Float16)(acc[cb][i] * mult);
+          *reinterpret_cast<f16x4*>(po + cb * 16) = v;
+        }
+        if (lane < 16)
+          a.part_scale[((size_t)slot * H + head) * 4 + k] = __builtin_amdgcn_ldexpf(1.f, ex);
+      }
       if (lane < 16) a.part_lse[(size_t)slot * H + head] = lse_v;
     }
   } else {
@@ -325,15 +353,24 @@ __device__ __forceinline__ void write_head_block(const DecodeArgs& a, f32x4 (&ac
         *reinterpret_cast<bf16x8*>(a.o + ((size_t)b * H + hd) * 512 + col) = v;
         if (ts == 0 && (e % (kCols / 8)) == 0) a.lse[(size_t)b * H + hd] = lse_v;
       } else {
-        float* po = a.part_o + ((size_t)slot * H + hd) * 512 + col;
-        f32x4 y0, y1;
+        // fp16 with a scale per 128-column block: its 16 threads of 8 columns
+        // are 16 consecutive lanes, aligned (kCols / 8 items per head, a
+        // multiple of 16)
+        static_assert((kCols / 8) % 16 == 0, "whole 128-column blocks per head and wave");
+        float mx = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          y0[i] = o8[i] * inv;
-          y1[i] = o8[4 + i] * inv;
-        }
-        *reinterpret_cast<f32x4*>(po) = y0;
-        *reinterpret_cast<f32x4*>(po + 4) = y1;
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf(o8[i]));
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const int ex = scale_exp(mx * inv);
+        const float mult = __builtin_amdgcn_ldexpf(inv, -ex);
+        f16x8 y;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = (_Float16)(o8[i] * mult);
+        *reinterpret_cast<f16x8*>(reinterpret_cast<uint16_t*>(a.part_o) +
+                                  ((size_t)slot * H + hd) * 512 + col) = y;
+        if ((e & 15) == 0)
+          a.part_scale[((size_t)slot * H + hd) * 4 + (col >> 7)] = __builtin_amdgcn_ldexpf(1.f, ex);
         if (ts == 0 && (e % (kCols / 8)) == 0) a.part_lse[(size_t)slot * H + hd] = lse_v;
       }
     }
@@ -2006,12 +2043,10 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       if (lane < 32) a.lse[(size_t)b * H + 32 * wave + lane] = lse_v;
     } else {
       // Partial of a chunk, merged by the combine kernel after this launch:
-      // fp16 with one power-of-two scale per (head, 128-column block) that
-      // puts the block's largest |value| in [2^14, 2^15), so each value is
-      // kept to 2^-11 of that largest one, relative (half the bytes of fp32;
-      // a 64 MB round trip at batch 64 x 4096 tokens becomes 32 MB).  This
-      // wave's block of head 32 hb + l32 is spread over lanes l32 and
-      // l32 + 32.
+      // fp16 with one scale per (head, 128-column block) (scale_exp; half the
+      // bytes of fp32: a 64 MB round trip at batch 64 x 4096 tokens becomes
+      // 32 MB).  This wave's block of head 32 hb + l32 is spread over lanes
+      // l32 and l32 + 32.
       uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (size_t)slot * H * 512;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
@@ -2024,7 +2059,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
         mx = fmaxf(lo, hi) * inv[hb];
         // mx < 2^e (frexp); the scale 2^(e - 15) maps mx into [2^14, 2^15)
-        const int ex = min(max(__builtin_amdgcn_frexp_expf(mx) - 15, -126), 127);
+        const int ex = scale_exp(mx);
         const float mult = __builtin_amdgcn_ldexpf(inv[hb], -ex);
         uint16_t* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
 #pragma unroll
@@ -2512,21 +2547,37 @@ __global__ void __launch_bounds__(256) mla_decode_pair_kernel(const DecodeArgs a
       }
       if (wave < 2 && lane < 32) a.lse[(size_t)b * H + 32 * wave + l32] = lse_v;
     } else {
-      // partial of a chunk: merged by the combine kernel after this launch
-      float* po = a.part_o + (size_t)slot * H * 512;
+      // partial of a chunk, merged by the combine kernel after this launch:
+      // fp16 with one scale per (head, 128-column block) (scale_exp); this
+      // wave's block of head 32 hb + l32 is spread over lanes l32, l32 + 32
+      uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (size_t)slot * H * 512;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        float* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
+        // the merged values are formed twice (for the block max, then stored)
+        // rather than held in 64 more registers
+        float mx = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            mx = fmaxf(mx, fabsf(acc[cb][hb][i] * c0[hb] + acc[cb][hb + 2][i] * c1[hb]));
+        float lo = mx, hi = mx;
+        asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
+        const int ex = scale_exp(fmaxf(lo, hi));
+        const float d0 = __builtin_amdgcn_ldexpf(c0[hb], -ex), d1 = __builtin_amdgcn_ldexpf(c1[hb], -ex);
+        uint16_t* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            f32x4 v;
+            f16x4 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              v[i] = acc[cb][hb][4 * q + i] * c0[hb] + acc[cb][hb + 2][4 * q + i] * c1[hb];
-            *reinterpret_cast<f32x4*>(prow + 32 * cb + 8 * q) = v;
+              v[i] = (_Float16)(acc[cb][hb][4 * q + i] * d0 + acc[cb][hb + 2][4 * q + i] * d1);
+            *reinterpret_cast<f16x4*>(prow + 32 * cb + 8 * q) = v;
           }
+        if (g == 0)
+          a.part_scale[((size_t)slot * H + 32 * hb + l32) * 4 + wave] = __builtin_amdgcn_ldexpf(1.f, ex);
       }
       if (wave < 2 && lane < 32) a.part_lse[(size_t)slot * H + 32 * wave + l32] = lse_v;
     }
@@ -2557,24 +2608,17 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
   const int slot0 = ld_const(cl + 1);
   const int n = min(ld_const(cl + 2), K);
   const float* pl = a.part_lse + (size_t)slot0 * H + hd;
-  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
-  // 128 heads: fp16 partials and the scale of their 128-column block
+  // fp16 partials and the scale of their 128-column block
   const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.part_o) + ((size_t)slot0 * H + hd) * 512 + col;
   const float* ps = a.part_scale + ((size_t)slot0 * H + hd) * 4 + (col >> 7);
   float lv[K], sv[K];
-  f32x4 x[K][2];
   f16x8 xh[K];
 #pragma unroll
   for (int v = 0; v < K; ++v) {
     const int i = min(v, n - 1);
     lv[v] = pl[(size_t)i * H];
-    if constexpr (H == 128) {
-      xh[v] = *reinterpret_cast<const f16x8*>(ph + (size_t)i * H * 512);
-      sv[v] = ps[(size_t)i * H * 4];
-    } else {
-      x[v][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
-      x[v][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
-    }
+    xh[v] = *reinterpret_cast<const f16x8*>(ph + (size_t)i * H * 512);
+    sv[v] = ps[(size_t)i * H * 4];
   }
   float M = -INFINITY;
 #pragma unroll
@@ -2593,18 +2637,9 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
 #pragma unroll
   for (int v = 0; v < K; ++v) {
     if (v < n) {
-      const float w = empty ? 0.f : __expf(lv[v] - lse_v);
-      if constexpr (H == 128) {
-        const float ws = w * sv[v];
+      const float ws = empty ? 0.f : __expf(lv[v] - lse_v) * sv[v];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) o8[j] += ws * (float)xh[v][j];
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          o8[j] += w * x[v][0][j];
-          o8[4 + j] += w * x[v][1][j];
-        }
-      }
+      for (int j = 0; j < 8; ++j) o8[j] += ws * (float)xh[v][j];
     }
   }
   bf16x8 v;
@@ -2648,24 +2683,17 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
 
   const int q = tid % kItems, j = tid / kItems;
   const int col = ch * (8 * kItems) + q * 8;
-  const float* po = a.part_o + ((size_t)slot0 * H + hd) * 512 + col;
-  // 128 heads: fp16 partials and the scale of their 128-column block
+  // fp16 partials and the scale of their 128-column block
   const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.part_o) + ((size_t)slot0 * H + hd) * 512 + col;
   const float* ps = a.part_scale + ((size_t)slot0 * H + hd) * 4 + (col >> 7);
-  f32x4 x[kBatch][2];
   f16x8 xh[kBatch];
   float sv[kBatch];
   auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = min(i0 + u * L, n - 1);
-      if constexpr (H == 128) {
-        xh[u] = *reinterpret_cast<const f16x8*>(ph + (size_t)i * H * 512);
-        sv[u] = ps[(size_t)i * H * 4];
-      } else {
-        x[u][0] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512);
-        x[u][1] = *reinterpret_cast<const f32x4*>(po + (size_t)i * H * 512 + 4);
-      }
+      xh[u] = *reinterpret_cast<const f16x8*>(ph + (size_t)i * H * 512);
+      sv[u] = ps[(size_t)i * H * 4];
     }
   };
   load_batch(j);  // in flight through the LSE reduction
@@ -2701,18 +2729,9 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
     for (int u = 0; u < kBatch; ++u) {
       const int i = i0 + u * L;
       if (i < n) {
-        const float w = s_w[i];
-        if constexpr (H == 128) {
-          const float ws = w * sv[u];
+        const float ws = s_w[i] * sv[u];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) o8[c] += ws * (float)xh[u][c];
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            o8[c] += w * x[u][0][c];
-            o8[4 + c] += w * x[u][1][c];
-          }
-        }
+        for (int c = 0; c < 8; ++c) o8[c] += ws * (float)xh[u][c];
       }
     }
   }

@@ -20,7 +20,7 @@ namespace mla_abi {
 // uploads; the partial regions are written and read by every run.
 struct Layout {
   size_t segs, wptr, clist, plse, po, total, meta_bytes;
-  size_t pscale;  // 128-head rows: the partials' block scales, inside the partial-O area
+  size_t pscale;  // the partials' block scales, inside the partial-O area (after the fp16 data)
 };
 
 // Records the text returned by mla_last_error on this thread.
