@@ -29,8 +29,9 @@
 //     is lane-local.
 //
 // Output: each segment is either a whole request (o bf16 and lse fp32 written
-// directly) or a chunk of one (normalised fp32 partial O and its LSE written to
-// a partial slot with plain stores).  A second launch after the decode kernel
+// directly) or a chunk of one (normalised partial O in fp16 with a power-of-two
+// scale per 128-column block, and its fp32 LSE, written to a partial slot with
+// plain stores).  A second launch after the decode kernel
 // (mla_combine_kernel / mla_combine_many_kernel) merges the chunks of every
 // split request in chunk order, weighting each by exp(LSE_i - LSE), so results
 // are deterministic and no state survives from one launch to the next.

@@ -3,7 +3,8 @@
 // Cost model, in token-equivalents of KV traffic (one token = one 1152-byte
 // latent row in bf16): a chunk of n tokens costs n + kFixed + H (loading the
 // request's H query rows, 1152 B each) and, when the request is cut, another
-// 4H for writing and re-reading its fp32 partial output (2048 B per head, twice).
+// 4H for its partial output (written, read back by the merge launch: 1 KiB of
+// fp16 per head each way) and its share of that launch.
 // For each candidate chunk size C (a multiple of the granularity) every
 // request is cut into ceil(L / C) near-equal chunks; the chunks are assigned
 // longest-first to the least-loaded worker (ties to the lower index) and the
