@@ -108,10 +108,16 @@ def synth_heads(name: str) -> int:
 
 
 def kernel_sha() -> str:
+    """Hash of the sources that decide what the GPU runs, without comments and
+    whitespace (so that an edit of the text alone keeps measured counters valid)."""
+    import re
     h = hashlib.sha256()
     for name in ("kernels.hip", "kernels.h", "api.cpp", "planner.cpp"):
-        with open(os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mla_paged_kv_decode_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)  # block comments
+        text = re.sub(r"//[^\n]*", " ", text)               # line comments
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
