@@ -45,6 +45,8 @@ CASES = [
     (16, 8, synth.KV_FP8_E4M3),   # 128 wide, 8-bit
     (64, 2, synth.KV_INT8),       # 128 wide, 8-bit
     (128, 2, synth.KV_INT8),      # two 128-wide rows, 8-bit
+    (32, 2, synth.KV_FP16),       # 64 wide, fp16
+    (16, 8, synth.KV_FP16),       # 128 wide, fp16
 ]
 
 
@@ -63,7 +65,7 @@ def test_multiquery_matches_oracle(heads, q, kvd, page):
 
 @pytest.mark.parametrize("heads,q,kvd", [(16, 4, synth.KV_BF16), (16, 8, synth.KV_BF16),
                                          (128, 2, synth.KV_BF16), (16, 2, synth.KV_FP8_E4M3),
-                                         (16, 8, synth.KV_INT8)])
+                                         (16, 8, synth.KV_INT8), (32, 2, synth.KV_FP16)])
 @pytest.mark.parametrize("splits", [2, 5])
 def test_multiquery_forced_splits(heads, q, kvd, splits):
     # with 16-token chunks, the last chunk of the 65-token request holds one
