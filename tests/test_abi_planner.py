@@ -360,3 +360,64 @@ def test_run_rejects_metadata_that_differs_from_the_plan():
     # with the right sizes, the next check is the device one
     with pytest.raises(ValueError, match="device"):
         plan.run(q_nope, q_pe, ckv, kpe, None, *good, 0.07, o, lse)
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <stdlib.h>
+#include "mla_decode.h"
+#include "mla_peaks.h"
+
+/* a host-only plan through the public header, from C: three requests of
+   1000, 0 and 33 tokens in 16-token pages; every token planned once */
+int main(void) {
+  const int32_t indptr[4] = {0, 63, 63, 66};
+  const int32_t last[3] = {8, 1, 1};
+  mla_plan_opts opts = {0};
+  opts.num_cus = 256;
+  size_t ws = mla_decode_workspace_bytes(3, 64, &opts);
+  mla_plan_t plan = NULL;
+  mla_status st = mla_decode_plan(&plan, indptr, last, 3, 64, 16, MLA_KV_BF16, &opts, NULL, 0,
+                                  NULL);
+  if (ws == 0 || st != MLA_OK) {
+    printf("plan failed: %s %s\n", mla_status_string(st), mla_last_error());
+    return 1;
+  }
+  int32_t info[15];
+  if (mla_decode_plan_info(plan, info) != MLA_OK) return 2;
+  int32_t* seg = (int32_t*)malloc(sizeof(int32_t) * 4 * (size_t)(info[5] > 0 ? info[5] : 1));
+  int32_t* wp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(info[4] + 1));
+  if (mla_decode_plan_segments(plan, seg, wp) != MLA_OK) return 3;
+  long covered[3] = {0, 0, 0};
+  for (int i = 0; i < info[5]; ++i) covered[seg[4 * i]] += seg[4 * i + 2] - seg[4 * i + 1];
+  printf("%ld %ld %ld %d\n", covered[0], covered[1], covered[2], info[4]);
+  free(seg);
+  free(wp);
+  mla_decode_plan_destroy(plan);
+  /* an invalid kv_dtype is an error, not undefined behaviour */
+  st = mla_decode_plan(&plan, indptr, last, 3, 64, 16, 99, &opts, NULL, 0, NULL);
+  return st == MLA_OK ? 4 : 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_plans_from_c(lib, tmp_path):
+    # the public headers compile as C99 with warnings as errors, and a C
+    # program linked to the library plans a batch (host only)
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc missing")
+    src = tmp_path / "plan.c"
+    src.write_text(C_PROGRAM)
+    exe = str(tmp_path / "plan")
+    libdir = os.path.dirname(mla.LIB_PATH)
+    subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                    "-I", os.path.join(ROOT, "include"), str(src), "-o", exe,
+                    "-L", libdir, "-l:libmla_decode.so", "-Wl,-rpath," + libdir],
+                   check=True, capture_output=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    covered = [int(x) for x in r.stdout.split()]
+    assert covered[:3] == [1000, 0, 33] and covered[3] > 0
