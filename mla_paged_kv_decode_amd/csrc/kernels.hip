@@ -2652,15 +2652,19 @@ __global__ void __launch_bounds__(256) mla_combine_kernel(const DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Merge of split requests cut into many chunks (more than kCombineFewMax;
-// up to 256), as long contexts at small batch are.  One workgroup per (split request, head, column chunk), so the
-// n partials of a request are read by many workgroups at once rather than by
-// one.  L partial lanes per 8 columns (L = 16 for up to 16 chunks, else 32;
-// the workgroup covers 8 * 256 / L columns): thread (q, j) (q = tid % (256 /
-// L), j = tid / (256 / L)) sums w_i O_i over its 8 columns for partials i = j,
-// j + L, ...  Its first partials' loads are issued before the LSE reduction,
-// which they do not depend on: the workgroup reads the head's n partial LSEs
-// (one per thread), reduces them to LSE = M + ln sum_i exp(LSE_i - M) and
-// keeps w_i = exp(LSE_i - LSE) in LDS.  The L sums per 8 columns are added by
+// up to 256), as long contexts at small batch are.  One workgroup per (split
+// request, head, column chunk), so the n partials of a request are read by
+// many workgroups at once rather than by one.  L partial lanes per 8 columns;
+// the workgroup covers 8 * 256 / L columns: L = 4 (the whole 512-column row,
+// each wave taking every fourth partial) when the (request, head) pairs alone
+// give enough workgroups, else L = 16 (128 columns) up to 16 chunks and 32 (64
+// columns) beyond.  Thread (q, j) (q = tid % (256 / L), j = tid / (256 / L))
+// sums w_i O_i over its 8 columns for partials i = j, j + L, ..., kBatch
+// partials' loads in flight and the next batch requested before the current
+// one is added.  Its first loads are issued before the LSE reduction, which
+// they do not depend on: the workgroup reads the head's n partial LSEs (one
+// per thread), reduces them to LSE = M + ln sum_i exp(LSE_i - M) and keeps
+// w_i = exp(LSE_i - LSE) in LDS.  The L sums per 8 columns are added by
 // xor-shuffles within a wave and then wave by wave.  Every reduction has a
 // fixed order, so reruns are bit-identical.
 // ---------------------------------------------------------------------------
@@ -2668,7 +2672,7 @@ template <int H, bool F16, int L>
 __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs a) {
   constexpr int kItems = 256 / L;           // 8-column items per workgroup
   constexpr int kChunks = 512 / (8 * kItems);
-  constexpr int kBatch = 4;                 // partials in flight per thread
+  constexpr int kBatch = L == 4 ? 8 : 4;    // partials in flight per thread
   __shared__ float s_w[256];
   __shared__ float s_red[2][4];
   __shared__ f32x4 s_o[4][kItems][2];
@@ -2687,9 +2691,12 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
   // fp16 partials and the scale of their 128-column block
   const uint16_t* ph = reinterpret_cast<const uint16_t*>(a.part_o) + ((size_t)slot0 * H + hd) * 512 + col;
   const float* ps = a.part_scale + ((size_t)slot0 * H + hd) * 4 + (col >> 7);
-  f16x8 xh[kBatch];
-  float sv[kBatch];
-  auto load_batch = [&](int i0) __attribute__((always_inline)) {
+  // two batches of registers: the next batch is requested before the current
+  // one is added
+  f16x8 xa[kBatch], xb[kBatch];
+  float sa[kBatch], sb[kBatch];
+  auto load_batch = [&](int i0, f16x8 (&xh)[kBatch], float (&sv)[kBatch])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = min(i0 + u * L, n - 1);
@@ -2697,7 +2704,7 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
       sv[u] = ps[(size_t)i * H * 4];
     }
   };
-  load_batch(j);  // in flight through the LSE reduction
+  load_batch(j, xa, sa);  // in flight through the LSE reduction
 
   // ---- LSE over the n partials ---------------------------------------------
   const float* pl = a.part_lse + (size_t)slot0 * H + hd;
@@ -2724,8 +2731,8 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
   float o8[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) o8[c] = 0.f;
-  for (int i0 = j; i0 < n; i0 += kBatch * L) {
-    if (i0 != j) load_batch(i0);
+  auto add_batch = [&](int i0, const f16x8 (&xh)[kBatch], const float (&sv)[kBatch])
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
       const int i = i0 + u * L;
@@ -2735,6 +2742,14 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
         for (int c = 0; c < 8; ++c) o8[c] += ws * (float)xh[u][c];
       }
     }
+  };
+  constexpr int kStep = kBatch * L;  // partials per batch of the workgroup
+  for (int i0 = j; i0 < n; i0 += 2 * kStep) {
+    if (i0 + kStep < n) load_batch(i0 + kStep, xb, sb);
+    add_batch(i0, xa, sa);
+    if (i0 + kStep >= n) break;
+    if (i0 + 2 * kStep < n) load_batch(i0 + 2 * kStep, xa, sa);
+    add_batch(i0 + kStep, xb, sb);
   }
   // a wave holds lanes j = (64 / kItems) wave + 0 .. 64 / kItems - 1 of every
   // item: lanes that differ in the bits above log2(kItems)
@@ -2958,8 +2973,16 @@ template <int H>
 static hipError_t launch_combine_h(const DecodeArgs& a, int ncomb, int max_splits,
                                    hipStream_t stream) {
   if (max_splits > kCombineFewMax) {
-    // 16 partial lanes (4 column chunks of a head) up to 16 chunks, else 32 (8)
-    if (max_splits <= 16) {
+    // whole rows (4 partial lanes) when the (request, head) pairs fill a
+    // device's CUs; else 16 partial lanes (4 column chunks of a head) up to 16
+    // chunks, 32 (8) beyond
+    if ((long)ncomb * H >= 256) {
+      const dim3 grid(ncomb * H);
+      if (a.o_fp16)
+        hipLaunchKernelGGL((mla_combine_many_kernel<H, true, 4>), grid, dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((mla_combine_many_kernel<H, false, 4>), grid, dim3(256), 0, stream, a);
+    } else if (max_splits <= 16) {
       const dim3 grid(ncomb * H * 4);
       if (a.o_fp16)
         hipLaunchKernelGGL((mla_combine_many_kernel<H, true, 16>), grid, dim3(256), 0, stream, a);
