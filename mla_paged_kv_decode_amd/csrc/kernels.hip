@@ -784,13 +784,17 @@ struct StreamShape {
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kHeads = 16 * HB;
   static constexpr int kBufBytes = 18 * 1024;       // one 16-row bf16 group per wave
-  static constexpr int kQBytes = HB * 72 * 16 * 16;  // Q^T: [block][chunk][head] x 16 B
+  static constexpr bool kCache16 = KVT == 0 || KVT == 5;  // bf16 or fp16 cache
+  // Q^T: in registers with the 580-byte 8-bit record (its group registers are
+  // half the size); in LDS, [block][chunk][head] x 16 B, otherwise (with the
+  // 644-byte record, registers for Q^T cost spills at every segment start)
+  static constexpr bool kQRegs = KVT == 1 || KVT == 2;
+  static constexpr int kQBytes = kQRegs ? 0 : HB * 72 * 16 * 16;
   static constexpr int kQOffset = kWaves * kBufBytes;
   static constexpr int kMergeBytes = merge_bytes<16, 1, kWaves>();  // one head block at a time
   static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
                                                                     : kMergeBytes;
   // 16-byte loads per lane per group: bf16 18; 8-bit ckv 8 + kpe 1 (8-bit) or 2 (bf16)
-  static constexpr bool kCache16 = KVT == 0 || KVT == 5;  // bf16 or fp16 cache
   static constexpr int kLoads = kCache16 ? 18 : (KVT == 3 || KVT == 4 ? 10 : 9);
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
@@ -887,19 +891,38 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     const int ngroups = t1 > t0 ? (t1 - t0 + 15) >> 4 : 0;
     const int nmine = ngroups > wave ? (ngroups - 1 - wave) / TS + 1 : 0;
 
-    // Q^T for the row block into LDS: item (block, chunk c, head h) at
-    // ((block * 72 + c) * 16 + h) * 16.  Its loads go out first, then the
-    // loads of this wave's first NB groups (into registers), and only then is
-    // Q written to LDS: the group loads are in flight during Q's round trip.
-    constexpr int kQItems = (HB * 72 * 16 + S::kThreads - 1) / S::kThreads;
+    // Q^T of the row block.  16-bit cache: into LDS, item (block, chunk c,
+    // head h) at ((block * 72 + c) * 16 + h) * 16.  Its loads go out first,
+    // then the loads of this wave's first NB groups (into registers), and only
+    // then is Q written to LDS: the group loads are in flight during Q's round
+    // trip.  580-byte 8-bit record: in registers, as the QK B operand of
+    // k-step s (head 16 hb + (lane & 15), dims 32 s + 8 (lane >> 4) .. + 7),
+    // loaded before the groups; this saves each 16-token group 18 KiB of LDS
+    // reads.
+    constexpr int kQItems = S::kQRegs ? 1 : (HB * 72 * 16 + S::kThreads - 1) / S::kThreads;
     u32x4 qv[kQItems];
+    bf16x8 qreg[S::kQRegs ? HB : 1][S::kQRegs ? 18 : 1];
+    if constexpr (S::kQRegs) {
 #pragma unroll
-    for (int k = 0; k < kQItems; ++k) {
-      const int x = min(tid + k * S::kThreads, HB * 72 * 16 - 1);
-      const int hb = x / (72 * 16);
-      const int c = (x >> 4) % 72, h = hb * 16 + (x & 15);
-      qv[k] = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
-                     : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
+      for (int hb = 0; hb < HB; ++hb) {
+        const int h = hb * 16 + (lane & 15);
+#pragma unroll
+        for (int s = 0; s < 18; ++s) {
+          const int c = 4 * s + (lane >> 4);
+          qreg[hb][s] =
+              c < 64 ? *reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
+                     : *reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kQItems; ++k) {
+        const int x = min(tid + k * S::kThreads, HB * 72 * 16 - 1);
+        const int hb = x / (72 * 16);
+        const int c = (x >> 4) % 72, h = hb * 16 + (x & 15);
+        qv[k] = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
+                       : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
+      }
     }
 
     // Fetch this wave's j-th group into registers: NL 16-byte loads per lane
@@ -965,7 +988,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
 
     uint8_t* qlds = smem + S::kQOffset;
     lds_barrier();  // previous segment's merge / combine done with this LDS
-    {
+    if constexpr (!S::kQRegs) {
       // (computed here, not hoisted out of the segment loop: kept live across
       // the loop, these addresses would be spilled, and a spill reload waits
       // for every load in flight, the group fetches above included)
@@ -976,8 +999,8 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       for (int k = 0; k < kQItems; ++k)
         if ((k + 1) * S::kThreads <= HB * 72 * 16 || t + k * S::kThreads < HB * 72 * 16)
           *reinterpret_cast<u32x4*>(qw + k * S::kThreads * 16) = qv[k];
+      lds_barrier();
     }
-    lds_barrier();
     const uint8_t* qbase = qlds + ((lane >> 4) * 16 + qr) * 16;  // + (hb * 72 + s * 4) * 256
 
     float m_ref[HB], l_run[HB];
@@ -1024,7 +1047,8 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
         for (int i = 0; i < 4; ++i) sig[i] = (row0 + i < t1) ? sig[i] : 0.f;
       }
 
-      // QK: S^T[16 tokens][16 heads] per head block; K and Q^T from LDS
+      // QK: S^T[16 tokens][16 heads] per head block; K from LDS, Q^T from LDS
+      // or registers (kQRegs)
       const uint8_t* gbase = wbuf + qk_base;
       f32x4 sacc[HB];
 #pragma unroll
@@ -1042,9 +1066,13 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
         for (int hb = 0; hb < HB; ++hb) {
           bf16x8 qf[6];
 #pragma unroll
-          for (int u = 0; u < 6; ++u)
-            qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
-                (const LDS_AS uint8_t*)(qbase + (hb * 72 + (s0 + u) * 4) * 256));
+          for (int u = 0; u < 6; ++u) {
+            if constexpr (S::kQRegs)
+              qf[u] = qreg[hb][s0 + u];
+            else
+              qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
+                  (const LDS_AS uint8_t*)(qbase + (hb * 72 + (s0 + u) * 4) * 256));
+          }
 #pragma unroll
           for (int u = 0; u < 6; ++u) {
             // 644-byte record: the scale is ckv's, applied before the kpe steps
