@@ -789,8 +789,11 @@ struct StreamShape {
   // half the size); in LDS, [block][chunk][head] x 16 B, otherwise (with the
   // 644-byte record, registers for Q^T cost spills at every segment start)
   static constexpr bool kQRegs = KVT == 1 || KVT == 2;
+  // with Q^T out of LDS, each wave has two group buffers and computes two
+  // groups at once (see the kernel)
+  static constexpr bool kPipe = kQRegs;
   static constexpr int kQBytes = kQRegs ? 0 : HB * 72 * 16 * 16;
-  static constexpr int kQOffset = kWaves * kBufBytes;
+  static constexpr int kQOffset = kWaves * kBufBytes * (kPipe ? 2 : 1);
   static constexpr int kMergeBytes = merge_bytes<16, 1, kWaves>();  // one head block at a time
   static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
                                                                     : kMergeBytes;
@@ -840,7 +843,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
   const int lane = tid & 63;
   const int page_shift = a.page_shift;
   const int page_mask = (1 << page_shift) - 1;
-  uint8_t* wbuf = smem + wave * S::kBufBytes;
+  uint8_t* wbuf = smem + wave * S::kBufBytes * (S::kPipe ? 2 : 1);
 
   const int ld_r_lo = lane >> 3;
   // QK operand: token row lane & 15, chunk 4 s + (lane >> 4)
@@ -1013,46 +1016,56 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       for (int i = 0; i < 32; ++i) acc[hb][i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto consume = [&](int j, u32x4 (&st)[NL], f32x4& sc) __attribute__((always_inline)) {
+    // The four stages of group j: write (the group, converted, into a wave
+    // buffer; then the refill of its registers, NB groups ahead, which is
+    // issued also past the last group so that every path keeps the same loads
+    // in flight and the compiler's vmcnt waits cover exactly the group
+    // consumed), QK, online softmax (with the rescale of O^T) and PV.
+    auto stage_write = [&](int j, u32x4 (&st)[NL], f32x4& sc, uint8_t* buf)
+        __attribute__((always_inline)) {
       f32x4 sig = sc;
       if constexpr (kC16) {
 #pragma unroll
         for (int blk = 0; blk < 18; ++blk)
-          *reinterpret_cast<u32x4*>(wbuf + blk * 1024 + lane * 16) = st[blk];
+          *reinterpret_cast<u32x4*>(buf + blk * 1024 + lane * 16) = st[blk];
       } else {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int rh = u >> 2, cb = u & 3;
-          *reinterpret_cast<u32x4*>(wbuf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][0]) =
+          *reinterpret_cast<u32x4*>(buf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][0]) =
               codes_to_bf16<KVT>(st[u][0], st[u][1]);
-          *reinterpret_cast<u32x4*>(wbuf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][1]) =
+          *reinterpret_cast<u32x4*>(buf + rh * kHalfGroupBytes + cb * 2048 + st8[rh][1]) =
               codes_to_bf16<KVT>(st[u][2], st[u][3]);
         }
         if constexpr (KVT == 3 || KVT == 4) {
 #pragma unroll
           for (int rh = 0; rh < 2; ++rh)
-            *reinterpret_cast<u32x4*>(wbuf + (rh * 9 + 8) * 1024 + lane * 16) = st[8 + rh];
+            *reinterpret_cast<u32x4*>(buf + (rh * 9 + 8) * 1024 + lane * 16) = st[8 + rh];
         } else {
-          *reinterpret_cast<u32x4*>(wbuf + st8k[0]) = codes_to_bf16<KVT>(st[8][0], st[8][1]);
-          *reinterpret_cast<u32x4*>(wbuf + st8k[1]) = codes_to_bf16<KVT>(st[8][2], st[8][3]);
+          *reinterpret_cast<u32x4*>(buf + st8k[0]) = codes_to_bf16<KVT>(st[8][0], st[8][1]);
+          *reinterpret_cast<u32x4*>(buf + st8k[1]) = codes_to_bf16<KVT>(st[8][2], st[8][3]);
         }
       }
       fetch(j + NB, st, sc);  // registers free again: NB groups ahead in flight
-      if (j >= nmine) return;
-
       // scales of rows past the end are zeroed (NaN padding may sit there)
-      const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
       if constexpr (!kC16) {
+        const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) sig[i] = (row0 + i < t1) ? sig[i] : 0.f;
       }
+      return sig;
+    };
 
-      // QK: S^T[16 tokens][16 heads] per head block; K from LDS, Q^T from LDS
-      // or registers (kQRegs)
-      const uint8_t* gbase = wbuf + qk_base;
-      f32x4 sacc[HB];
+    // QK: S^T[16 tokens][16 heads] per head block; K from LDS, Q^T from LDS
+    // or registers (kQRegs)
+    struct Scores {
+      f32x4 v[HB];
+    };
+    auto stage_qk = [&](const uint8_t* buf, const f32x4& sig) __attribute__((always_inline)) {
+      const uint8_t* gbase = buf + qk_base;
+      Scores sc;
 #pragma unroll
-      for (int hb = 0; hb < HB; ++hb) sacc[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int hb = 0; hb < HB; ++hb) sc.v[hb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s0 = 0; s0 < 18; s0 += 6) {
         bf16x8 kf[6];
@@ -1077,22 +1090,29 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
           for (int u = 0; u < 6; ++u) {
             // 644-byte record: the scale is ckv's, applied before the kpe steps
             if constexpr (KVT == 3 || KVT == 4)
-              if (s0 + u == 16) sacc[hb] = sacc[hb] * sig;
-            sacc[hb] = mma_16x16x32<kF16>(kf[u], qf[u], sacc[hb]);
+              if (s0 + u == 16) sc.v[hb] = sc.v[hb] * sig;
+            sc.v[hb] = mma_16x16x32<kF16>(kf[u], qf[u], sc.v[hb]);
           }
         }
       }
+      return sc;
+    };
 
-      // online softmax, log2 domain, lazy rescale; rows past the end masked
-      s16x4 pv[HB];
+    // online softmax, log2 domain, lazy rescale; rows past the end masked
+    struct Probs {
+      s16x4 v[HB];
+    };
+    auto stage_sm = [&](int j, Scores sacc, const f32x4& sig) __attribute__((always_inline)) {
+      const int row0 = t0 + 16 * (wave + TS * j) + 4 * (lane >> 4);
+      Probs pv;
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
         float tmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float raw = (KVT == 1 || KVT == 2) ? sacc[hb][i] * sig[i] : sacc[hb][i];
+          const float raw = (KVT == 1 || KVT == 2) ? sacc.v[hb][i] * sig[i] : sacc.v[hb][i];
           const float x = (row0 + i < tlim[hb]) ? raw * a.scale_log2 : -INFINITY;
-          sacc[hb][i] = x;
+          sacc.v[hb][i] = x;
           tmax = fmaxf(tmax, x);
         }
         tmax = wave_max_16(tmax);
@@ -1109,15 +1129,18 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
         bf16x4 pb;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = __builtin_amdgcn_exp2f(sacc[hb][i] - m_use);
+          const float p = __builtin_amdgcn_exp2f(sacc.v[hb][i] - m_use);
           psum += p;
           pb[i] = to16<kF16>(kC16 ? p : p * sig[i]);  // 8-bit: V = scale x codes
         }
         l_run[hb] += psum;
-        pv[hb] = __builtin_bit_cast(s16x4, pb);
+        pv.v[hb] = __builtin_bit_cast(s16x4, pb);
       }
+      return pv;
+    };
 
-      // PV: O^T[c][h] += V^T[c][t] P^T[t][h]
+    // PV: O^T[c][h] += V^T[c][t] P^T[t][h]
+    auto stage_pv = [&](const uint8_t* buf, const Probs& pv) __attribute__((always_inline)) {
 #pragma unroll
       for (int c8 = 0; c8 < 32; c8 += 8) {
         s16x4 vf[8];
@@ -1125,20 +1148,51 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
         for (int u = 0; u < 8; ++u) {
           const int cb = c8 + u;
           vf[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (LDS_AS s16x4*)((LDS_AS uint8_t*)(wbuf + (cb >> 2) * 1024 + tr_off[cb & 3])));
+              (LDS_AS s16x4*)((LDS_AS uint8_t*)(buf + (cb >> 2) * 1024 + tr_off[cb & 3])));
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
 #pragma unroll
           for (int hb = 0; hb < HB; ++hb)
-            acc[hb][c8 + u] =
-                mma_16x16x16<kF16>(vf[u], pv[hb], acc[hb][c8 + u]);
+            acc[hb][c8 + u] = mma_16x16x16<kF16>(vf[u], pv.v[hb], acc[hb][c8 + u]);
       }
     };
 
-    for (int j = 0; j < nmine; j += NB) {
+    if constexpr (S::kPipe) {
+      // Two groups in the compute at once: group j + 1 is written to the
+      // other buffer, then the QK of group j + 1 and the PV of group j are
+      // issued together (independent work: their MFMA chains and LDS
+      // latencies overlap), then the softmax of group j + 1.  The arithmetic
+      // of every group is the one of the plain sequence.
+      static_assert(NB == 2, "pipelined groups alternate two register sets");
+      uint8_t* const buf0 = wbuf;
+      uint8_t* const buf1 = wbuf + S::kBufBytes;
+      Probs pcur;
+      {
+        const f32x4 sig = stage_write(0, st[0], sc[0], buf0);
+        if (nmine > 0) pcur = stage_sm(0, stage_qk(buf0, sig), sig);
+      }
+      // group j is in `cur`; group j + 1 goes to `nxt` from register set u
+      auto step = [&](int j, const uint8_t* cur, uint8_t* nxt, u32x4 (&stn)[NL], f32x4& scn)
+          __attribute__((always_inline)) {
+        const f32x4 sig = stage_write(j + 1, stn, scn, nxt);
+        const Scores sn = stage_qk(nxt, sig);  // past the last group: not used
+        stage_pv(cur, pcur);
+        if (j + 1 < nmine) pcur = stage_sm(j + 1, sn, sig);
+      };
+      for (int j = 0; j < nmine; j += 2) {
+        step(j, buf0, buf1, st[1], sc[1]);
+        if (j + 1 >= nmine) break;
+        step(j + 1, buf1, buf0, st[0], sc[0]);
+      }
+    } else {
+      for (int j = 0; j < nmine; j += NB) {
 #pragma unroll
-      for (int u = 0; u < NB; ++u) consume(j + u, st[u], sc[u]);
+        for (int u = 0; u < NB; ++u) {
+          const f32x4 sig = stage_write(j + u, st[u], sc[u], wbuf);
+          if (j + u < nmine) stage_pv(wbuf, stage_sm(j + u, stage_qk(wbuf, sig), sig));
+        }
+      }
     }
 
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
