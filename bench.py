@@ -16,17 +16,23 @@ separate copies of the inputs (at least `--copies`, and enough that the other
 copies stream 512 MB between two reads of one), so that a step cannot reuse
 what earlier ones left in the 256 MB Infinity Cache.
 
-Each workload also reports `timing`: the mean, median, min and max of the
-per-step decode time (HIP events around the library's kernels) and the step
-time when the same steps replay from hipGraphs (one captured per input copy)
-beside the eager one.
+The K timed steps run back to back between two HIP events and nothing else:
+`ms_per_step` (and `value`) is their total time / K, gaps between steps
+included.  The same K steps then run again with events around each decode
+kernel and each call, which give the breakdown; events between the steps
+add gaps of their own, so that pass is not the step time.  Each workload
+also reports `timing`: the mean, median, min and max of the per-step decode
+time (HIP events around the library's kernels), of the whole call, and the
+step time when the same steps replay from hipGraphs (one captured per input
+copy) beside the eager one.
 
 `roofline.achieved` divides the algorithmic bytes (or flops) of one launch by
 the decode kernel's own average duration, measured with HIP events that the
-library records right before and right after that kernel on its stream over
-the timed steps; `decode_plus_merge` gives the same figures for the whole
-mla_decode_run (decode kernel and, for split requests, the merge launch),
-from events the bench records around each call on the same stream.
+library records right before and right after that kernel on its stream (the
+second pass of the timed steps); `decode_plus_merge` gives the same figures
+for the whole mla_decode_run (decode kernel and, for split requests, the
+merge launch), from events the bench records around each call on the same
+stream.
 """
 from __future__ import annotations
 
@@ -197,18 +203,25 @@ def measure(name: str, steps: int, warmup: int, copies: int, hip: Hip, head_spli
     call_end = [hip.event() for _ in range(steps)]  # end of the whole call
     start, stop = hip.event(), hip.event()
     stream = torch.cuda.current_stream().cuda_stream
+    # the timed steps: nothing but the steps between the two events
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     hip.lib.hipEventRecord(start, ctypes.c_void_p(stream))
     for i in range(steps):
-        plan.set_events(before[i], after[i])
         step(i)
-        hip.lib.hipEventRecord(call_end[i], ctypes.c_void_p(stream))
     hip.lib.hipEventRecord(stop, ctypes.c_void_p(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    plan.set_events(None, None)
     total_ms = hip.elapsed_ms(start, stop)
+    # the same steps again with events around each decode kernel and each call
+    # (the breakdown; the events add gaps of their own, so this pass is not the
+    # step time)
+    for i in range(steps):
+        plan.set_events(before[i], after[i])
+        step(i)
+        hip.lib.hipEventRecord(call_end[i], ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    plan.set_events(None, None)
     kern = sorted(hip.elapsed_ms(before[i], after[i]) for i in range(steps))
     call = sorted(hip.elapsed_ms(before[i], call_end[i]) for i in range(steps))
     graph_ms = None
