@@ -27,9 +27,10 @@ step time when the same steps replay from hipGraphs (one captured per input
 copy) beside the eager one.
 
 `roofline.achieved` divides the algorithmic bytes (or flops) of one launch by
-the decode kernel's own average duration, measured with HIP events that the
-library records right before and right after that kernel on its stream (the
-second pass of the timed steps); `decode_plus_merge` gives the same figures
+the decode kernel's own average duration, from HIP events that the kernel's
+launch takes from its own dispatch (its start and its end, the way
+hipExtLaunchKernel records them; the second pass of the timed steps);
+`decode_plus_merge` gives the same figures
 for the whole mla_decode_run (decode kernel and, for split requests, the
 merge launch), from events the bench records around each call on the same
 stream.

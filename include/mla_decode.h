@@ -221,10 +221,12 @@ mla_status mla_decode_run_noalloc(mla_plan_t plan, const void* q_nope, const voi
 
 /*
  * Optional instrumentation for measuring the decode kernel on its own: when
- * set, mla_decode_run (and mla_decode_run_noalloc) records `before` on its
- * stream right before the decode kernel and `after` right after it, before
- * the merge launch of split requests (hipEvent_t values passed as void*; the
- * caller owns them).  Passing NULL for both turns it off.  Host-only call.
+ * set, mla_decode_run (and mla_decode_run_noalloc) launches the decode kernel
+ * so that `before` takes the start and `after` the end of that kernel's
+ * execution, from its own dispatch (hipExtLaunchKernel), not the merge launch
+ * of split requests that follows; a run with no decode launch records them
+ * on its stream back to back.  hipEvent_t values passed as void*; the caller
+ * owns them.  Passing NULL for both turns it off.  Host-only call.
  */
 mla_status mla_decode_plan_set_events(mla_plan_t plan, void* before, void* after);
 

@@ -198,17 +198,19 @@ mla_status run_on_workspace(mla_plan_s* p, uint8_t* ws, const void* q_nope, cons
   a.head_log2 = log2_exact(p->heads);
   a.one_seg = p->one_seg;
   a.req_div = p->req_div;
-  if (p->ev_before) {
-    hipError_t e = hipEventRecord(p->ev_before, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
-  }
   if (p->plan.num_workers > 0) {
-    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s);
+    // the events (if set) take the decode kernel's own start and end, without
+    // the merge below
+    hipError_t e = mla_gpu::launch_decode(p->kernel_heads, p->kv_dtype, a, p->plan.num_workers, s,
+                                          p->ev_before, p->ev_after);
     if (e != hipSuccess) return hip_fail(e, "decode launch");
-  }
-  if (p->ev_after) {  // the decode kernel alone, without the merge below
-    hipError_t e = hipEventRecord(p->ev_after, s);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  } else {
+    // no decode launch: the events are recorded back to back
+    for (hipEvent_t ev : {p->ev_before, p->ev_after}) {
+      if (!ev) continue;
+      hipError_t e = hipEventRecord(ev, s);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+    }
   }
   const int ncomb = (int)(p->plan.combine.size() / 4);
   if (p->plan.num_workers > 0 && ncomb > 0) {

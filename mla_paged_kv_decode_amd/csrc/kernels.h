@@ -56,8 +56,17 @@ int decode_config(int heads, int kv_dtype, DecodeConfig* cfg);
 // Workgroups of that kernel resident on one CU (HIP occupancy query on the
 // current device; an LDS-based estimate if the query fails).
 int decode_blocks_per_cu(int heads, int kv_dtype);
+// start / stop (either may be null): events the launch takes from its own
+// dispatch, the start and the end of the kernel's execution
+// (hipExtLaunchKernel), so that no marker between kernels adds to what they
+// measure.
 hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
-                         hipStream_t stream);
+                         hipStream_t stream, hipEvent_t start = nullptr,
+                         hipEvent_t stop = nullptr);
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
 // Merge of the ncomb split requests listed in a.clist, each cut into at most
 // max_splits chunks, after the decode kernel (which leaves their partials):
 // writes o and lse of those rows.

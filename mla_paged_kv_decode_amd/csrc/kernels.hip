@@ -35,6 +35,7 @@
 // (mla_combine_kernel / mla_combine_many_kernel) merges the chunks of every
 // split request in chunk order, weighting each by exp(LSE_i - LSE), so results
 // are deterministic and no state survives from one launch to the next.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -2860,32 +2861,30 @@ __global__ void __launch_bounds__(256) mla_combine_many_kernel(const DecodeArgs 
 
 // ---------------------------------------------------------------- launchers
 template <int HG, int HB, int TS, int MB, int NSTAGE>
-static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
+static hipError_t launch_decode_cfg(const DecodeArgs& a, int grid, hipStream_t stream,
+                                    const LaunchEvents& ev) {
   using S = RingShape<HG, HB, TS, MB, NSTAGE>;
-  hipLaunchKernelGGL((mla_decode_ring_kernel<HG, HB, TS, MB, NSTAGE>), dim3(grid),
-                     dim3(S::kThreads), 0, stream, a);
+  hipExtLaunchKernelGGL((mla_decode_ring_kernel<HG, HB, TS, MB, NSTAGE>), dim3(grid), dim3(S::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
 template <int KVT>
-static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream) {
+static hipError_t launch_wide(const DecodeArgs& a, int grid, hipStream_t stream,
+                              const LaunchEvents& ev) {
   if (a.qo_len > 1)
-    hipLaunchKernelGGL((mla_decode_wide_kernel<KVT, true>), dim3(grid),
-                       dim3(WideShape<KVT>::kThreads), 0, stream, a);
+    hipExtLaunchKernelGGL((mla_decode_wide_kernel<KVT, true>), dim3(grid), dim3(WideShape<KVT>::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((mla_decode_wide_kernel<KVT, false>), dim3(grid),
-                       dim3(WideShape<KVT>::kThreads), 0, stream, a);
+    hipExtLaunchKernelGGL((mla_decode_wide_kernel<KVT, false>), dim3(grid), dim3(WideShape<KVT>::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
 template <int KVT>
-static hipError_t launch_pair(const DecodeArgs& a, int grid, hipStream_t stream) {
+static hipError_t launch_pair(const DecodeArgs& a, int grid, hipStream_t stream,
+                              const LaunchEvents& ev) {
   if (a.qo_len > 1)
-    hipLaunchKernelGGL((mla_decode_pair_kernel<KVT, true>), dim3(grid), dim3(PairShape::kThreads),
-                       0, stream, a);
+    hipExtLaunchKernelGGL((mla_decode_pair_kernel<KVT, true>), dim3(grid), dim3(PairShape::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   else
-    hipLaunchKernelGGL((mla_decode_pair_kernel<KVT, false>), dim3(grid), dim3(PairShape::kThreads),
-                       0, stream, a);
+    hipExtLaunchKernelGGL((mla_decode_pair_kernel<KVT, false>), dim3(grid), dim3(PairShape::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
@@ -2927,10 +2926,10 @@ static DecodeConfig config_of() {
 }
 
 template <int HB, int KVT, int NB>
-static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t stream) {
+static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t stream,
+                                    const LaunchEvents& ev) {
   using S = StreamShape<HB, KVT, NB>;
-  hipLaunchKernelGGL((mla_decode_stream_kernel<HB, KVT, NB>), dim3(grid), dim3(S::kThreads), 0,
-                     stream, a);
+  hipExtLaunchKernelGGL((mla_decode_stream_kernel<HB, KVT, NB>), dim3(grid), dim3(S::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
@@ -2967,33 +2966,33 @@ static int occupancy_of() {
 // One switch describes the kernel chosen for (heads per workgroup, cache
 // dtype); `op` is 0 = config, 1 = occupancy, 2 = launch.
 static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const DecodeArgs* a,
-                    int grid, hipStream_t stream, hipError_t* err) {
+                    int grid, hipStream_t stream, hipError_t* err, const LaunchEvents& ev = {}) {
 #define MLA_STREAM(...)                                                     \
   do {                                                                      \
     if (op == 0) *cfg = stream_config_of<__VA_ARGS__>();                    \
     if (op == 1) return stream_occupancy_of<__VA_ARGS__>();                 \
-    if (op == 2) *err = launch_stream_cfg<__VA_ARGS__>(*a, grid, stream);   \
+    if (op == 2) *err = launch_stream_cfg<__VA_ARGS__>(*a, grid, stream, ev);   \
     return 1;                                                               \
   } while (0)
 #define MLA_WIDE(K)                                                         \
   do {                                                                      \
     if (op == 0) *cfg = wide_config<K>();                                   \
     if (op == 1) return wide_occupancy<K>();                                \
-    if (op == 2) *err = launch_wide<K>(*a, grid, stream);                   \
+    if (op == 2) *err = launch_wide<K>(*a, grid, stream, ev);                   \
     return 1;                                                               \
   } while (0)
 #define MLA_PAIR(K)                                                         \
   do {                                                                      \
     if (op == 0) *cfg = pair_config();                                      \
     if (op == 1) return pair_occupancy<K>();                                \
-    if (op == 2) *err = launch_pair<K>(*a, grid, stream);                   \
+    if (op == 2) *err = launch_pair<K>(*a, grid, stream, ev);                   \
     return 1;                                                               \
   } while (0)
 #define MLA_RING(...)                                                       \
   do {                                                                      \
     if (op == 0) *cfg = config_of<__VA_ARGS__>();                           \
     if (op == 1) return occupancy_of<__VA_ARGS__>();                        \
-    if (op == 2) *err = launch_decode_cfg<__VA_ARGS__>(*a, grid, stream);   \
+    if (op == 2) *err = launch_decode_cfg<__VA_ARGS__>(*a, grid, stream, ev);   \
     return 1;                                                               \
   } while (0)
   // ring-kernel shapes: <16-head blocks, blocks per wave, token-split waves,
@@ -3106,9 +3105,10 @@ int decode_blocks_per_cu(int heads, int kv_dtype) {
 }
 
 hipError_t launch_decode(int heads, int kv_dtype, const DecodeArgs& a, int grid,
-                         hipStream_t stream) {
+                         hipStream_t stream, hipEvent_t start, hipEvent_t stop) {
   hipError_t err = hipErrorInvalidValue;
-  if (!dispatch(heads, kv_dtype, 2, nullptr, &a, grid, stream, &err)) return hipErrorInvalidValue;
+  if (!dispatch(heads, kv_dtype, 2, nullptr, &a, grid, stream, &err, LaunchEvents{start, stop}))
+    return hipErrorInvalidValue;
   return err;
 }
 
