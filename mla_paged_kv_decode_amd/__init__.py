@@ -211,8 +211,9 @@ class Plan:
         return seg[:inf["num_segments"]], wp
 
     def set_events(self, before, after) -> None:
-        """Record raw hipEvent_t handles (ints) around the decode kernel alone in
-        run() (the merge launch of split requests comes after ``after``)."""
+        """Raw hipEvent_t handles (ints) that run() fills with the start and the
+        end of the decode kernel alone, from its own dispatch (the merge launch of
+        split requests is not included)."""
         st = self._lib.mla_decode_plan_set_events(self._h, before, after)
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_plan_set_events")

@@ -244,6 +244,56 @@ def test_graph_replay_matches_eager(heads, kvd):
     check(*host(o, lse), *ref(inp))
 
 
+@pytest.mark.parametrize("heads", [16, 64, 128])
+def test_timing_events_keep_results(heads):
+    # mla_decode_plan_set_events: the decode kernel's launch fills the two
+    # events from its own dispatch.  A run with them is bit-identical to a run
+    # without, the events bracket a positive time, and turning them off again
+    # changes nothing either.
+    import ctypes
+    import mla_paged_kv_decode_amd as mla
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    inp = synth.make_inputs([1000, 4000, 64, 0], heads, 64, seed=17 + heads)
+    print("case heads=%d" % heads, flush=True)
+    t = dev(inp)
+    B, H = 4, heads
+    ws = torch.empty(mla.workspace_bytes(B, H), dtype=torch.uint8, device="cuda")
+    plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, H, 64, inp.kv_dtype, workspace=ws)
+    args = (t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_scale"], t["kv_indptr"],
+            t["kv_indices"], t["kv_last_page_len"], inp.sm_scale)
+
+    def run():
+        o = torch.empty((B, H, 512), dtype=torch.bfloat16, device="cuda")
+        lse = torch.empty((B, H), dtype=torch.float32, device="cuda")
+        plan.run(*args, o, lse)
+        torch.cuda.synchronize()
+        return o, lse
+
+    o0, l0 = run()
+    ev = [ctypes.c_void_p(), ctypes.c_void_p()]
+    for e in ev:
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+    try:
+        plan.set_events(ev[0].value, ev[1].value)
+        o1, l1 = run()
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0
+        assert 0.0 < ms.value < 1000.0, ms.value
+        plan.set_events(0, 0)
+        o2, l2 = run()
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(e)
+    for o, lse in ((o1, l1), (o2, l2)):
+        assert torch.equal(o.view(torch.int16), o0.view(torch.int16))
+        assert torch.equal(lse.view(torch.int32), l0.view(torch.int32))
+    check(*host(o0, l0), *ref(inp))
+
+
 FULL_WORKLOADS = ["mem_b64_h16_l4096_p64", "compute_b64_h128_l4096_p64",
                   "varlen_b768_h64_l1to2048_p16", "fp8_b64_h16_l8192_p64",
                   "fp8_b64_h128_l8192_p64", "int8_b64_h16_l8192_p64", "int8_b64_h128_l8192_p64",
