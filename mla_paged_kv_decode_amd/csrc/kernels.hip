@@ -1318,6 +1318,31 @@ __device__ __forceinline__ void agpr_settle() {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
 }
 
+// A 16-register accumulator block read out of its AGPRs (after agpr_settle),
+// as assembly, so that the epilogue takes one block at a time and the
+// compiler does not move the 256 accumulators around to make room.
+__device__ __forceinline__ f32x16 agpr_read16(const f32x16& acc) {
+  f32x16 v;
+  asm volatile(
+#define MLA_READ_ONE(i) "v_accvgpr_read_b32 %" #i ", %" #i "\n\t"
+      "v_accvgpr_read_b32 %0, %16\n\tv_accvgpr_read_b32 %1, %17\n\t"
+      "v_accvgpr_read_b32 %2, %18\n\tv_accvgpr_read_b32 %3, %19\n\t"
+      "v_accvgpr_read_b32 %4, %20\n\tv_accvgpr_read_b32 %5, %21\n\t"
+      "v_accvgpr_read_b32 %6, %22\n\tv_accvgpr_read_b32 %7, %23\n\t"
+      "v_accvgpr_read_b32 %8, %24\n\tv_accvgpr_read_b32 %9, %25\n\t"
+      "v_accvgpr_read_b32 %10, %26\n\tv_accvgpr_read_b32 %11, %27\n\t"
+      "v_accvgpr_read_b32 %12, %28\n\tv_accvgpr_read_b32 %13, %29\n\t"
+      "v_accvgpr_read_b32 %14, %30\n\tv_accvgpr_read_b32 %15, %31"
+#undef MLA_READ_ONE
+      : "=v"(v[0]), "=v"(v[1]), "=v"(v[2]), "=v"(v[3]), "=v"(v[4]), "=v"(v[5]), "=v"(v[6]),
+        "=v"(v[7]), "=v"(v[8]), "=v"(v[9]), "=v"(v[10]), "=v"(v[11]), "=v"(v[12]), "=v"(v[13]),
+        "=v"(v[14]), "=v"(v[15])
+      : "a"(acc[0]), "a"(acc[1]), "a"(acc[2]), "a"(acc[3]), "a"(acc[4]), "a"(acc[5]),
+        "a"(acc[6]), "a"(acc[7]), "a"(acc[8]), "a"(acc[9]), "a"(acc[10]), "a"(acc[11]),
+        "a"(acc[12]), "a"(acc[13]), "a"(acc[14]), "a"(acc[15]));
+  return v;
+}
+
 // LDS of the wide kernel.  bf16 cache: a ring of kStages bf16 tiles (36 KiB,
 // the swizzled 16-row group layout) filled by direct-to-LDS loads.  8-bit
 // cache: a ring of kStages code tiles (ckv codes [32][512], kpe codes
@@ -2115,14 +2140,16 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       for (int hb = 0; hb < 4; ++hb) {
         uint16_t* op = a.o + ((size_t)b * H + 32 * hb + l32) * 512 + 128 * wave + 4 * g;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb) {
+          const f32x16 x = agpr_read16(acc[cb][hb]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             bf16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = to16<kF16>(acc[cb][hb][4 * q + i] * inv[hb]);
+            for (int i = 0; i < 4; ++i) v[i] = to16<kF16>(x[4 * q + i] * inv[hb]);
             *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * q) = v;
           }
+        }
       }
       if (lane < 32) a.lse[(size_t)b * H + 32 * wave + lane] = lse_v;
     } else {
@@ -2134,11 +2161,14 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       uint16_t* po = reinterpret_cast<uint16_t*>(a.part_o) + (size_t)slot * H * 512;
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
+        f32x16 x[4];
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) x[cb] = agpr_read16(acc[cb][hb]);
         float mx = 0.f;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(acc[cb][hb][i]));
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(x[cb][i]));
         float lo = mx, hi = mx;
         asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
         mx = fmaxf(lo, hi) * inv[hb];
@@ -2152,7 +2182,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           for (int q = 0; q < 4; ++q) {
             f16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (_Float16)(acc[cb][hb][4 * q + i] * mult);
+            for (int i = 0; i < 4; ++i) v[i] = (_Float16)(x[cb][4 * q + i] * mult);
             *reinterpret_cast<f16x4*>(prow + 32 * cb + 8 * q) = v;
           }
         if (g == 0)
