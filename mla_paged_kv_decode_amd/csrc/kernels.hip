@@ -2649,15 +2649,17 @@ __global__ void __launch_bounds__(256) mla_decode_pair_kernel(const DecodeArgs a
       for (int hb = 0; hb < 2; ++hb) {
         uint16_t* op = a.o + ((size_t)b * H + 32 * hb + l32) * 512 + 128 * wave + 4 * g;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb) {
+          const f32x16 x0 = agpr_read16(acc[cb][hb]), x1 = agpr_read16(acc[cb][hb + 2]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             bf16x4 v;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-              v[i] = to16<kF16>(acc[cb][hb][4 * q + i] * c0[hb] + acc[cb][hb + 2][4 * q + i] * c1[hb]);
+              v[i] = to16<kF16>(x0[4 * q + i] * c0[hb] + x1[4 * q + i] * c1[hb]);
             *reinterpret_cast<bf16x4*>(op + 32 * cb + 8 * q) = v;
           }
+        }
       }
       if (wave < 2 && lane < 32) a.lse[(size_t)b * H + 32 * wave + l32] = lse_v;
     } else {
@@ -2668,28 +2670,31 @@ __global__ void __launch_bounds__(256) mla_decode_pair_kernel(const DecodeArgs a
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
         // the merged values are formed twice (for the block max, then stored)
-        // rather than held in 64 more registers
+        // rather than held in 64 more registers; the accumulators are read out
+        // of their AGPRs a block at a time (agpr_read16)
         float mx = 0.f;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb) {
+          const f32x16 x0 = agpr_read16(acc[cb][hb]), x1 = agpr_read16(acc[cb][hb + 2]);
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            mx = fmaxf(mx, fabsf(acc[cb][hb][i] * c0[hb] + acc[cb][hb + 2][i] * c1[hb]));
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fabsf(x0[i] * c0[hb] + x1[i] * c1[hb]));
+        }
         float lo = mx, hi = mx;
         asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(lo), "+v"(hi));
         const int ex = scale_exp(fmaxf(lo, hi));
         const float d0 = __builtin_amdgcn_ldexpf(c0[hb], -ex), d1 = __builtin_amdgcn_ldexpf(c1[hb], -ex);
         uint16_t* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb) {
+          const f32x16 x0 = agpr_read16(acc[cb][hb]), x1 = agpr_read16(acc[cb][hb + 2]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             f16x4 v;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              v[i] = (_Float16)(acc[cb][hb][4 * q + i] * d0 + acc[cb][hb + 2][4 * q + i] * d1);
+            for (int i = 0; i < 4; ++i) v[i] = (_Float16)(x0[4 * q + i] * d0 + x1[4 * q + i] * d1);
             *reinterpret_cast<f16x4*>(prow + 32 * cb + 8 * q) = v;
           }
+        }
         if (g == 0)
           a.part_scale[((size_t)slot * H + 32 * hb + l32) * 4 + wave] = __builtin_amdgcn_ldexpf(1.f, ex);
       }
