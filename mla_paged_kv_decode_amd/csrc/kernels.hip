@@ -1433,6 +1433,12 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
   const int seg_end = a.one_seg ? seg_begin + 1 : ld_const(a.worker_ptr + blockIdx.x + 1);
 
   for (int si = seg_begin; si < seg_end; ++si) {
+    // (580-byte 8-bit record: the per-lane offsets of the code loads and of the
+    // conversion are formed from these copies, which the compiler cannot take
+    // out of the segment loop: formed once at entry and kept across the
+    // segments, they were spilled and reloaded at every segment)
+    int lane_s = lane, tid_s = tid;
+    if constexpr (KVT == 1 || KVT == 2) asm volatile("" : "+v"(lane_s), "+v"(tid_s));
     const SegMeta sm = load_seg(a, si);
     const int b = sm.b, t0 = sm.t0, send = sm.send, slot = sm.slot;
     const int kvb = sm.kvb, pbeg = sm.pbeg;
@@ -1556,19 +1562,19 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           int t, off;
           uint32_t dst;
           if (d < 16) {
-            t = 2 * d + (lane >> 5);
-            off = (lane & 31) * 16;
+            t = 2 * d + (lane_s >> 5);
+            off = (lane_s & 31) * 16;
             dst = dst0 + d * 1024;
           } else if (S::kKpe16 && d < 20) {
-            t = 8 * (d - 16) + (lane >> 3);
-            off = (lane & 7) * 16;
+            t = 8 * (d - 16) + (lane_s >> 3);
+            off = (lane_s & 7) * 16;
             dst = dst0 + S::kCodeKpe + (d - 16) * 1024;
           } else if (!S::kKpe16 && d < 18) {
-            t = 16 * (d - 16) + (lane >> 2);
-            off = (lane & 3) * 16;
+            t = 16 * (d - 16) + (lane_s >> 2);
+            off = (lane_s & 3) * 16;
             dst = dst0 + S::kCodeKpe + (d - 16) * 1024;
           } else {
-            t = 4 * min(lane, 7);  // lanes 8.. load again what lane 7 loads
+            t = 4 * min(lane_s, 7);  // lanes 8.. load again what lane 7 loads
             off = 0;
             dst = dst0 + S::kCodeScale;
           }
@@ -1595,7 +1601,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       const uint8_t* cod = smem + cs * S::kCodeBytes;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {  // ckv: 1024 pieces of 16 codes
-        const int p = i * 256 + tid;
+        const int p = i * 256 + tid_s;
         const int t = p >> 5, u = p & 31, r = t & 15;
         const u32x4 c = *reinterpret_cast<const u32x4*>(cod + t * 512 + u * 16);
         uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + (u >> 2) * 1024 +
@@ -1606,13 +1612,13 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             codes_to_bf16<KVT>(c[2], c[3]);
       }
       if constexpr (S::kKpe16) {  // bf16 kpe: 256 pieces of 8 values, copied
-        const int t = tid >> 3, u = tid & 7, r = t & 15;
+        const int t = tid_s >> 3, u = tid_s & 7, r = t & 15;
         const u32x4 c = *reinterpret_cast<const u32x4*>(cod + S::kCodeKpe + t * 128 + u * 16);
         uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + 8 * 1024 +
                        (r & 7) * 128;
         *reinterpret_cast<u32x4*>(row + ((u ^ swz(r)) * 16)) = c;
       } else if (wave < 2) {  // kpe: 128 pieces
-        const int t = tid >> 2, u = tid & 3, r = t & 15;
+        const int t = tid_s >> 2, u = tid_s & 3, r = t & 15;
         const u32x4 c = *reinterpret_cast<const u32x4*>(cod + S::kCodeKpe + t * 64 + u * 16);
         uint8_t* row = dst + (t >> 4) * kGroupBytes + (r >> 3) * kHalfGroupBytes + 8 * 1024 +
                        (r & 7) * 128;
