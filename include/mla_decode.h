@@ -95,9 +95,10 @@ typedef struct {
                            16, 64 or 128 (fp16), 16 or 128 (8-bit caches). */
   int32_t qo_len;       /* queries per request, 1..64; 0 means 1 */
   int32_t l2_domains;   /* L2 domains (XCDs) that workgroups are dealt to round-robin in
-                           launch order; the rows of one request are placed in one of them
-                           so that they share its latent cache through one L2.  0 = 8 (a
-                           whole MI355X); 1 = no placement (e.g. a one-XCD partition). */
+                           launch order; the rows of one request, with all their token
+                           chunks, are placed in one of them so that they share its latent
+                           cache and query rows through one L2.  0 = 8 (a whole MI355X);
+                           1 = no placement (e.g. a one-XCD partition). */
 } mla_plan_opts;
 
 typedef struct mla_plan_s* mla_plan_t;
@@ -249,7 +250,10 @@ const char* mla_last_error(void);
  *   index (the kernels then skip the worker_ptr load), [14] c > 0 when, in
  *   addition, segment i reads the latent cache of request i / c (the kernels
  *   then load the segment record and the request's page-table entries in one
- *   round trip), else 0.  With a head split n > 1, segment requests count groups: row r
+ *   round trip), else 0, [15] X > 0 when [14] applies to the rank of the
+ *   segment before the workgroups were dealt to X L2 domains, rank(i) =
+ *   (i % X) * (info[4] / X) + i / X, rather than to i itself.  With a head
+ *   split n > 1, segment requests count groups: row r
  *   covers query vectors (r % n) * W .. (r % n) * W + W - 1 (W = info[11]) of
  *   request r / n, where query vector j is head j % num_heads of query
  *   j / num_heads.
@@ -259,7 +263,7 @@ const char* mla_last_error(void);
  * each request to the request's run-time length), and worker_ptr[w], worker_ptr[w+1] delimit the
  * segments of workgroup w (worker_ptr has num_workers + 1 entries).
  */
-mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[15]);
+mla_status mla_decode_plan_info(mla_plan_t plan, int32_t info[16]);
 mla_status mla_decode_plan_segments(mla_plan_t plan, int32_t* seg, int32_t* worker_ptr);
 
 /*

@@ -191,13 +191,13 @@ class Plan:
             self._h = None
 
     def info(self) -> dict:
-        buf = np.zeros(15, np.int32)
+        buf = np.zeros(16, np.int32)
         st = self._lib.mla_decode_plan_info(self._h, buf.ctypes.data_as(ctypes.c_void_p))
         if st != MLA_OK:
             raise MlaError(st, "mla_decode_plan_info")
         keys = ("batch", "num_heads", "page_size", "kv_dtype", "num_workers", "num_segments",
                 "num_partials", "num_split_requests", "granularity", "waves", "head_split",
-                "kernel_heads", "qo_len", "one_seg", "req_div")
+                "kernel_heads", "qo_len", "one_seg", "req_div", "req_deal")
         return {k: int(v) for k, v in zip(keys, buf)}
 
     def segments(self):

@@ -198,6 +198,7 @@ mla_status run_on_workspace(mla_plan_s* p, uint8_t* ws, const void* q_nope, cons
   a.head_log2 = log2_exact(p->heads);
   a.one_seg = p->one_seg;
   a.req_div = p->req_div;
+  a.req_deal = p->req_deal;
   if (p->plan.num_workers > 0) {
     // the events (if set) take the decode kernel's own start and end, without
     // the merge below
@@ -320,13 +321,29 @@ mla_status mla_decode_plan(mla_plan_t* out, const int32_t* kv_indptr_host,
   for (size_t w = 0; p->one_seg && w < pl.worker_ptr.size(); ++w)
     if (pl.worker_ptr[w] != (int32_t)w) p->one_seg = 0;
   if (p->one_seg && !pl.segments.empty()) {
-    const int32_t first = pl.segments[0].request / head_split;
-    int32_t c = 0;
-    while (c < (int32_t)pl.segments.size() && pl.segments[c].request / head_split == first) ++c;
-    bool ok = true;
-    for (size_t i = 0; ok && i < pl.segments.size(); ++i)
-      ok = pl.segments[i].request / head_split == (int32_t)i / c;
-    p->req_div = ok ? c : 0;
+    // Segment i reads request rank(i) / c, with rank(i) = i (launch order) or,
+    // when the planner dealt the workers to X L2 domains (domain d taking
+    // ranks d * per .. d * per + per - 1 at launch positions d, d + X, ...,
+    // per = n / X), rank(i) = (i % X) * per + i / X.
+    const int64_t n = (int64_t)pl.segments.size();
+    for (int32_t deal : {0, pp.xcd_count}) {
+      if (deal == 1 || (deal > 1 && n % deal != 0)) continue;
+      const int64_t per = deal > 1 ? n / deal : n;
+      auto req_of_rank = [&](int64_t r) {
+        const int64_t pos = deal > 1 ? r / per + deal * (r % per) : r;
+        return pl.segments[(size_t)pos].request / head_split;
+      };
+      const int32_t first = req_of_rank(0);
+      int32_t c = 0;
+      while (c < n && req_of_rank(c) == first) ++c;
+      bool ok = true;
+      for (int64_t r = 0; ok && r < n; ++r) ok = req_of_rank(r) == (int32_t)(r / c);
+      if (ok) {
+        p->req_div = c;
+        p->req_deal = deal;
+        break;
+      }
+    }
   }
   const int64_t ncomb = (int64_t)pl.combine.size() / 4;
   p->layout = layout_for((int64_t)pl.segments.size(), pl.num_workers, ncomb, pl.num_partials,
@@ -386,7 +403,7 @@ mla_status mla_decode_plan_set_events(mla_plan_t p, void* before, void* after) {
   return MLA_OK;
 }
 
-mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[15]) {
+mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[16]) {
   if (!p || !info) return MLA_ERR_INVALID_ARG;
   info[0] = p->batch;
   info[1] = p->heads;
@@ -403,6 +420,7 @@ mla_status mla_decode_plan_info(mla_plan_t p, int32_t info[15]) {
   info[12] = p->qo_len;
   info[13] = p->one_seg;
   info[14] = p->req_div;
+  info[15] = p->req_deal;
   return MLA_OK;
 }
 

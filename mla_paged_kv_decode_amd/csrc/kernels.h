@@ -41,6 +41,9 @@ struct DecodeArgs {
   int32_t req_div;            // > 0 (only with one_seg): segment i reads the latent cache of
                               // request i / req_div, so its page-table loads need not wait
                               // for the segment record
+  int32_t req_deal;           // > 0 (only with req_div): the workers were dealt to req_deal
+                              // L2 domains, and segment i reads request rank(i) / req_div,
+                              // rank(i) = (i % X) * (grid / X) + i / X (X = req_deal)
 };
 
 struct DecodeConfig {

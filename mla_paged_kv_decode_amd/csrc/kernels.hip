@@ -420,9 +420,11 @@ struct RingShape {
 
 // Metadata of segment si: its record (request row, token range, partial slot)
 // and the device page-table entries of the request whose latent cache it reads.
-// When the plan fixes that request as si / req_div, the page-table loads do not
-// wait for the record, so all of them arrive in one memory round trip; the
-// last-page length is loaded unconditionally (in bounds for every request).
+// When the plan fixes that request as r / req_div, where r is si or, with the
+// workgroups dealt to req_deal L2 domains, the rank si had before the dealing,
+// the page-table loads do not wait for the record, so all of them arrive in
+// one memory round trip; the last-page length is loaded unconditionally (in
+// bounds for every request).
 struct SegMeta {
   int b, t0, send, slot, kvb, pbeg, npg, last_len;
 };
@@ -433,7 +435,12 @@ __device__ __forceinline__ SegMeta load_seg(const DecodeArgs& a, int si) {
     // One asm statement issues the three scalar loads and waits for them, so
     // the compiler can neither sink the record load below the others nor read
     // a destination before the wait.
-    m.kvb = si / a.req_div;
+    int rank = si;
+    if (a.req_deal > 0) {
+      const int per = (int)gridDim.x / a.req_deal;
+      rank = (si % a.req_deal) * per + si / a.req_deal;
+    }
+    m.kvb = rank / a.req_div;
     typedef int i32x4s __attribute__((ext_vector_type(4)));
     typedef int i32x2s __attribute__((ext_vector_type(2)));
     i32x4s rec;

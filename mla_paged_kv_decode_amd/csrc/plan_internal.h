@@ -37,6 +37,8 @@ struct mla_plan_s {
   int32_t max_splits = 0;  // most chunks of one split request
   int32_t one_seg = 0;     // every worker runs exactly the segment of its own index
   int32_t req_div = 0;     // with one_seg: segment i reads request i / req_div (0: no such c)
+  int32_t req_deal = 0;    // X > 0: the workers were dealt to X L2 domains and segment i
+                           // reads request rank(i) / req_div, rank(i) = (i % X) * (n / X) + i / X
   mla_abi::Layout layout{};
   std::vector<uint8_t> host_meta;  // staged work list (kept alive for the async copy)
   uint8_t* workspace = nullptr;

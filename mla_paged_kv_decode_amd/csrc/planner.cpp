@@ -194,7 +194,10 @@ int64_t refine(const std::vector<Piece>& pieces, int32_t workers, int64_t bound,
 // Reorder workers so that the workers serving the hs rows of one request
 // (the row groups that share its latent cache, with all their chunks) get
 // launch positions congruent modulo the number of L2 domains: workgroups are
-// dealt to XCDs round-robin in launch order, so they then share one L2.
+// dealt to XCDs round-robin in launch order, so they then share one L2.  The
+// chunks of one row read the same query rows, which then cross HBM once per
+// domain rather than once per chunk (the L2 merges the misses of the chunks'
+// concurrent loads of Q; L2s of different domains do not share lines).
 // Workers are sorted by the first row they serve and the domains are filled
 // one after the other (domain d takes sorted workers d * per .. d * per + per - 1,
 // per = used / xcds, at positions d, d + xcds, d + 2 xcds, ...), so a request
@@ -325,7 +328,9 @@ int32_t build_plan(const int32_t* kv_indptr, const int32_t* kv_last_page_len, in
   int32_t used = 0;
   for (int32_t w = 0; w < p.num_workers; ++w)
     if (count[w] > 0) remap[w] = used++;
-  if (hs > 1) xcd_colocate(best_pieces, best_owner, p.xcd_count, used, &remap);
+  bool cut = false;
+  for (const Piece& pc : best_pieces) cut = cut || pc.nsplit > 1;
+  if (hs > 1 || cut) xcd_colocate(best_pieces, best_owner, p.xcd_count, used, &remap);
   out->batch = batch;
   out->num_workers = used;
   out->worker_ptr.assign((size_t)used + 1, 0);

@@ -250,6 +250,33 @@ def test_head_split_rows_share_an_xcd(lib):
     assert all(len(x) == 1 for x in xcd_of_request.values())
 
 
+@pytest.mark.parametrize("heads,kvd", [(16, mla.KV_BF16), (128, mla.KV_BF16),
+                                       (128, mla.KV_FP8_E4M3)])
+def test_chunks_of_a_request_share_an_xcd(lib, heads, kvd):
+    # one row per request, cut into 4 token chunks: the chunks read the same
+    # query rows, so they get launch positions congruent mod 8 (one L2), and
+    # the kernels still find each segment's request from its index alone
+    ip, lp = _table([4096] * 64, 64)
+    plan = mla.Plan(ip, lp, heads, 64, kvd, num_cus=256)
+    info = plan.info()
+    assert info["head_split"] == 1
+    seg, wp, _ = _check_plan(plan, [4096] * 64, info["granularity"])
+    assert len(seg) == 256 and info["num_workers"] == 256
+    xcd = {}
+    for w in range(len(wp) - 1):
+        for s_ in seg[wp[w]:wp[w + 1]]:
+            xcd.setdefault(int(s_[0]), set()).add(w % 8)
+    assert len(xcd) == 64 and all(len(x) == 1 for x in xcd.values())
+    # the fast path's closed form: segment i reads request rank(i) / c
+    assert info["one_seg"] == 1 and info["req_div"] == 4 and info["req_deal"] == 8
+    n, X = info["num_workers"], info["req_deal"]
+    rank = [(i % X) * (n // X) + i // X for i in range(n)]
+    assert [int(seg[i, 0]) for i in range(n)] == [r // info["req_div"] for r in rank]
+    # without placement: launch order is request order
+    flat = mla.Plan(ip, lp, heads, 64, kvd, num_cus=256, l2_domains=1).info()
+    assert flat["req_div"] == 4 and flat["req_deal"] == 0
+
+
 @pytest.mark.parametrize("heads,q,kvd", [(128, 2, mla.KV_BF16), (64, 1, mla.KV_FP8_E4M3),
                                          (16, 4, mla.KV_INT8)])
 def test_rows_of_a_request_share_an_xcd_with_token_splits(lib, heads, q, kvd):
@@ -383,7 +410,7 @@ int main(void) {
     printf("plan failed: %s %s\n", mla_status_string(st), mla_last_error());
     return 1;
   }
-  int32_t info[15];
+  int32_t info[16];
   if (mla_decode_plan_info(plan, info) != MLA_OK) return 2;
   int32_t* seg = (int32_t*)malloc(sizeof(int32_t) * 4 * (size_t)(info[5] > 0 ? info[5] : 1));
   int32_t* wp = (int32_t*)malloc(sizeof(int32_t) * (size_t)(info[4] + 1));

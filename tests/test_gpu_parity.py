@@ -475,14 +475,18 @@ def test_many_chunk_merge_reruns_bit_identical(heads, lengths):
     assert info["num_partials"] // info["num_split_requests"] > 4
 
 
-@pytest.mark.parametrize("heads,hs", [(16, 0), (64, 0), (128, 0), (128, 2)])
-def test_one_segment_fast_path_matches_general_path(heads, hs):
+@pytest.mark.parametrize("heads,hs,l2", [(16, 0, 1), (64, 0, 1), (128, 0, 1), (128, 2, 1),
+                                         (16, 0, 0), (128, 0, 0), (128, 2, 0)])
+def test_one_segment_fast_path_matches_general_path(heads, hs, l2):
     # The same chunks, run one per workgroup (the workgroup's segment is its own
     # index and its request is computed from it, so the segment record and the
     # page-table loads go out together: plan info one_seg = 1, req_div > 0) and
     # two per workgroup (segment range from worker_ptr, request from the
     # record): the partials and their merge are the same, so the results are
-    # bit-identical, and both match the oracle on every row.
+    # bit-identical, and both match the oracle on every row.  With l2 = 0 the
+    # workgroups are dealt to the 8 L2 domains (the chunks of a request on one
+    # of them), and the request follows from the segment's rank before the
+    # dealing (plan info req_deal = 8).
     import mla_paged_kv_decode_amd as mla
     B = 64
     splits = 4 // max(hs, 1)  # 256 segments: one per workgroup of a 256-CU device
@@ -493,11 +497,12 @@ def test_one_segment_fast_path_matches_general_path(heads, hs):
         ws = torch.empty(mla.workspace_bytes(B, heads, head_split=hs), dtype=torch.uint8,
                          device="cuda")
         plan = mla.Plan(inp.kv_indptr, inp.kv_last_page_len, heads, 64, inp.kv_dtype, ws,
-                        force_splits=splits, max_workers=mw, head_split=hs, l2_domains=1)
+                        force_splits=splits, max_workers=mw, head_split=hs, l2_domains=l2)
         info = plan.info()
-        print("case heads=%d head_split=%d max_workers=%d workers=%d segments=%d one_seg=%d "
-              "req_div=%d" % (heads, info["head_split"], mw, info["num_workers"],
-                              info["num_segments"], info["one_seg"], info["req_div"]), flush=True)
+        print("case heads=%d head_split=%d l2_domains=%d max_workers=%d workers=%d segments=%d "
+              "one_seg=%d req_div=%d req_deal=%d" % (
+                  heads, info["head_split"], l2, mw, info["num_workers"], info["num_segments"],
+                  info["one_seg"], info["req_div"], info["req_deal"]), flush=True)
         o = torch.empty((B, heads, 512), dtype=torch.bfloat16, device="cuda")
         lse = torch.empty((B, heads), dtype=torch.float32, device="cuda")
         plan.run(t["q_nope"], t["q_pe"], t["ckv"], t["kpe"], t["kv_scale"], t["kv_indptr"],
@@ -507,6 +512,7 @@ def test_one_segment_fast_path_matches_general_path(heads, hs):
     rows = res[0][2]["head_split"]
     assert res[0][2]["num_workers"] == res[0][2]["num_segments"] == splits * B * rows
     assert res[0][2]["one_seg"] == 1 and res[0][2]["req_div"] == splits * rows
+    assert res[0][2]["req_deal"] == (8 if l2 == 0 else 0)
     assert res[1][2]["num_workers"] < res[1][2]["num_segments"] == splits * B * rows
     assert res[1][2]["one_seg"] == 0 and res[1][2]["req_div"] == 0
     assert torch.equal(res[0][0].view(torch.int16), res[1][0].view(torch.int16))
