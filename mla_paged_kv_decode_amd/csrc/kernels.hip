@@ -1446,6 +1446,9 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     // segments, they were spilled and reloaded at every segment)
     int lane_s = lane, tid_s = tid;
     if constexpr (KVT == 1 || KVT == 2) asm volatile("" : "+v"(lane_s), "+v"(tid_s));
+    int lane_e = lane_s;
+    if constexpr (KVT == 3 || KVT == 4) asm volatile("" : "+v"(lane_e));
+    const int l32_s = lane_e & 31, g_s = lane_e >> 5;
     const SegMeta sm = load_seg(a, si);
     const int b = sm.b, t0 = sm.t0, send = sm.send, slot = sm.slot;
     const int kvb = sm.kvb, pbeg = sm.pbeg;
@@ -1638,8 +1641,8 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     // Q^T of heads 32 w .. 32 w + 31: k-step s holds dims 16 s + 8 g .. + 7.
     constexpr int QR = S::kQRegSteps;
     bf16x8 qf[QR];
-    uint8_t* const qlds = smem + S::kQOffset + wave * (36 - QR) * 1024 + lane * 16;
-    const int qhead = 32 * wave + l32;
+    uint8_t* const qlds = smem + S::kQOffset + wave * (36 - QR) * 1024 + lane_e * 16;
+    const int qhead = 32 * wave + l32_s;
     const bf16x8* qn = reinterpret_cast<const bf16x8*>(a.q_nope + ((size_t)b * H + qhead) * 512);
     const bf16x8* qp = reinterpret_cast<const bf16x8*>(a.q_pe + ((size_t)b * H + qhead) * 64);
     if constexpr (kC16) {
@@ -1648,7 +1651,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       // the whole prologue
 #pragma unroll
       for (int s = 0; s < 36; ++s)
-        qf[s] = load16_untracked(s < 32 ? qn + 2 * s + g : qp + 2 * (s - 32) + g);
+        qf[s] = load16_untracked(s < 32 ? qn + 2 * s + g_s : qp + 2 * (s - 32) + g_s);
       // (tiles past the last one load the last tile again, into a ring slot
       // that is not read: every wait below is then the same constant)
       if (ntiles > 0) {
@@ -1666,7 +1669,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
       }
 #pragma unroll
       for (int s = 0; s < 36; ++s) {
-        const bf16x8 v = s < 32 ? qn[2 * s + g] : qp[2 * (s - 32) + g];
+        const bf16x8 v = s < 32 ? qn[2 * s + g_s] : qp[2 * (s - 32) + g_s];
         if (s < QR)
           qf[s < QR ? s : 0] = v;
         else
@@ -2143,15 +2146,15 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     const bool empty = !(l_tot > 0.f);
     const float lse_v = empty ? -INFINITY : (m_ref + __log2f(l_tot)) * kLn2;
-    if (lane < 32) stat[32 * wave + lane] = empty ? 0.f : 1.f / l_tot;
+    if (lane_e < 32) stat[32 * wave + lane_e] = empty ? 0.f : 1.f / l_tot;
     lds_barrier();
     float inv[4];
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) inv[hb] = stat[32 * hb + l32];
+    for (int hb = 0; hb < 4; ++hb) inv[hb] = stat[32 * hb + l32_s];
     if (slot < 0) {
 #pragma unroll
       for (int hb = 0; hb < 4; ++hb) {
-        uint16_t* op = a.o + ((size_t)b * H + 32 * hb + l32) * 512 + 128 * wave + 4 * g;
+        uint16_t* op = a.o + ((size_t)b * H + 32 * hb + l32_s) * 512 + 128 * wave + 4 * g_s;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           const f32x16 x = agpr_read16(acc[cb][hb]);
@@ -2164,7 +2167,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
           }
         }
       }
-      if (lane < 32) a.lse[(size_t)b * H + 32 * wave + lane] = lse_v;
+      if (lane_e < 32) a.lse[(size_t)b * H + 32 * wave + lane_e] = lse_v;
     } else {
       // Partial of a chunk, merged by the combine kernel after this launch:
       // fp16 with one scale per (head, 128-column block) (scale_exp; half the
@@ -2188,7 +2191,7 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
         // mx < 2^e (frexp); the scale 2^(e - 15) maps mx into [2^14, 2^15)
         const int ex = scale_exp(mx);
         const float mult = __builtin_amdgcn_ldexpf(inv[hb], -ex);
-        uint16_t* prow = po + (32 * hb + l32) * 512 + 128 * wave + 4 * g;
+        uint16_t* prow = po + (32 * hb + l32_s) * 512 + 128 * wave + 4 * g_s;
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -2198,11 +2201,11 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
             for (int i = 0; i < 4; ++i) v[i] = (_Float16)(x[cb][4 * q + i] * mult);
             *reinterpret_cast<f16x4*>(prow + 32 * cb + 8 * q) = v;
           }
-        if (g == 0)
-          a.part_scale[((size_t)slot * H + 32 * hb + l32) * 4 + wave] =
+        if (g_s == 0)
+          a.part_scale[((size_t)slot * H + 32 * hb + l32_s) * 4 + wave] =
               __builtin_amdgcn_ldexpf(1.f, ex);
       }
-      if (lane < 32) a.part_lse[(size_t)slot * H + 32 * wave + lane] = lse_v;
+      if (lane_e < 32) a.part_lse[(size_t)slot * H + 32 * wave + lane_e] = lse_v;
     }
     lds_barrier();  // stat read by every wave before the next segment rewrites it
   }
