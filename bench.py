@@ -72,8 +72,8 @@ DTYPE_NAMES = {0: "bf16", 1: "bf16", 2: "bf16", 3: "bf16", 4: "bf16", 5: "f16"}
 def kernel_name(info: dict) -> str:
     """The decode kernel a plan launches (as rocprofv3 names it)."""
     w, k, q = info["kernel_heads"], info["kv_dtype"], info["qo_len"]
-    if w == 16:
-        return "mla_decode_stream_kernel<1, %d, 2>" % k
+    if w == 16:  # <head blocks, layout, groups staged per wave, waves>
+        return "mla_decode_stream_kernel<1, %d, %s>" % (k, "1, 8" if k == 2 else "2, 4")
     if w == 32:
         return "mla_decode_ring_kernel<2, 1, 2, 1, 4>"
     causal = "true" if q > 1 else "false"

@@ -768,16 +768,18 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
 // record with fp8 / int8 ckv and bf16 kpe (KVT 3 / 4).  At these head
 // counts the work is memory bound, so what matters is the number of bytes in
 // flight per CU and keeping the waves out of each other's way:
-//   * 4 waves split a segment's 16-token groups round-robin (wave w takes
-//     groups w, w + 4, ...); each wave runs its own pipeline with no workgroup
-//     barrier until the end of the segment;
+//   * NW waves (4, or 8 for int8) split a segment's 16-token groups
+//     round-robin (wave w takes groups w, w + NW, ...); each wave runs its own
+//     pipeline with no workgroup barrier until the end of the segment;
 //   * a group is fetched with coalesced 16-byte loads per lane into registers,
-//     two groups ahead, so the vector register file (not LDS) holds the data
-//     in flight;
+//     NB groups ahead (2 with 4 waves, 1 with 8), so the vector register file
+//     (not LDS) holds the data in flight;
 //   * the group is then written to a wave-private 18 KiB LDS buffer in the
 //     swizzled bf16 layout of the LDS ring (8-bit codes are converted exactly
 //     to bf16 on the way) and consumed by the QK and PV MFMAs;
-//   * Q^T (HB x 16 heads x 576) sits in LDS once per segment, [chunk][head].
+//   * Q^T (HB x 16 heads x 576) sits in LDS once per segment, [chunk][head]
+//     (in registers with the fp8 580-byte record; its kpe part in registers
+//     with eight waves).
 // 8-bit caches (FlashMLA Ampere v2, "What is added": FP8 e4m3 or INT8 with one
 // scale per token, dequantised in the kernel): codes become bf16 exactly; the
 // token's scale multiplies its score (after QK, in fp32) and its probability
@@ -786,9 +788,9 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
 // only), the scale multiplies the accumulator after the 512 ckv dimensions
 // and before the 64 kpe dimensions are added.
 // ---------------------------------------------------------------------------
-template <int HB, int KVT, int NB>
+template <int HB, int KVT, int NB, int NW>
 struct StreamShape {
-  static constexpr int kWaves = 4;
+  static constexpr int kWaves = NW;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kHeads = 16 * HB;
   static constexpr int kBufBytes = 18 * 1024;       // one 16-row bf16 group per wave
@@ -796,15 +798,28 @@ struct StreamShape {
   // Q^T: in registers with the 580-byte 8-bit record (its group registers are
   // half the size); in LDS, [block][chunk][head] x 16 B, otherwise (with the
   // 644-byte record, registers for Q^T cost spills at every segment start)
-  static constexpr bool kQRegs = KVT == 1 || KVT == 2;
+  static constexpr bool kQRegs = (KVT == 1 || KVT == 2) && NW == 4;
   // with Q^T out of LDS, each wave has two group buffers and computes two
   // groups at once (see the kernel)
   static constexpr bool kPipe = kQRegs;
-  static constexpr int kQBytes = kQRegs ? 0 : HB * 72 * 16 * 16;
+  // Eight waves (two per SIMD, 256 registers each; 580-byte 8-bit record,
+  // one group staged per wave): eight group buffers leave LDS room for the
+  // Q^T of the 512 ckv dimensions only; the 64 kpe dimensions (QK k-steps 16
+  // and 17) stay in registers.
+  static constexpr bool kQKpeRegs = NW == 8;
+  static constexpr int kQChunks = kQKpeRegs ? 64 : 72;  // 8-dimension chunks of Q^T in LDS
+  static constexpr int kQBytes = kQRegs ? 0 : HB * kQChunks * 16 * 16;
   static constexpr int kQOffset = kWaves * kBufBytes * (kPipe ? 2 : 1);
-  static constexpr int kMergeBytes = merge_bytes<16, 1, kWaves>();  // one head block at a time
-  static constexpr int kLdsBytes = kQOffset + kQBytes > kMergeBytes ? kQOffset + kQBytes
-                                                                    : kMergeBytes;
+  // end of a segment: eight waves first fold into four (waves 4..7 hand
+  // their O^T, reference max and row sums to waves 0..3, lane by lane:
+  // [wave & 3][32 column blocks][64 lanes] x 16 B, then 64 maxima, 64 sums),
+  // then the four-wave merge (one head block at a time)
+  static constexpr int kFoldFloats = 32 * 64 * 4 + 2 * 64;
+  static constexpr int kFoldBytes = NW == 8 ? 4 * kFoldFloats * 4 : 0;
+  static constexpr int kMergeBytes = merge_bytes<16, 1, NW == 8 ? 4 : NW>();
+  static constexpr int kEndBytes = kFoldBytes > kMergeBytes ? kFoldBytes : kMergeBytes;
+  static constexpr int kLdsBytes = kQOffset + kQBytes > kEndBytes ? kQOffset + kQBytes
+                                                                  : kEndBytes;
   // 16-byte loads per lane per group: bf16 18; 8-bit ckv 8 + kpe 1 (8-bit) or 2 (bf16)
   static constexpr int kLoads = kCache16 ? 18 : (KVT == 3 || KVT == 4 ? 10 : 9);
   static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
@@ -836,9 +851,10 @@ __device__ __forceinline__ u32x4 codes_to_bf16(unsigned lo, unsigned hi) {
   return r;
 }
 
-template <int HB, int KVT, int NB>
-__global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs a) {
-  using S = StreamShape<HB, KVT, NB>;
+template <int HB, int KVT, int NB, int NW>
+__global__ void __launch_bounds__(64 * NW) mla_decode_stream_kernel(const DecodeArgs a) {
+  using S = StreamShape<HB, KVT, NB, NW>;
+  static_assert(NW == 4 || (NW == 8 && HB == 1 && NB == 1), "eight waves: one head block, one group each");
   constexpr int H = S::kHeads;
   constexpr bool kC16 = S::kCache16;
   constexpr bool kF16 = KVT == 5;  // fp16 q, cache, P and O
@@ -910,9 +926,11 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     // k-step s (head 16 hb + (lane & 15), dims 32 s + 8 (lane >> 4) .. + 7),
     // loaded before the groups; this saves each 16-token group 18 KiB of LDS
     // reads.
-    constexpr int kQItems = S::kQRegs ? 1 : (HB * 72 * 16 + S::kThreads - 1) / S::kThreads;
+    constexpr int QC = S::kQChunks;
+    constexpr int kQItems = S::kQRegs ? 1 : (HB * QC * 16 + S::kThreads - 1) / S::kThreads;
     u32x4 qv[kQItems];
     bf16x8 qreg[S::kQRegs ? HB : 1][S::kQRegs ? 18 : 1];
+    bf16x8 qkpe[S::kQKpeRegs ? HB : 1][2];  // eight waves: k-steps 16, 17 (kpe)
     if constexpr (S::kQRegs) {
 #pragma unroll
       for (int hb = 0; hb < HB; ++hb) {
@@ -928,11 +946,19 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     } else {
 #pragma unroll
       for (int k = 0; k < kQItems; ++k) {
-        const int x = min(tid + k * S::kThreads, HB * 72 * 16 - 1);
-        const int hb = x / (72 * 16);
-        const int c = (x >> 4) % 72, h = hb * 16 + (x & 15);
+        const int x = min(tid + k * S::kThreads, HB * QC * 16 - 1);
+        const int hb = x / (QC * 16);
+        const int c = (x >> 4) % QC, h = hb * 16 + (x & 15);
         qv[k] = c < 64 ? *reinterpret_cast<const u32x4*>(a.q_nope + ((size_t)b * H + h) * 512 + c * 8)
                        : *reinterpret_cast<const u32x4*>(a.q_pe + ((size_t)b * H + h) * 64 + (c - 64) * 8);
+      }
+      if constexpr (S::kQKpeRegs) {
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+          for (int s = 16; s < 18; ++s)  // chunks 4 s + (lane >> 4) = 64 .. 71: kpe
+            qkpe[hb][s - 16] = *reinterpret_cast<const bf16x8*>(
+                a.q_pe + ((size_t)b * H + hb * 16 + (lane & 15)) * 64 + (4 * s + (lane >> 4) - 64) * 8);
       }
     }
 
@@ -1008,7 +1034,7 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
       uint8_t* qw = qlds + t * 16;  // item t + k kThreads at qw + k kThreads 16
 #pragma unroll
       for (int k = 0; k < kQItems; ++k)
-        if ((k + 1) * S::kThreads <= HB * 72 * 16 || t + k * S::kThreads < HB * 72 * 16)
+        if ((k + 1) * S::kThreads <= HB * QC * 16 || t + k * S::kThreads < HB * QC * 16)
           *reinterpret_cast<u32x4*>(qw + k * S::kThreads * 16) = qv[k];
       lds_barrier();
     }
@@ -1090,9 +1116,11 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
           for (int u = 0; u < 6; ++u) {
             if constexpr (S::kQRegs)
               qf[u] = qreg[hb][s0 + u];
+            else if (S::kQKpeRegs && s0 + u >= 16)
+              qf[u] = qkpe[hb][(s0 + u) & 1];
             else
               qf[u] = *reinterpret_cast<const LDS_AS bf16x8*>(
-                  (const LDS_AS uint8_t*)(qbase + (hb * 72 + (s0 + u) * 4) * 256));
+                  (const LDS_AS uint8_t*)(qbase + (hb * QC + (s0 + u) * 4) * 256));
           }
 #pragma unroll
           for (int u = 0; u < 6; ++u) {
@@ -1204,10 +1232,45 @@ __global__ void __launch_bounds__(256) mla_decode_stream_kernel(const DecodeArgs
     }
 
     lds_barrier();  // every wave is done with its group buffer (the merge area overlaps)
+    if constexpr (NW == 8) {
+      // fold waves 4..7 into waves 0..3: (m, l, O^T) of the same lane (same
+      // head, same columns) combine as M = max(m, m'), O = 2^(m - M) O +
+      // 2^(m' - M) O', l likewise, in a fixed order
+      float* fold = reinterpret_cast<float*>(smem) + (wave & 3) * S::kFoldFloats;
+      if (wave >= 4) {
 #pragma unroll
-    for (int hb = 0; hb < HB; ++hb)
-      write_head_block<H, 1, TS, kF16>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave, lane,
-                                 smem);
+        for (int cb = 0; cb < 32; ++cb)
+          *reinterpret_cast<f32x4*>(fold + (cb * 64 + lane) * 4) = acc[0][cb];
+        fold[32 * 256 + lane] = m_ref[0];
+        fold[32 * 256 + 64 + lane] = l_run[0];
+      }
+      lds_barrier();
+      if (wave < 4) {
+        const float mp = fold[32 * 256 + lane], lp = fold[32 * 256 + 64 + lane];
+        const float M = fmaxf(m_ref[0], mp);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        const float wm = __builtin_amdgcn_exp2f(m_ref[0] - Mu);
+        const float wp = __builtin_amdgcn_exp2f(mp - Mu);
+#pragma unroll
+        for (int cb = 0; cb < 32; ++cb)
+          acc[0][cb] = acc[0][cb] * wm + *reinterpret_cast<const f32x4*>(fold + (cb * 64 + lane) * 4) * wp;
+        l_run[0] = l_run[0] * wm + lp * wp;
+        m_ref[0] = M;
+      }
+      lds_barrier();  // fold area read before the merge overwrites it
+      if (wave < 4) {
+        write_head_block<H, 1, 4, kF16>(a, acc[0], m_ref[0], l_run[0], b, slot, 0, 0, wave, lane,
+                                        smem);
+      } else {  // the merge's two barriers
+        lds_barrier();
+        lds_barrier();
+      }
+    } else {
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb)
+        write_head_block<H, 1, TS, kF16>(a, acc[hb], m_ref[hb], l_run[hb], b, slot, hb, 0, wave,
+                                         lane, smem);
+    }
   }
 }
 
@@ -2976,26 +3039,26 @@ static DecodeConfig config_of() {
   return DecodeConfig{S::kWaves, S::kTile, S::kLdsBytes};
 }
 
-template <int HB, int KVT, int NB>
+template <int HB, int KVT, int NB, int NW>
 static hipError_t launch_stream_cfg(const DecodeArgs& a, int grid, hipStream_t stream,
                                     const LaunchEvents& ev) {
-  using S = StreamShape<HB, KVT, NB>;
-  hipExtLaunchKernelGGL((mla_decode_stream_kernel<HB, KVT, NB>), dim3(grid), dim3(S::kThreads), 0, stream, ev.start, ev.stop, 0, a);
+  using S = StreamShape<HB, KVT, NB, NW>;
+  hipExtLaunchKernelGGL((mla_decode_stream_kernel<HB, KVT, NB, NW>), dim3(grid), dim3(S::kThreads), 0, stream, ev.start, ev.stop, 0, a);
   return hipGetLastError();
 }
 
-template <int HB, int KVT, int NB>
+template <int HB, int KVT, int NB, int NW>
 static DecodeConfig stream_config_of() {
-  using S = StreamShape<HB, KVT, NB>;
+  using S = StreamShape<HB, KVT, NB, NW>;
   return DecodeConfig{S::kWaves, 16, S::kLdsBytes};
 }
 
-template <int HB, int KVT, int NB>
+template <int HB, int KVT, int NB, int NW>
 static int stream_occupancy_of() {
-  using S = StreamShape<HB, KVT, NB>;
+  using S = StreamShape<HB, KVT, NB, NW>;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, reinterpret_cast<const void*>(&mla_decode_stream_kernel<HB, KVT, NB>), S::kThreads,
+          &n, reinterpret_cast<const void*>(&mla_decode_stream_kernel<HB, KVT, NB, NW>), S::kThreads,
           0) != hipSuccess ||
       n < 1)
     n = (160 * 1024) / S::kLdsBytes;
@@ -3048,10 +3111,11 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   } while (0)
   // ring-kernel shapes: <16-head blocks, blocks per wave, token-split waves,
   // row groups per wave per tile, ring stages>; stream-kernel shapes: <head
-  // blocks, cache layout, groups staged in registers per wave>
+  // blocks, cache layout, groups staged in registers per wave, waves> (int8:
+  // eight waves, whose second wave per SIMD hides more of the conversion)
   if (kv_dtype == 0) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 0, 2);
+      case 16: MLA_STREAM(1, 0, 2, 4);
       case 32: MLA_RING(2, 1, 2, 1, 4);
       case 64: MLA_PAIR(0);
       case 128: MLA_WIDE(0);
@@ -3060,35 +3124,35 @@ static int dispatch(int heads, int kv_dtype, int op, DecodeConfig* cfg, const De
   }
   if (kv_dtype == 1) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 1, 2);
+      case 16: MLA_STREAM(1, 1, 2, 4);
       case 128: MLA_WIDE(1);
       default: return 0;
     }
   }
   if (kv_dtype == 2) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 2, 2);
+      case 16: MLA_STREAM(1, 2, 1, 8);
       case 128: MLA_WIDE(2);
       default: return 0;
     }
   }
   if (kv_dtype == 3) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 3, 2);
+      case 16: MLA_STREAM(1, 3, 2, 4);
       case 128: MLA_WIDE(3);
       default: return 0;
     }
   }
   if (kv_dtype == 4) {
     switch (heads) {
-      case 16: MLA_STREAM(1, 4, 2);
+      case 16: MLA_STREAM(1, 4, 2, 4);
       case 128: MLA_WIDE(4);
       default: return 0;
     }
   }
   if (kv_dtype == 5) {  // fp16: 32- and 64-wide requests run as 16-wide rows
     switch (heads) {
-      case 16: MLA_STREAM(1, 5, 2);
+      case 16: MLA_STREAM(1, 5, 2, 4);
       case 64: MLA_PAIR(5);
       case 128: MLA_WIDE(5);
       default: return 0;
