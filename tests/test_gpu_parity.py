@@ -54,13 +54,13 @@ def test_head_split_matches_oracle(heads, hs):
 @pytest.mark.parametrize("heads,kvd", [(16, synth.KV_BF16), (32, synth.KV_BF16),
                                        (64, synth.KV_BF16), (64, synth.KV_FP16),
                                        (128, synth.KV_BF16), (16, synth.KV_FP8_E4M3),
-                                       (128, synth.KV_INT8)])
+                                       (16, synth.KV_INT8), (128, synth.KV_INT8)])
 @pytest.mark.parametrize("splits", [0, 3])
 def test_many_segments_per_workgroup(heads, kvd, splits):
     # few workgroups, so each runs a long list of segments: empty requests,
     # one- and two-tile ones, tile-aligned ends, chunks of split requests
-    # (partials) and whole requests in one list (the 64-head kernel fetches
-    # the next segment's first tiles while it finishes the current one)
+    # (partials) and whole requests in one list (16-head int8: eight waves,
+    # folded into four at the end of every segment)
     import mla_paged_kv_decode_amd as mla
     rng = np.random.default_rng(900 + heads + splits)
     lengths = [0, 1, 31, 32, 33, 64, 65, 96, 0, 17, 700, 1500, 2, 128, 129, 0, 250, 1000]
