@@ -778,8 +778,8 @@ __global__ void __launch_bounds__(64 * (HG / HB) * TS)
 //     swizzled bf16 layout of the LDS ring (8-bit codes are converted exactly
 //     to bf16 on the way) and consumed by the QK and PV MFMAs;
 //   * Q^T (HB x 16 heads x 576) sits in LDS once per segment, [chunk][head]
-//     (in registers with the fp8 580-byte record; its kpe part in registers
-//     with eight waves).
+//     (in registers with the fp8 580-byte and int8 644-byte records; its kpe
+//     part in registers with eight waves).
 // 8-bit caches (FlashMLA Ampere v2, "What is added": FP8 e4m3 or INT8 with one
 // scale per token, dequantised in the kernel): codes become bf16 exactly; the
 // token's scale multiplies its score (after QK, in fp32) and its probability
@@ -795,10 +795,10 @@ struct StreamShape {
   static constexpr int kHeads = 16 * HB;
   static constexpr int kBufBytes = 18 * 1024;       // one 16-row bf16 group per wave
   static constexpr bool kCache16 = KVT == 0 || KVT == 5;  // bf16 or fp16 cache
-  // Q^T: in registers with the 580-byte 8-bit record (its group registers are
-  // half the size); in LDS, [block][chunk][head] x 16 B, otherwise (with the
-  // 644-byte record, registers for Q^T cost spills at every segment start)
-  static constexpr bool kQRegs = (KVT == 1 || KVT == 2) && NW == 4;
+  // Q^T: in registers (four waves) with the fp8 580-byte record and the int8
+  // 644-byte one; in LDS, [block][chunk][head] x 16 B, otherwise (measured:
+  // the fp8 644-byte record runs faster with Q^T in LDS and one buffer)
+  static constexpr bool kQRegs = (KVT == 1 || KVT == 2 || KVT == 4) && NW == 4;
   // with Q^T out of LDS, each wave has two group buffers and computes two
   // groups at once (see the kernel)
   static constexpr bool kPipe = kQRegs;
