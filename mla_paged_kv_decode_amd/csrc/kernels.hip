@@ -1509,6 +1509,10 @@ __global__ void __launch_bounds__(256) mla_decode_wide_kernel(const DecodeArgs a
     // segments, they were spilled and reloaded at every segment)
     int lane_s = lane, tid_s = tid;
     if constexpr (KVT == 1 || KVT == 2) asm volatile("" : "+v"(lane_s), "+v"(tid_s));
+    // (every 8-bit record: the Q^T loads and the epilogue's row, column and
+    // lane-half take their lane indices from a per-segment copy too; the
+    // 644-byte record gets one of its own for these two places only, since a
+    // copy in its tile loop costs spills there)
     int lane_e = lane_s;
     if constexpr (KVT == 3 || KVT == 4) asm volatile("" : "+v"(lane_e));
     const int l32_s = lane_e & 31, g_s = lane_e >> 5;
